@@ -1,0 +1,114 @@
+"""The oracle's pins fail on plausible mistakes (CPU).
+
+Each test plants one mistake in a copy of an oracle function, swaps it into a
+pin test's namespace and checks that the pin then fails. This shows that a
+dropped term, a wrong sign, a wrong pairing or a wrong visibility rule in the
+oracle would not go unnoticed.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.rope as rope_mod
+import tests.test_oracle_attention as t_attn
+import tests.test_oracle_entropy as t_ent
+import tests.test_oracle_rope as t_rope
+import tests.test_oracle_select_commit as t_sel
+from oracle import attention as attn_mod
+from oracle import select as select_mod
+from oracle.entropy import vocab_entropy_argmax as _orig_entropy
+
+
+def _rope_sign_flipped(x, positions, theta):
+    x = np.asarray(x, np.float64)
+    half = x.shape[-1] // 2
+    ang = np.asarray(positions, np.float64)[..., None] * rope_mod.rope_frequencies(x.shape[-1], theta)
+    c, s = np.cos(ang), np.sin(ang)
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c + hi * s, hi * c - lo * s], axis=-1)
+
+
+def _rope_interleaved(x, positions, theta):
+    x = np.asarray(x, np.float64)
+    D = x.shape[-1]
+    ang = np.asarray(positions, np.float64)[..., None] * rope_mod.rope_frequencies(D, theta)
+    c, s = np.cos(ang), np.sin(ang)
+    ev, od = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = ev * c - od * s
+    y[..., 1::2] = od * c + ev * s
+    return y
+
+
+def test_rope_sign_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(t_rope, "rope_rotate", _rope_sign_flipped)
+    with pytest.raises(AssertionError):
+        t_rope.test_d2_is_complex_multiplication()
+
+
+def test_rope_pairing_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(t_rope, "rope_rotate", _rope_interleaved)
+    with pytest.raises(AssertionError):
+        t_rope.test_rotate_half_pairing_closed_form()
+
+
+def test_entropy_dropped_term_is_caught(monkeypatch):
+    def no_t_term(logits):
+        z = np.asarray(logits, np.float64)
+        m = z.max(-1, keepdims=True)
+        return np.log(np.exp(z - m).sum(-1)), np.argmax(z, -1)
+    monkeypatch.setattr(t_ent, "vocab_entropy_argmax", no_t_term)
+    with pytest.raises(AssertionError):
+        t_ent.test_two_level_closed_form(512, 1, 8.0, 0.0)
+
+
+def test_entropy_last_index_argmax_is_caught(monkeypatch):
+    def last_argmax(logits):
+        H, _ = _orig_entropy(logits)
+        z = np.asarray(logits, np.float64)
+        return H, z.shape[-1] - 1 - np.argmax(z[..., ::-1], -1)
+    monkeypatch.setattr(t_ent, "vocab_entropy_argmax", last_argmax)
+    with pytest.raises(AssertionError):
+        t_ent.test_argmax_lowest_index_on_ties()
+
+
+def test_visibility_mistake_is_caught(monkeypatch):
+    def masks_see_only_earlier(filled):
+        f = np.asarray(filled, bool)
+        W = f.size
+        return np.tril(np.ones((W, W), bool))          # plain slot-order causal mask
+    monkeypatch.setattr(attn_mod, "visible_mask", masks_see_only_earlier)
+    with pytest.raises(AssertionError):
+        t_attn.test_form_r_equals_form_m_every_pattern_tiny_shape()
+
+
+def test_missing_scale_is_caught(monkeypatch):
+    orig = attn_mod.window_attention_reordered
+
+    def unscaled(q, k, v, kc, vc, scale=None):
+        return orig(q, k, v, kc, vc, scale=1.0)
+    monkeypatch.setattr(t_attn, "window_attention_reordered", unscaled)
+    with pytest.raises(AssertionError):
+        t_attn.test_all_filled_window_is_ordinary_causal_attention(8, 8)
+
+
+def test_penalty_sign_mistake_is_caught(monkeypatch):
+    orig = select_mod.select_slots
+
+    def minus_penalty(entropy, filled, lam, tau, min_fill=1, tie_eps=1e-4):
+        return orig(entropy, filled, -lam, tau, min_fill, tie_eps)
+    monkeypatch.setattr(t_sel, "select_slots", minus_penalty)
+    case = next(c for c in t_sel.CASES if c["name"] == "distance_penalty_orders_slots")
+    with pytest.raises(AssertionError):
+        t_sel.test_golden_case(case)
+
+
+def test_page_offset_mistake_is_caught(monkeypatch):
+    import oracle.commit as commit_mod
+
+    def wrong_slot(row, position, page_size):
+        return int(row[position % len(row)]) * page_size + position % page_size
+    monkeypatch.setattr(commit_mod, "cache_slot_of", wrong_slot)
+    case = next(c for c in t_sel.CASES if c["name"] == "run_then_gap_commit_across_pages")
+    with pytest.raises(AssertionError):
+        t_sel.test_golden_case(case)

@@ -1,0 +1,579 @@
+// Causal GQA window attention over [paged KV prefix ; reordered window].
+//
+// hyper.ai summary of WeDLM, "Method": one causal forward pass over the
+// reordered window, conditioned on the persistent KV cache; sai.science review,
+// "Strengths": the causal mask is the plain one. FlashAttention's online softmax
+// and PagedAttention's block table (mlsanity.com page, "Builds on") are the
+// prior art; this kernel is written for CDNA4 from scratch.
+//
+// bf16 path (D = 128, page P = 16). One workgroup per (layer, sequence, kv
+// head, key-range split); each of its wavefronts owns one 16-row tile of the
+// group's M = W*g query rows (physical row p, query head h of the group). The
+// group's key pages stream through a double-buffered LDS ring, two pages
+// (32 keys, 16 KB of K and V) per stage: every thread loads a few 16-byte
+// vectors of the next page pair into registers while the waves compute the
+// current one from LDS, then writes them to the other stage (one barrier per
+// page pair). Each key byte is read from HBM once per workgroup.
+//
+//   S^T (16 keys x 16 rows)  = K (16 x 128) . Q^T        v_mfma_f32_16x16x32_bf16
+//   O^T (16 dims x 16 rows) += V^T (16 x 32 keys) . P^T  v_mfma_f32_16x16x32_bf16
+//
+// Cache page layouts make every access a contiguous, conflict-free vector:
+//   K page [Hkv][D/8][P][8]: the A operand of k-step s for lane l is the 16 B at
+//     s*1024 + 16 l (a wave reads 1 KB contiguous);
+//   V page [Hkv][D][P]: lane l reads 8 B holding 4 consecutive keys of one
+//     dimension (a wave reads 512 B contiguous).
+// S^T's accumulator layout (a lane holds 4 keys of one row) is the B operand
+// layout P^T needs, so probabilities feed the second MFMA with no shuffle: the
+// 8 k-values of a lane are keys 4q..4q+3 of the first page and the same of the
+// second page, and V^T is read in the same key order. Row max and row sum need
+// two cross-lane steps (the 4 lanes holding one row).
+//
+// When there are too few groups to fill the GPU, a group's pages are split
+// across workgroups; each split writes (max, sum, unnormalised O) and a combine
+// kernel merges them. The window's own keys are processed by the last split
+// with the causal rule (row p sees window rows 0..p), staged into LDS in the
+// same page layout.
+#include "common.hpp"
+
+namespace wedlm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 16;
+constexpr int kMaxRows = 256;                    // M = W*g rows: at most 16 wavefronts
+constexpr int kChunkVecs = 4 * 256;              // 16-byte vectors per page pair (K0 K1 V0 V1)
+constexpr int kPartElems = 2048;                 // bf16 elements of one 4 KB page part
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+  const uint16_t* q;   // [nl][B][W][Hq][D] physical order, rotated
+  const uint16_t* k;   // [nl][B][W][Hkv][D]
+  const uint16_t* v;
+  const uint16_t* kc;  // [nl][num_pages][Hkv][D/8][P][8]
+  const uint16_t* vc;  // [nl][num_pages][Hkv][D][P]
+  const int32_t* block_table;
+  const int32_t* prefix_len;
+  uint16_t* out;       // [nl][B][W][Hq][D]
+  float* ws_o;         // [groups][splits][M][D]
+  float* ws_ml;        // [groups][splits][M][2]
+  int B, W, Hq, Hkv, g, M;
+  int num_pages, max_pages, max_prefix_len, n_splits;
+  long long cache_layer_stride;  // elements per layer of one cache
+  float scale_log2;
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ bf16x8 pack_p(const f32x4& a, const f32x4& b) {
+  const u32x4 u = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                   pack_bf16x2(b[2], b[3])};
+  return as_bf16x8(u);
+}
+
+// One 32-key stage in LDS: K page 0, K page 1, V page 0, V page 1 (4 KB each).
+struct Stage {
+  uint16_t part[4][kPartElems];
+};
+
+struct RowState {
+  f32x4 o[8];  // O^T accumulators per 16-dim tile: lane holds dims 4q..4q+3 of row (lane & 15)
+  float m;     // running max of scaled scores (log2 units)
+  float l;     // running sum of probabilities
+};
+
+// Scores, online softmax and PV for one stage. Key kk of the stage (0..31) is
+// visible for this lane's row iff kk < lim.
+__device__ __forceinline__ void attend_stage(RowState& st, const bf16x8 (&qr)[4], const Stage& sg,
+                                             int lane, int lim, float scale_log2) {
+  const int col = lane & 15, grp = lane >> 4;
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const u32x4 k0 = *reinterpret_cast<const u32x4*>(&sg.part[0][s * 512 + lane * 8]);
+    const u32x4 k1 = *reinterpret_cast<const u32x4*>(&sg.part[1][s * 512 + lane * 8]);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), qr[s], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), qr[s], s1, 0, 0, 0);
+  }
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = grp * 4 + i < lim ? s0[i] * scale_log2 : -INFINITY;
+    x[4 + i] = 16 + grp * 4 + i < lim ? s1[i] * scale_log2 : -INFINITY;
+  }
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  const float m_new = fmaxf(st.m, mx);
+  const float base = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - base);
+  f32x4 p0, p1;
+  float rs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p0[i] = __builtin_amdgcn_exp2f(x[i] - base);
+    p1[i] = __builtin_amdgcn_exp2f(x[4 + i] - base);
+    rs += p0[i] + p1[i];
+  }
+  rs += __shfl_xor(rs, 16, kWave);
+  rs += __shfl_xor(rs, 32, kWave);
+  st.l = st.l * alpha + rs;
+  st.m = m_new;
+  const bf16x8 pb = pack_p(p0, p1);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const int off = (dt * 16 + col) * kPage + grp * 4;
+    const u32x2 v0 = *reinterpret_cast<const u32x2*>(&sg.part[2][off]);
+    const u32x2 v1 = *reinterpret_cast<const u32x2*>(&sg.part[3][off]);
+    const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
+    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb, st.o[dt] * alpha, 0,
+                                                        0, 0);
+  }
+}
+
+// Page-pair staging: thread tid moves vectors tid, tid + NT, ... of the 1024
+// 16-byte vectors of a stage (parts: K of pages pg, pg+1, then V of pg, pg+1).
+template <int NT, int VPT>
+__device__ __forceinline__ void stage_gload(u32x4 (&stg)[VPT], int tid, int pg, int pg_end,
+                                            const int32_t* bt, int num_pages, int Hkv, int kvh,
+                                            const uint16_t* kc_layer, const uint16_t* vc_layer) {
+  constexpr size_t page_elems = static_cast<size_t>(kHeadDim) * kPage;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = tid + i * NT;
+    const int part = idx >> 8;
+    const int page = min(pg + (part & 1), pg_end - 1);
+    const int pid = min(max(bt[page], 0), num_pages - 1);
+    const uint16_t* base =
+        (part < 2 ? kc_layer : vc_layer) + (static_cast<size_t>(pid) * Hkv + kvh) * page_elems;
+    stg[i] = *reinterpret_cast<const u32x4*>(base + (idx & 255) * 8);
+  }
+}
+
+template <int NT, int VPT>
+__device__ __forceinline__ void stage_lwrite(const u32x4 (&stg)[VPT], Stage& sg, int tid) {
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int idx = tid + i * NT;
+    *reinterpret_cast<u32x4*>(&sg.part[idx >> 8][(idx & 255) * 8]) = stg[i];
+  }
+}
+
+// NW wavefronts per workgroup; each thread moves VPT 16-byte vectors per stage.
+template <int NW>
+__global__ void __launch_bounds__(kWave * NW)
+k_window_attn_bf16(AttnArgs a) {
+  constexpr int NT = kWave * NW;
+  constexpr int VPT = kChunkVecs / NT;
+  __shared__ Stage stage[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+
+  int bid = blockIdx.x;
+  const int split = bid % a.n_splits;
+  bid /= a.n_splits;
+  const int kvh = bid % a.Hkv;
+  bid /= a.Hkv;
+  const int b = bid % a.B;
+  const int layer = bid / a.B;
+  const int group = (layer * a.B + b) * a.Hkv + kvh;
+
+  const int L = min(max(a.prefix_len[b], 0), a.max_prefix_len);
+  const int npages = (L + kPage - 1) / kPage;
+  const int per_split = (npages + a.n_splits - 1) / a.n_splits;
+  const int pg_begin = min(npages, split * per_split);
+  const int pg_end = min(npages, pg_begin + per_split);
+  const bool with_window = split == a.n_splits - 1;
+
+  // ---- this wave's 16 query rows (B operand of S^T = K Q^T) ---------------
+  const size_t lb = static_cast<size_t>(layer) * a.B + b;
+  const int row = wave * 16 + col;
+  const bool row_ok = row < a.M;
+  const int prow = row / a.g, hh = row % a.g;
+  bf16x8 qr[4];
+  {
+    const uint16_t* qrow =
+        a.q + ((lb * a.W + (row_ok ? prow : 0)) * a.Hq + kvh * a.g + (row_ok ? hh : 0)) * kHeadDim;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (row_ok) z = *reinterpret_cast<const u32x4*>(qrow + s * 32 + grp * 8);
+      qr[s] = as_bf16x8(z);
+    }
+  }
+  RowState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool computes = wave * 16 < a.M;  // waves past the last row tile only move data
+
+  // ---- paged prefix: page pairs through the LDS ring -----------------------
+  const int32_t* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
+  const uint16_t* kc_layer = a.kc + static_cast<size_t>(layer) * a.cache_layer_stride;
+  const uint16_t* vc_layer = a.vc + static_cast<size_t>(layer) * a.cache_layer_stride;
+  const int nch = (pg_end - pg_begin + 1) / 2;
+  if (nch > 0) {
+    u32x4 stg[VPT];
+    stage_gload<NT, VPT>(stg, tid, pg_begin, pg_end, bt, a.num_pages, a.Hkv, kvh, kc_layer,
+                         vc_layer);
+    stage_lwrite<NT, VPT>(stg, stage[0], tid);
+  }
+  __syncthreads();
+  for (int i = 0; i < nch; ++i) {
+    const int pg = pg_begin + 2 * i;
+    const bool more = i + 1 < nch;
+    // the next page pair is in flight while this one is computed
+    u32x4 stg[VPT];
+    if (more)
+      stage_gload<NT, VPT>(stg, tid, pg + 2, pg_end, bt, a.num_pages, a.Hkv, kvh, kc_layer,
+                           vc_layer);
+    if (computes) {
+      // keys pg*16 .. pg*16+31 are valid below L and below the split's end
+      const int lim = min(L, pg_end * kPage) - pg * kPage;
+      attend_stage(st, qr, stage[i & 1], lane, lim, a.scale_log2);
+    }
+    if (more) stage_lwrite<NT, VPT>(stg, stage[(i + 1) & 1], tid);
+    __syncthreads();
+  }
+
+  // ---- the window's own keys, causal over physical order -------------------
+  if (with_window) {
+    const int row_stride = a.Hkv * kHeadDim;
+    const uint16_t* kwin = a.k + lb * a.W * row_stride + kvh * kHeadDim;
+    const uint16_t* vwin = a.v + lb * a.W * row_stride + kvh * kHeadDim;
+    for (int kw0 = 0; kw0 < a.W; kw0 += 32) {
+      Stage& sg = stage[0];
+      // 32 keys x 16 slices of 8 dims: K goes to [slice][key][8], V is transposed
+      for (int idx = tid; idx < 32 * 16; idx += NT) {
+        const int j = idx >> 4, sl = idx & 15;
+        const int key = kw0 + j;
+        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+        if (key < a.W) {
+          kv = *reinterpret_cast<const u32x4*>(kwin + key * row_stride + sl * 8);
+          vv = *reinterpret_cast<const u32x4*>(vwin + key * row_stride + sl * 8);
+        }
+        const int pg = j >> 4, kk = j & 15;
+        *reinterpret_cast<u32x4*>(&sg.part[pg][(sl * kPage + kk) * 8]) = kv;
+        uint16_t* vt = &sg.part[2 + pg][(sl * 8) * kPage + kk];
+        vt[0 * kPage] = static_cast<uint16_t>(vv.x);
+        vt[1 * kPage] = static_cast<uint16_t>(vv.x >> 16);
+        vt[2 * kPage] = static_cast<uint16_t>(vv.y);
+        vt[3 * kPage] = static_cast<uint16_t>(vv.y >> 16);
+        vt[4 * kPage] = static_cast<uint16_t>(vv.z);
+        vt[5 * kPage] = static_cast<uint16_t>(vv.z >> 16);
+        vt[6 * kPage] = static_cast<uint16_t>(vv.w);
+        vt[7 * kPage] = static_cast<uint16_t>(vv.w >> 16);
+      }
+      __syncthreads();
+      if (computes) {
+        const int lim = min(a.W, prow + 1) - kw0;  // window key kw0 + kk visible iff kk < lim
+        attend_stage(st, qr, sg, lane, lim, a.scale_log2);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- write out ------------------------------------------------------------
+  if (!row_ok) return;
+  if (a.n_splits == 1) {
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    uint16_t* orow = a.out + ((lb * a.W + prow) * a.Hq + kvh * a.g + hh) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const u32x2 w = {pack_bf16x2(st.o[dt][0] * inv, st.o[dt][1] * inv),
+                       pack_bf16x2(st.o[dt][2] * inv, st.o[dt][3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + dt * 16 + grp * 4) = w;
+    }
+  } else {
+    const size_t part = static_cast<size_t>(group) * a.n_splits + split;
+    float* o = a.ws_o + (part * a.M + row) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(o + dt * 16 + grp * 4) =
+          make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
+    if (grp == 0) {
+      float* ml = a.ws_ml + (part * a.M + row) * 2;
+      ml[0] = st.m;
+      ml[1] = st.l;
+    }
+  }
+}
+
+// Merge of the per-split partials: out = sum_s O_s 2^(m_s - m) / sum_s l_s 2^(m_s - m).
+// One thread per (group, row, 4 dims).
+__global__ void __launch_bounds__(256)
+k_window_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
+                      uint16_t* __restrict__ out, int n_groups, int M, int n_splits, int B, int W,
+                      int Hq, int Hkv, int g) {
+  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int quads = kHeadDim / 4;
+  const long long total = static_cast<long long>(n_groups) * M * quads;
+  if (idx >= total) return;
+  const int d4 = static_cast<int>(idx % quads);
+  const int row = static_cast<int>((idx / quads) % M);
+  const int group = static_cast<int>(idx / (static_cast<long long>(quads) * M));
+  float mmax = -INFINITY;
+  for (int s = 0; s < n_splits; ++s)
+    mmax = fmaxf(mmax, ws_ml[((static_cast<size_t>(group) * n_splits + s) * M + row) * 2]);
+  const float base = mmax == -INFINITY ? 0.f : mmax;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float lsum = 0.f;
+  for (int s = 0; s < n_splits; ++s) {
+    const size_t part = static_cast<size_t>(group) * n_splits + s;
+    const float m = ws_ml[(part * M + row) * 2];
+    const float l = ws_ml[(part * M + row) * 2 + 1];
+    if (l == 0.f) continue;  // a split with no keys contributes nothing
+    const float w = __builtin_amdgcn_exp2f(m - base);
+    const float4 o = *reinterpret_cast<const float4*>(ws_o + (part * M + row) * kHeadDim + d4 * 4);
+    acc.x += o.x * w;
+    acc.y += o.y * w;
+    acc.z += o.z * w;
+    acc.w += o.w * w;
+    lsum += l * w;
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const int kvh = group % Hkv;
+  const int lbi = group / Hkv;  // layer * B + b
+  const int p = row / g, hh = row % g;
+  uint16_t* orow = out + ((static_cast<size_t>(lbi) * W + p) * Hq + kvh * g + hh) * kHeadDim;
+  uint2 w;
+  w.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+  w.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2*>(orow + d4 * 4) = w;
+}
+
+// ---------------------------------------------------------------------------
+// f32 path (small shapes): one wavefront per (layer, sequence, query head,
+// physical row); 64 keys per step, one key per lane for the scores, then every
+// lane accumulates its own output dimensions. K page [Hkv][D/4][P][4],
+// V page [Hkv][D][P] as for bf16 with 16-byte slices of 4 floats.
+// ---------------------------------------------------------------------------
+constexpr int kF32MaxD = 256;
+
+__global__ void __launch_bounds__(kWave)
+k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
+                  const float* __restrict__ v, const float* __restrict__ kc,
+                  const float* __restrict__ vc, const int32_t* __restrict__ block_table,
+                  const int32_t* __restrict__ prefix_len, float* __restrict__ out, int B, int W,
+                  int Hq, int Hkv, int D, int num_pages, int max_pages, int max_prefix_len,
+                  long long cache_layer_stride, float scale_log2) {
+  __shared__ float qs[kF32MaxD];
+  const int lane = threadIdx.x;
+  int bid = blockIdx.x;
+  const int p = bid % W;
+  bid /= W;
+  const int h = bid % Hq;
+  bid /= Hq;
+  const int b = bid % B;
+  const int layer = bid / B;
+  const int g = Hq / Hkv, kvh = h / g;
+  const size_t lb = static_cast<size_t>(layer) * B + b;
+  for (int d = lane; d < D; d += kWave) qs[d] = q[((lb * W + p) * Hq + h) * D + d];
+  __syncthreads();
+  const int L = min(max(prefix_len[b], 0), max_prefix_len);
+  const int nkeys = L + p + 1;
+  const int32_t* bt = block_table + static_cast<size_t>(b) * max_pages;
+  const float* kcl = kc + static_cast<size_t>(layer) * cache_layer_stride;
+  const float* vcl = vc + static_cast<size_t>(layer) * cache_layer_stride;
+  const size_t page_elems = static_cast<size_t>(D) * kPage;
+  float m = -INFINITY, l = 0.f;
+  float o[kF32MaxD / kWave];
+#pragma unroll
+  for (int i = 0; i < kF32MaxD / kWave; ++i) o[i] = 0.f;
+  for (int k0 = 0; k0 < nkeys; k0 += kWave) {
+    const int key = k0 + lane;
+    float sc = -INFINITY;
+    if (key < nkeys) {
+      float dot = 0.f;
+      if (key < L) {
+        const int pid = min(max(bt[key / kPage], 0), num_pages - 1);
+        const float* kp = kcl + (static_cast<size_t>(pid) * Hkv + kvh) * page_elems;
+        const int off = key % kPage;
+        for (int d = 0; d < D; ++d) dot += qs[d] * kp[((d >> 2) * kPage + off) * 4 + (d & 3)];
+      } else {
+        const float* kr = k + ((lb * W + (key - L)) * Hkv + kvh) * D;
+        for (int d = 0; d < D; ++d) dot += qs[d] * kr[d];
+      }
+      sc = dot * scale_log2;
+    }
+    const float mx = wave_max(sc);
+    const float m_new = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    const float pk = key < nkeys ? __builtin_amdgcn_exp2f(sc - m_new) : 0.f;
+    l = l * alpha + wave_sum(pk);
+    m = m_new;
+#pragma unroll
+    for (int i = 0; i < kF32MaxD / kWave; ++i) o[i] *= alpha;
+    const int nk = min(kWave, nkeys - k0);
+    for (int j = 0; j < nk; ++j) {
+      const float pj = __shfl(pk, j, kWave);
+      const int kj = k0 + j;
+      if (kj < L) {
+        const int pid = min(max(bt[kj / kPage], 0), num_pages - 1);
+        const float* vp = vcl + (static_cast<size_t>(pid) * Hkv + kvh) * page_elems;
+        const int off = kj % kPage;
+#pragma unroll
+        for (int i = 0; i < kF32MaxD / kWave; ++i) {
+          const int d = lane + i * kWave;
+          if (d < D) o[i] += pj * vp[d * kPage + off];
+        }
+      } else {
+        const float* vr = v + ((lb * W + (kj - L)) * Hkv + kvh) * D;
+#pragma unroll
+        for (int i = 0; i < kF32MaxD / kWave; ++i) {
+          const int d = lane + i * kWave;
+          if (d < D) o[i] += pj * vr[d];
+        }
+      }
+    }
+  }
+  const float inv = 1.f / l;
+  float* orow = out + ((lb * W + p) * Hq + h) * D;
+#pragma unroll
+  for (int i = 0; i < kF32MaxD / kWave; ++i) {
+    const int d = lane + i * kWave;
+    if (d < D) orow[d] = o[i] * inv;
+  }
+}
+
+// ---- launch planning -------------------------------------------------------
+struct AttnPlan {
+  int n_splits;
+  int waves;  // wavefronts per workgroup: 4, 8 or 16 (one 16-row tile each)
+  size_t ws_o_bytes, ws_ml_bytes;
+};
+
+static AttnPlan plan_bf16(int n_layers, int B, int W, int Hq, int Hkv, int max_prefix_len) {
+  AttnPlan pl{};
+  const int g = Hq / Hkv;
+  const int M = W * g;
+  const int tiles = ceil_div(M, 16);
+  pl.waves = tiles <= 4 ? 4 : (tiles <= 8 ? 8 : 16);
+  const long long groups = 1LL * n_layers * B * Hkv;
+  // aim for >= 1024 workgroups (4 per CU) but keep >= 4 pages (64 keys) per split
+  const int npages = ceil_div(max(max_prefix_len, 1), kPage);
+  int splits = 1;
+  if (groups < 1024) splits = static_cast<int>((1024 + groups - 1) / groups);
+  splits = max(1, min(splits, npages / 4));
+  pl.n_splits = splits;
+  if (splits > 1) {
+    pl.ws_o_bytes = static_cast<size_t>(groups) * splits * M * kHeadDim * sizeof(float);
+    pl.ws_ml_bytes = static_cast<size_t>(groups) * splits * M * 2 * sizeof(float);
+  }
+  return pl;
+}
+
+}  // namespace wedlm
+
+using namespace wedlm;
+
+static int validate_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D,
+                         int page_size, int max_prefix_len) {
+  if (!valid_dtype(dtype)) return WEDLM_ERR_UNSUPPORTED;
+  if (n_layers <= 0 || B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW || Hq <= 0 || Hkv <= 0 || D <= 0)
+    return WEDLM_ERR_INVALID;
+  if (Hq % Hkv != 0 || max_prefix_len < 0) return WEDLM_ERR_INVALID;
+  if (page_size != kPage) return WEDLM_ERR_UNSUPPORTED;
+  if (dtype == WEDLM_BF16) {
+    if (D != kHeadDim) return WEDLM_ERR_UNSUPPORTED;
+    if (W * (Hq / Hkv) > kMaxRows) return WEDLM_ERR_UNSUPPORTED;
+  } else {
+    if (D % 4 != 0 || D > kF32MaxD) return WEDLM_ERR_UNSUPPORTED;
+  }
+  return WEDLM_OK;
+}
+
+extern "C" size_t wedlm_window_attn_workspace_size(int dtype, int n_layers, int B, int W, int Hq,
+                                                   int Hkv, int D, int page_size,
+                                                   int max_prefix_len) {
+  if (validate_attn(dtype, n_layers, B, W, Hq, Hkv, D, page_size, max_prefix_len) != WEDLM_OK)
+    return 0;
+  if (dtype != WEDLM_BF16) return 0;
+  const AttnPlan pl = plan_bf16(n_layers, B, W, Hq, Hkv, max_prefix_len);
+  return pl.ws_o_bytes + pl.ws_ml_bytes;
+}
+
+extern "C" int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D,
+                                 int page_size, int num_pages, int max_pages, int max_prefix_len,
+                                 float scale, const void* q_phys, const void* k_phys,
+                                 const void* v_phys, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* prefix_len,
+                                 void* out_phys, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  int st = validate_attn(dtype, n_layers, B, W, Hq, Hkv, D, page_size, max_prefix_len);
+  if (st != WEDLM_OK) return st;
+  if (num_pages <= 0 || max_pages <= 0 || static_cast<long long>(max_pages) * page_size <
+                                               static_cast<long long>(max_prefix_len))
+    return WEDLM_ERR_INVALID;
+  if (!q_phys || !k_phys || !v_phys || !k_cache || !v_cache || !block_table || !prefix_len ||
+      !out_phys)
+    return WEDLM_ERR_INVALID;
+  if (!(scale > 0.f)) return WEDLM_ERR_INVALID;
+  hipStream_t s = as_stream(stream);
+  const long long cache_layer_stride = 1LL * num_pages * Hkv * D * page_size;
+  const float scale_log2 = scale * kLog2e;
+  if (dtype == WEDLM_F32) {
+    const long long blocks = 1LL * n_layers * B * Hq * W;
+    if (blocks > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(k_window_attn_f32, dim3(static_cast<unsigned>(blocks)), dim3(kWave), 0, s,
+                       static_cast<const float*>(q_phys), static_cast<const float*>(k_phys),
+                       static_cast<const float*>(v_phys), static_cast<const float*>(k_cache),
+                       static_cast<const float*>(v_cache), block_table, prefix_len,
+                       static_cast<float*>(out_phys), B, W, Hq, Hkv, D, num_pages, max_pages,
+                       max_prefix_len, cache_layer_stride, scale_log2);
+    return launch_status();
+  }
+  const AttnPlan pl = plan_bf16(n_layers, B, W, Hq, Hkv, max_prefix_len);
+  const size_t need = pl.ws_o_bytes + pl.ws_ml_bytes;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return WEDLM_ERR_WORKSPACE;
+  AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q_phys);
+  a.k = static_cast<const uint16_t*>(k_phys);
+  a.v = static_cast<const uint16_t*>(v_phys);
+  a.kc = static_cast<const uint16_t*>(k_cache);
+  a.vc = static_cast<const uint16_t*>(v_cache);
+  a.block_table = block_table;
+  a.prefix_len = prefix_len;
+  a.out = static_cast<uint16_t*>(out_phys);
+  a.ws_o = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_o_bytes) : nullptr;
+  a.B = B;
+  a.W = W;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.g = Hq / Hkv;
+  a.M = W * a.g;
+  a.num_pages = num_pages;
+  a.max_pages = max_pages;
+  a.max_prefix_len = max_prefix_len;
+  a.n_splits = pl.n_splits;
+  a.cache_layer_stride = cache_layer_stride;
+  a.scale_log2 = scale_log2;
+  const long long groups = 1LL * n_layers * B * Hkv;
+  const long long blocks = groups * pl.n_splits;
+  if (blocks > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (pl.waves == 4)
+    hipLaunchKernelGGL(k_window_attn_bf16<4>, grid, dim3(kWave * 4), 0, s, a);
+  else if (pl.waves == 8)
+    hipLaunchKernelGGL(k_window_attn_bf16<8>, grid, dim3(kWave * 8), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_window_attn_bf16<16>, grid, dim3(kWave * 16), 0, s, a);
+  st = launch_status();
+  if (st != WEDLM_OK || pl.n_splits == 1) return st;
+  const long long threads = groups * a.M * (kHeadDim / 4);
+  hipLaunchKernelGGL(k_window_attn_combine, dim3(static_cast<unsigned>((threads + 255) / 256)),
+                     dim3(256), 0, s, a.ws_o, a.ws_ml, a.out, static_cast<int>(groups), a.M,
+                     pl.n_splits, B, W, Hq, Hkv, a.g);
+  return launch_status();
+}

@@ -1,0 +1,76 @@
+// Shared device/host helpers of the wedlm HIP library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wedlm.h"
+
+namespace wedlm {
+
+constexpr int kWave = 64;
+
+// ---- bf16 storage as raw 16-bit words --------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// float -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.f));
+}
+
+// Low / high bf16 of a packed 32-bit word, as float.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Element load/store through float for the f32 / bf16 template paths.
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float x) { *p = x; }
+};
+template <> struct Elt<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void store(uint16_t* p, float x) { *p = f32_to_bf16(x); }
+};
+
+// ---- wave reductions (64 lanes) --------------------------------------------
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+// ---- host helpers -----------------------------------------------------------
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? WEDLM_OK : WEDLM_ERR_HIP;
+}
+
+inline size_t elt_size(int dtype) { return dtype == WEDLM_BF16 ? 2 : 4; }
+
+inline bool valid_dtype(int dtype) { return dtype == WEDLM_F32 || dtype == WEDLM_BF16; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace wedlm

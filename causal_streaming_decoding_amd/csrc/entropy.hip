@@ -1,0 +1,256 @@
+// Full-vocabulary softmax entropy, argmax and distance-penalised selection.
+//
+// hyper.ai summary of WeDLM, "Method": the decoder fills positions chosen by a
+// distance-penalised entropy rule that favours earlier positions. sai.science
+// review, "Weaknesses": the adjusted entropy's equation is missing from the
+// text (read here as entropy + lambda * slot); "Reproducibility & code": an
+// entropy threshold controls filling, and a None threshold decodes one token
+// per step.
+//
+// Entropy of softmax(z) in one streaming pass, in base-2 units: with
+// u = (z - m) log2(e), s = sum 2^u and t = sum u 2^u, H = ln2 (log2 s - t / s).
+// Each thread keeps (m, s, t) for its strided 16-byte vectors; when a vector
+// raises the running max the sums are rescaled by 2^(m_old - m_new) (exact
+// identity: t' = (t + d s) 2^d with d = (m_old - m_new) log2 e). The argmax is
+// tracked as the vector index where the thread's max last rose; the winning
+// vector is re-read once at the end to find the lowest index holding the max.
+//
+// k_entropy_partial: grid (chunks, rows); each block reduces one chunk of one
+//   row to (m, s, t, argmax) in the workspace.
+// k_entropy_select: one wavefront per sequence merges the chunks of its W
+//   rows, forms entropy and score, and applies the threshold / floor rule.
+#include "common.hpp"
+
+namespace wedlm {
+
+constexpr int kEntThreads = 256;
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kLn2F = 0.6931471805599453f;
+// A start value below any finite logit that keeps (m_old - m_new) * log2e finite.
+constexpr float kNegBig = -1.0e30f;
+
+struct EntPartial {
+  float m, s, t;
+  int idx;
+};
+
+__device__ __forceinline__ void merge(EntPartial& a, const EntPartial& b) {
+  const float mn = fmaxf(a.m, b.m);
+  const float da = (a.m - mn) * kLog2eF, db = (b.m - mn) * kLog2eF;
+  const float fa = __builtin_amdgcn_exp2f(da), fb = __builtin_amdgcn_exp2f(db);
+  const float s = a.s * fa + b.s * fb;
+  const float t = (a.t + da * a.s) * fa + (b.t + db * b.s) * fb;
+  int idx;
+  if (a.m > b.m) idx = a.idx;
+  else if (b.m > a.m) idx = b.idx;
+  else idx = min(a.idx, b.idx);
+  a.m = mn;
+  a.s = s;
+  a.t = t;
+  a.idx = idx;
+}
+
+template <typename T>
+struct EVec {
+  static constexpr int N = 16 / sizeof(T);
+  union {
+    uint4 raw;
+    T e[N];
+  };
+};
+
+// VEC: rows are 16-byte aligned and V is a multiple of the vector width.
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(kEntThreads)
+k_entropy_partial(const T* __restrict__ logits, int V, int chunk_elems, int n_chunks,
+                  EntPartial* __restrict__ part) {
+  constexpr int N = VEC ? EVec<T>::N : 1;
+  const int chunk = blockIdx.x;
+  const int row = blockIdx.y;
+  const int begin = chunk * chunk_elems;
+  const int end = min(V, begin + chunk_elems);
+  const T* z = logits + static_cast<size_t>(row) * V;
+  float m = kNegBig, s = 0.f, t = 0.f;
+  int best_it = -1;
+  int it = 0;
+  for (int i0 = begin + threadIdx.x * N; i0 < end; i0 += kEntThreads * N, ++it) {
+    float x[N];
+    if constexpr (VEC) {
+      EVec<T> vv;
+      vv.raw = *reinterpret_cast<const uint4*>(z + i0);
+#pragma unroll
+      for (int e = 0; e < N; ++e) x[e] = Elt<T>::load(&vv.e[e]);
+    } else {
+      x[0] = Elt<T>::load(z + i0);
+    }
+    float mz = x[0];
+#pragma unroll
+    for (int e = 1; e < N; ++e) mz = fmaxf(mz, x[e]);
+    if (mz > m) best_it = it;
+    const float mn = fmaxf(m, mz);
+    const float d = (m - mn) * kLog2eF;
+    const float f = __builtin_amdgcn_exp2f(d);
+    t = (t + d * s) * f;
+    s = s * f;
+    m = mn;
+    const float mb = mn * kLog2eF;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      const float u = fmaf(x[e], kLog2eF, -mb);
+      const float p = __builtin_amdgcn_exp2f(u);
+      s += p;
+      t = fmaf(p, u, t);
+    }
+  }
+  EntPartial acc{m, s, t, 0x7fffffff};
+  if (best_it >= 0) {
+    const int i0 = begin + (best_it * kEntThreads + threadIdx.x) * N;
+#pragma unroll
+    for (int e = N - 1; e >= 0; --e)
+      if (Elt<T>::load(z + i0 + e) == m) acc.idx = i0 + e;
+  }
+  // wavefront then block reduction
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    EntPartial o;
+    o.m = __shfl_xor(acc.m, off, kWave);
+    o.s = __shfl_xor(acc.s, off, kWave);
+    o.t = __shfl_xor(acc.t, off, kWave);
+    o.idx = __shfl_xor(acc.idx, off, kWave);
+    merge(acc, o);
+  }
+  __shared__ EntPartial red[kEntThreads / kWave];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    EntPartial r = red[0];
+    for (int w = 1; w < kEntThreads / kWave; ++w) merge(r, red[w]);
+    part[static_cast<size_t>(row) * n_chunks + chunk] = r;
+  }
+}
+
+__global__ void __launch_bounds__(kWave)
+k_entropy_select(const EntPartial* __restrict__ part, int n_chunks, int W,
+                 const uint8_t* __restrict__ filled, float lambda, float tau, int min_fill,
+                 float* __restrict__ entropy, float* __restrict__ score,
+                 int32_t* __restrict__ argmax_tok, uint8_t* __restrict__ selected) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const bool in_window = i < W;
+  float sc = INFINITY;
+  bool cand = false;
+  if (in_window) {
+    const int row = b * W + i;
+    EntPartial acc = part[static_cast<size_t>(row) * n_chunks];
+    for (int c = 1; c < n_chunks; ++c) merge(acc, part[static_cast<size_t>(row) * n_chunks + c]);
+    const float H = kLn2F * (log2f(acc.s) - acc.t / acc.s);
+    // product rounded, then the sum: no fused multiply-add
+    sc = __fadd_rn(H, __fmul_rn(lambda, static_cast<float>(i)));
+    entropy[row] = H;
+    score[row] = sc;
+    argmax_tok[row] = acc.idx;
+    cand = filled[row] == 0;
+  }
+  bool sel = cand && sc < tau;
+  const uint64_t any_sel = __ballot(sel);
+  const uint64_t any_cand = __ballot(cand);
+  if (any_sel == 0 && any_cand != 0 && min_fill == 1) {
+    // lowest score among candidates, lowest slot on equal scores
+    float best = cand ? sc : INFINITY;
+    int who = cand ? i : kWave;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ob = __shfl_xor(best, off, kWave);
+      const int ow = __shfl_xor(who, off, kWave);
+      if (ob < best || (ob == best && ow < who)) {
+        best = ob;
+        who = ow;
+      }
+    }
+    sel = (i == who);
+  }
+  if (in_window) selected[b * W + i] = sel ? 1 : 0;
+}
+
+struct EntPlan {
+  int chunk_elems, n_chunks;
+  bool vec;
+};
+
+static EntPlan plan_entropy(int dtype, int B, int W, int V) {
+  EntPlan pl{};
+  const int N = 16 / static_cast<int>(elt_size(dtype));
+  pl.vec = (V % N) == 0;
+  const int step = kEntThreads * (pl.vec ? N : 1);  // elements per block iteration
+  const long long rows = 1LL * B * W;
+  long long want = (4096 + rows - 1) / rows;         // ~16 blocks per CU in total
+  const long long max_chunks = (V + step - 1) / step;
+  want = want < 1 ? 1 : (want > max_chunks ? max_chunks : want);
+  int per = static_cast<int>((V + want - 1) / want);
+  per = ((per + step - 1) / step) * step;
+  pl.chunk_elems = per;
+  pl.n_chunks = (V + per - 1) / per;
+  return pl;
+}
+
+}  // namespace wedlm
+
+using namespace wedlm;
+
+extern "C" size_t wedlm_entropy_select_workspace_size(int dtype, int B, int W, int V) {
+  if (!valid_dtype(dtype) || B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW || V <= 0) return 0;
+  const EntPlan pl = plan_entropy(dtype, B, W, V);
+  return static_cast<size_t>(B) * W * pl.n_chunks * sizeof(EntPartial);
+}
+
+extern "C" int wedlm_entropy_select(int dtype, int B, int W, int V, const void* logits,
+                                    const uint8_t* filled, float lambda, float tau, int min_fill,
+                                    float* entropy, float* score, int32_t* argmax_tok,
+                                    uint8_t* selected, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (!valid_dtype(dtype)) return WEDLM_ERR_UNSUPPORTED;
+  if (B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW || V <= 0) return WEDLM_ERR_INVALID;
+  if (min_fill != 0 && min_fill != 1) return WEDLM_ERR_INVALID;
+  if (lambda != lambda || tau != tau) return WEDLM_ERR_INVALID;  // NaN
+  if (!logits || !filled || !entropy || !score || !argmax_tok || !selected)
+    return WEDLM_ERR_INVALID;
+  if (1LL * B * W > 65535) return WEDLM_ERR_UNSUPPORTED;
+  EntPlan pl = plan_entropy(dtype, B, W, V);
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) {
+    pl.vec = false;
+    const int step = kEntThreads;
+    int per = ((pl.chunk_elems + step - 1) / step) * step;
+    pl.chunk_elems = per;
+    pl.n_chunks = (V + per - 1) / per;
+  }
+  const size_t need = static_cast<size_t>(B) * W * pl.n_chunks * sizeof(EntPartial);
+  if (need > wedlm_entropy_select_workspace_size(dtype, B, W, V) ||
+      workspace == nullptr || workspace_bytes < need)
+    return WEDLM_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  EntPartial* part = static_cast<EntPartial*>(workspace);
+  const dim3 grid(pl.n_chunks, B * W);
+  if (dtype == WEDLM_BF16) {
+    const uint16_t* z = static_cast<const uint16_t*>(logits);
+    if (pl.vec)
+      hipLaunchKernelGGL((k_entropy_partial<uint16_t, true>), grid, dim3(kEntThreads), 0, s, z, V,
+                         pl.chunk_elems, pl.n_chunks, part);
+    else
+      hipLaunchKernelGGL((k_entropy_partial<uint16_t, false>), grid, dim3(kEntThreads), 0, s, z, V,
+                         pl.chunk_elems, pl.n_chunks, part);
+  } else {
+    const float* z = static_cast<const float*>(logits);
+    if (pl.vec)
+      hipLaunchKernelGGL((k_entropy_partial<float, true>), grid, dim3(kEntThreads), 0, s, z, V,
+                         pl.chunk_elems, pl.n_chunks, part);
+    else
+      hipLaunchKernelGGL((k_entropy_partial<float, false>), grid, dim3(kEntThreads), 0, s, z, V,
+                         pl.chunk_elems, pl.n_chunks, part);
+  }
+  int st = launch_status();
+  if (st != WEDLM_OK) return st;
+  hipLaunchKernelGGL(k_entropy_select, dim3(B), dim3(kWave), 0, s, part, pl.n_chunks, W, filled,
+                     lambda, tau, min_fill, entropy, score, argmax_tok, selected);
+  return launch_status();
+}

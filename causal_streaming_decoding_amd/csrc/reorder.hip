@@ -1,0 +1,62 @@
+// Topological reorder of the sliding window: one 64-lane wavefront per sequence.
+//
+// hyper.ai summary of WeDLM, "Method": filled (observed) tokens are placed
+// physically before the mask tokens and every token keeps its logical
+// position; the streaming decoder does this to its W-slot window each step.
+//
+// Lane i owns slot i. A ballot over the filled flags gives the whole window as
+// one 64-bit mask; a slot's physical index is then a popcount of the flags
+// below it (filled slots) or n_obs plus the popcount of the masks below it
+// (mask slots), which is the stable partition. The leading filled run, used by
+// the commit, is the count of trailing ones of the ballot.
+#include "common.hpp"
+
+namespace wedlm {
+
+constexpr int kReorderWaves = 4;
+
+__global__ void __launch_bounds__(kWave * kReorderWaves)
+k_window_reorder(int B, int W, const uint8_t* __restrict__ filled,
+                 const int32_t* __restrict__ prefix_len, int32_t* __restrict__ perm,
+                 int32_t* __restrict__ inv_perm, int32_t* __restrict__ pos,
+                 int32_t* __restrict__ n_obs, int32_t* __restrict__ run_len) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.x * kReorderWaves + (threadIdx.x >> 6);
+  if (b >= B) return;  // uniform per wavefront
+  const bool in_window = lane < W;
+  const bool f = in_window && filled[b * W + lane] != 0;
+  const uint64_t fm = __ballot(f);
+  const uint64_t window = (W == kWave) ? ~0ull : ((1ull << W) - 1ull);
+  const uint64_t mm = ~fm & window;
+  const uint64_t below = (1ull << lane) - 1ull;  // lane < 64, so the shift is defined
+  const int nobs = __popcll(fm);
+  const int phys = f ? __popcll(fm & below) : nobs + __popcll(mm & below);
+  const int L = max(prefix_len[b], 0);
+  if (in_window) {
+    inv_perm[b * W + lane] = phys;
+    perm[b * W + phys] = lane;
+    pos[b * W + phys] = L + lane;
+  }
+  if (lane == 0) {
+    n_obs[b] = nobs;
+    // lanes >= W contribute 0 bits, so the first zero is at most W
+    const uint64_t zeros = ~fm;
+    run_len[b] = zeros == 0 ? kWave : __builtin_ctzll(zeros);
+  }
+}
+
+}  // namespace wedlm
+
+extern "C" int wedlm_window_reorder(int B, int W, const uint8_t* filled, const int32_t* prefix_len,
+                                    int32_t* perm, int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
+                                    int32_t* run_len, void* stream) {
+  using namespace wedlm;
+  if (B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW) return WEDLM_ERR_INVALID;
+  if (!filled || !prefix_len || !perm || !inv_perm || !pos || !n_obs || !run_len)
+    return WEDLM_ERR_INVALID;
+  const int blocks = ceil_div(B, kReorderWaves);
+  hipLaunchKernelGGL(k_window_reorder, dim3(blocks), dim3(kWave * kReorderWaves), 0,
+                     as_stream(stream), B, W, filled, prefix_len, perm, inv_perm, pos, n_obs,
+                     run_len);
+  return launch_status();
+}

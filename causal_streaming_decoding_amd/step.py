@@ -1,0 +1,165 @@
+"""Window-step driver: the five C entry points in order on one stream.
+
+hyper.ai summary of WeDLM, "Method" (Streaming Parallel Decoding): reorder the
+window, run the causal forward over it against the KV cache, select by
+distance-penalised entropy, commit the leftmost filled run and refill. Here the
+forward's projections and logits are inputs (synthetic), so one step is:
+reorder -> RoPE at logical positions -> window attention -> entropy/select ->
+commit. Device buffers are allocated once; ``run`` only enqueues kernels and
+never synchronises, so steps can be chained or timed back to back.
+"""
+
+from dataclasses import dataclass
+
+import torch
+
+from . import wedlm as W_
+
+
+@dataclass
+class StreamState:
+    """Device-resident decoding state of a batch of sequences."""
+    tokens: torch.Tensor       # [B, W] int32, mask id where not filled
+    filled: torch.Tensor       # [B, W] uint8
+    prefix_len: torch.Tensor   # [B] int32
+    block_table: torch.Tensor  # [B, max_pages] int32
+    k_cache: torch.Tensor      # [nl, num_pages, Hkv, D/X, P, X]
+    v_cache: torch.Tensor      # [nl, num_pages, Hkv, D, P]
+
+    def snapshot(self):
+        return (self.tokens.clone(), self.filled.clone(), self.prefix_len.clone())
+
+    def restore(self, snap):
+        self.tokens.copy_(snap[0])
+        self.filled.copy_(snap[1])
+        self.prefix_len.copy_(snap[2])
+
+
+class WindowStep:
+    """Buffers and launches of one window step for fixed shapes."""
+
+    def __init__(self, n_layers, B, W, Hq, Hkv, D, V, page_size, num_pages, max_pages, dtype,
+                 device, max_prefix_len, theta, lam, tau, min_fill=1, mask_id=-1, scale=None):
+        self.n_layers, self.B, self.W, self.Hq, self.Hkv, self.D, self.V = (
+            n_layers, B, W, Hq, Hkv, D, V)
+        self.page_size, self.num_pages, self.max_pages = page_size, num_pages, max_pages
+        self.dtype, self.device = dtype, device
+        self.dt = W_.dtype_code(dtype)
+        self.theta, self.lam, self.tau, self.min_fill, self.mask_id = theta, lam, tau, min_fill, mask_id
+        self.scale = scale if scale is not None else D ** -0.5
+        self.max_prefix_len = max_prefix_len
+        i32 = dict(dtype=torch.int32, device=device)
+        self.perm = torch.empty((B, W), **i32)
+        self.inv = torch.empty((B, W), **i32)
+        self.pos = torch.empty((B, W), **i32)
+        self.n_obs = torch.empty((B,), **i32)
+        self.run_len = torch.empty((B,), **i32)
+        fl = dict(dtype=dtype, device=device)
+        self.q_phys = torch.empty((n_layers, B, W, Hq, D), **fl)
+        self.k_phys = torch.empty((n_layers, B, W, Hkv, D), **fl)
+        self.v_phys = torch.empty((n_layers, B, W, Hkv, D), **fl)
+        self.out_phys = torch.empty((n_layers, B, W, Hq, D), **fl)
+        self.entropy = torch.empty((B, W), dtype=torch.float32, device=device)
+        self.score = torch.empty((B, W), dtype=torch.float32, device=device)
+        self.argmax = torch.empty((B, W), **i32)
+        self.selected = torch.empty((B, W), dtype=torch.uint8, device=device)
+        self.commit_len = torch.empty((B,), **i32)
+        self.cache_slot = torch.empty((B, W), **i32)
+        self._size_attn_workspace(max_prefix_len)
+        self.ent_ws_bytes = W_.wedlm_entropy_select_workspace_size(self.dt, B, W, V)
+        self.ent_ws = torch.empty((max(self.ent_ws_bytes, 1),), dtype=torch.uint8, device=device)
+
+    def _size_attn_workspace(self, max_prefix_len):
+        self.attn_ws_bytes = W_.wedlm_window_attn_workspace_size(
+            self.dt, self.n_layers, self.B, self.W, self.Hq, self.Hkv, self.D, self.page_size,
+            max_prefix_len)
+        self.attn_ws = torch.empty((max(self.attn_ws_bytes, 1),), dtype=torch.uint8,
+                                   device=self.device)
+
+    # -- the five calls -------------------------------------------------------
+    def reorder(self, st, stream=None):
+        W_.wedlm_window_reorder(self.B, self.W, st.filled, st.prefix_len, self.perm, self.inv,
+                                self.pos, self.n_obs, self.run_len, stream)
+
+    def rope(self, q, k, v, stream=None):
+        W_.wedlm_rope_logical(self.dt, self.n_layers, self.B, self.W, self.Hq, self.Hkv, self.D,
+                              self.theta, q, k, v, self.perm, self.pos, self.q_phys, self.k_phys,
+                              self.v_phys, stream)
+
+    def attn(self, st, max_prefix_len=None, stream=None):
+        mpl = self.max_prefix_len if max_prefix_len is None else max_prefix_len
+        need = W_.wedlm_window_attn_workspace_size(self.dt, self.n_layers, self.B, self.W, self.Hq,
+                                                   self.Hkv, self.D, self.page_size, mpl)
+        if need > self.attn_ws_bytes:
+            self._size_attn_workspace(mpl)
+        W_.wedlm_window_attn(self.dt, self.n_layers, self.B, self.W, self.Hq, self.Hkv, self.D,
+                             self.page_size, self.num_pages, self.max_pages, mpl, self.scale,
+                             self.q_phys, self.k_phys, self.v_phys, st.k_cache, st.v_cache,
+                             st.block_table, st.prefix_len, self.out_phys, self.attn_ws,
+                             self.attn_ws_bytes, stream)
+
+    def entropy_select(self, st, logits, stream=None):
+        W_.wedlm_entropy_select(self.dt, self.B, self.W, self.V, logits, st.filled, self.lam,
+                                self.tau, self.min_fill, self.entropy, self.score, self.argmax,
+                                self.selected, self.ent_ws, self.ent_ws_bytes, stream)
+
+    def commit(self, st, commit_len=None, stream=None):
+        W_.wedlm_commit_prefix(self.dt, self.n_layers, self.B, self.W, self.Hkv, self.D,
+                               self.page_size, self.num_pages, self.max_pages, self.run_len,
+                               self.selected, self.argmax, self.k_phys, self.v_phys,
+                               st.block_table, st.k_cache, st.v_cache, st.tokens, st.filled,
+                               st.prefix_len, self.commit_len if commit_len is None else commit_len,
+                               self.cache_slot, self.mask_id, stream)
+
+    def run(self, st, q, k, v, logits, max_prefix_len=None, commit_len=None, stream=None,
+            attn_events=None):
+        """One whole window step; ``attn_events`` = (start, end) events around attention."""
+        self.reorder(st, stream)
+        self.rope(q, k, v, stream)
+        if attn_events is not None:
+            attn_events[0].record(stream)
+        self.attn(st, max_prefix_len, stream)
+        if attn_events is not None:
+            attn_events[1].record(stream)
+        self.entropy_select(st, logits, stream)
+        self.commit(st, commit_len, stream)
+
+
+def upload_step_inputs(wl, inp, device):
+    """Device state and window inputs from ``synth.make_step_inputs`` output.
+
+    Returns (state, q, k, v, logits, max_prefix_len). Layers whose prefix cache
+    was not drawn stay zero.
+    """
+    from . import layout
+    from .synth import torch_dtype
+
+    dt = torch_dtype(wl)
+    table = torch.as_tensor(inp["block_table"], dtype=torch.int32)
+    kc, vc = layout.alloc_caches(wl.n_layers, inp["num_pages"], wl.Hkv, wl.D, wl.page_size, dt,
+                                 device)
+    for layer in range(wl.n_layers):
+        if inp["k_cache"][layer] is None:
+            continue
+        for b in range(wl.B):
+            layout.write_rows(kc, vc, layer, table[b], 0, torch.from_numpy(inp["k_cache"][layer][b]),
+                              torch.from_numpy(inp["v_cache"][layer][b]))
+    st = StreamState(
+        tokens=torch.as_tensor(inp["tokens"], dtype=torch.int32).to(device),
+        filled=torch.as_tensor(inp["filled"], dtype=torch.uint8).to(device),
+        prefix_len=torch.as_tensor(inp["prefix_len"], dtype=torch.int32).to(device),
+        block_table=table.to(device), k_cache=kc, v_cache=vc)
+    q = torch.from_numpy(inp["q"]).to(device=device, dtype=dt)
+    k = torch.from_numpy(inp["k"]).to(device=device, dtype=dt)
+    v = torch.from_numpy(inp["v"]).to(device=device, dtype=dt)
+    logits = torch.from_numpy(inp["logits"]).to(device=device, dtype=dt)
+    return st, q, k, v, logits, int(inp["prefix_len"].max())
+
+
+def make_window_step(wl, inp, device, max_prefix_len):
+    """WindowStep sized for a workload and its inputs."""
+    from .synth import torch_dtype
+
+    return WindowStep(wl.n_layers, wl.B, wl.W, wl.Hq, wl.Hkv, wl.D, wl.V, wl.page_size,
+                      inp["num_pages"], inp["block_table"].shape[1], torch_dtype(wl), device,
+                      max_prefix_len, wl.theta, wl.lam, wl.tau, wl.min_fill, wl.mask_id)

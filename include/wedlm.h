@@ -1,0 +1,217 @@
+/*
+ * wedlm.h - C ABI of one window step of WeDLM's Streaming Parallel Decoding,
+ * implemented as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The step (hyper.ai summary of WeDLM, "Method"; sai.science review, "Summary"):
+ *   1. wedlm_window_reorder  - filled slots of the sliding window are placed
+ *      physically before the mask slots; every slot keeps its logical position.
+ *   2. wedlm_rope_logical    - rotary embedding (RoFormer, listed under
+ *      "Builds on" on the mlsanity.com page) applied at the logical positions,
+ *      gathering the window into physical order.
+ *   3. wedlm_window_attn     - causal GQA attention of the reordered window over
+ *      the persistent paged KV-cache prefix plus the window itself.
+ *   4. wedlm_entropy_select  - softmax entropy over the full vocabulary per slot,
+ *      distance-penalised score, fill of the mask slots that clear a threshold.
+ *   5. wedlm_commit_prefix   - the leftmost contiguous filled run is appended to
+ *      the paged cache and the window is refilled with masks.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, unless a
+ *    comment says "host". The library never allocates, frees or synchronises:
+ *    every call only enqueues kernels on `stream` (a hipStream_t passed as
+ *    void*; NULL is the default stream) and returns.
+ *  - Host-side arguments are validated before any launch. On error nothing is
+ *    enqueued and a negative status is returned (see wedlm_status).
+ *  - Device-resident values that steer the kernels (prefix lengths, block-table
+ *    entries, run lengths) are clamped to the documented ranges inside the
+ *    kernels, so out-of-contract values give wrong results but never an
+ *    out-of-bounds access.
+ *  - The library keeps no mutable global state: calls are re-entrant; calls on
+ *    different streams that write the same buffers race, as usual.
+ *  - Element type: WEDLM_F32 or WEDLM_BF16 for every floating-point tensor of a
+ *    call (window projections, caches, outputs, logits). Accumulation is fp32.
+ *
+ * Tensor layouts (row-major, innermost last; B sequences, W window slots,
+ * Hq query heads, Hkv kv heads, g = Hq / Hkv, D head dim, P page size, V vocab)
+ *  - window q   [n_layers][B][W][Hq][D],  k, v [n_layers][B][W][Hkv][D]
+ *    (slot order before wedlm_rope_logical, physical order after it).
+ *  - k_cache    [n_layers][num_pages][Hkv][D / X][P][X] with X = 16 / sizeof(elt)
+ *    (8 for bf16, 4 for f32): in a page, the X-wide slices of each position's
+ *    key are stored position-major, so the keys of a page are read as contiguous
+ *    16-byte vectors. Keys are stored AFTER RoPE.
+ *  - v_cache    [n_layers][num_pages][Hkv][D][P]: a page stores each value
+ *    dimension's P positions contiguously (a transposed page).
+ *  - block_table [B][max_pages] int32: logical position t of sequence b lives in
+ *    page block_table[b][t / P] at offset t % P. All layers share the table.
+ *  - logits     [B][W][V] in slot order.
+ */
+#ifndef WEDLM_H
+#define WEDLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum wedlm_status {
+  WEDLM_OK = 0,
+  WEDLM_ERR_INVALID = -1,     /* null pointer, size <= 0, Hq % Hkv != 0, W > 64, ... */
+  WEDLM_ERR_UNSUPPORTED = -2, /* a shape or dtype this build has no kernel for     */
+  WEDLM_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required    */
+  WEDLM_ERR_HIP = -4          /* the HIP runtime reported an error at launch        */
+};
+
+/* Element types. */
+enum wedlm_dtype { WEDLM_F32 = 0, WEDLM_BF16 = 1 };
+
+/* Largest window the kernels accept (one 64-lane wavefront per sequence). */
+#define WEDLM_MAX_WINDOW 64
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* wedlm_status_string(int status);
+
+/* Version of this ABI: (major << 16) | minor. */
+int wedlm_abi_version(void);
+
+/*
+ * wedlm_window_reorder - topological reorder of the window.
+ * hyper.ai summary of WeDLM, "Method": observed tokens move to the physical
+ * front, masks to the end, logical position IDs are kept; the streaming decoder
+ * reorders its window at every step.
+ *
+ * in : filled[B][W] uint8 (nonzero = filled), prefix_len[B] int32 (L_b >= 0).
+ * out: perm[B][W]      slot held at physical index p (filled slots in ascending
+ *                      order, then mask slots in ascending order);
+ *      inv_perm[B][W]  physical index of slot i;
+ *      pos[B][W]       logical position of physical row p = L_b + perm[p];
+ *      n_obs[B]        number of filled slots;
+ *      run_len[B]      length of the leading all-filled run of the window.
+ * Requires 1 <= W <= WEDLM_MAX_WINDOW, B >= 1. Any output pointer may not be NULL.
+ */
+int wedlm_window_reorder(int B, int W, const uint8_t* filled, const int32_t* prefix_len,
+                         int32_t* perm, int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
+                         int32_t* run_len, void* stream);
+
+/*
+ * wedlm_rope_logical - rotary embedding at logical positions, gathered into
+ * physical order. RoFormer rotation (mlsanity.com page, "Builds on"), kept at
+ * logical positions through the reordering (hyper.ai summary, "Method").
+ *
+ * Pairing: dimension j rotates with j + D/2 (j < D/2) by angle pos * theta^(-2j/D):
+ *   y_j = x_j cos - x_{j+D/2} sin,  y_{j+D/2} = x_{j+D/2} cos + x_j sin.
+ * Angles are formed and their sine/cosine evaluated in double precision; the
+ * rotation is done in fp32 and rounded once to the element type.
+ *
+ * in : q (slot order, [n_layers][B][W][Hq][D]), k, v ([n_layers][B][W][Hkv][D]),
+ *      perm, pos from wedlm_window_reorder.
+ * out: q_phys[l][b][p] = R(pos[b][p]) q[l][b][perm[b][p]], k_phys likewise,
+ *      v_phys[l][b][p] = v[l][b][perm[b][p]] (no rotation), same layouts.
+ * Outputs must not alias inputs. D must be even; D <= 256.
+ */
+int wedlm_rope_logical(int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D, double theta,
+                       const void* q, const void* k, const void* v, const int32_t* perm,
+                       const int32_t* pos, void* q_phys, void* k_phys, void* v_phys, void* stream);
+
+/*
+ * Bytes of workspace wedlm_window_attn needs for these sizes. max_prefix_len is
+ * a host-side upper bound of every prefix_len[b]. Returns 0 when no workspace is
+ * needed (no key-range split) and also for invalid sizes.
+ */
+size_t wedlm_window_attn_workspace_size(int dtype, int n_layers, int B, int W, int Hq, int Hkv,
+                                        int D, int page_size, int max_prefix_len);
+
+/*
+ * wedlm_window_attn - causal GQA attention of the reordered window over
+ * [paged KV prefix ; window]. hyper.ai summary, "Method": a causal forward pass
+ * over the window conditioned on the persistent KV cache; sai.science review,
+ * "Strengths": the plain causal mask is kept (prior art for the kernels:
+ * FlashAttention and PagedAttention, mlsanity.com page, "Builds on").
+ *
+ * For physical row p of sequence b and query head h (kv head h / g):
+ *   keys   = the L_b cached keys (positions 0..L_b-1) then window rows 0..p,
+ *   out[l][b][p][h] = softmax(scale * q_phys . keys) @ values.
+ * Online softmax with fp32 accumulation; output rounded once to the element type.
+ *
+ * in : q_phys, k_phys, v_phys (physical order, rotated q/k) as written by
+ *      wedlm_rope_logical; k_cache, v_cache (layouts above, num_pages pages per
+ *      layer); block_table[B][max_pages]; prefix_len[B] (device; clamped to
+ *      [0, max_prefix_len]).
+ * out: out_phys [n_layers][B][W][Hq][D], physical order.
+ * Host sizes: page_size P in {16}; max_prefix_len <= max_pages * P; bf16 needs
+ * D == 128; f32 needs D even and <= 256. workspace: at least
+ * wedlm_window_attn_workspace_size(...) bytes (may be NULL if that is 0).
+ * Block-table entries are clamped to [0, num_pages).
+ */
+int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D, int page_size,
+                      int num_pages, int max_pages, int max_prefix_len, float scale,
+                      const void* q_phys, const void* k_phys, const void* v_phys, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table, const int32_t* prefix_len,
+                      void* out_phys, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace wedlm_entropy_select needs (per-chunk partial reductions). */
+size_t wedlm_entropy_select_workspace_size(int dtype, int B, int W, int V);
+
+/*
+ * wedlm_entropy_select - per-slot softmax entropy and distance-penalised fill.
+ * hyper.ai summary, "Method": positions are chosen by a distance-penalised
+ * entropy rule favouring earlier positions; sai.science review, "Weaknesses":
+ * the adjusted-entropy equation is missing from the text; "Reproducibility &
+ * code": an entropy threshold controls filling and a None threshold decodes one
+ * token per step.
+ *
+ * For every slot i of sequence b (all W slots are reduced; only masks are used):
+ *   entropy  = Shannon entropy in nats of softmax(logits[b][i][:]) over all V,
+ *   argmax   = lowest vocabulary id holding the maximum logit,
+ *   score    = entropy + lambda * i   (fp32: product rounded, then the sum).
+ * Selection among mask slots (filled[b][i] == 0): selected = score < tau.
+ * If no mask slot is selected, min_fill == 1 and a mask slot exists, the mask
+ * slot with the lowest score (lowest i on equal scores) is selected.
+ * tau = -INFINITY with min_fill = 1 is one-token-per-step decoding.
+ *
+ * in : logits [B][W][V], filled [B][W].
+ * out: entropy, score [B][W] float32; argmax_tok [B][W] int32; selected [B][W]
+ *      uint8 (0/1). workspace >= wedlm_entropy_select_workspace_size(...).
+ */
+int wedlm_entropy_select(int dtype, int B, int W, int V, const void* logits, const uint8_t* filled,
+                         float lambda, float tau, int min_fill, float* entropy, float* score,
+                         int32_t* argmax_tok, uint8_t* selected, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * wedlm_commit_prefix - commit of the leading filled run, paged append, refill.
+ * hyper.ai summary, "Method": the leftmost contiguous filled prefix is committed
+ * to the cache at once (under the causal mask its KV depends only on earlier
+ * tokens) and new masks are appended to keep the window W wide.
+ *
+ * With c = run_len[b] (the run at forward time; physical rows 0..c-1 are slots
+ * 0..c-1) and L = prefix_len[b]:
+ *   - for every layer, k_phys/v_phys rows 0..c-1 are written to cache positions
+ *     L..L+c-1 through block_table; cache_slot[b][j] = page * P + offset for
+ *     j < c, -1 otherwise;
+ *   - the window is updated in place: slots chosen by `selected` become filled
+ *     with argmax_tok; the window shifts left by c; c masks (token mask_id,
+ *     filled 0) are appended; prefix_len[b] += c; commit_len[b] = c.
+ * c is clamped to [0, W] and to the pages the table holds (max_pages * P - L).
+ *
+ * in : run_len, selected, argmax_tok (from the reorder / select calls of the
+ *      same step), k_phys, v_phys (physical order), block_table.
+ * in/out: k_cache, v_cache (rows written), tokens [B][W] int32, filled [B][W]
+ *      uint8, prefix_len [B] int32.
+ * out: commit_len [B] int32, cache_slot [B][W] int32.
+ */
+int wedlm_commit_prefix(int dtype, int n_layers, int B, int W, int Hkv, int D, int page_size,
+                        int num_pages, int max_pages, const int32_t* run_len,
+                        const uint8_t* selected, const int32_t* argmax_tok, const void* k_phys,
+                        const void* v_phys, const int32_t* block_table, void* k_cache,
+                        void* v_cache, int32_t* tokens, uint8_t* filled, int32_t* prefix_len,
+                        int32_t* commit_len, int32_t* cache_slot, int32_t mask_id, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WEDLM_H */

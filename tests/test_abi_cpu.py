@@ -1,0 +1,114 @@
+"""The C-ABI library loads and exports what include/wedlm.h declares (CPU, no launches).
+
+Host-side argument validation is checked too: each invalid call returns its
+documented status before any HIP call is made.
+"""
+
+import os
+
+import pytest
+import torch
+
+from causal_streaming_decoding_amd import layout
+from causal_streaming_decoding_amd import wedlm as W
+
+pytestmark = pytest.mark.skipif(not os.path.exists(W.LIB_PATH),
+                                reason="libwedlm.so not built (run __graft_entry__.build())")
+
+
+def test_exports_every_declared_function():
+    declared = W.header_functions()
+    assert len(declared) == 9
+    lib = W.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(W._SIGNATURES)
+
+
+def test_status_strings_and_version():
+    assert W.wedlm_status_string(0) == "ok"
+    assert "invalid" in W.wedlm_status_string(-1)
+    assert "unsupported" in W.wedlm_status_string(-2)
+    assert "workspace" in W.wedlm_status_string(-3)
+    assert W.wedlm_abi_version() >> 16 == 1
+
+
+def _raw(name, *args):
+    return getattr(W.lib(), name)(*args)
+
+
+def test_reorder_validation():
+    assert _raw("wedlm_window_reorder", 0, 8, 1, 1, 1, 1, 1, 1, 1, None) == -1
+    assert _raw("wedlm_window_reorder", 1, 65, 1, 1, 1, 1, 1, 1, 1, None) == -1
+    assert _raw("wedlm_window_reorder", 1, 8, None, 1, 1, 1, 1, 1, 1, None) == -1
+
+
+def test_rope_validation():
+    args = [1, 1, 1, 8, 4, 2, 128, 1e6] + [1] * 8 + [None]
+    a = list(args); a[5] = 3
+    assert _raw("wedlm_rope_logical", *a) == -1          # Hq % Hkv
+    a = list(args); a[6] = 127
+    assert _raw("wedlm_rope_logical", *a) == -1          # odd D
+    a = list(args); a[6] = 512
+    assert _raw("wedlm_rope_logical", *a) == -2          # D too large
+    a = list(args); a[0] = 7
+    assert _raw("wedlm_rope_logical", *a) == -2          # dtype
+
+
+def test_attn_validation_and_workspace():
+    # bf16 needs D = 128; page size 16 only; rows W*g <= 256
+    assert W.wedlm_window_attn_workspace_size(1, 1, 1, 16, 32, 8, 64, 16, 2048) == 0
+    base = [1, 1, 4, 16, 32, 8, 128, 16, 8196, 2049, 32768, 0.088] + [1] * 9 + [0, None]
+    assert _raw("wedlm_window_attn", *base) == -3        # split planned, no workspace
+    need = W.wedlm_window_attn_workspace_size(1, 1, 4, 16, 32, 8, 128, 16, 32768)
+    assert need > 0
+    a = list(base); a[6] = 64
+    assert _raw("wedlm_window_attn", *a) == -2
+    a = list(base); a[7] = 32
+    assert _raw("wedlm_window_attn", *a) == -2
+    a = list(base); a[9] = 10                             # table too short for max_prefix_len
+    assert _raw("wedlm_window_attn", *a) == -1
+    a = list(base); a[3] = 64; a[4] = 64; a[5] = 8       # 64 * 8 rows > 256
+    assert _raw("wedlm_window_attn", *a) == -2
+    # a c5-sized call needs no split workspace
+    assert W.wedlm_window_attn_workspace_size(1, 36, 16, 16, 32, 8, 128, 16, 1024) == 0
+
+
+def test_entropy_validation_and_workspace():
+    ws = W.wedlm_entropy_select_workspace_size(1, 16, 16, 151936)
+    assert ws > 0 and ws % 16 == 0
+    args = [1, 16, 16, 151936, 16, 1, 0.1, 1.0, 1, 1, 1, 1, 1, 1, 0, None]
+    assert _raw("wedlm_entropy_select", *args) == -3
+    a = list(args); a[8] = 2
+    assert _raw("wedlm_entropy_select", *a) == -1
+    a = list(args); a[7] = float("nan")
+    assert _raw("wedlm_entropy_select", *a) == -1
+
+
+def test_commit_validation():
+    args = [1, 36, 16, 16, 8, 128, 16, 100, 10] + [1] * 13 + [-1, None]
+    a = list(args); a[5] = 100
+    assert _raw("wedlm_commit_prefix", *a) == -2         # D not a multiple of 8
+    a = list(args); a[9] = None
+    assert _raw("wedlm_commit_prefix", *a) == -1
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_layout_round_trip_cpu(dtype):
+    g = torch.Generator().manual_seed(0)
+    nl, pages, Hkv, D, P = 2, 12, 3, 32, 16
+    kc, vc = layout.alloc_caches(nl, pages, Hkv, D, P, dtype, "cpu")
+    table = torch.randperm(pages, generator=g)[:5].to(torch.int32)
+    k = torch.randn(70, Hkv, D, generator=g).to(dtype)
+    v = torch.randn(70, Hkv, D, generator=g).to(dtype)
+    layout.write_rows(kc, vc, 1, table, 0, k[:40], v[:40])
+    layout.write_rows(kc, vc, 1, table, 40, k[40:], v[40:])
+    k2, v2 = layout.read_rows(kc, vc, 1, table, 0, 70)
+    assert torch.equal(k2, k) and torch.equal(v2, v)
+    assert kc[0].abs().sum() == 0
+    # K page layout: position t, dims 8j..8j+7 (bf16) are contiguous 16 bytes
+    X = layout.vec_elems(dtype)
+    t = 21
+    page, off = int(table[t // P]), t % P
+    assert torch.equal(kc[1, page, 2, 1, off], k[t, 2, X:2 * X])
+    assert torch.equal(vc[1, page, 2, :, off], v[t, 2])

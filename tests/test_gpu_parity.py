@@ -1,0 +1,99 @@
+"""GPU window step against the fp64 oracle, through the C ABI (needs an MI355X).
+
+Each workload's inputs are drawn by the seeded generator on the host, uploaded,
+run through the five entry points, and compared output by output with the
+oracle on identical values (bars in tests/parity.py).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from causal_streaming_decoding_amd import workloads as WL
+from causal_streaming_decoding_amd.synth import make_step_inputs
+
+from .parity import compare_step, gpu_step, oracle_step
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(wl, seed=None, layers=None, steps=1):
+    print(f"[parity] {wl.name} seed={seed}", flush=True)
+    inp = make_step_inputs(wl, seed=seed, steps=steps)
+    gpu = gpu_step(wl, inp)
+    ref = oracle_step(wl, inp, gpu=gpu, layers=layers)
+    rep = compare_step(wl, gpu, ref, layers=layers)
+    print(f"[parity] {wl.name}: {rep}", flush=True)
+    return rep
+
+
+def test_tiny_fp32():
+    _check(WL.TINY_FP32)
+
+
+def test_tiny_fp32_other_seeds():
+    for seed in (1, 2, 3):
+        _check(WL.TINY_FP32, seed=seed)
+
+
+def test_qwen3_8b_bs1_L2048():
+    _check(WL.QWEN3_8B_BS1)
+
+
+def test_qwen25_7b_bs16_ragged():
+    _check(WL.QWEN25_7B_RAGGED)
+
+
+def test_qwen3_8b_bs4_L32768():
+    _check(WL.QWEN3_8B_LONG)
+
+
+def _variant(base, **kw):
+    return dataclasses.replace(base, **kw)
+
+
+@pytest.mark.parametrize("name,wl", [
+    ("empty_prefix", _variant(WL.QWEN3_8B_BS1, name="edge_empty_prefix", prefix=("fixed", 0),
+                              V=4096, B=2)),
+    ("ragged_tail", _variant(WL.QWEN3_8B_BS1, name="edge_ragged_tail", prefix=("fixed", 77),
+                             V=4100, B=3)),
+    ("w64_max_rows", _variant(WL.QWEN3_8B_BS1, name="edge_w64", W=64, Hq=16, Hkv=4,
+                              prefix=("fixed", 300), V=2048, B=2)),
+    ("w1", _variant(WL.QWEN3_8B_BS1, name="edge_w1", W=1, prefix=("fixed", 33), V=1000, B=2,
+                    fill=("count", 1))),
+    ("all_filled", _variant(WL.QWEN3_8B_BS1, name="edge_all_filled", fill=("count", 16),
+                            prefix=("fixed", 129), V=3000, B=2)),
+    ("no_filled", _variant(WL.QWEN3_8B_BS1, name="edge_no_filled", fill=("none",),
+                           prefix=("fixed", 1000), V=3000, B=2)),
+    ("mha", _variant(WL.QWEN3_8B_BS1, name="edge_mha", Hq=8, Hkv=8, prefix=("fixed", 513),
+                     V=2000, B=2)),
+    ("gqa7_split_ragged", _variant(WL.QWEN25_7B_RAGGED, name="edge_gqa7_small", B=3,
+                                   prefix=("uniform", 1, 700), V=5000)),
+    ("low_entropy_threshold_fires", _variant(WL.QWEN3_8B_BS1, name="edge_low_entropy",
+                                             spike=("all_uniform", 16.0, 20.0), V=4096, B=4)),
+    ("tiny_fp32_multi_layer", _variant(WL.TINY_FP32, name="edge_fp32_layers", n_layers=3, B=3,
+                                       prefix=("uniform", 0, 45))),
+    ("stream_shape_short", _variant(WL.QWEN3_8B_STREAM, name="edge_stream_layers", n_layers=3,
+                                    B=4, V=3000, fill=("frac", 0.0, 1.0), steps=1)),
+])
+def test_edge_cases(name, wl):
+    _check(wl)
+
+
+def test_deterministic_bitwise():
+    wl = _variant(WL.QWEN25_7B_RAGGED, name="determinism", B=4, V=20000)
+    inp = make_step_inputs(wl)
+    a = gpu_step(wl, inp)
+    b = gpu_step(wl, inp, repeat=2)
+    for key in ("attn_out_phys", "entropy", "score", "q_phys", "tokens", "cache_slot"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_invalid_host_arguments_raise():
+    from causal_streaming_decoding_amd import wedlm as W
+    t = torch.zeros(16, dtype=torch.int32, device="cuda")
+    u = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(W.WedlmError):
+        W.wedlm_window_reorder(1, 65, u, t, t, t, t, t, t)

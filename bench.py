@@ -1,0 +1,195 @@
+"""Benchmark of the WeDLM streaming window step on one MI355X.
+
+Default workload: the Qwen3-8B-shaped streaming loop - 36 independent layers'
+paged KV caches, 16 sequences, initial prefix 1024, window 16, vocabulary
+151936, bf16 - run for --steps window steps (256 by default: the whole loop)
+after --warmup steps from the same start state. Every timed step is the whole
+path: reorder, RoPE at logical positions, window attention over all 36 layers,
+entropy/selection over the full vocabulary, commit and refill. Inputs are
+synthetic and already resident in HBM when timing starts.
+
+Prints one JSON line: window-steps/s (value), committed tokens/s, the HBM rate
+of the algorithmic bytes (KV prefix + window + logits) per step, the roofline
+of the dominant kernel (window attention) timed with HIP events on its own
+stream, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="qwen3_8b_36L_bs16_L1024_W16_stream256")
+    ap.add_argument("--cpu-baseline-steps", type=int, default=1,
+                    help="window steps of the oracle timed on the host (0 disables)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def step_bytes(wl, prefix_lens):
+    """Algorithmic HBM bytes of one window step, split by tensor (each byte once)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    kv = int(sum(prefix_lens)) * wl.n_layers * wl.Hkv * wl.D * 2 * e
+    win_in = wl.n_layers * wl.B * wl.W * (wl.Hq + 2 * wl.Hkv) * wl.D * e
+    attn_out = wl.n_layers * wl.B * wl.W * wl.Hq * wl.D * e
+    logits = wl.B * wl.W * wl.V * e
+    return {"kv": kv, "window": win_in, "attn_out": attn_out, "logits": logits}
+
+
+def cpu_baseline(wl, inp, host_steps):
+    """The oracle (never tuned) on the first steps of the same workload, on the host."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    kc = [[np.asarray(x, np.float64) for x in inp["k_cache"][l]] for l in range(wl.n_layers)]
+    vc = [[np.asarray(x, np.float64) for x in inp["v_cache"][l]] for l in range(wl.n_layers)]
+    t0 = time.perf_counter()
+    out = oracle.stream_loop(inp["filled"], inp["tokens"], inp["prefix_len"], kc, vc,
+                             inp["block_table"], len(host_steps), lambda s: host_steps[s], wl.theta,
+                             wl.lam, wl.tau, wl.page_size, wl.min_fill, wl.mask_id,
+                             attend=lambda s: range(wl.n_layers), track_layers=range(wl.n_layers))
+    dt = time.perf_counter() - t0
+    n = len(host_steps)
+    return {"value": n / dt, "unit": "window-steps/s", "cores": max(threads, 1),
+            "host_cpus": cores, "kind": "oracle",
+            "sample": f"first {n} window steps of the same workload, all {wl.n_layers} layers and "
+                      f"{wl.B} sequences (fp64 NumPy oracle, {dt:.1f} s, "
+                      f"{out['total_committed']} tokens committed)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from causal_streaming_decoding_amd import workloads as WL
+    from causal_streaming_decoding_amd.step import make_window_step, upload_step_inputs
+    from causal_streaming_decoding_amd.synth import make_step_inputs, stream_step_inputs, to_f64
+
+    wl = WL.BY_NAME[args.workload]
+    dev = "cuda:0"
+    K, Wm = args.steps, args.warmup
+    n_inputs = max(K, Wm, 1)
+    print(f"[bench] {wl.name}: building inputs ({n_inputs} steps)", file=sys.stderr, flush=True)
+    inp = make_step_inputs(wl, steps=n_inputs)
+    st, _, _, _, _, L0 = upload_step_inputs(wl, inp, dev)
+    step = make_window_step(wl, inp, dev, L0 + wl.W * n_inputs)
+    ins = [stream_step_inputs(wl, s, dev) for s in range(n_inputs)]
+    commit_log = torch.zeros((n_inputs, wl.B), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    snap = st.snapshot()
+
+    print(f"[bench] warmup {Wm} steps", file=sys.stderr, flush=True)
+    for s in range(Wm):
+        q, k, v, logits = ins[s]
+        step.run(st, q, k, v, logits, max_prefix_len=L0 + wl.W * s, commit_len=commit_log[s])
+    torch.cuda.synchronize()
+    st.restore(snap)
+    commit_log.zero_()
+    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(K)] for name in ("attn", "entropy")}
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for s in range(K):
+        q, k, v, logits = ins[s % n_inputs]
+        step.run(st, q, k, v, logits, max_prefix_len=L0 + wl.W * s, commit_len=commit_log[s],
+                 events={"attn": ev["attn"][s], "entropy": ev["entropy"][s]})
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    commits = commit_log[:K].cpu().numpy().astype(np.int64)
+    attn_ms = np.array([a.elapsed_time(b) for a, b in ev["attn"]])
+    ent_ms = np.array([a.elapsed_time(b) for a, b in ev["entropy"]])
+    L = np.asarray(inp["prefix_len"], np.int64).copy()
+    tot = {"kv": 0, "window": 0, "attn_out": 0, "logits": 0}
+    attn_bytes = 0
+    for s in range(K):
+        b = step_bytes(wl, L)
+        for key in tot:
+            tot[key] += b[key]
+        attn_bytes += b["kv"] + b["window"] + b["attn_out"]
+        L += commits[s]
+    total_bytes = sum(tot.values())
+    committed = int(commits.sum())
+    attn_gbps = attn_bytes / (attn_ms.sum() * 1e-3) / 1e9
+    ent_gbps = tot["logits"] / (ent_ms.sum() * 1e-3) / 1e9
+    both_gbps = (attn_bytes + tot["logits"]) / ((attn_ms.sum() + ent_ms.sum()) * 1e-3) / 1e9
+    step_gbps = total_bytes / elapsed / 1e9
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if args.cpu_baseline_steps > 0:
+        n = min(args.cpu_baseline_steps, n_inputs)
+        print(f"[bench] cpu baseline: oracle on {n} steps", file=sys.stderr, flush=True)
+        host_steps = [tuple(to_f64(t) for t in ins[s]) for s in range(n)]
+        cpu = cpu_baseline(wl, inp, host_steps)
+
+    result = {
+        "metric": "window-steps/s + committed tokens/s; KV+logits HBM GB/s as % of peak",
+        "value": K / elapsed,
+        "unit": "window-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": elapsed / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_layers": wl.n_layers, "batch": wl.B, "q_heads": wl.Hq,
+                   "kv_heads": wl.Hkv, "head_dim": wl.D, "window": wl.W, "vocab": wl.V,
+                   "initial_prefix": int(L0), "page_size": wl.page_size,
+                   "parallelism": "single GPU"},
+        "committed_tokens": committed,
+        "committed_tokens_per_s": committed / elapsed,
+        "step_hbm_gbps": step_gbps,
+        "step_hbm_frac": step_gbps / HBM_PEAK_GBPS,
+        "attn_plus_entropy_hbm_gbps": both_gbps,
+        "attn_plus_entropy_hbm_frac": both_gbps / HBM_PEAK_GBPS,
+        "entropy_hbm_gbps": ent_gbps,
+        "bytes_per_step_avg": {k_: v_ / K for k_, v_ in tot.items()},
+        "roofline": {"kernel": "k_window_attn_bf16", "bound": "hbm", "achieved": attn_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": attn_gbps / HBM_PEAK_GBPS,
+                     "traffic": None, "avg_launch_ms": float(attn_ms.mean()),
+                     "algorithmic_bytes_per_launch": attn_bytes / K},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

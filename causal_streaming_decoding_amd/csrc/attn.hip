@@ -18,6 +18,9 @@
 //   S^T (16 keys x 16 rows)  = K (16 x 128) . Q^T        v_mfma_f32_16x16x32_bf16
 //   O^T (16 dims x 16 rows) += V^T (16 x 32 keys) . P^T  v_mfma_f32_16x16x32_bf16
 //
+// P is split into a bf16 hi and lo part (two PV MFMAs) so that rounding the
+// probabilities costs no accuracy; the kernel is HBM-bound and has MFMA to spare.
+//
 // Cache page layouts make every access a contiguous, conflict-free vector:
 //   K page [Hkv][D/8][P][8]: the A operand of k-step s for lane l is the 16 B at
 //     s*1024 + 16 l (a wave reads 1 KB contiguous);
@@ -125,15 +128,27 @@ __device__ __forceinline__ void attend_stage(RowState& st, const bf16x8 (&qr)[4]
   rs += __shfl_xor(rs, 32, kWave);
   st.l = st.l * alpha + rs;
   st.m = m_new;
+  // P enters the PV product as a bf16 pair hi + lo (hi = RNE(p), lo = RNE(p - hi)),
+  // so the probabilities carry ~16 mantissa bits instead of bf16's 8.
+  f32x4 r0, r1;
   const bf16x8 pb = pack_p(p0, p1);
+  const u32x4 hi = __builtin_bit_cast(u32x4, pb);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    r0[2 * i] = p0[2 * i] - bf16_lo(hi[i]);
+    r0[2 * i + 1] = p0[2 * i + 1] - bf16_hi(hi[i]);
+    r1[2 * i] = p1[2 * i] - bf16_lo(hi[2 + i]);
+    r1[2 * i + 1] = p1[2 * i + 1] - bf16_hi(hi[2 + i]);
+  }
+  const bf16x8 pl = pack_p(r0, r1);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     const int off = (dt * 16 + col) * kPage + grp * 4;
     const u32x2 v0 = *reinterpret_cast<const u32x2*>(&sg.part[2][off]);
     const u32x2 v1 = *reinterpret_cast<const u32x2*>(&sg.part[3][off]);
-    const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
-    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb, st.o[dt] * alpha, 0,
-                                                        0, 0);
+    const bf16x8 va = as_bf16x8(u32x4{v0.x, v0.y, v1.x, v1.y});
+    f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.o[dt] * alpha, 0, 0, 0);
+    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc, 0, 0, 0);
   }
 }
 

@@ -112,16 +112,27 @@ class WindowStep:
                                self.cache_slot, self.mask_id, stream)
 
     def run(self, st, q, k, v, logits, max_prefix_len=None, commit_len=None, stream=None,
-            attn_events=None):
-        """One whole window step; ``attn_events`` = (start, end) events around attention."""
+            events=None):
+        """One whole window step.
+
+        ``events``: optional dict with "attn" and/or "entropy" -> (start, end)
+        torch.cuda.Event pairs recorded around those calls on ``stream``.
+        """
+        def mark(name, i):
+            if events is not None and name in events:
+                if stream is None:
+                    events[name][i].record()
+                else:
+                    events[name][i].record(stream)
+
         self.reorder(st, stream)
         self.rope(q, k, v, stream)
-        if attn_events is not None:
-            attn_events[0].record(stream)
+        mark("attn", 0)
         self.attn(st, max_prefix_len, stream)
-        if attn_events is not None:
-            attn_events[1].record(stream)
+        mark("attn", 1)
+        mark("entropy", 0)
         self.entropy_select(st, logits, stream)
+        mark("entropy", 1)
         self.commit(st, commit_len, stream)
 
 

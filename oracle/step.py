@@ -21,7 +21,7 @@ from .commit import commit_and_refill
 
 def window_step(filled, tokens, prefix_len, q, k, v, k_cache, v_cache, logits, block_table,
                 theta, lam, tau, page_size, min_fill=1, mask_id=-1, layers=None, scale=None,
-                override_selected=None):
+                override_selected=None, store=None):
     """One window step for a batch of sequences and n_layers independent layers.
 
     Args:
@@ -35,6 +35,11 @@ def window_step(filled, tokens, prefix_len, q, k, v, k_cache, v_cache, logits, b
       layers: layer indices whose attention is computed (default: all).
       override_selected: optional callable(b, selection_dict) -> [W] bool used
         to adopt another decision for a flagged near tie.
+      store: optional callable mapping a float64 array to the values a storage
+        type holds (e.g. one round-to-nearest-even to bf16). When given, the
+        rotated window rows are stored through it before they are attended to
+        and committed: the rows a bf16 cache receives are bf16 values. The
+        returned q_phys / k_phys / v_phys stay unrounded.
 
     Returns a dict of float64 / int64 numpy results (see keys below).
     """
@@ -75,12 +80,14 @@ def window_step(filled, tokens, prefix_len, q, k, v, k_cache, v_cache, logits, b
         v_phys[:, b] = np.asarray(v[:, b][:, perm], np.float64)
     out["q_phys"], out["k_phys"], out["v_phys"] = q_phys, k_phys, v_phys
 
+    keep = store if store is not None else (lambda x: x)
     attn = {}
     for layer in layers:
         o = np.empty((B, W, Hq, D), np.float64)
         for b in range(B):
-            o[b] = window_attention_reordered(q_phys[layer, b], k_phys[layer, b], v_phys[layer, b],
-                                              k_cache[layer][b], v_cache[layer][b], scale)
+            o[b] = window_attention_reordered(keep(q_phys[layer, b]), keep(k_phys[layer, b]),
+                                              keep(v_phys[layer, b]), k_cache[layer][b],
+                                              v_cache[layer][b], scale)
         attn[layer] = o
     out["attn_out_phys"] = attn
 
@@ -142,7 +149,7 @@ class _Growable:
 
 def stream_loop(filled, tokens, prefix_len, k_cache, v_cache, block_table, steps, inputs_for_step,
                 theta, lam, tau, page_size, min_fill=1, mask_id=-1, attend=None, track_layers=(),
-                override_selected=None, on_step=None):
+                override_selected=None, on_step=None, store=None):
     """Run the streaming decoder for ``steps`` window steps.
 
     Args:
@@ -155,6 +162,8 @@ def stream_loop(filled, tokens, prefix_len, k_cache, v_cache, block_table, steps
         they must be tracked layers.
       override_selected(s, b, selection) -> [W] bool for flagged near ties.
       on_step(s, result) is called after each step with window_step's result.
+      store: as in ``window_step``; committed rows enter the tracked caches
+        through it too.
 
     Returns dict with per-step commit lengths [steps, B], the final state and
     the total committed tokens.
@@ -165,8 +174,10 @@ def stream_loop(filled, tokens, prefix_len, k_cache, v_cache, block_table, steps
     track_layers = list(track_layers)
     caches = {}
     for layer in track_layers:
-        caches[layer] = ([_Growable(k_cache[layer][b], 4096) for b in range(len(prefix_len))],
-                         [_Growable(v_cache[layer][b], 4096) for b in range(len(prefix_len))])
+        caches[layer] = ([_Growable(k_cache[layer][b], len(k_cache[layer][b]) + 64)
+                          for b in range(len(prefix_len))],
+                         [_Growable(v_cache[layer][b], len(v_cache[layer][b]) + 64)
+                          for b in range(len(prefix_len))])
     commit_log = []
     for s in range(steps):
         q, k, v, logits = inputs_for_step(s)
@@ -181,13 +192,15 @@ def stream_loop(filled, tokens, prefix_len, k_cache, v_cache, block_table, steps
         if override_selected is not None:
             ov = (lambda b, sel, _s=s: override_selected(_s, b, sel))
         r = window_step(filled, tokens, prefix_len, q, k, v, kc, vc, logits, block_table, theta, lam,
-                        tau, page_size, min_fill, mask_id, layers=layers, override_selected=ov)
+                        tau, page_size, min_fill, mask_id, layers=layers, override_selected=ov,
+                        store=store)
+        keep = store if store is not None else (lambda x: x)
         for layer in track_layers:
             for b in range(len(prefix_len)):
                 c = int(r["commit_len"][b])
                 if c:
-                    caches[layer][0][b].append(r["k_phys"][layer, b, :c])
-                    caches[layer][1][b].append(r["v_phys"][layer, b, :c])
+                    caches[layer][0][b].append(keep(r["k_phys"][layer, b, :c]))
+                    caches[layer][1][b].append(keep(r["v_phys"][layer, b, :c]))
         commit_log.append(r["commit_len"].copy())
         if on_step is not None:
             on_step(s, r)

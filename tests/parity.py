@@ -20,6 +20,17 @@ ATTN_ATOL, ATTN_RTOL = 2e-3, 1e-2
 ENTROPY_ATOL = 1e-3
 
 
+def storage_rounding(dtype):
+    """The values a window row holds once stored in the workload's type (None: f32).
+
+    bf16: one round-to-nearest-even of the float64 value (torch's conversion).
+    """
+    if dtype != "bf16":
+        return None
+    return lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float64)).to(
+        torch.bfloat16).to(torch.float64).numpy()
+
+
 def stored_rotation_bound(ref, dtype):
     """Allowed |gpu - ref| for a value rounded once to the storage type (fp32 rotation)."""
     if dtype == "bf16":
@@ -71,7 +82,8 @@ def oracle_step(wl, inp, gpu=None, layers=None):
     return oracle.window_step(inp["filled"], inp["tokens"], inp["prefix_len"], inp["q"], inp["k"],
                               inp["v"], k_cache, v_cache, inp["logits"], inp["block_table"],
                               wl.theta, wl.lam, wl.tau, wl.page_size, wl.min_fill, wl.mask_id,
-                              layers=layers, override_selected=override)
+                              layers=layers, override_selected=override,
+                              store=storage_rounding(wl.dtype))
 
 
 def compare_step(wl, gpu, ref, layers=None):

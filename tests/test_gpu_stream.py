@@ -1,0 +1,117 @@
+"""Streaming loop at the full 36-layer, BS=16 Qwen3-8B shape against the oracle (GPU).
+
+The GPU runs every layer of every step; the oracle replays the same steps on
+host copies of the same inputs. Every step's reorder, entropies, argmax,
+selection, commit lengths, cache slots and window state are compared; the
+attention output and the committed cache rows are compared on sampled layers
+(the oracle tracks only those layers' caches). Flagged near ties adopt the
+GPU's choice, as in the single-step tests.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from causal_streaming_decoding_amd import layout
+from causal_streaming_decoding_amd import workloads as WL
+from causal_streaming_decoding_amd.step import make_window_step, upload_step_inputs
+from causal_streaming_decoding_amd.synth import make_step_inputs, stream_step_inputs, to_f64
+
+from .parity import ATTN_ATOL, ATTN_RTOL, ENTROPY_ATOL, stored_rotation_bound, storage_rounding
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_stream(wl, steps, sampled_layers, attend_steps):
+    print(f"[stream] {wl.name} steps={steps} layers={sampled_layers}", flush=True)
+    dev = "cuda"
+    inp = make_step_inputs(wl, steps=wl.steps)
+    st, _, _, _, _, L0 = upload_step_inputs(wl, inp, dev)
+    step = make_window_step(wl, inp, dev, L0 + wl.W * steps)
+    gpu_log, host_inputs = [], []
+    for s in range(steps):
+        q, k, v, logits = stream_step_inputs(wl, s, dev)
+        mpl = L0 + wl.W * s
+        step.run(st, q, k, v, logits, max_prefix_len=mpl)
+        torch.cuda.synchronize()
+        rec = {key: getattr(step, key).cpu().numpy() for key in
+               ("perm", "inv", "pos", "run_len", "entropy", "argmax", "selected", "commit_len",
+                "cache_slot")}
+        rec["tokens"] = st.tokens.cpu().numpy()
+        rec["filled"] = st.filled.cpu().numpy()
+        rec["prefix_len"] = st.prefix_len.cpu().numpy()
+        if s in attend_steps:
+            rec["attn"] = {i: to_f64(step.out_phys[l]) for i, l in enumerate(sampled_layers)}
+        gpu_log.append(rec)
+        host_inputs.append((to_f64(q[sampled_layers]), to_f64(k[sampled_layers]),
+                            to_f64(v[sampled_layers]), to_f64(logits)))
+    # committed rows of the sampled layers, read back from the pages
+    final_len = st.prefix_len.cpu().numpy()
+    gpu_rows = {}
+    for i, l in enumerate(sampled_layers):
+        for b in range(wl.B):
+            n = int(final_len[b]) - int(inp["prefix_len"][b])
+            kr, vr = layout.read_rows(st.k_cache, st.v_cache, l, st.block_table[b].cpu(),
+                                      int(inp["prefix_len"][b]), n)
+            gpu_rows[(i, b)] = (to_f64(kr), to_f64(vr))
+
+    ref_log = []
+    kc = [[np.asarray(x, np.float64) for x in inp["k_cache"][l]] for l in sampled_layers]
+    vc = [[np.asarray(x, np.float64) for x in inp["v_cache"][l]] for l in sampled_layers]
+    out = oracle.stream_loop(
+        inp["filled"], inp["tokens"], inp["prefix_len"], kc, vc, inp["block_table"], steps,
+        lambda s: host_inputs[s], wl.theta, wl.lam, wl.tau, wl.page_size, wl.min_fill, wl.mask_id,
+        attend=lambda s: range(len(sampled_layers)) if s in attend_steps else [],
+        track_layers=range(len(sampled_layers)),
+        override_selected=lambda s, b, sel: gpu_log[s]["selected"][b].astype(bool),
+        on_step=lambda s, r: ref_log.append(r), store=storage_rounding(wl.dtype))
+
+    flags = 0
+    for s in range(steps):
+        g, r = gpu_log[s], ref_log[s]
+        assert np.array_equal(g["perm"], r["perm"]), ("perm", s)
+        assert np.array_equal(g["run_len"], r["run"]), ("run", s)
+        assert (np.abs(g["entropy"] - r["entropy"]) <= ENTROPY_ATOL).all(), ("entropy", s)
+        assert np.array_equal(g["argmax"], r["argmax"]), ("argmax", s)
+        flagged = {b for b, _, _ in r["flags"]}
+        flags += len(r["flags"])
+        for b in range(wl.B):
+            if b not in flagged:
+                assert np.array_equal(g["selected"][b].astype(bool), r["selected"][b]), ("sel", s, b)
+        assert np.array_equal(g["commit_len"], r["commit_len"]), ("commit_len", s)
+        assert np.array_equal(g["cache_slot"], r["cache_slot"]), ("cache_slot", s)
+        assert np.array_equal(g["tokens"], r["tokens"]), ("tokens", s)
+        assert np.array_equal(g["filled"].astype(bool), r["filled"]), ("filled", s)
+        assert np.array_equal(g["prefix_len"], r["prefix_len"]), ("prefix_len", s)
+        if "attn" in g:
+            for i in g["attn"]:
+                err = np.abs(g["attn"][i] - r["attn_out_phys"][i])
+                ok = err <= ATTN_ATOL + ATTN_RTOL * np.abs(r["attn_out_phys"][i])
+                assert ok.all(), ("attn", s, i, float(err.max()))
+    for (i, b), (kr, vr) in gpu_rows.items():
+        L = int(inp["prefix_len"][b])
+        ref_k = out["caches"][i][0][b][L:]
+        ref_v = out["caches"][i][1][b][L:]
+        assert kr.shape == ref_k.shape
+        assert (np.abs(kr - ref_k) <= stored_rotation_bound(ref_k, wl.dtype)).all(), ("cache k", i, b)
+        assert np.array_equal(vr, ref_v), ("cache v", i, b)
+    total = int(sum(g["commit_len"].sum() for g in gpu_log))
+    longest = int(max(g["commit_len"].max() for g in gpu_log))
+    print(f"[stream] {wl.name}: {steps} steps ok, committed {total}, longest commit {longest}, "
+          f"flags {flags}", flush=True)
+    return total, longest
+
+
+def test_stream_full_shape_first_steps():
+    _run_stream(WL.QWEN3_8B_STREAM, steps=12, sampled_layers=[0, 17, 35], attend_steps={0, 5, 11})
+
+
+def test_stream_low_entropy_multi_commit():
+    # big spikes make the threshold fire, so runs longer than one token are committed
+    wl = dataclasses.replace(WL.QWEN3_8B_STREAM, name="stream_low_entropy", n_layers=4, B=8,
+                             V=30000, spike=("prob", 0.9, 16.0, 20.0))
+    _, longest = _run_stream(wl, steps=24, sampled_layers=[0, 3], attend_steps={3, 23})
+    assert longest > 1  # multi-token commits happened

@@ -38,6 +38,17 @@ def stored_rotation_bound(ref, dtype):
     return np.abs(ref) * 1e-6 + 1e-6
 
 
+def stored_pair_bound(ref_stored, dtype):
+    """Allowed |a - b| between two values each rounded once to the storage type.
+
+    Both come from nearly equal unrounded values, so they are equal or adjacent:
+    one bf16 ulp (2^-7 relative) at most.
+    """
+    if dtype == "bf16":
+        return np.abs(ref_stored) * 2.0 ** -7 + 1e-6
+    return np.abs(ref_stored) * 2e-6 + 1e-6
+
+
 def gpu_step(wl, inp, device="cuda", repeat=1):
     """Run the step on the GPU; returns host numpy copies of every output."""
     st, q, k, v, logits, mpl = upload_step_inputs(wl, inp, device)

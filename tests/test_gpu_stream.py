@@ -20,7 +20,7 @@ from causal_streaming_decoding_amd import workloads as WL
 from causal_streaming_decoding_amd.step import make_window_step, upload_step_inputs
 from causal_streaming_decoding_amd.synth import make_step_inputs, stream_step_inputs, to_f64
 
-from .parity import ATTN_ATOL, ATTN_RTOL, ENTROPY_ATOL, stored_rotation_bound, storage_rounding
+from .parity import ATTN_ATOL, ATTN_RTOL, ENTROPY_ATOL, stored_pair_bound, storage_rounding
 
 pytestmark = pytest.mark.gpu
 
@@ -96,7 +96,8 @@ def _run_stream(wl, steps, sampled_layers, attend_steps):
         ref_k = out["caches"][i][0][b][L:]
         ref_v = out["caches"][i][1][b][L:]
         assert kr.shape == ref_k.shape
-        assert (np.abs(kr - ref_k) <= stored_rotation_bound(ref_k, wl.dtype)).all(), ("cache k", i, b)
+        # the oracle's cache holds its rows as stored (rounded once), like the GPU's
+        assert (np.abs(kr - ref_k) <= stored_pair_bound(ref_k, wl.dtype)).all(), ("cache k", i, b)
         assert np.array_equal(vr, ref_v), ("cache v", i, b)
     total = int(sum(g["commit_len"].sum() for g in gpu_log))
     longest = int(max(g["commit_len"].max() for g in gpu_log))

@@ -51,6 +51,7 @@ constexpr int kPage = 16;
 constexpr int kMaxRows = 256;                    // M = W*g rows: at most 16 wavefronts
 constexpr int kChunkVecs = 4 * 256;              // 16-byte vectors per page pair (K0 K1 V0 V1)
 constexpr int kPartElems = 2048;                 // bf16 elements of one 4 KB page part
+constexpr int kStages = 3;                       // LDS ring depth (16 KB per stage)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnArgs {
@@ -152,41 +153,91 @@ __device__ __forceinline__ void attend_stage(RowState& st, const bf16x8 (&qr)[4]
   }
 }
 
-// Page-pair staging: thread tid moves vectors tid, tid + NT, ... of the 1024
-// 16-byte vectors of a stage (parts: K of pages pg, pg+1, then V of pg, pg+1).
-template <int NT, int VPT>
-__device__ __forceinline__ void stage_gload(u32x4 (&stg)[VPT], int tid, int pg, int pg_end,
-                                            const int32_t* bt, int num_pages, int Hkv, int kvh,
-                                            const uint16_t* kc_layer, const uint16_t* vc_layer) {
+// Asynchronous page-pair staging: global -> LDS DMA (global_load_lds_dwordx4).
+// Each instruction moves 64 lanes x 16 B = 1 KB: lane l's 16 bytes land at
+// M0 + 16 l in LDS. A stage is 1024 vectors (K of pages pg, pg+1, then V of
+// pg, pg+1); wavefront w issues instructions for vectors (i*NW + w)*64 .. +63.
+// The DMA is issued from inline asm so that the compiler does not add its own
+// conservative vmcnt waits before every LDS read of the ring; the waits are
+// explicit (stage_wait_barrier) and counted per thread in issue order.
+// M0 is a reserved register: it is saved and restored around the DMA.
+__device__ __forceinline__ void lds_dma_16(const void* gptr, uint32_t lds_byte_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(lds_byte_addr)
+      : "memory");
+}
+
+// Two wave-uniform block-table entries through the scalar cache (read only).
+// Scalar loads count against lgkmcnt, not vmcnt, so reading the table never
+// waits for the DMAs in flight.
+__device__ __forceinline__ void load_page_ids(const int32_t* p0, const int32_t* p1, int& a,
+                                              int& b) {
+  const uint64_t u0 = reinterpret_cast<uint64_t>(p0), u1 = reinterpret_cast<uint64_t>(p1);
+  const uint64_t s0 = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(
+                           static_cast<uint32_t>(u0 >> 32))) << 32) |
+                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u0)));
+  const uint64_t s1 = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(
+                           static_cast<uint32_t>(u1 >> 32))) << 32) |
+                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u1)));
+  asm volatile(
+      "s_load_dword %0, %2, 0x0\n\t"
+      "s_load_dword %1, %3, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=s"(a), "=s"(b)
+      : "s"(s0), "s"(s1)
+      : "memory");
+}
+
+template <int NW>
+__device__ __forceinline__ void stage_dma(Stage& sg, int wave, int lane, int pg, int pg_end,
+                                          const int32_t* bt, int num_pages, int Hkv, int kvh,
+                                          const uint16_t* kc_layer, const uint16_t* vc_layer) {
   constexpr size_t page_elems = static_cast<size_t>(kHeadDim) * kPage;
+  constexpr int kInstr = kChunkVecs / (kWave * NW);  // DMA instructions per wave per stage
+  // generic -> LDS address space: the 32-bit LDS byte address of the stage
+  const uint32_t lds_base = static_cast<uint32_t>(
+      reinterpret_cast<size_t>((__attribute__((address_space(3))) char*)(&sg)));
+  // page ids are wave-uniform: keep them in SGPRs so the block table is read
+  // with scalar loads, which do not count against vmcnt (the DMA counter)
+  const int pg0 = __builtin_amdgcn_readfirstlane(pg);
+  const int pg1 = __builtin_amdgcn_readfirstlane(min(pg + 1, pg_end - 1));
+  int raw0, raw1;
+  load_page_ids(bt + pg0, bt + pg1, raw0, raw1);
+  const int pid0 = min(max(raw0, 0), num_pages - 1);
+  const int pid1 = min(max(raw1, 0), num_pages - 1);
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int idx = tid + i * NT;
-    const int part = idx >> 8;
-    const int page = min(pg + (part & 1), pg_end - 1);
-    const int pid = min(max(bt[page], 0), num_pages - 1);
+  for (int i = 0; i < kInstr; ++i) {
+    const int v0 = (i * NW + wave) * kWave;  // first vector of this instruction (wave-uniform)
+    const int part = v0 >> 8;                // 0,1: K of pages pg, pg+1; 2,3: V of pg, pg+1
+    const int pid = (part & 1) ? pid1 : pid0;
     const uint16_t* base =
         (part < 2 ? kc_layer : vc_layer) + (static_cast<size_t>(pid) * Hkv + kvh) * page_elems;
-    stg[i] = *reinterpret_cast<const u32x4*>(base + (idx & 255) * 8);
+    const uint16_t* src = base + ((v0 & 255) + lane) * 8;
+    lds_dma_16(src, __builtin_amdgcn_readfirstlane(lds_base + v0 * 16));
   }
 }
 
-template <int NT, int VPT>
-__device__ __forceinline__ void stage_lwrite(const u32x4 (&stg)[VPT], Stage& sg, int tid) {
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int idx = tid + i * NT;
-    *reinterpret_cast<u32x4*>(&sg.part[idx >> 8][(idx & 255) * 8]) = stg[i];
-  }
+// Wait until at most N of this thread's vector-memory operations are in
+// flight, then synchronise the workgroup. The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void stage_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-// NW wavefronts per workgroup; each thread moves VPT 16-byte vectors per stage.
+// NW wavefronts per workgroup, one 16-row tile each.
 template <int NW>
 __global__ void __launch_bounds__(kWave * NW)
 k_window_attn_bf16(AttnArgs a) {
   constexpr int NT = kWave * NW;
-  constexpr int VPT = kChunkVecs / NT;
-  __shared__ Stage stage[2];
+  constexpr int kDma = kChunkVecs / NT;  // DMA instructions per thread per stage
+  __shared__ Stage stage[kStages];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -224,6 +275,10 @@ k_window_attn_bf16(AttnArgs a) {
       if (row_ok) z = *reinterpret_cast<const u32x4*>(qrow + s * 32 + grp * 8);
       qr[s] = as_bf16x8(z);
     }
+    // Retire the query loads here, once: the registers are re-defined by this
+    // asm, so the compiler does not re-wait on vmcnt (which also counts the
+    // ring's DMAs) before every MFMA that reads them inside the loop.
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(qr[0]), "+v"(qr[1]), "+v"(qr[2]), "+v"(qr[3]));
   }
   RowState st;
   st.m = -INFINITY;
@@ -236,30 +291,34 @@ k_window_attn_bf16(AttnArgs a) {
   const int32_t* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
   const uint16_t* kc_layer = a.kc + static_cast<size_t>(layer) * a.cache_layer_stride;
   const uint16_t* vc_layer = a.vc + static_cast<size_t>(layer) * a.cache_layer_stride;
+  // Ring of kStages stages: page pairs i+1 and i+2 are in flight while pair i
+  // is computed. Before computing pair i each thread waits for its own DMAs of
+  // pair i (only pair i+1's may still be outstanding), then the barrier makes
+  // every wave's DMAs visible and guarantees that pair i-1's stage - the one
+  // refilled next - is no longer being read.
   const int nch = (pg_end - pg_begin + 1) / 2;
-  if (nch > 0) {
-    u32x4 stg[VPT];
-    stage_gload<NT, VPT>(stg, tid, pg_begin, pg_end, bt, a.num_pages, a.Hkv, kvh, kc_layer,
-                         vc_layer);
-    stage_lwrite<NT, VPT>(stg, stage[0], tid);
-  }
-  __syncthreads();
+  if (nch > 0)
+    stage_dma<NW>(stage[0], wave, lane, pg_begin, pg_end, bt, a.num_pages, a.Hkv, kvh, kc_layer,
+                  vc_layer);
+  if (nch > 1)
+    stage_dma<NW>(stage[1], wave, lane, pg_begin + 2, pg_end, bt, a.num_pages, a.Hkv, kvh,
+                  kc_layer, vc_layer);
   for (int i = 0; i < nch; ++i) {
     const int pg = pg_begin + 2 * i;
-    const bool more = i + 1 < nch;
-    // the next page pair is in flight while this one is computed
-    u32x4 stg[VPT];
-    if (more)
-      stage_gload<NT, VPT>(stg, tid, pg + 2, pg_end, bt, a.num_pages, a.Hkv, kvh, kc_layer,
-                           vc_layer);
+    if (i + 1 < nch)
+      stage_wait_barrier<kDma>();
+    else
+      stage_wait_barrier<0>();
+    if (i + 2 < nch)
+      stage_dma<NW>(stage[(i + 2) % kStages], wave, lane, pg + 4, pg_end, bt, a.num_pages, a.Hkv,
+                    kvh, kc_layer, vc_layer);
     if (computes) {
       // keys pg*16 .. pg*16+31 are valid below L and below the split's end
       const int lim = min(L, pg_end * kPage) - pg * kPage;
-      attend_stage(st, qr, stage[i & 1], lane, lim, a.scale_log2);
+      attend_stage(st, qr, stage[i % kStages], lane, lim, a.scale_log2);
     }
-    if (more) stage_lwrite<NT, VPT>(stg, stage[(i + 1) & 1], tid);
-    __syncthreads();
   }
+  __syncthreads();  // the window reuses stage 0
 
   // ---- the window's own keys, causal over physical order -------------------
   if (with_window) {

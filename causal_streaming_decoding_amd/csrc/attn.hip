@@ -9,11 +9,10 @@
 // bf16 path (D = 128, page P = 16). One workgroup per (layer, sequence, kv
 // head, key-range split); each of its wavefronts owns one 16-row tile of the
 // group's M = W*g query rows (physical row p, query head h of the group). The
-// group's key pages stream through a double-buffered LDS ring, two pages
-// (32 keys, 16 KB of K and V) per stage: every thread loads a few 16-byte
-// vectors of the next page pair into registers while the waves compute the
-// current one from LDS, then writes them to the other stage (one barrier per
-// page pair). Each key byte is read from HBM once per workgroup.
+// group's key pages stream through a 3-stage LDS ring, two pages (32 keys,
+// 16 KB of K and V) per stage, filled by global->LDS DMA: two page pairs are in
+// flight while the waves compute the third (one barrier per page pair). Each
+// key byte is read from HBM once per workgroup.
 //
 //   S^T (16 keys x 16 rows)  = K (16 x 128) . Q^T        v_mfma_f32_16x16x32_bf16
 //   O^T (16 dims x 16 rows) += V^T (16 x 32 keys) . P^T  v_mfma_f32_16x16x32_bf16
@@ -21,15 +20,15 @@
 // P is split into a bf16 hi and lo part (two PV MFMAs) so that rounding the
 // probabilities costs no accuracy; the kernel is HBM-bound and has MFMA to spare.
 //
-// Cache page layouts make every access a contiguous, conflict-free vector:
-//   K page [Hkv][D/8][P][8]: the A operand of k-step s for lane l is the 16 B at
-//     s*1024 + 16 l (a wave reads 1 KB contiguous);
-//   V page [Hkv][D][P]: lane l reads 8 B holding 4 consecutive keys of one
-//     dimension (a wave reads 512 B contiguous).
-// S^T's accumulator layout (a lane holds 4 keys of one row) is the B operand
-// layout P^T needs, so probabilities feed the second MFMA with no shuffle: the
-// 8 k-values of a lane are keys 4q..4q+3 of the first page and the same of the
-// second page, and V^T is read in the same key order. Row max and row sum need
+// Cache page layouts (16-byte vectors, contiguous per wave instruction):
+//   K page [Hkv][D/8][P][8]: 16-byte slices of the 16 keys side by side, so a
+//     page of one kv head is 4 KB contiguous and a DMA instruction moves 1 KB;
+//   V page [Hkv][D][P]: each value dimension's 16 keys contiguous (32 B), so a
+//     lane reads 8 consecutive keys of one dimension as one 16-byte vector.
+// The score MFMAs take their key rows in the order that leaves 8 consecutive
+// keys of one query row in each lane, which is both the P^T operand layout of
+// the PV product and the key order of that 16-byte V^T read: probabilities go
+// from the softmax to the second MFMA with no shuffle. Row max and row sum need
 // two cross-lane steps (the 4 lanes holding one row).
 //
 // When there are too few groups to fill the GPU, a group's pages are split
@@ -90,50 +89,83 @@ struct RowState {
   float l;     // running sum of probabilities
 };
 
-// Scores, online softmax and PV for one stage. Key kk of the stage (0..31) is
-// visible for this lane's row iff kk < lim.
+// Scores, online softmax and PV for one stage.
+//
+// Key order: the two score MFMAs of a stage take their 16 A-operand rows as
+// keys {8q + i} and {8q + 4 + i} (q = 0..3, i = 0..3) of the 32-key stage, so
+// the lane holding output rows 4q..4q+3 of both holds the 8 consecutive keys
+// 8q..8q+7 of its query row. Those 8 keys are one page's 16-byte run of a
+// value dimension in the transposed V page, so the V^T operand of the PV
+// product is a single 16-byte LDS read, and the probabilities are already in
+// the P^T operand layout.
+//
+// Softmax: scores are scaled into log2 units inside one FMA. The running
+// reference max m is raised only when a row's new max exceeds it by more than
+// kRescaleLog2 (then O and l are rescaled by 2^(m_old - m_new)); otherwise
+// probabilities are taken against the stale m and stay below 2^kRescaleLog2.
+// Numerator and denominator share the same reference, so the result is exact
+// up to rounding; the rescale runs only in the rare chunks that need it.
+constexpr float kRescaleLog2 = 8.f;
+
 __device__ __forceinline__ void attend_stage(RowState& st, const bf16x8 (&qr)[4], const Stage& sg,
                                              int lane, int lim, float scale_log2) {
   const int col = lane & 15, grp = lane >> 4;
+  // A-operand key of this lane's row in the two score MFMAs
+  const int ka = (col >> 2) * 8 + (col & 3);  // 0..3, 8..11, 16..19, 24..27
+  const int pa = ka >> 4, kpa = ka & 15;      // page and key in page (kb = ka + 4, same page)
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const u32x4 k0 = *reinterpret_cast<const u32x4*>(&sg.part[0][s * 512 + lane * 8]);
-    const u32x4 k1 = *reinterpret_cast<const u32x4*>(&sg.part[1][s * 512 + lane * 8]);
+    const int base_e = ((4 * s + grp) * kPage + kpa) * 8;
+    const u32x4 k0 = *reinterpret_cast<const u32x4*>(&sg.part[pa][base_e]);
+    const u32x4 k1 = *reinterpret_cast<const u32x4*>(&sg.part[pa][base_e + 4 * 8]);
     s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), qr[s], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), qr[s], s1, 0, 0, 0);
   }
+  // s0[i] is key 8*grp + i, s1[i] is key 8*grp + 4 + i of the stage
   float x[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    x[i] = grp * 4 + i < lim ? s0[i] * scale_log2 : -INFINITY;
-    x[4 + i] = 16 + grp * 4 + i < lim ? s1[i] * scale_log2 : -INFINITY;
+    x[i] = s0[i];
+    x[4 + i] = s1[i];
+  }
+  if (lim < 32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (grp * 8 + i >= lim) x[i] = -INFINITY;
   }
   float mx = x[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
   mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
   mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-  const float m_new = fmaxf(st.m, mx);
-  const float base = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - base);
+  const float mc = mx * scale_log2;  // candidate max in log2 units (-inf if no visible key)
+  const bool raise = mc > st.m + kRescaleLog2;
+  if (__ballot(raise)) {
+    const float m_new = raise ? mc : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 when st.m = -inf
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
+    st.m = m_new;
+  }
+  const float base = st.m == -INFINITY ? 0.f : st.m;
   f32x4 p0, p1;
   float rs = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    p0[i] = __builtin_amdgcn_exp2f(x[i] - base);
-    p1[i] = __builtin_amdgcn_exp2f(x[4 + i] - base);
+    p0[i] = __builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -base));
+    p1[i] = __builtin_amdgcn_exp2f(fmaf(x[4 + i], scale_log2, -base));
     rs += p0[i] + p1[i];
   }
   rs += __shfl_xor(rs, 16, kWave);
   rs += __shfl_xor(rs, 32, kWave);
-  st.l = st.l * alpha + rs;
-  st.m = m_new;
+  st.l += rs;
   // P enters the PV product as a bf16 pair hi + lo (hi = RNE(p), lo = RNE(p - hi)),
   // so the probabilities carry ~16 mantissa bits instead of bf16's 8.
-  f32x4 r0, r1;
   const bf16x8 pb = pack_p(p0, p1);
   const u32x4 hi = __builtin_bit_cast(u32x4, pb);
+  f32x4 r0, r1;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     r0[2 * i] = p0[2 * i] - bf16_lo(hi[i]);
@@ -142,13 +174,13 @@ __device__ __forceinline__ void attend_stage(RowState& st, const bf16x8 (&qr)[4]
     r1[2 * i + 1] = p1[2 * i + 1] - bf16_hi(hi[2 + i]);
   }
   const bf16x8 pl = pack_p(r0, r1);
+  // V^T operand: dimension dt*16 + col, keys 8*grp .. 8*grp+7 = page grp/2, keys 8*(grp&1)..
+  const uint16_t* vpart = sg.part[2 + (grp >> 1)];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    const int off = (dt * 16 + col) * kPage + grp * 4;
-    const u32x2 v0 = *reinterpret_cast<const u32x2*>(&sg.part[2][off]);
-    const u32x2 v1 = *reinterpret_cast<const u32x2*>(&sg.part[3][off]);
-    const bf16x8 va = as_bf16x8(u32x4{v0.x, v0.y, v1.x, v1.y});
-    f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.o[dt] * alpha, 0, 0, 0);
+    const bf16x8 va =
+        as_bf16x8(*reinterpret_cast<const u32x4*>(&vpart[(dt * 16 + col) * kPage + (grp & 1) * 8]));
+    f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.o[dt], 0, 0, 0);
     st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc, 0, 0, 0);
   }
 }
@@ -196,8 +228,9 @@ __device__ __forceinline__ void load_page_ids(const int32_t* p0, const int32_t* 
 
 template <int NW>
 __device__ __forceinline__ void stage_dma(Stage& sg, int wave, int lane, int pg, int pg_end,
-                                          const int32_t* bt, int num_pages, int Hkv, int kvh,
-                                          const uint16_t* kc_layer, const uint16_t* vc_layer) {
+                                          const int32_t* bt, int max_pages, int num_pages, int Hkv,
+                                          int kvh, const uint16_t* kc_layer,
+                                          const uint16_t* vc_layer) {
   constexpr size_t page_elems = static_cast<size_t>(kHeadDim) * kPage;
   constexpr int kInstr = kChunkVecs / (kWave * NW);  // DMA instructions per wave per stage
   // generic -> LDS address space: the 32-bit LDS byte address of the stage
@@ -205,8 +238,8 @@ __device__ __forceinline__ void stage_dma(Stage& sg, int wave, int lane, int pg,
       reinterpret_cast<size_t>((__attribute__((address_space(3))) char*)(&sg)));
   // page ids are wave-uniform: keep them in SGPRs so the block table is read
   // with scalar loads, which do not count against vmcnt (the DMA counter)
-  const int pg0 = __builtin_amdgcn_readfirstlane(pg);
-  const int pg1 = __builtin_amdgcn_readfirstlane(min(pg + 1, pg_end - 1));
+  const int pg0 = __builtin_amdgcn_readfirstlane(min(max(pg, 0), max_pages - 1));
+  const int pg1 = __builtin_amdgcn_readfirstlane(min(max(min(pg + 1, pg_end - 1), 0), max_pages - 1));
   int raw0, raw1;
   load_page_ids(bt + pg0, bt + pg1, raw0, raw1);
   const int pid0 = min(max(raw0, 0), num_pages - 1);
@@ -261,24 +294,23 @@ k_window_attn_bf16(AttnArgs a) {
   const bool with_window = split == a.n_splits - 1;
 
   // ---- this wave's 16 query rows (B operand of S^T = K Q^T) ---------------
+  // Loaded through asm, before the first page pairs' DMAs, and retired below
+  // with an explicit vmcnt that lets those DMAs stay in flight. (Rows past M
+  // read row 0 of the group - valid memory - and are never stored.)
   const size_t lb = static_cast<size_t>(layer) * a.B + b;
   const int row = wave * 16 + col;
   const bool row_ok = row < a.M;
   const int prow = row / a.g, hh = row % a.g;
-  bf16x8 qr[4];
+  u32x4 qv[4];
   {
     const uint16_t* qrow =
         a.q + ((lb * a.W + (row_ok ? prow : 0)) * a.Hq + kvh * a.g + (row_ok ? hh : 0)) * kHeadDim;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (row_ok) z = *reinterpret_cast<const u32x4*>(qrow + s * 32 + grp * 8);
-      qr[s] = as_bf16x8(z);
-    }
-    // Retire the query loads here, once: the registers are re-defined by this
-    // asm, so the compiler does not re-wait on vmcnt (which also counts the
-    // ring's DMAs) before every MFMA that reads them inside the loop.
-    asm volatile("s_waitcnt vmcnt(0)" : "+v"(qr[0]), "+v"(qr[1]), "+v"(qr[2]), "+v"(qr[3]));
+    for (int s = 0; s < 4; ++s)
+      asm volatile("global_load_dwordx4 %0, %1, off"
+                   : "=v"(qv[s])
+                   : "v"(qrow + s * 32 + grp * 8)
+                   : "memory");
   }
   RowState st;
   st.m = -INFINITY;
@@ -297,12 +329,20 @@ k_window_attn_bf16(AttnArgs a) {
   // every wave's DMAs visible and guarantees that pair i-1's stage - the one
   // refilled next - is no longer being read.
   const int nch = (pg_end - pg_begin + 1) / 2;
-  if (nch > 0)
-    stage_dma<NW>(stage[0], wave, lane, pg_begin, pg_end, bt, a.num_pages, a.Hkv, kvh, kc_layer,
-                  vc_layer);
-  if (nch > 1)
-    stage_dma<NW>(stage[1], wave, lane, pg_begin + 2, pg_end, bt, a.num_pages, a.Hkv, kvh,
-                  kc_layer, vc_layer);
+  // The first two stages are always requested (page ids clamped to valid
+  // entries when the split has fewer pairs; unused stages are simply not read),
+  // so the number of DMAs in flight here is a compile-time constant.
+  stage_dma<NW>(stage[0], wave, lane, pg_begin, pg_end, bt, a.max_pages, a.num_pages, a.Hkv, kvh,
+                kc_layer, vc_layer);
+  stage_dma<NW>(stage[1], wave, lane, pg_begin + 2, pg_end, bt, a.max_pages, a.num_pages, a.Hkv,
+                kvh, kc_layer, vc_layer);
+  // Retire the query loads: only the 2*kDma DMAs issued after them may remain.
+  asm volatile("s_waitcnt vmcnt(%4)"
+               : "+v"(qv[0]), "+v"(qv[1]), "+v"(qv[2]), "+v"(qv[3])
+               : "n"(2 * kDma));
+  bf16x8 qr[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qr[s] = as_bf16x8(qv[s]);
   for (int i = 0; i < nch; ++i) {
     const int pg = pg_begin + 2 * i;
     if (i + 1 < nch)
@@ -310,8 +350,8 @@ k_window_attn_bf16(AttnArgs a) {
     else
       stage_wait_barrier<0>();
     if (i + 2 < nch)
-      stage_dma<NW>(stage[(i + 2) % kStages], wave, lane, pg + 4, pg_end, bt, a.num_pages, a.Hkv,
-                    kvh, kc_layer, vc_layer);
+      stage_dma<NW>(stage[(i + 2) % kStages], wave, lane, pg + 4, pg_end, bt, a.max_pages,
+                    a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
     if (computes) {
       // keys pg*16 .. pg*16+31 are valid below L and below the split's end
       const int lim = min(L, pg_end * kPage) - pg * kPage;

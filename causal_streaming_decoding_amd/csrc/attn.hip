@@ -44,14 +44,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
-constexpr int kMaxRows = 256;                    // M = W*g rows: at most 16 wavefronts
-constexpr int kChunkVecs = 4 * 256;              // 16-byte vectors per page pair (K0 K1 V0 V1)
-constexpr int kPartElems = 2048;                 // bf16 elements of one 4 KB page part
-constexpr int kStages = 3;                       // LDS ring depth (16 KB per stage)
+constexpr int kMaxRows = 256;       // M = W*g rows: at most 16 wavefronts
+constexpr int kPageVecs = 512;      // 16-byte vectors of one page of one kv head (K 4 KB + V 4 KB)
+constexpr int kPartElems = 2048;    // bf16 elements of one 4 KB page part
+constexpr int kStages = 3;          // LDS ring depth (one 8 KB page per stage)
+constexpr int kAhead = kStages - 1; // pages in flight while one is computed
+constexpr int kWavesPerSimd = 5;    // register budget: 5 wavefronts per SIMD, 5 workgroups per CU
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleLog2 = 8.f;
 
 struct AttnArgs {
   const uint16_t* q;   // [nl][B][W][Hq][D] physical order, rotated
@@ -72,71 +76,70 @@ struct AttnArgs {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-__device__ __forceinline__ bf16x8 pack_p(const f32x4& a, const f32x4& b) {
-  const u32x4 u = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
-                   pack_bf16x2(b[2], b[3])};
-  return as_bf16x8(u);
-}
-
-// One 32-key stage in LDS: K page 0, K page 1, V page 0, V page 1 (4 KB each).
+// One stage of the ring: one page of one kv head in the cache layout.
 struct Stage {
-  uint16_t part[4][kPartElems];
+  uint16_t k[kPartElems];  // [D/8][16 keys][8]
+  uint16_t v[kPartElems];  // [D][16 keys]
 };
 
 struct RowState {
   f32x4 o[8];  // O^T accumulators per 16-dim tile: lane holds dims 4q..4q+3 of row (lane & 15)
-  float m;     // running max of scaled scores (log2 units)
-  float l;     // running sum of probabilities
+  float m;     // reference max of scaled scores (log2 units)
+  float l;     // sum of probabilities against m
 };
 
-// Scores, online softmax and PV for one stage.
+// Wait states between an MFMA that writes a VGPR and the first VALU or memory
+// instruction that reads it (or a VALU that overwrites its SrcC). The compiler
+// inserts them inside one basic block, but misses them when the reader sits in
+// a successor block reached by a branch (here: the masking branch right after
+// the score MFMAs), and a too-early read sees a partial accumulation. Sixteen
+// wait states cover every MFMA used here; the tied operands pin the order.
+__device__ __forceinline__ void mfma_result_guard(f32x4& x) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x));
+}
+__device__ __forceinline__ void mfma_result_guard(f32x4 (&o)[8]) {
+  asm volatile("s_nop 7\n\ts_nop 7"
+               : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]), "+v"(o[4]), "+v"(o[5]),
+                 "+v"(o[6]), "+v"(o[7]));
+}
+
+// Scores, online softmax and PV for one 16-key stage.
 //
-// Key order: the two score MFMAs of a stage take their 16 A-operand rows as
-// keys {8q + i} and {8q + 4 + i} (q = 0..3, i = 0..3) of the 32-key stage, so
-// the lane holding output rows 4q..4q+3 of both holds the 8 consecutive keys
-// 8q..8q+7 of its query row. Those 8 keys are one page's 16-byte run of a
-// value dimension in the transposed V page, so the V^T operand of the PV
-// product is a single 16-byte LDS read, and the probabilities are already in
-// the P^T operand layout.
+// S^T = K Q^T (four v_mfma_f32_16x16x32_bf16 over the 128 dimensions) leaves
+// keys 4q..4q+3 of one query row in each lane - exactly the B operand of the
+// v_mfma_f32_16x16x16_bf16 that forms O^T += V^T P^T, whose A operand is the
+// 8 bytes holding the same 4 keys of one value dimension in the transposed V
+// page: no shuffle between the two products. Row max and row sum take two
+// cross-lane steps (the 4 lanes holding a row).
 //
-// Softmax: scores are scaled into log2 units inside one FMA. The running
-// reference max m is raised only when a row's new max exceeds it by more than
+// Softmax: scores are scaled into log2 units inside one FMA. The reference
+// max m is raised only when a row's new max exceeds it by more than
 // kRescaleLog2 (then O and l are rescaled by 2^(m_old - m_new)); otherwise
 // probabilities are taken against the stale m and stay below 2^kRescaleLog2.
-// Numerator and denominator share the same reference, so the result is exact
-// up to rounding; the rescale runs only in the rare chunks that need it.
-constexpr float kRescaleLog2 = 8.f;
-
-__device__ __forceinline__ void attend_stage(RowState& st, const bf16x8 (&qr)[4], const Stage& sg,
-                                             int lane, int lim, float scale_log2) {
+// Numerator and denominator share the reference, so the result is exact up
+// to rounding, and the rescale runs only in the rare stages that need it.
+//
+// P enters the PV product as a bf16 pair hi + lo (hi = RNE(p), lo = RNE(p - hi)),
+// so the probabilities carry ~16 mantissa bits instead of bf16's 8.
+__device__ __forceinline__ void attend_page(RowState& st, const bf16x8 (&qr)[4], const Stage& sg,
+                                            int lane, int lim, float scale_log2) {
   const int col = lane & 15, grp = lane >> 4;
-  // A-operand key of this lane's row in the two score MFMAs
-  const int ka = (col >> 2) * 8 + (col & 3);  // 0..3, 8..11, 16..19, 24..27
-  const int pa = ka >> 4, kpa = ka & 15;      // page and key in page (kb = ka + 4, same page)
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const int base_e = ((4 * s + grp) * kPage + kpa) * 8;
-    const u32x4 k0 = *reinterpret_cast<const u32x4*>(&sg.part[pa][base_e]);
-    const u32x4 k1 = *reinterpret_cast<const u32x4*>(&sg.part[pa][base_e + 4 * 8]);
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), qr[s], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), qr[s], s1, 0, 0, 0);
+    const u32x4 kk = *reinterpret_cast<const u32x4*>(&sg.k[s * 512 + lane * 8]);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kk), qr[s], sc, 0, 0, 0);
   }
-  // s0[i] is key 8*grp + i, s1[i] is key 8*grp + 4 + i of the stage
-  float x[8];
+  // also separates the previous stage's PV MFMAs from the rescale below
+  mfma_result_guard(sc);
+  // sc[i] is key 4*grp + i of the page for query row `col`
+  float x[4] = {sc[0], sc[1], sc[2], sc[3]};
+  if (lim < kPage) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = s0[i];
-    x[4 + i] = s1[i];
+    for (int i = 0; i < 4; ++i)
+      if (grp * 4 + i >= lim) x[i] = -INFINITY;
   }
-  if (lim < 32) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (grp * 8 + i >= lim) x[i] = -INFINITY;
-  }
-  float mx = x[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
   mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
   mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
   const float mc = mx * scale_log2;  // candidate max in log2 units (-inf if no visible key)
@@ -150,45 +153,31 @@ __device__ __forceinline__ void attend_stage(RowState& st, const bf16x8 (&qr)[4]
     st.m = m_new;
   }
   const float base = st.m == -INFINITY ? 0.f : st.m;
-  f32x4 p0, p1;
-  float rs = 0.f;
+  float p[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p0[i] = __builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -base));
-    p1[i] = __builtin_amdgcn_exp2f(fmaf(x[4 + i], scale_log2, -base));
-    rs += p0[i] + p1[i];
-  }
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -base));
+  float rs = (p[0] + p[1]) + (p[2] + p[3]);
   rs += __shfl_xor(rs, 16, kWave);
   rs += __shfl_xor(rs, 32, kWave);
   st.l += rs;
-  // P enters the PV product as a bf16 pair hi + lo (hi = RNE(p), lo = RNE(p - hi)),
-  // so the probabilities carry ~16 mantissa bits instead of bf16's 8.
-  const bf16x8 pb = pack_p(p0, p1);
-  const u32x4 hi = __builtin_bit_cast(u32x4, pb);
-  f32x4 r0, r1;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    r0[2 * i] = p0[2 * i] - bf16_lo(hi[i]);
-    r0[2 * i + 1] = p0[2 * i + 1] - bf16_hi(hi[i]);
-    r1[2 * i] = p1[2 * i] - bf16_lo(hi[2 + i]);
-    r1[2 * i + 1] = p1[2 * i + 1] - bf16_hi(hi[2 + i]);
-  }
-  const bf16x8 pl = pack_p(r0, r1);
-  // V^T operand: dimension dt*16 + col, keys 8*grp .. 8*grp+7 = page grp/2, keys 8*(grp&1)..
-  const uint16_t* vpart = sg.part[2 + (grp >> 1)];
+  const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
+  const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+  const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+  const s16x4 ph = __builtin_bit_cast(s16x4, u32x2{h01, h23});
+  const s16x4 pl = __builtin_bit_cast(s16x4, u32x2{l01, l23});
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    const bf16x8 va =
-        as_bf16x8(*reinterpret_cast<const u32x4*>(&vpart[(dt * 16 + col) * kPage + (grp & 1) * 8]));
-    f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.o[dt], 0, 0, 0);
-    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, acc, 0, 0, 0);
+    const s16x4 va = *reinterpret_cast<const s16x4*>(&sg.v[(dt * 16 + col) * kPage + grp * 4]);
+    f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, st.o[dt], 0, 0, 0);
+    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc, 0, 0, 0);
   }
 }
 
-// Asynchronous page-pair staging: global -> LDS DMA (global_load_lds_dwordx4).
+// Asynchronous page staging: global -> LDS DMA (global_load_lds_dwordx4).
 // Each instruction moves 64 lanes x 16 B = 1 KB: lane l's 16 bytes land at
-// M0 + 16 l in LDS. A stage is 1024 vectors (K of pages pg, pg+1, then V of
-// pg, pg+1); wavefront w issues instructions for vectors (i*NW + w)*64 .. +63.
+// M0 + 16 l in LDS. A stage is 512 vectors (K then V of one page); wavefront w
+// issues instructions for vectors (i*NW + w)*64 .. +63, and wavefronts past the
+// eighth issue none when NW = 16.
 // The DMA is issued from inline asm so that the compiler does not add its own
 // conservative vmcnt waits before every LDS read of the ring; the waits are
 // explicit (stage_wait_barrier) and counted per thread in issue order.
@@ -205,54 +194,44 @@ __device__ __forceinline__ void lds_dma_16(const void* gptr, uint32_t lds_byte_a
       : "memory");
 }
 
-// Two wave-uniform block-table entries through the scalar cache (read only).
+// A wave-uniform block-table entry through the scalar cache (read only).
 // Scalar loads count against lgkmcnt, not vmcnt, so reading the table never
 // waits for the DMAs in flight.
-__device__ __forceinline__ void load_page_ids(const int32_t* p0, const int32_t* p1, int& a,
-                                              int& b) {
-  const uint64_t u0 = reinterpret_cast<uint64_t>(p0), u1 = reinterpret_cast<uint64_t>(p1);
-  const uint64_t s0 = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(
-                           static_cast<uint32_t>(u0 >> 32))) << 32) |
-                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u0)));
-  const uint64_t s1 = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(
-                           static_cast<uint32_t>(u1 >> 32))) << 32) |
-                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u1)));
-  asm volatile(
-      "s_load_dword %0, %2, 0x0\n\t"
-      "s_load_dword %1, %3, 0x0\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=s"(a), "=s"(b)
-      : "s"(s0), "s"(s1)
-      : "memory");
+__device__ __forceinline__ int load_page_id(const int32_t* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint64_t su =
+      (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32))) << 32) |
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u)));
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(su) : "memory");
+  return v;
 }
 
 template <int NW>
-__device__ __forceinline__ void stage_dma(Stage& sg, int wave, int lane, int pg, int pg_end,
-                                          const int32_t* bt, int max_pages, int num_pages, int Hkv,
-                                          int kvh, const uint16_t* kc_layer,
-                                          const uint16_t* vc_layer) {
+struct DmaShape {
+  static constexpr int kPerWave = kPageVecs / (kWave * NW) > 0 ? kPageVecs / (kWave * NW) : 1;
+  static constexpr int kIssuers = kPageVecs / (kWave * kPerWave);  // waves that issue
+};
+
+template <int NW>
+__device__ __forceinline__ void stage_dma(Stage& sg, int wave, int lane, int pg, const int32_t* bt,
+                                          int max_pages, int num_pages, int Hkv, int kvh,
+                                          const uint16_t* kc_layer, const uint16_t* vc_layer) {
   constexpr size_t page_elems = static_cast<size_t>(kHeadDim) * kPage;
-  constexpr int kInstr = kChunkVecs / (kWave * NW);  // DMA instructions per wave per stage
+  using S = DmaShape<NW>;
+  if (wave >= S::kIssuers) return;  // wave-uniform
   // generic -> LDS address space: the 32-bit LDS byte address of the stage
   const uint32_t lds_base = static_cast<uint32_t>(
       reinterpret_cast<size_t>((__attribute__((address_space(3))) char*)(&sg)));
-  // page ids are wave-uniform: keep them in SGPRs so the block table is read
-  // with scalar loads, which do not count against vmcnt (the DMA counter)
-  const int pg0 = __builtin_amdgcn_readfirstlane(min(max(pg, 0), max_pages - 1));
-  const int pg1 = __builtin_amdgcn_readfirstlane(min(max(min(pg + 1, pg_end - 1), 0), max_pages - 1));
-  int raw0, raw1;
-  load_page_ids(bt + pg0, bt + pg1, raw0, raw1);
-  const int pid0 = min(max(raw0, 0), num_pages - 1);
-  const int pid1 = min(max(raw1, 0), num_pages - 1);
+  // the page id is wave-uniform: keep it in SGPRs
+  const int pgc = __builtin_amdgcn_readfirstlane(min(max(pg, 0), max_pages - 1));
+  const int pid = min(max(load_page_id(bt + pgc), 0), num_pages - 1);
+  const size_t off = (static_cast<size_t>(pid) * Hkv + kvh) * page_elems;
 #pragma unroll
-  for (int i = 0; i < kInstr; ++i) {
-    const int v0 = (i * NW + wave) * kWave;  // first vector of this instruction (wave-uniform)
-    const int part = v0 >> 8;                // 0,1: K of pages pg, pg+1; 2,3: V of pg, pg+1
-    const int pid = (part & 1) ? pid1 : pid0;
-    const uint16_t* base =
-        (part < 2 ? kc_layer : vc_layer) + (static_cast<size_t>(pid) * Hkv + kvh) * page_elems;
-    const uint16_t* src = base + ((v0 & 255) + lane) * 8;
-    lds_dma_16(src, __builtin_amdgcn_readfirstlane(lds_base + v0 * 16));
+  for (int i = 0; i < S::kPerWave; ++i) {
+    const int v0 = (i * S::kIssuers + wave) * kWave;  // first vector (wave-uniform)
+    const uint16_t* base = (v0 < 256 ? kc_layer + off : vc_layer + off - 256 * 8);
+    lds_dma_16(base + (v0 + lane) * 8, __builtin_amdgcn_readfirstlane(lds_base + v0 * 16));
   }
 }
 
@@ -264,12 +243,26 @@ __device__ __forceinline__ void stage_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
+// Wait for the oldest in-flight stage when `behind` later stages (kDma DMAs
+// each) may stay in flight, then synchronise the workgroup.
+template <int kDma>
+__device__ __forceinline__ void stage_wait_behind(int behind) {
+  if (behind >= 3)
+    stage_wait_barrier<3 * kDma>();
+  else if (behind == 2)
+    stage_wait_barrier<2 * kDma>();
+  else if (behind == 1)
+    stage_wait_barrier<kDma>();
+  else
+    stage_wait_barrier<0>();
+}
+
 // NW wavefronts per workgroup, one 16-row tile each.
 template <int NW>
 __global__ void __launch_bounds__(kWave * NW)
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
 k_window_attn_bf16(AttnArgs a) {
-  constexpr int NT = kWave * NW;
-  constexpr int kDma = kChunkVecs / NT;  // DMA instructions per thread per stage
+  constexpr int kDma = DmaShape<NW>::kPerWave;  // DMA instructions per issuing thread per stage
   __shared__ Stage stage[kStages];
 
   const int tid = threadIdx.x;
@@ -294,9 +287,9 @@ k_window_attn_bf16(AttnArgs a) {
   const bool with_window = split == a.n_splits - 1;
 
   // ---- this wave's 16 query rows (B operand of S^T = K Q^T) ---------------
-  // Loaded through asm, before the first page pairs' DMAs, and retired below
-  // with an explicit vmcnt that lets those DMAs stay in flight. (Rows past M
-  // read row 0 of the group - valid memory - and are never stored.)
+  // Loaded through asm, before the first pages' DMAs, and retired below with
+  // an explicit vmcnt that lets those DMAs stay in flight. (Rows past M read
+  // row 0 of the group - valid memory - and are never stored.)
   const size_t lb = static_cast<size_t>(layer) * a.B + b;
   const int row = wave * 16 + col;
   const bool row_ok = row < a.M;
@@ -319,56 +312,60 @@ k_window_attn_bf16(AttnArgs a) {
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool computes = wave * 16 < a.M;  // waves past the last row tile only move data
 
-  // ---- paged prefix: page pairs through the LDS ring -----------------------
+  // ---- paged prefix: pages through the LDS ring ----------------------------
   const int32_t* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
   const uint16_t* kc_layer = a.kc + static_cast<size_t>(layer) * a.cache_layer_stride;
   const uint16_t* vc_layer = a.vc + static_cast<size_t>(layer) * a.cache_layer_stride;
-  // Ring of kStages stages: page pairs i+1 and i+2 are in flight while pair i
-  // is computed. Before computing pair i each thread waits for its own DMAs of
-  // pair i (only pair i+1's may still be outstanding), then the barrier makes
-  // every wave's DMAs visible and guarantees that pair i-1's stage - the one
-  // refilled next - is no longer being read.
-  const int nch = (pg_end - pg_begin + 1) / 2;
-  // The first two stages are always requested (page ids clamped to valid
-  // entries when the split has fewer pairs; unused stages are simply not read),
+  const int npg = pg_end - pg_begin;
+  // The first kAhead stages are always requested (page ids clamped to valid
+  // entries when the split has fewer pages; unused stages are simply not read),
   // so the number of DMAs in flight here is a compile-time constant.
-  stage_dma<NW>(stage[0], wave, lane, pg_begin, pg_end, bt, a.max_pages, a.num_pages, a.Hkv, kvh,
-                kc_layer, vc_layer);
-  stage_dma<NW>(stage[1], wave, lane, pg_begin + 2, pg_end, bt, a.max_pages, a.num_pages, a.Hkv,
-                kvh, kc_layer, vc_layer);
-  // Retire the query loads: only the 2*kDma DMAs issued after them may remain.
+#pragma unroll
+  for (int j = 0; j < kAhead; ++j)
+    stage_dma<NW>(stage[j], wave, lane, min(pg_begin + j, pg_end - 1), bt, a.max_pages,
+                  a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
+  // Retire the query loads: only the DMAs issued after them may remain. Waves
+  // that issue no DMA (NW = 16) wait for everything first; that asm has no
+  // register operands, so nothing touches the query registers before the
+  // tied wait below.
+  if (wave >= DmaShape<NW>::kIssuers) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   asm volatile("s_waitcnt vmcnt(%4)"
                : "+v"(qv[0]), "+v"(qv[1]), "+v"(qv[2]), "+v"(qv[3])
-               : "n"(2 * kDma));
+               : "n"(kAhead * kDma));
   bf16x8 qr[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) qr[s] = as_bf16x8(qv[s]);
-  for (int i = 0; i < nch; ++i) {
-    const int pg = pg_begin + 2 * i;
-    if (i + 1 < nch)
-      stage_wait_barrier<kDma>();
-    else
-      stage_wait_barrier<0>();
-    if (i + 2 < nch)
-      stage_dma<NW>(stage[(i + 2) % kStages], wave, lane, pg + 4, pg_end, bt, a.max_pages,
+
+  // Ring of kStages stages: pages i+1 .. i+kAhead are in flight while page i
+  // is computed. Before computing page i each thread waits for its own DMAs of
+  // page i (the later requested pages may stay in flight), then the barrier
+  // makes every wave's DMAs visible and guarantees that page i-1's stage - the
+  // one refilled next - is no longer being read.
+  for (int i = 0; i < npg; ++i) {
+    const int pg = pg_begin + i;
+    // stages requested after page i: kAhead - 1 in steady state (clamped
+    // dummy requests of the prologue count too), fewer near the end
+    stage_wait_behind<kDma>(min(kAhead - 1, max(npg - 1 - i, kAhead - 1 - i)));
+    if (i + kAhead < npg)
+      stage_dma<NW>(stage[(i + kAhead) % kStages], wave, lane, pg + kAhead, bt, a.max_pages,
                     a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
-    if (computes) {
-      // keys pg*16 .. pg*16+31 are valid below L and below the split's end
-      const int lim = min(L, pg_end * kPage) - pg * kPage;
-      attend_stage(st, qr, stage[i % kStages], lane, lim, a.scale_log2);
-    }
+    if (computes) attend_page(st, qr, stage[i % kStages], lane, L - pg * kPage, a.scale_log2);
   }
-  __syncthreads();  // the window reuses stage 0
+  // The window reuses stage 0: every DMA - including the clamped dummy
+  // requests of the prologue when this split has fewer pages than kAhead, or
+  // none - must have landed before it is overwritten. The compiler does not
+  // see the asm DMAs, so a plain __syncthreads() would not wait for them.
+  stage_wait_barrier<0>();
 
   // ---- the window's own keys, causal over physical order -------------------
   if (with_window) {
     const int row_stride = a.Hkv * kHeadDim;
     const uint16_t* kwin = a.k + lb * a.W * row_stride + kvh * kHeadDim;
     const uint16_t* vwin = a.v + lb * a.W * row_stride + kvh * kHeadDim;
-    for (int kw0 = 0; kw0 < a.W; kw0 += 32) {
+    for (int kw0 = 0; kw0 < a.W; kw0 += kPage) {
       Stage& sg = stage[0];
-      // 32 keys x 16 slices of 8 dims: K goes to [slice][key][8], V is transposed
-      for (int idx = tid; idx < 32 * 16; idx += NT) {
+      // 16 keys x 16 slices of 8 dims: K goes to [slice][key][8], V is transposed
+      for (int idx = tid; idx < kPage * 16; idx += kWave * NW) {
         const int j = idx >> 4, sl = idx & 15;
         const int key = kw0 + j;
         u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
@@ -376,9 +373,8 @@ k_window_attn_bf16(AttnArgs a) {
           kv = *reinterpret_cast<const u32x4*>(kwin + key * row_stride + sl * 8);
           vv = *reinterpret_cast<const u32x4*>(vwin + key * row_stride + sl * 8);
         }
-        const int pg = j >> 4, kk = j & 15;
-        *reinterpret_cast<u32x4*>(&sg.part[pg][(sl * kPage + kk) * 8]) = kv;
-        uint16_t* vt = &sg.part[2 + pg][(sl * 8) * kPage + kk];
+        *reinterpret_cast<u32x4*>(&sg.k[(sl * kPage + j) * 8]) = kv;
+        uint16_t* vt = &sg.v[(sl * 8) * kPage + j];
         vt[0 * kPage] = static_cast<uint16_t>(vv.x);
         vt[1 * kPage] = static_cast<uint16_t>(vv.x >> 16);
         vt[2 * kPage] = static_cast<uint16_t>(vv.y);
@@ -391,13 +387,14 @@ k_window_attn_bf16(AttnArgs a) {
       __syncthreads();
       if (computes) {
         const int lim = min(a.W, prow + 1) - kw0;  // window key kw0 + kk visible iff kk < lim
-        attend_stage(st, qr, sg, lane, lim, a.scale_log2);
+        attend_page(st, qr, sg, lane, lim, a.scale_log2);
       }
       __syncthreads();
     }
   }
 
   // ---- write out ------------------------------------------------------------
+  mfma_result_guard(st.o);
   if (!row_ok) return;
   if (a.n_splits == 1) {
     const float inv = st.l > 0.f ? 1.f / st.l : 0.f;

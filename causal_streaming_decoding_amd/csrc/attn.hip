@@ -9,27 +9,29 @@
 // bf16 path (D = 128, page P = 16). One workgroup per (layer, sequence, kv
 // head, key-range split); each of its wavefronts owns one 16-row tile of the
 // group's M = W*g query rows (physical row p, query head h of the group). The
-// group's key pages stream through a 3-stage LDS ring, two pages (32 keys,
-// 16 KB of K and V) per stage, filled by global->LDS DMA: two page pairs are in
-// flight while the waves compute the third (one barrier per page pair). Each
-// key byte is read from HBM once per workgroup.
+// group's key pages stream through a 3-stage LDS ring, one page (16 keys, 8 KB
+// of K and V) per stage, filled by global->LDS DMA. A stage is refilled as soon
+// as every wave has finished reading it, so three pages are in flight while
+// the waves wait and two while they compute. Each key byte is read from HBM
+// once per workgroup.
 //
 //   S^T (16 keys x 16 rows)  = K (16 x 128) . Q^T        v_mfma_f32_16x16x32_bf16
-//   O^T (16 dims x 16 rows) += V^T (16 x 32 keys) . P^T  v_mfma_f32_16x16x32_bf16
+//   O^T (16 dims x 16 rows) += [V^T V^T] . [P_hi; P_lo]^T v_mfma_f32_16x16x32_bf16
 //
-// P is split into a bf16 hi and lo part (two PV MFMAs) so that rounding the
-// probabilities costs no accuracy; the kernel is HBM-bound and has MFMA to spare.
+// P is split into a bf16 hi and lo part so that rounding the probabilities
+// costs no accuracy: the PV MFMA takes the 4 keys of a lane's hi parts and
+// the same 4 keys' lo parts in its 8 K slots, against the V rows duplicated.
 //
 // Cache page layouts (16-byte vectors, contiguous per wave instruction):
 //   K page [Hkv][D/8][P][8]: 16-byte slices of the 16 keys side by side, so a
 //     page of one kv head is 4 KB contiguous and a DMA instruction moves 1 KB;
 //   V page [Hkv][D][P]: each value dimension's 16 keys contiguous (32 B), so a
-//     lane reads 8 consecutive keys of one dimension as one 16-byte vector.
-// The score MFMAs take their key rows in the order that leaves 8 consecutive
-// keys of one query row in each lane, which is both the P^T operand layout of
-// the PV product and the key order of that 16-byte V^T read: probabilities go
-// from the softmax to the second MFMA with no shuffle. Row max and row sum need
-// two cross-lane steps (the 4 lanes holding one row).
+//     lane reads 4 consecutive keys of one dimension as one 8-byte vector.
+// The score MFMA leaves 4 consecutive keys of one query row in each lane,
+// which is both the P^T operand layout of the PV product and the key order of
+// that 8-byte V^T read: probabilities go from the softmax to the second MFMA
+// with no shuffle. Row max and row sum need two cross-lane steps (the 4 lanes
+// holding one row).
 //
 // When there are too few groups to fill the GPU, a group's pages are split
 // across workgroups; each split writes (max, sum, unnormalised O) and a combine
@@ -103,14 +105,46 @@ __device__ __forceinline__ void mfma_result_guard(f32x4 (&o)[8]) {
                  "+v"(o[6]), "+v"(o[7]));
 }
 
+// Reductions over the four lanes holding one query row (lanes c, c+16, c+32,
+// c+48) with the gfx950 row-swap permutes. v_permlane16_swap exchanges the
+// odd 16-lane rows of one register with the even rows of another, and
+// v_permlane32_swap the upper 32 lanes of one with the lower 32 of another:
+// applied to two copies of x, every lane ends up holding the values of both
+// rows of its pair, in the same two registers. Every lane therefore combines
+// the same operands in the same order, and all four lanes of a row get
+// bitwise equal results. The swaps are issued from asm because the compiler's
+// builtins for them treat the two results as one value; the s_nop provides the
+// wait states between a VALU write and a permute read.
+__device__ __forceinline__ void row_swap16(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void row_swap32(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float row_max4(float x) {
+  float a = x, b = x;
+  row_swap16(a, b);
+  float c = fmaxf(a, b), d = c;
+  row_swap32(c, d);
+  return fmaxf(c, d);
+}
+__device__ __forceinline__ float row_sum4(float x) {
+  float a = x, b = x;
+  row_swap16(a, b);
+  float c = a + b, d = c;
+  row_swap32(c, d);
+  return c + d;
+}
+
 // Scores, online softmax and PV for one 16-key stage.
 //
 // S^T = K Q^T (four v_mfma_f32_16x16x32_bf16 over the 128 dimensions) leaves
-// keys 4q..4q+3 of one query row in each lane - exactly the B operand of the
-// v_mfma_f32_16x16x16_bf16 that forms O^T += V^T P^T, whose A operand is the
-// 8 bytes holding the same 4 keys of one value dimension in the transposed V
-// page: no shuffle between the two products. Row max and row sum take two
-// cross-lane steps (the 4 lanes holding a row).
+// keys 4q..4q+3 of one query row in each lane - the B operand layout of the
+// v_mfma_f32_16x16x32_bf16 that forms O^T += V^T P^T (hi parts in K slots
+// 0-3, lo parts in 4-7), whose A operand is the 8 bytes holding the same 4
+// keys of one value dimension in the transposed V page, twice: no shuffle
+// between the two products. Row max and row sum take two row-swap permutes
+// (the 4 lanes holding a row).
 //
 // Softmax: scores are scaled into log2 units inside one FMA. The reference
 // max m is raised only when a row's new max exceeds it by more than
@@ -139,9 +173,7 @@ __device__ __forceinline__ void attend_page(RowState& st, const bf16x8 (&qr)[4],
     for (int i = 0; i < 4; ++i)
       if (grp * 4 + i >= lim) x[i] = -INFINITY;
   }
-  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  const float mx = row_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
   const float mc = mx * scale_log2;  // candidate max in log2 units (-inf if no visible key)
   const bool raise = mc > st.m + kRescaleLog2;
   if (__ballot(raise)) {
@@ -156,20 +188,18 @@ __device__ __forceinline__ void attend_page(RowState& st, const bf16x8 (&qr)[4],
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -base));
-  float rs = (p[0] + p[1]) + (p[2] + p[3]);
-  rs += __shfl_xor(rs, 16, kWave);
-  rs += __shfl_xor(rs, 32, kWave);
-  st.l += rs;
+  st.l += row_sum4((p[0] + p[1]) + (p[2] + p[3]));
   const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
   const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
   const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
-  const s16x4 ph = __builtin_bit_cast(s16x4, u32x2{h01, h23});
-  const s16x4 pl = __builtin_bit_cast(s16x4, u32x2{l01, l23});
+  // K slots 0-3 of this lane: hi parts of keys 4*grp..+3; slots 4-7: lo parts.
+  const u32x4 pb = {h01, h23, l01, l23};
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    const s16x4 va = *reinterpret_cast<const s16x4*>(&sg.v[(dt * 16 + col) * kPage + grp * 4]);
-    f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, st.o[dt], 0, 0, 0);
-    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc, 0, 0, 0);
+    // the same 4 keys of value dimension dt*16 + col against both halves
+    const u32x2 va = *reinterpret_cast<const u32x2*>(&sg.v[(dt * 16 + col) * kPage + grp * 4]);
+    const u32x4 a = {va.x, va.y, va.x, va.y};
+    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pb), st.o[dt], 0, 0, 0);
   }
 }
 
@@ -240,7 +270,14 @@ __device__ __forceinline__ void stage_dma(Stage& sg, int wave, int lane, int pg,
 // compiler from moving LDS accesses across it.
 template <int N>
 __device__ __forceinline__ void stage_wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+// Every wave has finished reading the stages it computed: its LDS reads have
+// returned (lgkmcnt) before the workgroup synchronises, so a DMA issued after
+// this barrier cannot overwrite data that is still being read.
+__device__ __forceinline__ void stage_release_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
 // Wait for the oldest in-flight stage when `behind` later stages (kDma DMAs
@@ -336,19 +373,22 @@ k_window_attn_bf16(AttnArgs a) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) qr[s] = as_bf16x8(qv[s]);
 
-  // Ring of kStages stages: pages i+1 .. i+kAhead are in flight while page i
-  // is computed. Before computing page i each thread waits for its own DMAs of
-  // page i (the later requested pages may stay in flight), then the barrier
-  // makes every wave's DMAs visible and guarantees that page i-1's stage - the
-  // one refilled next - is no longer being read.
+  // Ring of kStages stages. The prologue requested pages 0 .. kAhead-1. At
+  // iteration i the stage that held page i-1 is refilled with page i+kAhead as
+  // soon as every wave has finished reading it (first barrier), before anyone
+  // waits for page i: kStages pages are in flight while the waves wait, kAhead
+  // while they compute. Each thread then waits for its own DMAs of page i and
+  // the second barrier makes every wave's part of page i visible.
   for (int i = 0; i < npg; ++i) {
     const int pg = pg_begin + i;
-    // stages requested after page i: kAhead - 1 in steady state (clamped
-    // dummy requests of the prologue count too), fewer near the end
-    stage_wait_behind<kDma>(min(kAhead - 1, max(npg - 1 - i, kAhead - 1 - i)));
-    if (i + kAhead < npg)
+    if (i + kAhead < npg) {
+      if (i > 0) stage_release_barrier();  // page i-1's stage is free
       stage_dma<NW>(stage[(i + kAhead) % kStages], wave, lane, pg + kAhead, bt, a.max_pages,
                     a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
+    }
+    // requests issued after page i's: up to kAhead real pages, or the clamped
+    // dummy requests of the prologue when the split is shorter than kAhead
+    stage_wait_behind<kDma>(max(min(kAhead, npg - 1 - i), kAhead - 1 - i));
     if (computes) attend_page(st, qr, stage[i % kStages], lane, L - pg * kPage, a.scale_log2);
   }
   // The window reuses stage 0: every DMA - including the clamped dummy

@@ -25,6 +25,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+# counted HBM bytes of the attention launch (rocprofv3 FETCH_SIZE + WRITE_SIZE,
+# calibrated); used only while the kernel source still matches the record
+TRAFFIC_RECORD = "k_window_attn_bf16_qwen3_36L_bs16_stream256_traffic.txt"
 
 
 def parse():
@@ -150,6 +153,9 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
+    from causal_streaming_decoding_amd.profiling import read_traffic
+    traffic = read_traffic(os.path.join(ROOT, "profiles", TRAFFIC_RECORD), wl.name, K)
+
     cpu = None
     if args.cpu_baseline_steps > 0:
         n = min(args.cpu_baseline_steps, n_inputs)
@@ -184,7 +190,7 @@ def main():
         "bytes_per_step_avg": {k_: v_ / K for k_, v_ in tot.items()},
         "roofline": {"kernel": "k_window_attn_bf16", "bound": "hbm", "achieved": attn_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": attn_gbps / HBM_PEAK_GBPS,
-                     "traffic": None, "avg_launch_ms": float(attn_ms.mean()),
+                     "traffic": traffic, "avg_launch_ms": float(attn_ms.mean()),
                      "algorithmic_bytes_per_launch": attn_bytes / K},
         "cpu_baseline": cpu,
     }

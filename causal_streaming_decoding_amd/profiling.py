@@ -1,0 +1,196 @@
+"""Summaries of rocprofv3 runs of bench.py: kernel times and calibrated HBM bytes.
+
+Three runs of the same bench command feed it:
+
+* a kernel trace (``rocprofv3 --kernel-trace --stats --output-format csv``),
+* a ``FETCH_SIZE`` counter pass and a ``WRITE_SIZE`` counter pass
+  (``rocprofv3 --pmc ... --output-format csv``), each with ``--calibrate-copy``
+  so that the run ends with one 1 GiB device-to-device copy.
+
+The counters report KiB per dispatch in units that need not be bytes moved:
+each is scaled by what it reads for the calibration copy, whose true traffic
+is 1 GiB read and 1 GiB written. The window-attention record it writes holds a
+hash of the kernel's source files, so that a later reader can tell whether the
+counters still describe the kernel that is built.
+
+Usage::
+
+    python -m causal_streaming_decoding_amd.profiling \\
+        --trace gpurun_out/prof_trace --fetch gpurun_out/prof_fetch \\
+        --write gpurun_out/prof_write --bench-json gpurun_out/prof_bench.json \\
+        --steps 256 --out-md profiles/<name>.md --out-traffic profiles/<name>_traffic.txt
+"""
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ATTN_SOURCES = ("csrc/attn.hip", "csrc/common.hpp")
+ATTN_KERNEL = "k_window_attn_bf16"
+CALIBRATION_KIB = 1 << 20  # the 1 GiB copy, read once and written once
+
+
+def attn_source_hash():
+    """sha256 over the window-attention kernel's source files, in a fixed order."""
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()
+
+
+def short_name(name):
+    """'void wedlm::k_window_attn_bf16<4>(wedlm::AttnArgs)' -> 'wedlm::k_window_attn_bf16<4>'."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def kernel_stats(trace_dir, prefix="wedlm::"):
+    """[(kernel, calls, avg_us, min_us, max_us)] for the library's kernels, by total time."""
+    out = []
+    with open(os.path.join(trace_dir, "run_kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            n = short_name(r["Name"])
+            if n.startswith(prefix):
+                out.append((n, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                            float(r["TotalDurationNs"])))
+    out.sort(key=lambda t: -t[5])
+    return [t[:5] for t in out]
+
+
+def counter_values(pmc_dir, counter):
+    """({kernel: [KiB per dispatch in dispatch order]}, calibration-copy KiB)."""
+    per = {}
+    calib = None
+    with open(os.path.join(pmc_dir, "run_counter_collection.csv")) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        n = short_name(r["Kernel_Name"])
+        v = float(r["Counter_Value"])
+        if "copyBuffer" in n:
+            calib = v if calib is None else max(calib, v)  # the 1 GiB copy is the largest
+            continue
+        per.setdefault(n, []).append(v)
+    return per, calib
+
+
+def summarize(trace, fetch, write, bench_json, steps, out_md, out_traffic, command_trace,
+              command_fetch, command_write):
+    stats = kernel_stats(trace)
+    fetch_kib, fetch_cal = counter_values(fetch, "FETCH_SIZE")
+    write_kib, write_cal = counter_values(write, "WRITE_SIZE")
+    if fetch_cal is None or write_cal is None:
+        raise SystemExit("no calibration copy in the counter runs (bench.py --calibrate-copy)")
+    f_fac = fetch_cal / CALIBRATION_KIB
+    w_fac = write_cal / CALIBRATION_KIB
+    with open(bench_json) as f:
+        bench = json.loads([ln for ln in f if ln.startswith("{")][-1])
+    roof = bench["roofline"]
+
+    def per_launch(d, name, fac):
+        vals = d.get(name, [])[-steps:]  # the timed steps are the last dispatches
+        return (sum(vals) / len(vals)) * 1024.0 / fac if vals else None
+
+    attn = next(n for n, *_ in stats if ATTN_KERNEL in n)
+    a_fetch = per_launch(fetch_kib, attn, f_fac)
+    a_write = per_launch(write_kib, attn, w_fac)
+    alg = roof["algorithmic_bytes_per_launch"]
+    trace_avg = next(t[2] for t in stats if t[0] == attn)
+
+    lines = [f"# Window step kernels: {bench['config']['workload']}", "",
+             "MI355X (gfx950). Durations in microseconds; bytes are per dispatch, averaged over "
+             f"the last {steps} dispatches of each kernel (the timed steps). In the commands, "
+             "`<repo>` is the repository root.", "",
+             "## Kernel trace", "", "```", command_trace, "```", "",
+             "| kernel | calls | avg | min | max |", "|---|---|---|---|---|"]
+    for n, c, avg, mn, mx in stats:
+        lines.append(f"| `{n}` | {c} | {avg:.2f} | {mn:.2f} | {mx:.2f} |")
+    lines += ["", f"Bench line of the same command: {bench['value']:.1f} window-steps/s; HIP-event "
+              f"average of the attention launch {roof['avg_launch_ms'] * 1e3:.2f} us against "
+              f"{trace_avg:.2f} us in the trace "
+              f"({abs(roof['avg_launch_ms'] * 1e3 - trace_avg) / trace_avg * 100:.1f} % apart).", "",
+              "## HBM byte counters", "", "```", command_fetch, command_write, "```", "",
+              f"Calibration (1 GiB copy, read and written once): FETCH_SIZE {fetch_cal:.1f} KiB "
+              f"(factor {f_fac:.4f}), WRITE_SIZE {write_cal:.1f} KiB (factor {w_fac:.4f}). Bytes "
+              "below are counter / factor.", "",
+              "| kernel | read MB / dispatch | written MB / dispatch |", "|---|---|---|"]
+    for n, *_ in stats:
+        r = per_launch(fetch_kib, n, f_fac)
+        w = per_launch(write_kib, n, w_fac)
+        if r is None or w is None:
+            continue
+        lines.append(f"| `{n}` | {r / 1e6:.2f} | {w / 1e6:.2f} |")
+    lines += ["", f"Window attention: algorithmic {alg / 1e6:.1f} MB per launch (KV prefix + window "
+              f"q/k/v read, output written); counted {(a_fetch + a_write) / 1e6:.1f} MB "
+              f"({(a_fetch + a_write) / alg:.3f} x)."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(out_traffic, "w") as f:
+        f.write(f"kernel: {attn}\n")
+        f.write(f"source_sha256: {attn_source_hash()}\n")
+        f.write(f"workload: {bench['config']['workload']}\n")
+        f.write(f"steps: {steps}\n")
+        f.write(f"fetch_bytes_per_launch: {a_fetch:.0f}\n")
+        f.write(f"write_bytes_per_launch: {a_write:.0f}\n")
+        f.write(f"algorithmic_bytes_per_launch: {alg:.0f}\n")
+        f.write(f"fetch_factor: {f_fac:.6f}\n")
+        f.write(f"write_factor: {w_fac:.6f}\n")
+        f.write(f"command_fetch: {command_fetch}\n")
+        f.write(f"command_write: {command_write}\n")
+
+
+def read_traffic(path, workload, steps):
+    """Counted HBM bytes per attention launch, or None when the record does not apply.
+
+    The record applies only to the same workload and step count and to the
+    kernel source it was measured on.
+    """
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for ln in f:
+            if ": " in ln:
+                k, v = ln.rstrip("\n").split(": ", 1)
+                rec[k] = v
+    if (rec.get("source_sha256") != attn_source_hash() or rec.get("workload") != workload
+            or int(rec.get("steps", -1)) != steps):
+        return None
+    return float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--bench-json", required=True)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--out-md", required=True)
+    ap.add_argument("--out-traffic", required=True)
+    ap.add_argument("--command-trace", default="")
+    ap.add_argument("--command-fetch", default="")
+    ap.add_argument("--command-write", default="")
+    a = ap.parse_args()
+    summarize(a.trace, a.fetch, a.write, a.bench_json, a.steps, a.out_md, a.out_traffic,
+              a.command_trace, a.command_fetch, a.command_write)
+
+
+if __name__ == "__main__":
+    main()

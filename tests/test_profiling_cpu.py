@@ -1,0 +1,41 @@
+"""Host-side checks of the rocprofv3 summary helpers and the bench's traffic record."""
+
+import os
+
+from causal_streaming_decoding_amd import profiling
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_short_name_strips_return_type_and_arguments():
+    assert profiling.short_name("void wedlm::k_window_attn_bf16<4>(wedlm::AttnArgs)") == \
+        "wedlm::k_window_attn_bf16<4>"
+    assert profiling.short_name("wedlm::k_entropy_select(int, int)") == "wedlm::k_entropy_select"
+    assert profiling.short_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+
+
+def _record(tmp_path, sha, workload="w", steps=256):
+    p = tmp_path / "t.txt"
+    p.write_text(f"kernel: k\nsource_sha256: {sha}\nworkload: {workload}\nsteps: {steps}\n"
+                 "fetch_bytes_per_launch: 100\nwrite_bytes_per_launch: 20\n")
+    return str(p)
+
+
+def test_traffic_record_applies_only_to_the_measured_source(tmp_path):
+    good = _record(tmp_path, profiling.attn_source_hash())
+    assert profiling.read_traffic(good, "w", 256) == 120.0
+    assert profiling.read_traffic(good, "other", 256) is None
+    assert profiling.read_traffic(good, "w", 8) is None
+    stale = _record(tmp_path, "0" * 64)
+    assert profiling.read_traffic(stale, "w", 256) is None
+    assert profiling.read_traffic(str(tmp_path / "missing.txt"), "w", 256) is None
+
+
+def test_committed_record_is_well_formed():
+    path = os.path.join(ROOT, "profiles", "k_window_attn_bf16_qwen3_36L_bs16_stream256_traffic.txt")
+    rec = dict(ln.rstrip("\n").split(": ", 1) for ln in open(path) if ": " in ln)
+    assert len(rec["source_sha256"]) == 64
+    fetch = float(rec["fetch_bytes_per_launch"])
+    write = float(rec["write_bytes_per_launch"])
+    alg = float(rec["algorithmic_bytes_per_launch"])
+    assert 0.9 < (fetch + write) / alg < 1.2

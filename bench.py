@@ -43,6 +43,54 @@ def parse():
     return ap.parse_args()
 
 
+class HipEvents:
+    """Timing-only HIP events recorded on the launch stream.
+
+    Created with hipEventDisableSystemFence: recording them does not write
+    back and invalidate the caches, which a default timing event does and
+    which costs about 5 us of GPU time per record between kernels. The HIP
+    runtime is the one torch has already loaded (same soname).
+    """
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, stream_handle=0):
+        import ctypes
+        self.c = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.stream = ctypes.c_void_p(stream_handle)
+        self.events = []
+
+    def create(self):
+        e = self.c.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.c.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.events.append(e)
+        return e
+
+    def record(self, e):
+        rc = self.hip.hipEventRecord(e, self.stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b):
+        ms = self.c.c_float()
+        rc = self.hip.hipEventElapsedTime(self.c.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
 def step_bytes(wl, prefix_lens):
     """Algorithmic HBM bytes of one window step, split by tensor (each byte once)."""
     e = 2 if wl.dtype == "bf16" else 4
@@ -115,8 +163,11 @@ def main():
     torch.cuda.synchronize()
     st.restore(snap)
     commit_log.zero_()
-    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(K)] for name in ("attn", "entropy")}
+    # the library launches on the stream it is given; None is the null stream,
+    # which is torch's current stream here
+    hev = HipEvents(torch.cuda.current_stream().cuda_stream)
+    labels = ("attn_start", "attn_end", "entropy_end")
+    ev = [{lab: hev.create() for lab in labels} for _ in range(K)]
     torch.cuda.synchronize()
 
     print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
@@ -124,13 +175,14 @@ def main():
     for s in range(K):
         q, k, v, logits = ins[s % n_inputs]
         step.run(st, q, k, v, logits, max_prefix_len=L0 + wl.W * s, commit_len=commit_log[s],
-                 events={"attn": ev["attn"][s], "entropy": ev["entropy"][s]})
+                 mark=lambda lab, e=ev[s]: hev.record(e[lab]))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
     commits = commit_log[:K].cpu().numpy().astype(np.int64)
-    attn_ms = np.array([a.elapsed_time(b) for a, b in ev["attn"]])
-    ent_ms = np.array([a.elapsed_time(b) for a, b in ev["entropy"]])
+    attn_ms = np.array([hev.elapsed_ms(e["attn_start"], e["attn_end"]) for e in ev])
+    ent_ms = np.array([hev.elapsed_ms(e["attn_end"], e["entropy_end"]) for e in ev])
+    hev.destroy()
     L = np.asarray(inp["prefix_len"], np.int64).copy()
     tot = {"kv": 0, "window": 0, "attn_out": 0, "logits": 0}
     attn_bytes = 0

@@ -40,6 +40,8 @@
 // same page layout.
 #include "common.hpp"
 
+#include <cmath>
+
 namespace wedlm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -60,7 +62,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.f;
 
 struct AttnArgs {
-  const uint16_t* q;   // [nl][B][W][Hq][D] physical order, rotated
+  // physical order and rotated; with RoPE fused: slot order, before RoPE
+  const uint16_t* q;   // [nl][B][W][Hq][D]
   const uint16_t* k;   // [nl][B][W][Hkv][D]
   const uint16_t* v;
   const uint16_t* kc;  // [nl][num_pages][Hkv][D/8][P][8]
@@ -74,6 +77,11 @@ struct AttnArgs {
   int num_pages, max_pages, max_prefix_len, n_splits;
   long long cache_layer_stride;  // elements per layer of one cache
   float scale_log2;
+  // RoPE fused into the loads (else unused): physical row -> slot, logical
+  // position of each physical row, and the D/2 rotation frequencies
+  const int32_t* perm;
+  const int32_t* pos;
+  double omega[kHeadDim / 2];
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -294,13 +302,35 @@ __device__ __forceinline__ void stage_wait_behind(int behind) {
     stage_wait_barrier<0>();
 }
 
-// NW wavefronts per workgroup, one 16-row tile each.
-template <int NW>
+// Rotates a 16-byte slice pair of one row by RoPE: lo holds dims j0..j0+7,
+// hi dims j0+64..j0+71 (rotate-half pairing, D = 128), position t.
+__device__ __forceinline__ void rope_pair(u32x4& lo, u32x4& hi, double t, const double* omega,
+                                          int j0) {
+  u32x4 ylo, yhi;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float c0, s0, c1, s1;
+    rope_cos_sin(t, omega[j0 + 2 * w], c0, s0);
+    rope_cos_sin(t, omega[j0 + 2 * w + 1], c1, s1);
+    const float a0 = bf16_lo(lo[w]), a1 = bf16_hi(lo[w]);
+    const float h0 = bf16_lo(hi[w]), h1 = bf16_hi(hi[w]);
+    ylo[w] = pack_bf16x2(a0 * c0 - h0 * s0, a1 * c1 - h1 * s1);
+    yhi[w] = pack_bf16x2(h0 * c0 + a0 * s0, h1 * c1 + a1 * s1);
+  }
+  lo = ylo;
+  hi = yhi;
+}
+
+// NW wavefronts per workgroup, one 16-row tile each. kRope: q, k, v are in
+// slot order before RoPE; each query row and window key is gathered through
+// perm and rotated at its logical position as it is loaded.
+template <int NW, bool kRope>
 __global__ void __launch_bounds__(kWave * NW)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
 k_window_attn_bf16(AttnArgs a) {
   constexpr int kDma = DmaShape<NW>::kPerWave;  // DMA instructions per issuing thread per stage
   __shared__ Stage stage[kStages];
+  __shared__ double s_omega[kRope ? kHeadDim / 2 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -331,15 +361,27 @@ k_window_attn_bf16(AttnArgs a) {
   const int row = wave * 16 + col;
   const bool row_ok = row < a.M;
   const int prow = row / a.g, hh = row % a.g;
+  int qslot = row_ok ? prow : 0;  // window row holding this query row
+  int qpos = 0;
+  if constexpr (kRope) {
+    // frequencies to LDS and this row's slot and position, all before any
+    // asynchronous load is issued (the waits the compiler adds for these are
+    // then free)
+    if (tid < kHeadDim / 2) s_omega[tid] = a.omega[tid];
+    qslot = min(max(a.perm[b * a.W + qslot], 0), a.W - 1);
+    qpos = a.pos[b * a.W + (row_ok ? prow : 0)];
+    __syncthreads();
+  }
   u32x4 qv[4];
   {
     const uint16_t* qrow =
-        a.q + ((lb * a.W + (row_ok ? prow : 0)) * a.Hq + kvh * a.g + (row_ok ? hh : 0)) * kHeadDim;
+        a.q + ((lb * a.W + qslot) * a.Hq + kvh * a.g + (row_ok ? hh : 0)) * kHeadDim;
+    // qpos is an input so that its load has completed before the query loads
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       asm volatile("global_load_dwordx4 %0, %1, off"
                    : "=v"(qv[s])
-                   : "v"(qrow + s * 32 + grp * 8)
+                   : "v"(qrow + s * 32 + grp * 8), "v"(qpos)
                    : "memory");
   }
   RowState st;
@@ -369,6 +411,11 @@ k_window_attn_bf16(AttnArgs a) {
   asm volatile("s_waitcnt vmcnt(%4)"
                : "+v"(qv[0]), "+v"(qv[1]), "+v"(qv[2]), "+v"(qv[3])
                : "n"(kAhead * kDma));
+  if constexpr (kRope) {
+    // this lane holds dims s*32 + grp*8 .. +7: slices s and s+2 are a RoPE pair
+    rope_pair(qv[0], qv[2], static_cast<double>(qpos), s_omega, grp * 8);
+    rope_pair(qv[1], qv[3], static_cast<double>(qpos), s_omega, 32 + grp * 8);
+  }
   bf16x8 qr[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) qr[s] = as_bf16x8(qv[s]);
@@ -405,24 +452,67 @@ k_window_attn_bf16(AttnArgs a) {
     for (int kw0 = 0; kw0 < a.W; kw0 += kPage) {
       Stage& sg = stage[0];
       // 16 keys x 16 slices of 8 dims: K goes to [slice][key][8], V is transposed
-      for (int idx = tid; idx < kPage * 16; idx += kWave * NW) {
-        const int j = idx >> 4, sl = idx & 15;
-        const int key = kw0 + j;
-        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-        if (key < a.W) {
-          kv = *reinterpret_cast<const u32x4*>(kwin + key * row_stride + sl * 8);
-          vv = *reinterpret_cast<const u32x4*>(vwin + key * row_stride + sl * 8);
-        }
+      auto put = [&](int j, int sl, u32x4 kv, u32x4 vv) {
         *reinterpret_cast<u32x4*>(&sg.k[(sl * kPage + j) * 8]) = kv;
         uint16_t* vt = &sg.v[(sl * 8) * kPage + j];
-        vt[0 * kPage] = static_cast<uint16_t>(vv.x);
-        vt[1 * kPage] = static_cast<uint16_t>(vv.x >> 16);
-        vt[2 * kPage] = static_cast<uint16_t>(vv.y);
-        vt[3 * kPage] = static_cast<uint16_t>(vv.y >> 16);
-        vt[4 * kPage] = static_cast<uint16_t>(vv.z);
-        vt[5 * kPage] = static_cast<uint16_t>(vv.z >> 16);
-        vt[6 * kPage] = static_cast<uint16_t>(vv.w);
-        vt[7 * kPage] = static_cast<uint16_t>(vv.w >> 16);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          vt[(2 * w) * kPage] = static_cast<uint16_t>(vv[w]);
+          vt[(2 * w + 1) * kPage] = static_cast<uint16_t>(vv[w] >> 16);
+        }
+      };
+      if constexpr (kRope) {
+        // keys, gathered through perm: one task per (key, slice pair sl / sl+8,
+        // 32-bit word), the two dims of the word rotated with their partners
+        // (small tasks keep the registers of the running O free)
+        uint32_t* kw = reinterpret_cast<uint32_t*>(sg.k);
+        for (int idx = tid; idx < kPage * 8 * 4; idx += kWave * NW) {
+          const int j = idx >> 5, sl = (idx >> 2) & 7, w = idx & 3;
+          const int key = kw0 + j;
+          uint32_t lo = 0u, hi = 0u;
+          if (key < a.W) {
+            const int slot = min(max(a.perm[b * a.W + key], 0), a.W - 1);
+            const uint16_t* kr = kwin + slot * row_stride + sl * 8 + 2 * w;
+            const uint32_t x = *reinterpret_cast<const uint32_t*>(kr);
+            const uint32_t y = *reinterpret_cast<const uint32_t*>(kr + kHeadDim / 2);
+            const double t = static_cast<double>(a.pos[b * a.W + key]);
+            float c0, s0, c1, s1;
+            rope_cos_sin(t, s_omega[sl * 8 + 2 * w], c0, s0);
+            rope_cos_sin(t, s_omega[sl * 8 + 2 * w + 1], c1, s1);
+            const float a0 = bf16_lo(x), a1 = bf16_hi(x), h0 = bf16_lo(y), h1 = bf16_hi(y);
+            lo = pack_bf16x2(a0 * c0 - h0 * s0, a1 * c1 - h1 * s1);
+            hi = pack_bf16x2(h0 * c0 + a0 * s0, h1 * c1 + a1 * s1);
+          }
+          kw[((sl * kPage + j) * 8) / 2 + w] = lo;
+          kw[(((sl + 8) * kPage + j) * 8) / 2 + w] = hi;
+        }
+        // values, gathered through perm
+        for (int idx = tid; idx < kPage * 16; idx += kWave * NW) {
+          const int j = idx >> 4, sl = idx & 15;
+          const int key = kw0 + j;
+          u32x4 vv = {0u, 0u, 0u, 0u};
+          if (key < a.W) {
+            const int slot = min(max(a.perm[b * a.W + key], 0), a.W - 1);
+            vv = *reinterpret_cast<const u32x4*>(vwin + slot * row_stride + sl * 8);
+          }
+          uint16_t* vt = &sg.v[(sl * 8) * kPage + j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            vt[(2 * e) * kPage] = static_cast<uint16_t>(vv[e]);
+            vt[(2 * e + 1) * kPage] = static_cast<uint16_t>(vv[e] >> 16);
+          }
+        }
+      } else {
+        for (int idx = tid; idx < kPage * 16; idx += kWave * NW) {
+          const int j = idx >> 4, sl = idx & 15;
+          const int key = kw0 + j;
+          u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+          if (key < a.W) {
+            kv = *reinterpret_cast<const u32x4*>(kwin + key * row_stride + sl * 8);
+            vv = *reinterpret_cast<const u32x4*>(vwin + key * row_stride + sl * 8);
+          }
+          put(j, sl, kv, vv);
+        }
       }
       __syncthreads();
       if (computes) {
@@ -511,13 +601,21 @@ k_window_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ 
 // ---------------------------------------------------------------------------
 constexpr int kF32MaxD = 256;
 
+// RoPE inputs of the fused f32 path: row -> slot, positions, D/2 frequencies.
+struct RopeF32 {
+  const int32_t* perm;
+  const int32_t* pos;
+  double omega[kF32MaxD / 2];
+};
+
+template <bool kRope>
 __global__ void __launch_bounds__(kWave)
 k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
                   const float* __restrict__ v, const float* __restrict__ kc,
                   const float* __restrict__ vc, const int32_t* __restrict__ block_table,
                   const int32_t* __restrict__ prefix_len, float* __restrict__ out, int B, int W,
                   int Hq, int Hkv, int D, int num_pages, int max_pages, int max_prefix_len,
-                  long long cache_layer_stride, float scale_log2) {
+                  long long cache_layer_stride, float scale_log2, RopeF32 rp) {
   __shared__ float qs[kF32MaxD];
   const int lane = threadIdx.x;
   int bid = blockIdx.x;
@@ -529,7 +627,22 @@ k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
   const int layer = bid / B;
   const int g = Hq / Hkv, kvh = h / g;
   const size_t lb = static_cast<size_t>(layer) * B + b;
-  for (int d = lane; d < D; d += kWave) qs[d] = q[((lb * W + p) * Hq + h) * D + d];
+  const int half = D / 2;
+  // kRope: window rows are gathered through perm and rotated at their
+  // logical position as they are read
+  auto slot_of = [&](int row) { return kRope ? min(max(rp.perm[b * W + row], 0), W - 1) : row; };
+  if constexpr (kRope) {
+    const float* qr = q + ((lb * W + slot_of(p)) * Hq + h) * D;
+    const double tq = static_cast<double>(rp.pos[b * W + p]);
+    for (int j = lane; j < half; j += kWave) {
+      float c, sn;
+      rope_cos_sin(tq, rp.omega[j], c, sn);
+      qs[j] = qr[j] * c - qr[j + half] * sn;
+      qs[j + half] = qr[j + half] * c + qr[j] * sn;
+    }
+  } else {
+    for (int d = lane; d < D; d += kWave) qs[d] = q[((lb * W + p) * Hq + h) * D + d];
+  }
   __syncthreads();
   const int L = min(max(prefix_len[b], 0), max_prefix_len);
   const int nkeys = L + p + 1;
@@ -551,6 +664,16 @@ k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
         const float* kp = kcl + (static_cast<size_t>(pid) * Hkv + kvh) * page_elems;
         const int off = key % kPage;
         for (int d = 0; d < D; ++d) dot += qs[d] * kp[((d >> 2) * kPage + off) * 4 + (d & 3)];
+      } else if constexpr (kRope) {
+        const int r = key - L;
+        const float* kr = k + ((lb * W + slot_of(r)) * Hkv + kvh) * D;
+        const double tk = static_cast<double>(rp.pos[b * W + r]);
+        for (int j = 0; j < half; ++j) {
+          float c, sn;
+          rope_cos_sin(tk, rp.omega[j], c, sn);
+          const float k0 = kr[j], k1 = kr[j + half];
+          dot += qs[j] * (k0 * c - k1 * sn) + qs[j + half] * (k1 * c + k0 * sn);
+        }
       } else {
         const float* kr = k + ((lb * W + (key - L)) * Hkv + kvh) * D;
         for (int d = 0; d < D; ++d) dot += qs[d] * kr[d];
@@ -579,7 +702,7 @@ k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
           if (d < D) o[i] += pj * vp[d * kPage + off];
         }
       } else {
-        const float* vr = v + ((lb * W + (kj - L)) * Hkv + kvh) * D;
+        const float* vr = v + ((lb * W + slot_of(kj - L)) * Hkv + kvh) * D;
 #pragma unroll
         for (int i = 0; i < kF32MaxD / kWave; ++i) {
           const int d = lane + i * kWave;
@@ -654,43 +777,59 @@ extern "C" size_t wedlm_window_attn_workspace_size(int dtype, int n_layers, int 
   return pl.ws_o_bytes + pl.ws_ml_bytes;
 }
 
-extern "C" int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D,
-                                 int page_size, int num_pages, int max_pages, int max_prefix_len,
-                                 float scale, const void* q_phys, const void* k_phys,
-                                 const void* v_phys, const void* k_cache, const void* v_cache,
-                                 const int32_t* block_table, const int32_t* prefix_len,
-                                 void* out_phys, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+// Shared by both entry points; `rope` selects the fused-RoPE kernels (q, k, v
+// in slot order before RoPE, perm / pos / theta used), else q, k, v are the
+// rotated physical-order rows and perm / pos / theta are ignored.
+static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D,
+                       int page_size, int num_pages, int max_pages, int max_prefix_len, float scale,
+                       double theta, const void* q, const void* k, const void* v,
+                       const int32_t* perm, const int32_t* pos, const void* k_cache,
+                       const void* v_cache, const int32_t* block_table, const int32_t* prefix_len,
+                       void* out_phys, void* workspace, size_t workspace_bytes, void* stream) {
   int st = validate_attn(dtype, n_layers, B, W, Hq, Hkv, D, page_size, max_prefix_len);
   if (st != WEDLM_OK) return st;
   if (num_pages <= 0 || max_pages <= 0 || static_cast<long long>(max_pages) * page_size <
                                                static_cast<long long>(max_prefix_len))
     return WEDLM_ERR_INVALID;
-  if (!q_phys || !k_phys || !v_phys || !k_cache || !v_cache || !block_table || !prefix_len ||
-      !out_phys)
+  if (!q || !k || !v || !k_cache || !v_cache || !block_table || !prefix_len || !out_phys)
     return WEDLM_ERR_INVALID;
+  if (rope && (!perm || !pos || !(theta > 0.0) || D % 2 != 0)) return WEDLM_ERR_INVALID;
   if (!(scale > 0.f)) return WEDLM_ERR_INVALID;
   hipStream_t s = as_stream(stream);
   const long long cache_layer_stride = 1LL * num_pages * Hkv * D * page_size;
   const float scale_log2 = scale * kLog2e;
+  // rotation frequencies theta^(-2j/D), formed once on the host in double
+  double omega[kF32MaxD / 2] = {};
+  if (rope)
+    for (int j = 0; j < D / 2; ++j) omega[j] = std::pow(theta, -2.0 * j / D);
   if (dtype == WEDLM_F32) {
     const long long blocks = 1LL * n_layers * B * Hq * W;
     if (blocks > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(k_window_attn_f32, dim3(static_cast<unsigned>(blocks)), dim3(kWave), 0, s,
-                       static_cast<const float*>(q_phys), static_cast<const float*>(k_phys),
-                       static_cast<const float*>(v_phys), static_cast<const float*>(k_cache),
-                       static_cast<const float*>(v_cache), block_table, prefix_len,
-                       static_cast<float*>(out_phys), B, W, Hq, Hkv, D, num_pages, max_pages,
-                       max_prefix_len, cache_layer_stride, scale_log2);
+    RopeF32 rp{};
+    rp.perm = perm;
+    rp.pos = pos;
+    for (int j = 0; j < kF32MaxD / 2; ++j) rp.omega[j] = omega[j];
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kWave), 0, s,
+                         static_cast<const float*>(q), static_cast<const float*>(k),
+                         static_cast<const float*>(v), static_cast<const float*>(k_cache),
+                         static_cast<const float*>(v_cache), block_table, prefix_len,
+                         static_cast<float*>(out_phys), B, W, Hq, Hkv, D, num_pages, max_pages,
+                         max_prefix_len, cache_layer_stride, scale_log2, rp);
+    };
+    if (rope)
+      go(k_window_attn_f32<true>);
+    else
+      go(k_window_attn_f32<false>);
     return launch_status();
   }
   const AttnPlan pl = plan_bf16(n_layers, B, W, Hq, Hkv, max_prefix_len);
   const size_t need = pl.ws_o_bytes + pl.ws_ml_bytes;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return WEDLM_ERR_WORKSPACE;
   AttnArgs a;
-  a.q = static_cast<const uint16_t*>(q_phys);
-  a.k = static_cast<const uint16_t*>(k_phys);
-  a.v = static_cast<const uint16_t*>(v_phys);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
   a.kc = static_cast<const uint16_t*>(k_cache);
   a.vc = static_cast<const uint16_t*>(v_cache);
   a.block_table = block_table;
@@ -710,16 +849,22 @@ extern "C" int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, 
   a.n_splits = pl.n_splits;
   a.cache_layer_stride = cache_layer_stride;
   a.scale_log2 = scale_log2;
+  a.perm = perm;
+  a.pos = pos;
+  for (int j = 0; j < kHeadDim / 2; ++j) a.omega[j] = omega[j];
   const long long groups = 1LL * n_layers * B * Hkv;
   const long long blocks = groups * pl.n_splits;
   if (blocks > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
   const dim3 grid(static_cast<unsigned>(blocks));
+  auto go = [&](auto kernel, int waves) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kWave * waves), 0, s, a);
+  };
   if (pl.waves == 4)
-    hipLaunchKernelGGL(k_window_attn_bf16<4>, grid, dim3(kWave * 4), 0, s, a);
+    rope ? go(k_window_attn_bf16<4, true>, 4) : go(k_window_attn_bf16<4, false>, 4);
   else if (pl.waves == 8)
-    hipLaunchKernelGGL(k_window_attn_bf16<8>, grid, dim3(kWave * 8), 0, s, a);
+    rope ? go(k_window_attn_bf16<8, true>, 8) : go(k_window_attn_bf16<8, false>, 8);
   else
-    hipLaunchKernelGGL(k_window_attn_bf16<16>, grid, dim3(kWave * 16), 0, s, a);
+    rope ? go(k_window_attn_bf16<16, true>, 16) : go(k_window_attn_bf16<16, false>, 16);
   st = launch_status();
   if (st != WEDLM_OK || pl.n_splits == 1) return st;
   const long long threads = groups * a.M * (kHeadDim / 4);
@@ -727,4 +872,30 @@ extern "C" int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, 
                      dim3(256), 0, s, a.ws_o, a.ws_ml, a.out, static_cast<int>(groups), a.M,
                      pl.n_splits, B, W, Hq, Hkv, a.g);
   return launch_status();
+}
+
+extern "C" int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D,
+                                 int page_size, int num_pages, int max_pages, int max_prefix_len,
+                                 float scale, const void* q_phys, const void* k_phys,
+                                 const void* v_phys, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* prefix_len,
+                                 void* out_phys, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return launch_attn(false, dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages,
+                     max_prefix_len, scale, 0.0, q_phys, k_phys, v_phys, nullptr, nullptr, k_cache,
+                     v_cache, block_table, prefix_len, out_phys, workspace, workspace_bytes,
+                     stream);
+}
+
+extern "C" int wedlm_window_attn_rope(int dtype, int n_layers, int B, int W, int Hq, int Hkv,
+                                      int D, int page_size, int num_pages, int max_pages,
+                                      int max_prefix_len, float scale, double theta, const void* q,
+                                      const void* k, const void* v, const int32_t* perm,
+                                      const int32_t* pos, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_table,
+                                      const int32_t* prefix_len, void* out_phys, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return launch_attn(true, dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages,
+                     max_prefix_len, scale, theta, q, k, v, perm, pos, k_cache, v_cache,
+                     block_table, prefix_len, out_phys, workspace, workspace_bytes, stream);
 }

@@ -7,13 +7,16 @@
 // "Builds on").
 //
 // Two kernels on the caller's stream:
-//   k_commit_rows  grid (sequence, layer): copies the c committed rows of
+//   k_commit_rows  grid (sequence x kv head, layer): copies the c committed rows of
 //                  k_phys / v_phys (physical rows 0..c-1 are slots 0..c-1) into
 //                  the pages at positions L..L+c-1.
 //   k_commit_state one wavefront per sequence: cache slots, window shift with
 //                  the new fills, mask refill, prefix_len += c. It runs after
 //                  the copies (same stream), which read the old prefix_len.
 #include "common.hpp"
+
+#include <cmath>
+#include <type_traits>
 
 namespace wedlm {
 
@@ -25,15 +28,39 @@ __device__ __forceinline__ int commit_length(int run, int L, int W, int max_page
   return min(c, room);
 }
 
-template <typename T>
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Committed rows are written as whole 64-byte lines: a line holds 4 keys of
+// one 16-byte K slice, or 16 keys of 64 / (16 * sizeof(T)) value dimensions.
+// Each line touched by the commit is read, the committed keys are merged in
+// registers (static indices, so nothing goes to scratch) and the line is
+// stored back in full - partial-line stores would make the memory system
+// read-modify-write every 2- or 16-byte piece. One thread owns one line; one
+// block covers one (sequence, kv head, layer), so a commit of c <= 16 rows
+// touches at most 5 x D/8 key lines and 2 x D/2 value lines per block: one
+// round of 256 threads for D = 128.
+constexpr int kCommitMaxD = 256;
+
+// RoPE frequencies theta^(-2j/D) for the fused variant (host-computed).
+struct CommitRope {
+  double omega[kCommitMaxD / 2];
+};
+
+// kRope: k_phys / v_phys are the window rows in slot order before RoPE (the
+// committed rows 0..c-1 are slots 0..c-1 either way); each committed key is
+// rotated at its logical position L + j as it is written.
+template <typename T, bool kRope>
 __global__ void __launch_bounds__(kCommitThreads)
 k_commit_rows(int B, int W, int Hkv, int D, int P, int num_pages, int max_pages,
               const int32_t* __restrict__ run_len, const int32_t* __restrict__ prefix_len,
               const T* __restrict__ k_phys, const T* __restrict__ v_phys,
               const int32_t* __restrict__ block_table, T* __restrict__ k_cache,
-              T* __restrict__ v_cache, long long cache_layer_stride) {
-  constexpr int X = 16 / sizeof(T);  // elements per 16-byte key slice
-  const int b = blockIdx.x;
+              T* __restrict__ v_cache, long long cache_layer_stride, CommitRope rope) {
+  constexpr int X = 16 / sizeof(T);         // elements per 16-byte K slice
+  constexpr int kLineElems = 64 / sizeof(T);
+  constexpr int kDimsPerLine = kLineElems / 16;  // value dimensions per line (P = 16)
+  const int b = blockIdx.x / Hkv;
+  const int kvh = blockIdx.x % Hkv;
   const int layer = blockIdx.y;
   const int L = max(prefix_len[b], 0);
   const int c = commit_length(run_len[b], L, W, max_pages, P);
@@ -43,28 +70,79 @@ k_commit_rows(int B, int W, int Hkv, int D, int P, int num_pages, int max_pages,
   T* kcl = k_cache + static_cast<size_t>(layer) * cache_layer_stride;
   T* vcl = v_cache + static_cast<size_t>(layer) * cache_layer_stride;
   const int slices = D / X;
-  // keys: one 16-byte slice per task
-  const int ktasks = c * Hkv * slices;
+  const int end = L + c;  // committed positions are L .. end-1
+
+  // keys: lines of 4 positions within one slice of one page
+  const int line0 = L / 4, nlines = (end - 1) / 4 - line0 + 1;
+  const int ktasks = nlines * slices;
   for (int task = threadIdx.x; task < ktasks; task += kCommitThreads) {
     const int sl = task % slices;
-    const int kvh = (task / slices) % Hkv;
-    const int j = task / (slices * Hkv);
-    const int t = L + j;
-    const int pid = min(max(bt[t / P], 0), num_pages - 1);
-    const T* src = k_phys + ((lb * W + j) * Hkv + kvh) * D + sl * X;
-    T* dst = kcl + ((static_cast<size_t>(pid) * Hkv + kvh) * slices + sl) * P * X + (t % P) * X;
-    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    const int t0 = (line0 + task / slices) * 4;
+    const int pid = min(max(bt[t0 / P], 0), num_pages - 1);
+    u32x4* dst = reinterpret_cast<u32x4*>(
+        kcl + ((static_cast<size_t>(pid) * Hkv + kvh) * slices + sl) * P * X + (t0 % P) * X);
+    u32x4 line[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) line[e] = dst[e];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = t0 + e;
+      if (t >= L && t < end) {
+        const T* krow = k_phys + ((lb * W + (t - L)) * Hkv + kvh) * D;
+        line[e] = *reinterpret_cast<const u32x4*>(krow + sl * X);
+        if constexpr (kRope) {
+          // rotate-half: slice sl pairs with sl +- slices/2
+          const int hs = slices / 2;
+          const bool lower = sl < hs;
+          const int j0 = (lower ? sl : sl - hs) * X;  // first frequency index
+          union {
+            u32x4 v;
+            T e[X];
+          } own, mate, out;
+          own.v = line[e];
+          mate.v = *reinterpret_cast<const u32x4*>(krow + (lower ? sl + hs : sl - hs) * X);
+#pragma unroll
+          for (int x = 0; x < X; ++x) {
+            float c, sn;
+            rope_cos_sin(static_cast<double>(t), rope.omega[j0 + x], c, sn);
+            const float a = Elt<T>::load(&own.e[x]), m = Elt<T>::load(&mate.e[x]);
+            // lower half: a cos - mate sin; upper half: a cos + mate sin
+            Elt<T>::store(&out.e[x], lower ? a * c - m * sn : a * c + m * sn);
+          }
+          line[e] = out.v;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = line[e];
   }
-  // values: the page stores each dimension's P positions contiguously
-  const int vtasks = c * Hkv * D;
+
+  // values: lines of kDimsPerLine dimensions x 16 positions of one page
+  const int pg0 = L / P, npg = (end - 1) / P - pg0 + 1;
+  const int groups = D / kDimsPerLine;
+  const int vtasks = npg * groups;
   for (int task = threadIdx.x; task < vtasks; task += kCommitThreads) {
-    const int d = task % D;
-    const int kvh = (task / D) % Hkv;
-    const int j = task / (D * Hkv);
-    const int t = L + j;
-    const int pid = min(max(bt[t / P], 0), num_pages - 1);
-    vcl[((static_cast<size_t>(pid) * Hkv + kvh) * D + d) * P + (t % P)] =
-        v_phys[((lb * W + j) * Hkv + kvh) * D + d];
+    const int dg = task % groups;
+    const int pg = pg0 + task / groups;
+    const int pid = min(max(bt[pg], 0), num_pages - 1);
+    T* dst = vcl + ((static_cast<size_t>(pid) * Hkv + kvh) * D + dg * kDimsPerLine) * P;
+    union {
+      u32x4 v[4];
+      T e[kLineElems];
+    } line;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) line.v[i] = reinterpret_cast<const u32x4*>(dst)[i];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int t = pg * P + e;
+      if (t >= L && t < end) {
+        const T* src = v_phys + ((lb * W + (t - L)) * Hkv + kvh) * D + dg * kDimsPerLine;
+#pragma unroll
+        for (int dd = 0; dd < kDimsPerLine; ++dd) line.e[dd * 16 + e] = src[dd];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(dst)[i] = line.v[i];
   }
 }
 
@@ -115,6 +193,54 @@ k_commit_state(int W, int P, int num_pages, int max_pages, const int32_t* __rest
 
 using namespace wedlm;
 
+static int launch_commit(bool rope, int dtype, int n_layers, int B, int W, int Hkv, int D,
+                         int page_size, int num_pages, int max_pages, double theta,
+                         const int32_t* run_len, const uint8_t* selected,
+                         const int32_t* argmax_tok, const void* k_rows, const void* v_rows,
+                         const int32_t* block_table, void* k_cache, void* v_cache, int32_t* tokens,
+                         uint8_t* filled, int32_t* prefix_len, int32_t* commit_len,
+                         int32_t* cache_slot, int32_t mask_id, void* stream) {
+  if (!valid_dtype(dtype)) return WEDLM_ERR_UNSUPPORTED;
+  if (n_layers <= 0 || B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW || Hkv <= 0 || D <= 0 ||
+      page_size <= 0 || num_pages <= 0 || max_pages <= 0)
+    return WEDLM_ERR_INVALID;
+  if (rope && !(theta > 0.0)) return WEDLM_ERR_INVALID;
+  const int X = 16 / static_cast<int>(elt_size(dtype));
+  if (D % X != 0 || page_size != 16) return WEDLM_ERR_UNSUPPORTED;
+  if (rope && (D % (2 * X) != 0 || D > kCommitMaxD)) return WEDLM_ERR_UNSUPPORTED;
+  if (!run_len || !selected || !argmax_tok || !k_rows || !v_rows || !block_table || !k_cache ||
+      !v_cache || !tokens || !filled || !prefix_len || !commit_len || !cache_slot)
+    return WEDLM_ERR_INVALID;
+  if (n_layers > 65535) return WEDLM_ERR_UNSUPPORTED;
+  if (1LL * B * Hkv > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  const long long stride = 1LL * num_pages * Hkv * D * page_size;
+  CommitRope tab{};
+  if (rope)
+    for (int j = 0; j < D / 2; ++j) tab.omega[j] = std::pow(theta, -2.0 * j / D);
+  const dim3 grid(B * Hkv, n_layers);
+  auto go = [&](auto kernel, auto* tag) {
+    using T = std::remove_pointer_t<decltype(tag)>;
+    hipLaunchKernelGGL(kernel, grid, dim3(kCommitThreads), 0, s, B, W, Hkv, D, page_size,
+                       num_pages, max_pages, run_len, prefix_len, static_cast<const T*>(k_rows),
+                       static_cast<const T*>(v_rows), block_table, static_cast<T*>(k_cache),
+                       static_cast<T*>(v_cache), stride, tab);
+  };
+  if (dtype == WEDLM_BF16) {
+    uint16_t* tag = nullptr;
+    rope ? go(k_commit_rows<uint16_t, true>, tag) : go(k_commit_rows<uint16_t, false>, tag);
+  } else {
+    float* tag = nullptr;
+    rope ? go(k_commit_rows<float, true>, tag) : go(k_commit_rows<float, false>, tag);
+  }
+  int st = launch_status();
+  if (st != WEDLM_OK) return st;
+  hipLaunchKernelGGL(k_commit_state, dim3(B), dim3(kWave), 0, s, W, page_size, num_pages,
+                     max_pages, run_len, selected, argmax_tok, block_table, tokens, filled,
+                     prefix_len, commit_len, cache_slot, mask_id);
+  return launch_status();
+}
+
 extern "C" int wedlm_commit_prefix(int dtype, int n_layers, int B, int W, int Hkv, int D,
                                    int page_size, int num_pages, int max_pages,
                                    const int32_t* run_len, const uint8_t* selected,
@@ -123,35 +249,21 @@ extern "C" int wedlm_commit_prefix(int dtype, int n_layers, int B, int W, int Hk
                                    void* v_cache, int32_t* tokens, uint8_t* filled,
                                    int32_t* prefix_len, int32_t* commit_len, int32_t* cache_slot,
                                    int32_t mask_id, void* stream) {
-  if (!valid_dtype(dtype)) return WEDLM_ERR_UNSUPPORTED;
-  if (n_layers <= 0 || B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW || Hkv <= 0 || D <= 0 ||
-      page_size <= 0 || num_pages <= 0 || max_pages <= 0)
-    return WEDLM_ERR_INVALID;
-  const int X = 16 / static_cast<int>(elt_size(dtype));
-  if (D % X != 0) return WEDLM_ERR_UNSUPPORTED;
-  if (!run_len || !selected || !argmax_tok || !k_phys || !v_phys || !block_table || !k_cache ||
-      !v_cache || !tokens || !filled || !prefix_len || !commit_len || !cache_slot)
-    return WEDLM_ERR_INVALID;
-  if (n_layers > 65535) return WEDLM_ERR_UNSUPPORTED;
-  hipStream_t s = as_stream(stream);
-  const long long stride = 1LL * num_pages * Hkv * D * page_size;
-  const dim3 grid(B, n_layers);
-  if (dtype == WEDLM_BF16)
-    hipLaunchKernelGGL(k_commit_rows<uint16_t>, grid, dim3(kCommitThreads), 0, s, B, W, Hkv, D,
-                       page_size, num_pages, max_pages, run_len, prefix_len,
-                       static_cast<const uint16_t*>(k_phys), static_cast<const uint16_t*>(v_phys),
-                       block_table, static_cast<uint16_t*>(k_cache),
-                       static_cast<uint16_t*>(v_cache), stride);
-  else
-    hipLaunchKernelGGL(k_commit_rows<float>, grid, dim3(kCommitThreads), 0, s, B, W, Hkv, D,
-                       page_size, num_pages, max_pages, run_len, prefix_len,
-                       static_cast<const float*>(k_phys), static_cast<const float*>(v_phys),
-                       block_table, static_cast<float*>(k_cache), static_cast<float*>(v_cache),
-                       stride);
-  int st = launch_status();
-  if (st != WEDLM_OK) return st;
-  hipLaunchKernelGGL(k_commit_state, dim3(B), dim3(kWave), 0, s, W, page_size, num_pages,
-                     max_pages, run_len, selected, argmax_tok, block_table, tokens, filled,
-                     prefix_len, commit_len, cache_slot, mask_id);
-  return launch_status();
+  return launch_commit(false, dtype, n_layers, B, W, Hkv, D, page_size, num_pages, max_pages, 0.0,
+                       run_len, selected, argmax_tok, k_phys, v_phys, block_table, k_cache,
+                       v_cache, tokens, filled, prefix_len, commit_len, cache_slot, mask_id,
+                       stream);
+}
+
+extern "C" int wedlm_commit_prefix_rope(int dtype, int n_layers, int B, int W, int Hkv, int D,
+                                        int page_size, int num_pages, int max_pages, double theta,
+                                        const int32_t* run_len, const uint8_t* selected,
+                                        const int32_t* argmax_tok, const void* k, const void* v,
+                                        const int32_t* block_table, void* k_cache, void* v_cache,
+                                        int32_t* tokens, uint8_t* filled, int32_t* prefix_len,
+                                        int32_t* commit_len, int32_t* cache_slot,
+                                        int32_t mask_id, void* stream) {
+  return launch_commit(true, dtype, n_layers, B, W, Hkv, D, page_size, num_pages, max_pages,
+                       theta, run_len, selected, argmax_tok, k, v, block_table, k_cache, v_cache,
+                       tokens, filled, prefix_len, commit_len, cache_slot, mask_id, stream);
 }

@@ -44,6 +44,39 @@ template <> struct Elt<uint16_t> {
   static __device__ __forceinline__ void store(uint16_t* p, float x) { *p = f32_to_bf16(x); }
 };
 
+// ---- RoPE angle ---------------------------------------------------------------
+
+// cos and sin of t * omega radians (RoFormer rotation, mlsanity.com page on
+// WeDLM, "Builds on"). The angle is formed in double precision and reduced by
+// multiples of pi/2 (a two-part pi/2, so the remainder keeps ~1e-16 absolute
+// accuracy for angles up to 1e6 rad; an fp32 angle at position 1e4 would be
+// off by milliradians). On the remainder, |r| <= pi/4, the Taylor series of
+// sin to r^9 and of cos to r^10 are below 1e-8 of truncation error, and are
+// evaluated in fp32; the quadrant n mod 4 then rotates (sin, cos).
+__device__ __forceinline__ void rope_cos_sin(double t, double omega, float& c, float& s) {
+  constexpr double k2OverPi = 0.6366197723675814;
+  constexpr double kPiHalfHi = 1.5707963267948966;     // nearest double to pi/2
+  constexpr double kPiHalfLo = 6.123233995736766e-17;  // pi/2 - kPiHalfHi
+  const double a = t * omega;
+  const double n = rint(a * k2OverPi);
+  const float r = static_cast<float>(fma(-n, kPiHalfHi, a) - n * kPiHalfLo);
+  const float r2 = r * r;
+  const float sr =
+      r * fmaf(r2, fmaf(r2, fmaf(r2, fmaf(r2, 2.7557319e-6f, -1.9841270e-4f), 8.3333333e-3f),
+                        -1.6666667e-1f),
+               1.f);
+  const float cr = fmaf(
+      r2,
+      fmaf(r2, fmaf(r2, fmaf(r2, fmaf(r2, -2.7557319e-7f, 2.4801587e-5f), -1.3888889e-3f),
+                    4.1666668e-2f),
+           -0.5f),
+      1.f);
+  const int q = static_cast<int>(static_cast<long long>(n) & 3);
+  // sin(r + q pi/2) and cos(r + q pi/2)
+  s = q == 0 ? sr : (q == 1 ? cr : (q == 2 ? -sr : -cr));
+  c = q == 0 ? cr : (q == 1 ? -sr : (q == 2 ? -cr : sr));
+}
+
 // ---- wave reductions (64 lanes) --------------------------------------------
 
 __device__ __forceinline__ float wave_max(float x) {

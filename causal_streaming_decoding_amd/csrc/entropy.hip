@@ -12,8 +12,9 @@
 // Each thread keeps (m, s, t) for its strided 16-byte vectors; when a vector
 // raises the running max the sums are rescaled by 2^(m_old - m_new) (exact
 // identity: t' = (t + d s) 2^d with d = (m_old - m_new) log2 e). The argmax is
-// tracked as the vector index where the thread's max last rose; the winning
-// vector is re-read once at the end to find the lowest index holding the max.
+// tracked as the vector where the thread's max last rose, whose raw bits are
+// kept in registers; at the end the lowest index holding the max is found in
+// them, so no logit is read twice.
 //
 // k_entropy_partial: grid (chunks, rows); each block reduces one chunk of one
 //   row to (m, s, t, argmax) in the workspace.
@@ -50,14 +51,20 @@ __device__ __forceinline__ void merge(EntPartial& a, const EntPartial& b) {
   a.idx = idx;
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <typename T>
 struct EVec {
   static constexpr int N = 16 / sizeof(T);
   union {
-    uint4 raw;
+    u32x4 raw;
     T e[N];
   };
 };
+
+// Vectors (16 bytes, or single elements when !VEC) per thread per block: all
+// of a thread's loads are issued before any is reduced.
+constexpr int kEntIter = 4;
 
 // VEC: rows are 16-byte aligned and V is a multiple of the vector width.
 template <typename T, bool VEC>
@@ -71,43 +78,59 @@ k_entropy_partial(const T* __restrict__ logits, int V, int chunk_elems, int n_ch
   const int end = min(V, begin + chunk_elems);
   const T* z = logits + static_cast<size_t>(row) * V;
   float m = kNegBig, s = 0.f, t = 0.f;
-  int best_it = -1;
-  int it = 0;
-  for (int i0 = begin + threadIdx.x * N; i0 < end; i0 += kEntThreads * N, ++it) {
-    float x[N];
-    if constexpr (VEC) {
-      EVec<T> vv;
-      vv.raw = *reinterpret_cast<const uint4*>(z + i0);
+  int best = -1;       // first element index of the vector where the max last rose
+  u32x4 best_raw = {0u, 0u, 0u, 0u};
+  // one pass of this loop when VEC (the chunk is exactly kEntIter vectors per
+  // thread), 16 / sizeof(T) passes of single elements otherwise
+  for (int base = begin; base < end; base += kEntThreads * kEntIter * N) {
+    EVec<T> vv[kEntIter];
 #pragma unroll
-      for (int e = 0; e < N; ++e) x[e] = Elt<T>::load(&vv.e[e]);
-    } else {
-      x[0] = Elt<T>::load(z + i0);
+    for (int it = 0; it < kEntIter; ++it) {
+      const int i0 = base + (it * kEntThreads + threadIdx.x) * N;
+      if constexpr (VEC) {
+        vv[it].raw = i0 < end ? *reinterpret_cast<const u32x4*>(z + i0) : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        vv[it].raw = u32x4{0u, 0u, 0u, 0u};
+        if (i0 < end) vv[it].e[0] = z[i0];
+      }
     }
-    float mz = x[0];
 #pragma unroll
-    for (int e = 1; e < N; ++e) mz = fmaxf(mz, x[e]);
-    if (mz > m) best_it = it;
-    const float mn = fmaxf(m, mz);
-    const float d = (m - mn) * kLog2eF;
-    const float f = __builtin_amdgcn_exp2f(d);
-    t = (t + d * s) * f;
-    s = s * f;
-    m = mn;
-    const float mb = mn * kLog2eF;
+    for (int it = 0; it < kEntIter; ++it) {
+      const int i0 = base + (it * kEntThreads + threadIdx.x) * N;
+      if (i0 >= end) break;
+      float x[N];
 #pragma unroll
-    for (int e = 0; e < N; ++e) {
-      const float u = fmaf(x[e], kLog2eF, -mb);
-      const float p = __builtin_amdgcn_exp2f(u);
-      s += p;
-      t = fmaf(p, u, t);
+      for (int e = 0; e < N; ++e) x[e] = Elt<T>::load(&vv[it].e[e]);
+      float mz = x[0];
+#pragma unroll
+      for (int e = 1; e < N; ++e) mz = fmaxf(mz, x[e]);
+      if (mz > m) {
+        best = i0;
+        best_raw = vv[it].raw;
+      }
+      const float mn = fmaxf(m, mz);
+      const float d = (m - mn) * kLog2eF;
+      const float f = __builtin_amdgcn_exp2f(d);
+      t = (t + d * s) * f;
+      s = s * f;
+      m = mn;
+      const float mb = mn * kLog2eF;
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        const float u = fmaf(x[e], kLog2eF, -mb);
+        const float p = __builtin_amdgcn_exp2f(u);
+        s += p;
+        t = fmaf(p, u, t);
+      }
     }
   }
   EntPartial acc{m, s, t, 0x7fffffff};
-  if (best_it >= 0) {
-    const int i0 = begin + (best_it * kEntThreads + threadIdx.x) * N;
+  if (best >= 0) {
+    EVec<T> bv;
+    bv.raw = best_raw;
 #pragma unroll
     for (int e = N - 1; e >= 0; --e)
-      if (Elt<T>::load(z + i0 + e) == m) acc.idx = i0 + e;
+      if (Elt<T>::load(&bv.e[e]) == m) acc.idx = best + e;
   }
   // wavefront then block reduction
 #pragma unroll
@@ -142,8 +165,19 @@ k_entropy_select(const EntPartial* __restrict__ part, int n_chunks, int W,
   bool cand = false;
   if (in_window) {
     const int row = b * W + i;
-    EntPartial acc = part[static_cast<size_t>(row) * n_chunks];
-    for (int c = 1; c < n_chunks; ++c) merge(acc, part[static_cast<size_t>(row) * n_chunks + c]);
+    const EntPartial* pr = part + static_cast<size_t>(row) * n_chunks;
+    EntPartial acc = pr[0];
+    // partials are loaded 8 at a time so that their latencies overlap, and
+    // merged in chunk order
+    for (int c0 = 1; c0 < n_chunks; c0 += 8) {
+      EntPartial buf[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (c0 + k < n_chunks) buf[k] = pr[c0 + k];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (c0 + k < n_chunks) merge(acc, buf[k]);
+    }
     const float H = kLn2F * (log2f(acc.s) - acc.t / acc.s);
     // product rounded, then the sum: no fused multiply-add
     sc = __fadd_rn(H, __fmul_rn(lambda, static_cast<float>(i)));
@@ -182,15 +216,12 @@ static EntPlan plan_entropy(int dtype, int B, int W, int V) {
   EntPlan pl{};
   const int N = 16 / static_cast<int>(elt_size(dtype));
   pl.vec = (V % N) == 0;
-  const int step = kEntThreads * (pl.vec ? N : 1);  // elements per block iteration
-  const long long rows = 1LL * B * W;
-  long long want = (4096 + rows - 1) / rows;         // ~16 blocks per CU in total
-  const long long max_chunks = (V + step - 1) / step;
-  want = want < 1 ? 1 : (want > max_chunks ? max_chunks : want);
-  int per = static_cast<int>((V + want - 1) / want);
-  per = ((per + step - 1) / step) * step;
-  pl.chunk_elems = per;
-  pl.n_chunks = (V + per - 1) / per;
+  // a chunk is kEntIter 16-byte vectors per thread (the same element count on
+  // the single-element path, so the workspace does not depend on alignment)
+  pl.chunk_elems = kEntThreads * kEntIter * N;
+  pl.n_chunks = (V + pl.chunk_elems - 1) / pl.chunk_elems;
+  (void)B;
+  (void)W;
   return pl;
 }
 
@@ -217,13 +248,7 @@ extern "C" int wedlm_entropy_select(int dtype, int B, int W, int V, const void* 
     return WEDLM_ERR_INVALID;
   if (1LL * B * W > 65535) return WEDLM_ERR_UNSUPPORTED;
   EntPlan pl = plan_entropy(dtype, B, W, V);
-  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) {
-    pl.vec = false;
-    const int step = kEntThreads;
-    int per = ((pl.chunk_elems + step - 1) / step) * step;
-    pl.chunk_elems = per;
-    pl.n_chunks = (V + per - 1) / per;
-  }
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) pl.vec = false;
   const size_t need = static_cast<size_t>(B) * W * pl.n_chunks * sizeof(EntPartial);
   if (need > wedlm_entropy_select_workspace_size(dtype, B, W, V) ||
       workspace == nullptr || workspace_bytes < need)

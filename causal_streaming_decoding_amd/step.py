@@ -1,12 +1,15 @@
-"""Window-step driver: the five C entry points in order on one stream.
+"""Window-step driver: the C entry points in order on one stream.
 
 hyper.ai summary of WeDLM, "Method" (Streaming Parallel Decoding): reorder the
 window, run the causal forward over it against the KV cache, select by
 distance-penalised entropy, commit the leftmost filled run and refill. Here the
 forward's projections and logits are inputs (synthetic), so one step is:
 reorder -> RoPE at logical positions -> window attention -> entropy/select ->
-commit. Device buffers are allocated once; ``run`` only enqueues kernels and
-never synchronises, so steps can be chained or timed back to back.
+commit. With ``fused_rope`` (the default) the RoPE step runs inside the
+attention and commit calls (wedlm_window_attn_rope, wedlm_commit_prefix_rope)
+instead of as its own pass over the window. Device buffers are allocated once;
+``run`` only enqueues kernels and never synchronises, so steps can be chained
+or timed back to back.
 """
 
 from dataclasses import dataclass
@@ -39,7 +42,8 @@ class WindowStep:
     """Buffers and launches of one window step for fixed shapes."""
 
     def __init__(self, n_layers, B, W, Hq, Hkv, D, V, page_size, num_pages, max_pages, dtype,
-                 device, max_prefix_len, theta, lam, tau, min_fill=1, mask_id=-1, scale=None):
+                 device, max_prefix_len, theta, lam, tau, min_fill=1, mask_id=-1, scale=None,
+                 fused_rope=True):
         self.n_layers, self.B, self.W, self.Hq, self.Hkv, self.D, self.V = (
             n_layers, B, W, Hq, Hkv, D, V)
         self.page_size, self.num_pages, self.max_pages = page_size, num_pages, max_pages
@@ -48,6 +52,7 @@ class WindowStep:
         self.theta, self.lam, self.tau, self.min_fill, self.mask_id = theta, lam, tau, min_fill, mask_id
         self.scale = scale if scale is not None else D ** -0.5
         self.max_prefix_len = max_prefix_len
+        self.fused_rope = fused_rope
         i32 = dict(dtype=torch.int32, device=device)
         self.perm = torch.empty((B, W), **i32)
         self.inv = torch.empty((B, W), **i32)
@@ -55,9 +60,12 @@ class WindowStep:
         self.n_obs = torch.empty((B,), **i32)
         self.run_len = torch.empty((B,), **i32)
         fl = dict(dtype=dtype, device=device)
-        self.q_phys = torch.empty((n_layers, B, W, Hq, D), **fl)
-        self.k_phys = torch.empty((n_layers, B, W, Hkv, D), **fl)
-        self.v_phys = torch.empty((n_layers, B, W, Hkv, D), **fl)
+        # physical-order rotated copies: only the unfused path writes them
+        self.q_phys = self.k_phys = self.v_phys = None
+        if not fused_rope:
+            self.q_phys = torch.empty((n_layers, B, W, Hq, D), **fl)
+            self.k_phys = torch.empty((n_layers, B, W, Hkv, D), **fl)
+            self.v_phys = torch.empty((n_layers, B, W, Hkv, D), **fl)
         self.out_phys = torch.empty((n_layers, B, W, Hq, D), **fl)
         self.entropy = torch.empty((B, W), dtype=torch.float32, device=device)
         self.score = torch.empty((B, W), dtype=torch.float32, device=device)
@@ -86,22 +94,43 @@ class WindowStep:
                               self.theta, q, k, v, self.perm, self.pos, self.q_phys, self.k_phys,
                               self.v_phys, stream)
 
-    def attn(self, st, max_prefix_len=None, stream=None):
+    def _attn_mpl(self, max_prefix_len):
         mpl = self.max_prefix_len if max_prefix_len is None else max_prefix_len
         need = W_.wedlm_window_attn_workspace_size(self.dt, self.n_layers, self.B, self.W, self.Hq,
                                                    self.Hkv, self.D, self.page_size, mpl)
         if need > self.attn_ws_bytes:
             self._size_attn_workspace(mpl)
+        return mpl
+
+    def attn(self, st, max_prefix_len=None, stream=None):
+        mpl = self._attn_mpl(max_prefix_len)
         W_.wedlm_window_attn(self.dt, self.n_layers, self.B, self.W, self.Hq, self.Hkv, self.D,
                              self.page_size, self.num_pages, self.max_pages, mpl, self.scale,
                              self.q_phys, self.k_phys, self.v_phys, st.k_cache, st.v_cache,
                              st.block_table, st.prefix_len, self.out_phys, self.attn_ws,
                              self.attn_ws_bytes, stream)
 
+    def attn_rope(self, st, q, k, v, max_prefix_len=None, stream=None):
+        mpl = self._attn_mpl(max_prefix_len)
+        W_.wedlm_window_attn_rope(self.dt, self.n_layers, self.B, self.W, self.Hq, self.Hkv,
+                                  self.D, self.page_size, self.num_pages, self.max_pages, mpl,
+                                  self.scale, self.theta, q, k, v, self.perm, self.pos,
+                                  st.k_cache, st.v_cache, st.block_table, st.prefix_len,
+                                  self.out_phys, self.attn_ws, self.attn_ws_bytes, stream)
+
     def entropy_select(self, st, logits, stream=None):
         W_.wedlm_entropy_select(self.dt, self.B, self.W, self.V, logits, st.filled, self.lam,
                                 self.tau, self.min_fill, self.entropy, self.score, self.argmax,
                                 self.selected, self.ent_ws, self.ent_ws_bytes, stream)
+
+    def commit_rope(self, st, k, v, commit_len=None, stream=None):
+        W_.wedlm_commit_prefix_rope(self.dt, self.n_layers, self.B, self.W, self.Hkv, self.D,
+                                    self.page_size, self.num_pages, self.max_pages, self.theta,
+                                    self.run_len, self.selected, self.argmax, k, v,
+                                    st.block_table, st.k_cache, st.v_cache, st.tokens, st.filled,
+                                    st.prefix_len,
+                                    self.commit_len if commit_len is None else commit_len,
+                                    self.cache_slot, self.mask_id, stream)
 
     def commit(self, st, commit_len=None, stream=None):
         W_.wedlm_commit_prefix(self.dt, self.n_layers, self.B, self.W, self.Hkv, self.D,
@@ -112,28 +141,31 @@ class WindowStep:
                                self.cache_slot, self.mask_id, stream)
 
     def run(self, st, q, k, v, logits, max_prefix_len=None, commit_len=None, stream=None,
-            events=None):
+            mark=None):
         """One whole window step.
 
-        ``events``: optional dict with "attn" and/or "entropy" -> (start, end)
-        torch.cuda.Event pairs recorded around those calls on ``stream``.
+        ``mark``: optional callable invoked with "attn_start", "attn_end" (also
+        the start of entropy/select) and "entropy_end" at those points of the
+        launch sequence, e.g. to record timing events on ``stream``.
         """
-        def mark(name, i):
-            if events is not None and name in events:
-                if stream is None:
-                    events[name][i].record()
-                else:
-                    events[name][i].record(stream)
-
         self.reorder(st, stream)
-        self.rope(q, k, v, stream)
-        mark("attn", 0)
-        self.attn(st, max_prefix_len, stream)
-        mark("attn", 1)
-        mark("entropy", 0)
+        if not self.fused_rope:
+            self.rope(q, k, v, stream)
+        if mark is not None:
+            mark("attn_start")
+        if self.fused_rope:
+            self.attn_rope(st, q, k, v, max_prefix_len, stream)
+        else:
+            self.attn(st, max_prefix_len, stream)
+        if mark is not None:
+            mark("attn_end")
         self.entropy_select(st, logits, stream)
-        mark("entropy", 1)
-        self.commit(st, commit_len, stream)
+        if mark is not None:
+            mark("entropy_end")
+        if self.fused_rope:
+            self.commit_rope(st, k, v, commit_len, stream)
+        else:
+            self.commit(st, commit_len, stream)
 
 
 def upload_step_inputs(wl, inp, device):
@@ -167,10 +199,11 @@ def upload_step_inputs(wl, inp, device):
     return st, q, k, v, logits, int(inp["prefix_len"].max())
 
 
-def make_window_step(wl, inp, device, max_prefix_len):
+def make_window_step(wl, inp, device, max_prefix_len, fused_rope=True):
     """WindowStep sized for a workload and its inputs."""
     from .synth import torch_dtype
 
     return WindowStep(wl.n_layers, wl.B, wl.W, wl.Hq, wl.Hkv, wl.D, wl.V, wl.page_size,
                       inp["num_pages"], inp["block_table"].shape[1], torch_dtype(wl), device,
-                      max_prefix_len, wl.theta, wl.lam, wl.tau, wl.min_fill, wl.mask_id)
+                      max_prefix_len, wl.theta, wl.lam, wl.tau, wl.min_fill, wl.mask_id,
+                      fused_rope=fused_rope)

@@ -14,6 +14,10 @@
  *      distance-penalised score, fill of the mask slots that clear a threshold.
  *   5. wedlm_commit_prefix   - the leftmost contiguous filled run is appended to
  *      the paged cache and the window is refilled with masks.
+ * Fused forms of steps 2-3 and 2-5: wedlm_window_attn_rope and
+ * wedlm_commit_prefix_rope apply the RoPE of step 2 as they load the window,
+ * so a step can run reorder -> attn_rope -> entropy_select -> commit_rope
+ * without the separate RoPE pass and its physical-order copies.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -152,6 +156,29 @@ int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv, in
                       const void* v_cache, const int32_t* block_table, const int32_t* prefix_len,
                       void* out_phys, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * wedlm_window_attn_rope - wedlm_window_attn with the RoPE step fused into its
+ * loads (the same operation as wedlm_rope_logical followed by
+ * wedlm_window_attn; hyper.ai summary, "Method": tokens keep their logical
+ * positions through the reordering).
+ *
+ * q, k, v are the window rows in slot order before RoPE, as wedlm_rope_logical
+ * takes them. Physical row p reads slot perm[b][p] and is rotated at pos[b][p]
+ * (query rows and window keys; values are only gathered). The angle is formed
+ * and reduced to [-pi/4, pi/4] in double precision, its sine and cosine
+ * evaluated in fp32 (error ~1e-7), the rotation done in fp32 and rounded once
+ * to the element type before the products, as with wedlm_rope_logical.
+ * No q_phys / k_phys / v_phys is written. All other arguments, layouts, sizes,
+ * workspace and errors are those of wedlm_window_attn; theta > 0.
+ */
+int wedlm_window_attn_rope(int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D,
+                           int page_size, int num_pages, int max_pages, int max_prefix_len,
+                           float scale, double theta, const void* q, const void* k, const void* v,
+                           const int32_t* perm, const int32_t* pos, const void* k_cache,
+                           const void* v_cache, const int32_t* block_table,
+                           const int32_t* prefix_len, void* out_phys, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace wedlm_entropy_select needs (per-chunk partial reductions). */
 size_t wedlm_entropy_select_workspace_size(int dtype, int B, int W, int V);
 
@@ -196,6 +223,9 @@ int wedlm_entropy_select(int dtype, int B, int W, int V, const void* logits, con
  *     with argmax_tok; the window shifts left by c; c masks (token mask_id,
  *     filled 0) are appended; prefix_len[b] += c; commit_len[b] = c.
  * c is clamped to [0, W] and to the pages the table holds (max_pages * P - L).
+ * Page size P = page_size must be 16 (WEDLM_ERR_UNSUPPORTED otherwise). The
+ * cache lines holding the committed rows are rewritten whole: positions of
+ * those pages beyond L+c-1 keep their previous contents.
  *
  * in : run_len, selected, argmax_tok (from the reorder / select calls of the
  *      same step), k_phys, v_phys (physical order), block_table.
@@ -209,6 +239,25 @@ int wedlm_commit_prefix(int dtype, int n_layers, int B, int W, int Hkv, int D, i
                         const void* v_phys, const int32_t* block_table, void* k_cache,
                         void* v_cache, int32_t* tokens, uint8_t* filled, int32_t* prefix_len,
                         int32_t* commit_len, int32_t* cache_slot, int32_t mask_id, void* stream);
+
+/*
+ * wedlm_commit_prefix_rope - wedlm_commit_prefix taking the window rows in slot
+ * order before RoPE (k, v as given to wedlm_rope_logical) instead of k_phys /
+ * v_phys. The committed rows 0..c-1 are slots 0..c-1 (the leading filled run
+ * comes first in physical order), so values are copied as they are and each
+ * committed key row j is rotated at its logical position L + j (angle and
+ * rounding as in wedlm_window_attn_rope) before it is written. With
+ * wedlm_window_attn_rope this makes the step's RoPE pass unnecessary. Other
+ * arguments, layouts and errors are those of wedlm_commit_prefix; theta > 0;
+ * D <= 256.
+ */
+int wedlm_commit_prefix_rope(int dtype, int n_layers, int B, int W, int Hkv, int D, int page_size,
+                             int num_pages, int max_pages, double theta, const int32_t* run_len,
+                             const uint8_t* selected, const int32_t* argmax_tok, const void* k,
+                             const void* v, const int32_t* block_table, void* k_cache,
+                             void* v_cache, int32_t* tokens, uint8_t* filled,
+                             int32_t* prefix_len, int32_t* commit_len, int32_t* cache_slot,
+                             int32_t mask_id, void* stream);
 
 #ifdef __cplusplus
 }

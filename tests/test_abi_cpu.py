@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(W.LIB_PATH),
 
 def test_exports_every_declared_function():
     declared = W.header_functions()
-    assert len(declared) == 9
+    assert len(declared) == 11
     lib = W.lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -31,6 +31,7 @@ def test_status_strings_and_version():
     assert "unsupported" in W.wedlm_status_string(-2)
     assert "workspace" in W.wedlm_status_string(-3)
     assert W.wedlm_abi_version() >> 16 == 1
+    assert W.wedlm_abi_version() & 0xffff >= 1  # fused RoPE entry points
 
 
 def _raw(name, *args):
@@ -74,6 +75,26 @@ def test_attn_validation_and_workspace():
     assert W.wedlm_window_attn_workspace_size(1, 36, 16, 16, 32, 8, 128, 16, 1024) == 0
 
 
+def test_fused_rope_entry_points_validate():
+    # wedlm_window_attn_rope: same checks as wedlm_window_attn plus theta, perm, pos
+    base = [1, 1, 4, 16, 32, 8, 128, 16, 8196, 2049, 32768, 0.088, 1e6] + [1] * 11 + [0, None]
+    assert _raw("wedlm_window_attn_rope", *base) == -3    # split planned, no workspace
+    a = list(base); a[12] = 0.0
+    assert _raw("wedlm_window_attn_rope", *a) == -1       # theta must be > 0
+    a = list(base); a[16] = None
+    assert _raw("wedlm_window_attn_rope", *a) == -1       # perm
+    a = list(base); a[6] = 64
+    assert _raw("wedlm_window_attn_rope", *a) == -2
+    # wedlm_commit_prefix_rope: those of wedlm_commit_prefix plus theta
+    c = [1, 36, 16, 16, 8, 128, 16, 100, 10, 1e6] + [1] * 13 + [-1, None]
+    a = list(c); a[9] = -1.0
+    assert _raw("wedlm_commit_prefix_rope", *a) == -1
+    a = list(c); a[6] = 8
+    assert _raw("wedlm_commit_prefix_rope", *a) == -2
+    a = list(c); a[13] = None
+    assert _raw("wedlm_commit_prefix_rope", *a) == -1
+
+
 def test_entropy_validation_and_workspace():
     ws = W.wedlm_entropy_select_workspace_size(1, 16, 16, 151936)
     assert ws > 0 and ws % 16 == 0
@@ -91,6 +112,8 @@ def test_commit_validation():
     assert _raw("wedlm_commit_prefix", *a) == -2         # D not a multiple of 8
     a = list(args); a[9] = None
     assert _raw("wedlm_commit_prefix", *a) == -1
+    a = list(args); a[6] = 8
+    assert _raw("wedlm_commit_prefix", *a) == -2         # pages of 16 positions only
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

@@ -20,12 +20,20 @@ pytestmark = pytest.mark.gpu
 
 
 def _check(wl, seed=None, layers=None, steps=1):
+    """Both forms of the step - separate RoPE pass and RoPE fused into attention
+    and commit - against one oracle run, and against each other."""
     print(f"[parity] {wl.name} seed={seed}", flush=True)
     inp = make_step_inputs(wl, seed=seed, steps=steps)
     gpu = gpu_step(wl, inp)
+    fused = gpu_step(wl, inp, fused_rope=True)
     ref = oracle_step(wl, inp, gpu=gpu, layers=layers)
     rep = compare_step(wl, gpu, ref, layers=layers)
-    print(f"[parity] {wl.name}: {rep}", flush=True)
+    rep_f = compare_step(wl, fused, ref, layers=layers)
+    # the selection and state never depend on the RoPE form
+    for key in ("perm", "run", "entropy", "argmax", "selected", "commit_len", "cache_slot",
+                "tokens", "filled", "prefix_len"):
+        assert np.array_equal(gpu[key], fused[key]), key
+    print(f"[parity] {wl.name}: {rep}; fused {rep_f}", flush=True)
     return rep
 
 
@@ -85,10 +93,16 @@ def test_edge_cases(name, wl):
 def test_deterministic_bitwise():
     wl = _variant(WL.QWEN25_7B_RAGGED, name="determinism", B=4, V=20000)
     inp = make_step_inputs(wl)
-    a = gpu_step(wl, inp)
-    b = gpu_step(wl, inp, repeat=2)
-    for key in ("attn_out_phys", "entropy", "score", "q_phys", "tokens", "cache_slot"):
-        assert np.array_equal(a[key], b[key]), key
+    for fused in (False, True):
+        a = gpu_step(wl, inp, fused_rope=fused)
+        b = gpu_step(wl, inp, repeat=2, fused_rope=fused)
+        keys = ["attn_out_phys", "entropy", "score", "tokens", "cache_slot"]
+        if not fused:
+            keys.append("q_phys")
+        for key in keys:
+            assert np.array_equal(a[key], b[key]), (key, fused)
+        for rk in a["committed_rows"]:
+            assert np.array_equal(a["committed_rows"][rk][0], b["committed_rows"][rk][0]), rk
 
 
 def test_invalid_host_arguments_raise():

@@ -4,14 +4,18 @@ Default workload: the Qwen3-8B-shaped streaming loop - 36 independent layers'
 paged KV caches, 16 sequences, initial prefix 1024, window 16, vocabulary
 151936, bf16 - run for --steps window steps (256 by default: the whole loop)
 after --warmup steps from the same start state. Every timed step is the whole
-path: reorder, RoPE at logical positions, window attention over all 36 layers,
-entropy/selection over the full vocabulary, commit and refill. Inputs are
+path: reorder, window attention over all 36 layers with RoPE at the logical
+positions applied as the window is loaded (the same call appends the committed
+rows to the cache), entropy/selection over the full vocabulary, and the
+commit of the window state (shift and refill). Inputs are
 synthetic and already resident in HBM when timing starts.
 
 Prints one JSON line: window-steps/s (value), committed tokens/s, the HBM rate
-of the algorithmic bytes (KV prefix + window + logits) per step, the roofline
-of the dominant kernel (window attention) timed with HIP events on its own
-stream, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+of the algorithmic bytes (KV prefix + window + logits + committed rows) per
+step, the roofline of the dominant kernel (window attention, which in the
+fused step also appends the committed rows) timed with HIP events on the
+launch stream, and the fp64 CPU oracle timed on a bounded sample of the same
+workload.
 """
 
 import argparse
@@ -91,14 +95,19 @@ class HipEvents:
         self.events = []
 
 
-def step_bytes(wl, prefix_lens):
-    """Algorithmic HBM bytes of one window step, split by tensor (each byte once)."""
+def step_bytes(wl, prefix_lens, commits):
+    """Algorithmic HBM bytes of one window step, split by tensor (each byte once).
+
+    commits: rows committed per sequence this step (their K and V rows are
+    written to the cache, by the attention call in the fused step).
+    """
     e = 2 if wl.dtype == "bf16" else 4
     kv = int(sum(prefix_lens)) * wl.n_layers * wl.Hkv * wl.D * 2 * e
     win_in = wl.n_layers * wl.B * wl.W * (wl.Hq + 2 * wl.Hkv) * wl.D * e
     attn_out = wl.n_layers * wl.B * wl.W * wl.Hq * wl.D * e
+    commit = int(sum(commits)) * wl.n_layers * wl.Hkv * wl.D * 2 * e
     logits = wl.B * wl.W * wl.V * e
-    return {"kv": kv, "window": win_in, "attn_out": attn_out, "logits": logits}
+    return {"kv": kv, "window": win_in, "attn_out": attn_out, "commit": commit, "logits": logits}
 
 
 def cpu_baseline(wl, inp, host_steps):
@@ -184,13 +193,13 @@ def main():
     ent_ms = np.array([hev.elapsed_ms(e["attn_end"], e["entropy_end"]) for e in ev])
     hev.destroy()
     L = np.asarray(inp["prefix_len"], np.int64).copy()
-    tot = {"kv": 0, "window": 0, "attn_out": 0, "logits": 0}
+    tot = {"kv": 0, "window": 0, "attn_out": 0, "commit": 0, "logits": 0}
     attn_bytes = 0
     for s in range(K):
-        b = step_bytes(wl, L)
+        b = step_bytes(wl, L, commits[s])
         for key in tot:
             tot[key] += b[key]
-        attn_bytes += b["kv"] + b["window"] + b["attn_out"]
+        attn_bytes += b["kv"] + b["window"] + b["attn_out"] + b["commit"]
         L += commits[s]
     total_bytes = sum(tot.values())
     committed = int(commits.sum())

@@ -82,6 +82,11 @@ struct AttnArgs {
   const int32_t* perm;
   const int32_t* pos;
   double omega[kHeadDim / 2];
+  // optional append of the committed rows (RoPE fused path): run length per
+  // sequence, and the caches as writable pointers; null when not appending
+  const int32_t* commit_run;
+  uint16_t* kc_w;
+  uint16_t* vc_w;
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -321,6 +326,38 @@ __device__ __forceinline__ void rope_pair(u32x4& lo, u32x4& hi, double t, const 
   hi = yhi;
 }
 
+// Appends the committed window rows held by the staged chunk (physical rows
+// kw0 .. kw0+15, rotated) to the caches: rows 0..c-1 go to positions
+// L..L+c-1, with c the run length clamped to the window and to the pages the
+// table holds (the commit rule of the commit step). Keys as 16-byte slices,
+// values as 2-byte elements of the transposed page; positions of the page
+// other than the appended ones are not touched.
+__device__ __forceinline__ void append_committed(const AttnArgs& a, const Stage& sg,
+                                                 const int32_t* bt, int b, int layer, int kvh,
+                                                 int kw0, int tid, int nthreads) {
+  const int Lc = max(a.prefix_len[b], 0);
+  int c = min(max(a.commit_run[b], 0), a.W);
+  c = min(c, max(a.max_pages * kPage - Lc, 0));
+  const int rows = min(c - kw0, kPage);  // rows of this chunk to append (none if <= 0)
+  if (rows <= 0) return;
+  uint16_t* kcl = a.kc_w + static_cast<size_t>(layer) * a.cache_layer_stride;
+  uint16_t* vcl = a.vc_w + static_cast<size_t>(layer) * a.cache_layer_stride;
+  constexpr int kTasksPerRow = 16 + kHeadDim;  // 16 key slices, 128 value elements
+  for (int idx = tid; idx < rows * kTasksPerRow; idx += nthreads) {
+    const int j = idx / kTasksPerRow, r = idx % kTasksPerRow;
+    const int t = Lc + kw0 + j;
+    const int pid = min(max(bt[t / kPage], 0), a.num_pages - 1);
+    const size_t page = (static_cast<size_t>(pid) * a.Hkv + kvh) * kPartElems;
+    if (r < 16) {
+      *reinterpret_cast<u32x4*>(kcl + page + (r * kPage + t % kPage) * 8) =
+          *reinterpret_cast<const u32x4*>(&sg.k[(r * kPage + j) * 8]);
+    } else {
+      const int d = r - 16;
+      vcl[page + d * kPage + t % kPage] = sg.v[d * kPage + j];
+    }
+  }
+}
+
 // NW wavefronts per workgroup, one 16-row tile each. kRope: q, k, v are in
 // slot order before RoPE; each query row and window key is gathered through
 // perm and rotated at its logical position as it is loaded.
@@ -515,6 +552,9 @@ k_window_attn_bf16(AttnArgs a) {
         }
       }
       __syncthreads();
+      if constexpr (kRope) {
+        if (a.commit_run != nullptr) append_committed(a, sg, bt, b, layer, kvh, kw0, tid, kWave * NW);
+      }
       if (computes) {
         const int lim = min(a.W, prow + 1) - kw0;  // window key kw0 + kk visible iff kk < lim
         attend_page(st, qr, sg, lane, lim, a.scale_log2);
@@ -785,7 +825,8 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
                        double theta, const void* q, const void* k, const void* v,
                        const int32_t* perm, const int32_t* pos, const void* k_cache,
                        const void* v_cache, const int32_t* block_table, const int32_t* prefix_len,
-                       void* out_phys, void* workspace, size_t workspace_bytes, void* stream) {
+                       const int32_t* commit_run, void* out_phys, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   int st = validate_attn(dtype, n_layers, B, W, Hq, Hkv, D, page_size, max_prefix_len);
   if (st != WEDLM_OK) return st;
   if (num_pages <= 0 || max_pages <= 0 || static_cast<long long>(max_pages) * page_size <
@@ -821,7 +862,12 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
       go(k_window_attn_f32<true>);
     else
       go(k_window_attn_f32<false>);
-    return launch_status();
+    st = launch_status();
+    if (st != WEDLM_OK || commit_run == nullptr) return st;
+    // the f32 path appends the committed rows with the commit step's own kernel
+    return commit_rows_rope(dtype, n_layers, B, W, Hkv, D, page_size, num_pages, max_pages,
+                            theta, commit_run, prefix_len, k, v, block_table,
+                            const_cast<void*>(k_cache), const_cast<void*>(v_cache), s);
   }
   const AttnPlan pl = plan_bf16(n_layers, B, W, Hq, Hkv, max_prefix_len);
   const size_t need = pl.ws_o_bytes + pl.ws_ml_bytes;
@@ -852,6 +898,9 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   a.perm = perm;
   a.pos = pos;
   for (int j = 0; j < kHeadDim / 2; ++j) a.omega[j] = omega[j];
+  a.commit_run = commit_run;
+  a.kc_w = commit_run ? static_cast<uint16_t*>(const_cast<void*>(k_cache)) : nullptr;
+  a.vc_w = commit_run ? static_cast<uint16_t*>(const_cast<void*>(v_cache)) : nullptr;
   const long long groups = 1LL * n_layers * B * Hkv;
   const long long blocks = groups * pl.n_splits;
   if (blocks > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
@@ -883,19 +932,20 @@ extern "C" int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, 
                                  void* stream) {
   return launch_attn(false, dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages,
                      max_prefix_len, scale, 0.0, q_phys, k_phys, v_phys, nullptr, nullptr, k_cache,
-                     v_cache, block_table, prefix_len, out_phys, workspace, workspace_bytes,
-                     stream);
+                     v_cache, block_table, prefix_len, nullptr, out_phys, workspace,
+                     workspace_bytes, stream);
 }
 
 extern "C" int wedlm_window_attn_rope(int dtype, int n_layers, int B, int W, int Hq, int Hkv,
                                       int D, int page_size, int num_pages, int max_pages,
                                       int max_prefix_len, float scale, double theta, const void* q,
                                       const void* k, const void* v, const int32_t* perm,
-                                      const int32_t* pos, const void* k_cache,
-                                      const void* v_cache, const int32_t* block_table,
-                                      const int32_t* prefix_len, void* out_phys, void* workspace,
+                                      const int32_t* pos, void* k_cache, void* v_cache,
+                                      const int32_t* block_table, const int32_t* prefix_len,
+                                      const int32_t* commit_run, void* out_phys, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   return launch_attn(true, dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages,
                      max_prefix_len, scale, theta, q, k, v, perm, pos, k_cache, v_cache,
-                     block_table, prefix_len, out_phys, workspace, workspace_bytes, stream);
+                     block_table, prefix_len, commit_run, out_phys, workspace, workspace_bytes,
+                     stream);
 }

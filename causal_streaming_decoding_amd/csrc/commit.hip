@@ -189,9 +189,38 @@ k_commit_state(int W, int P, int num_pages, int max_pages, const int32_t* __rest
   }
 }
 
+
 }  // namespace wedlm
 
 using namespace wedlm;
+
+// Rows part of the fused commit (used by the f32 attention path, which has no
+// rows of its own to append): rotated keys and values of rows 0..c-1.
+int wedlm::commit_rows_rope(int dtype, int n_layers, int B, int W, int Hkv, int D, int page_size,
+                            int num_pages, int max_pages, double theta, const int32_t* run_len,
+                            const int32_t* prefix_len, const void* k_rows, const void* v_rows,
+                            const int32_t* block_table, void* k_cache, void* v_cache,
+                            hipStream_t s) {
+  const int X = 16 / static_cast<int>(elt_size(dtype));
+  if (D % (2 * X) != 0 || D > kCommitMaxD || page_size != 16) return WEDLM_ERR_UNSUPPORTED;
+  const long long stride = 1LL * num_pages * Hkv * D * page_size;
+  CommitRope tab{};
+  for (int j = 0; j < D / 2; ++j) tab.omega[j] = std::pow(theta, -2.0 * j / D);
+  const dim3 grid(B * Hkv, n_layers);
+  if (dtype == WEDLM_BF16)
+    hipLaunchKernelGGL((k_commit_rows<uint16_t, true>), grid, dim3(kCommitThreads), 0, s, B, W,
+                       Hkv, D, page_size, num_pages, max_pages, run_len, prefix_len,
+                       static_cast<const uint16_t*>(k_rows), static_cast<const uint16_t*>(v_rows),
+                       block_table, static_cast<uint16_t*>(k_cache),
+                       static_cast<uint16_t*>(v_cache), stride, tab);
+  else
+    hipLaunchKernelGGL((k_commit_rows<float, true>), grid, dim3(kCommitThreads), 0, s, B, W, Hkv,
+                       D, page_size, num_pages, max_pages, run_len, prefix_len,
+                       static_cast<const float*>(k_rows), static_cast<const float*>(v_rows),
+                       block_table, static_cast<float*>(k_cache), static_cast<float*>(v_cache),
+                       stride, tab);
+  return launch_status();
+}
 
 static int launch_commit(bool rope, int dtype, int n_layers, int B, int W, int Hkv, int D,
                          int page_size, int num_pages, int max_pages, double theta,
@@ -208,8 +237,11 @@ static int launch_commit(bool rope, int dtype, int n_layers, int B, int W, int H
   const int X = 16 / static_cast<int>(elt_size(dtype));
   if (D % X != 0 || page_size != 16) return WEDLM_ERR_UNSUPPORTED;
   if (rope && (D % (2 * X) != 0 || D > kCommitMaxD)) return WEDLM_ERR_UNSUPPORTED;
-  if (!run_len || !selected || !argmax_tok || !k_rows || !v_rows || !block_table || !k_cache ||
-      !v_cache || !tokens || !filled || !prefix_len || !commit_len || !cache_slot)
+  // fused form: k and v both NULL means the rows were appended already (by
+  // wedlm_window_attn_rope with commit_run); only the window state is updated
+  const bool rows = !(rope && k_rows == nullptr && v_rows == nullptr);
+  if (!run_len || !selected || !argmax_tok || (rows && (!k_rows || !v_rows)) || !block_table ||
+      !k_cache || !v_cache || !tokens || !filled || !prefix_len || !commit_len || !cache_slot)
     return WEDLM_ERR_INVALID;
   if (n_layers > 65535) return WEDLM_ERR_UNSUPPORTED;
   if (1LL * B * Hkv > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
@@ -226,15 +258,17 @@ static int launch_commit(bool rope, int dtype, int n_layers, int B, int W, int H
                        static_cast<const T*>(v_rows), block_table, static_cast<T*>(k_cache),
                        static_cast<T*>(v_cache), stride, tab);
   };
-  if (dtype == WEDLM_BF16) {
-    uint16_t* tag = nullptr;
-    rope ? go(k_commit_rows<uint16_t, true>, tag) : go(k_commit_rows<uint16_t, false>, tag);
-  } else {
-    float* tag = nullptr;
-    rope ? go(k_commit_rows<float, true>, tag) : go(k_commit_rows<float, false>, tag);
+  if (rows) {
+    if (dtype == WEDLM_BF16) {
+      uint16_t* tag = nullptr;
+      rope ? go(k_commit_rows<uint16_t, true>, tag) : go(k_commit_rows<uint16_t, false>, tag);
+    } else {
+      float* tag = nullptr;
+      rope ? go(k_commit_rows<float, true>, tag) : go(k_commit_rows<float, false>, tag);
+    }
+    const int st = launch_status();
+    if (st != WEDLM_OK) return st;
   }
-  int st = launch_status();
-  if (st != WEDLM_OK) return st;
   hipLaunchKernelGGL(k_commit_state, dim3(B), dim3(kWave), 0, s, W, page_size, num_pages,
                      max_pages, run_len, selected, argmax_tok, block_table, tokens, filled,
                      prefix_len, commit_len, cache_slot, mask_id);

@@ -106,4 +106,11 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Internal (not part of the C ABI): the rows half of wedlm_commit_prefix_rope,
+// enqueued on `s`. Defined in commit.hip.
+int commit_rows_rope(int dtype, int n_layers, int B, int W, int Hkv, int D, int page_size,
+                     int num_pages, int max_pages, double theta, const int32_t* run_len,
+                     const int32_t* prefix_len, const void* k_rows, const void* v_rows,
+                     const int32_t* block_table, void* k_cache, void* v_cache, hipStream_t s);
+
 }  // namespace wedlm

@@ -53,6 +53,9 @@ class WindowStep:
         self.scale = scale if scale is not None else D ** -0.5
         self.max_prefix_len = max_prefix_len
         self.fused_rope = fused_rope
+        # fused path: the attention call appends the committed rows (else the
+        # commit call writes them itself)
+        self.fused_append = True
         i32 = dict(dtype=torch.int32, device=device)
         self.perm = torch.empty((B, W), **i32)
         self.inv = torch.empty((B, W), **i32)
@@ -110,13 +113,16 @@ class WindowStep:
                              st.block_table, st.prefix_len, self.out_phys, self.attn_ws,
                              self.attn_ws_bytes, stream)
 
-    def attn_rope(self, st, q, k, v, max_prefix_len=None, stream=None):
+    def attn_rope(self, st, q, k, v, max_prefix_len=None, stream=None, append=True):
+        """Attention with RoPE fused; ``append`` also writes the rows the commit
+        will commit (run_len from this step's reorder) into the caches."""
         mpl = self._attn_mpl(max_prefix_len)
         W_.wedlm_window_attn_rope(self.dt, self.n_layers, self.B, self.W, self.Hq, self.Hkv,
                                   self.D, self.page_size, self.num_pages, self.max_pages, mpl,
                                   self.scale, self.theta, q, k, v, self.perm, self.pos,
                                   st.k_cache, st.v_cache, st.block_table, st.prefix_len,
-                                  self.out_phys, self.attn_ws, self.attn_ws_bytes, stream)
+                                  self.run_len if append else None, self.out_phys, self.attn_ws,
+                                  self.attn_ws_bytes, stream)
 
     def entropy_select(self, st, logits, stream=None):
         W_.wedlm_entropy_select(self.dt, self.B, self.W, self.V, logits, st.filled, self.lam,
@@ -124,6 +130,7 @@ class WindowStep:
                                 self.selected, self.ent_ws, self.ent_ws_bytes, stream)
 
     def commit_rope(self, st, k, v, commit_len=None, stream=None):
+        """Fused commit; k = v = None when attn_rope appended the rows already."""
         W_.wedlm_commit_prefix_rope(self.dt, self.n_layers, self.B, self.W, self.Hkv, self.D,
                                     self.page_size, self.num_pages, self.max_pages, self.theta,
                                     self.run_len, self.selected, self.argmax, k, v,
@@ -154,7 +161,7 @@ class WindowStep:
         if mark is not None:
             mark("attn_start")
         if self.fused_rope:
-            self.attn_rope(st, q, k, v, max_prefix_len, stream)
+            self.attn_rope(st, q, k, v, max_prefix_len, stream, append=self.fused_append)
         else:
             self.attn(st, max_prefix_len, stream)
         if mark is not None:
@@ -162,7 +169,10 @@ class WindowStep:
         self.entropy_select(st, logits, stream)
         if mark is not None:
             mark("entropy_end")
-        if self.fused_rope:
+        if self.fused_rope and self.fused_append:
+            # the committed rows were appended by attn_rope: window state only
+            self.commit_rope(st, None, None, commit_len, stream)
+        elif self.fused_rope:
             self.commit_rope(st, k, v, commit_len, stream)
         else:
             self.commit(st, commit_len, stream)

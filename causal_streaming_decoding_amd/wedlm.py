@@ -38,7 +38,7 @@ _SIGNATURES = {
     "wedlm_entropy_select": (_c_int, [_c_int] * 4 + [_p, _p, _c_float, _c_float, _c_int] + [_p] * 5
                              + [_c_size, _p]),
     "wedlm_commit_prefix": (_c_int, [_c_int] * 9 + [_p] * 13 + [ctypes.c_int32, _p]),
-    "wedlm_window_attn_rope": (_c_int, [_c_int] * 11 + [_c_float, _c_double] + [_p] * 11
+    "wedlm_window_attn_rope": (_c_int, [_c_int] * 11 + [_c_float, _c_double] + [_p] * 12
                                + [_c_size, _p]),
     "wedlm_commit_prefix_rope": (_c_int, [_c_int] * 9 + [_c_double] + [_p] * 13
                                  + [ctypes.c_int32, _p]),
@@ -171,13 +171,13 @@ def wedlm_commit_prefix(dtype, n_layers, B, W, Hkv, D, page_size, num_pages, max
 
 def wedlm_window_attn_rope(dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages,
                            max_prefix_len, scale, theta, q, k, v, perm, pos, k_cache, v_cache,
-                           block_table, prefix_len, out_phys, workspace, workspace_bytes,
-                           stream=None):
+                           block_table, prefix_len, commit_run, out_phys, workspace,
+                           workspace_bytes, stream=None):
     _check("wedlm_window_attn_rope", lib().wedlm_window_attn_rope(
         dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages, max_prefix_len,
         float(scale), float(theta), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(pos),
-        _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(prefix_len), _ptr(out_phys),
-        _ptr(workspace), workspace_bytes, _stream(stream)))
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(prefix_len), _ptr(commit_run),
+        _ptr(out_phys), _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def wedlm_commit_prefix_rope(dtype, n_layers, B, W, Hkv, D, page_size, num_pages, max_pages, theta,

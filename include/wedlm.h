@@ -170,13 +170,24 @@ int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv, in
  * to the element type before the products, as with wedlm_rope_logical.
  * No q_phys / k_phys / v_phys is written. All other arguments, layouts, sizes,
  * workspace and errors are those of wedlm_window_attn; theta > 0.
+ *
+ * commit_run (device [B], may be NULL): when given, the call also performs the
+ * cache half of the commit (hyper.ai summary, "Method": the leftmost filled
+ * run is committed at once): rows 0..c-1 of the window, rotated, are written to
+ * positions L..L+c-1 of k_cache / v_cache through block_table, with
+ * c = commit_run[b] clamped to [0, W] and to max_pages * P - L, and
+ * L = max(prefix_len[b], 0) - the rows wedlm_commit_prefix_rope would write.
+ * Pass run_len from wedlm_window_reorder, then call wedlm_commit_prefix_rope
+ * with k = v = NULL for the window-state half. The appended positions are
+ * never among those the call reads (they are >= L). k_cache / v_cache are
+ * written only when commit_run is non-NULL.
  */
 int wedlm_window_attn_rope(int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D,
                            int page_size, int num_pages, int max_pages, int max_prefix_len,
                            float scale, double theta, const void* q, const void* k, const void* v,
-                           const int32_t* perm, const int32_t* pos, const void* k_cache,
-                           const void* v_cache, const int32_t* block_table,
-                           const int32_t* prefix_len, void* out_phys, void* workspace,
+                           const int32_t* perm, const int32_t* pos, void* k_cache, void* v_cache,
+                           const int32_t* block_table, const int32_t* prefix_len,
+                           const int32_t* commit_run, void* out_phys, void* workspace,
                            size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace wedlm_entropy_select needs (per-chunk partial reductions). */
@@ -249,7 +260,9 @@ int wedlm_commit_prefix(int dtype, int n_layers, int B, int W, int Hkv, int D, i
  * rounding as in wedlm_window_attn_rope) before it is written. With
  * wedlm_window_attn_rope this makes the step's RoPE pass unnecessary. Other
  * arguments, layouts and errors are those of wedlm_commit_prefix; theta > 0;
- * D <= 256.
+ * D <= 256. k = v = NULL: the rows were appended by wedlm_window_attn_rope
+ * (commit_run = run_len) and only the window state is updated (cache_slot,
+ * tokens, filled, prefix_len, commit_len, exactly as otherwise).
  */
 int wedlm_commit_prefix_rope(int dtype, int n_layers, int B, int W, int Hkv, int D, int page_size,
                              int num_pages, int max_pages, double theta, const int32_t* run_len,

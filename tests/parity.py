@@ -49,15 +49,17 @@ def stored_pair_bound(ref_stored, dtype):
     return np.abs(ref_stored) * 2e-6 + 1e-6
 
 
-def gpu_step(wl, inp, device="cuda", repeat=1, fused_rope=False):
+def gpu_step(wl, inp, device="cuda", repeat=1, fused_rope=False, append=True):
     """Run the step on the GPU; returns host numpy copies of every output.
 
     fused_rope=False runs the five calls with the separate RoPE pass (its
     physical-order q/k/v are returned too); True runs the fused attention and
-    commit calls, which write no physical-order copies.
+    commit calls, which write no physical-order copies. append (fused only):
+    the attention call appends the committed rows, else the commit call does.
     """
     st, q, k, v, logits, mpl = upload_step_inputs(wl, inp, device)
     step = make_window_step(wl, inp, device, mpl, fused_rope=fused_rope)
+    step.fused_append = append
     before = st.snapshot()
     for _ in range(repeat):
         st.restore(before)

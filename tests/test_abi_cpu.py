@@ -77,7 +77,7 @@ def test_attn_validation_and_workspace():
 
 def test_fused_rope_entry_points_validate():
     # wedlm_window_attn_rope: same checks as wedlm_window_attn plus theta, perm, pos
-    base = [1, 1, 4, 16, 32, 8, 128, 16, 8196, 2049, 32768, 0.088, 1e6] + [1] * 11 + [0, None]
+    base = [1, 1, 4, 16, 32, 8, 128, 16, 8196, 2049, 32768, 0.088, 1e6] + [1] * 12 + [0, None]
     assert _raw("wedlm_window_attn_rope", *base) == -3    # split planned, no workspace
     a = list(base); a[12] = 0.0
     assert _raw("wedlm_window_attn_rope", *a) == -1       # theta must be > 0
@@ -92,7 +92,9 @@ def test_fused_rope_entry_points_validate():
     a = list(c); a[6] = 8
     assert _raw("wedlm_commit_prefix_rope", *a) == -2
     a = list(c); a[13] = None
-    assert _raw("wedlm_commit_prefix_rope", *a) == -1
+    assert _raw("wedlm_commit_prefix_rope", *a) == -1     # k without v
+    a = list(c); a[9] = 0.0; a[13] = None; a[14] = None
+    assert _raw("wedlm_commit_prefix_rope", *a) == -1     # state-only form still needs theta
 
 
 def test_entropy_validation_and_workspace():

@@ -14,7 +14,7 @@ import torch
 from causal_streaming_decoding_amd import workloads as WL
 from causal_streaming_decoding_amd.synth import make_step_inputs
 
-from .parity import compare_step, gpu_step, oracle_step
+from .parity import compare_step, gpu_step, oracle_step, stored_pair_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -103,6 +103,30 @@ def test_deterministic_bitwise():
             assert np.array_equal(a[key], b[key]), (key, fused)
         for rk in a["committed_rows"]:
             assert np.array_equal(a["committed_rows"][rk][0], b["committed_rows"][rk][0]), rk
+
+
+@pytest.mark.parametrize("wl", [
+    _variant(WL.QWEN3_8B_BS1, name="append_forms_bf16", fill=("count", 9), prefix=("fixed", 45),
+             V=2048, B=3),
+    _variant(WL.QWEN3_8B_BS1, name="append_forms_w64", W=64, Hq=16, Hkv=4, fill=("count", 64),
+             prefix=("fixed", 77), V=2048, B=2),  # all filled: 64 rows over 4 window chunks
+    _variant(WL.TINY_FP32, name="append_forms_fp32", n_layers=2, B=3, fill=("count", 5)),
+])
+def test_fused_commit_forms_agree(wl):
+    """The committed rows appended by the fused attention call and those the
+    fused commit call writes itself: same state, rows within one storage ulp."""
+    print(f"[parity] {wl.name}", flush=True)
+    inp = make_step_inputs(wl)
+    a = gpu_step(wl, inp, fused_rope=True, append=True)
+    b = gpu_step(wl, inp, fused_rope=True, append=False)
+    for key in ("commit_len", "cache_slot", "tokens", "filled", "prefix_len", "attn_out_phys"):
+        assert np.array_equal(a[key], b[key]), key
+    assert a["committed_rows"].keys() == b["committed_rows"].keys()
+    assert int(a["commit_len"].max()) > 0
+    for rk, (ka, va) in a["committed_rows"].items():
+        kb, vb = b["committed_rows"][rk]
+        assert np.array_equal(va, vb), rk
+        assert (np.abs(ka - kb) <= stored_pair_bound(kb, wl.dtype)).all(), rk
 
 
 def test_invalid_host_arguments_raise():

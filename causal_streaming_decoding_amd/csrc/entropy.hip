@@ -64,7 +64,7 @@ struct EVec {
 
 // Vectors (16 bytes, or single elements when !VEC) per thread per block: all
 // of a thread's loads are issued before any is reduced.
-constexpr int kEntIter = 4;
+constexpr int kEntIter = 8;
 
 // VEC: rows are 16-byte aligned and V is a multiple of the vector width.
 template <typename T, bool VEC>

@@ -44,6 +44,10 @@ def parse():
                     help="window steps of the oracle timed on the host (0 disables)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="instead: single-step latency of every other workload, one JSON line each")
+    ap.add_argument("--config-steps", type=int, default=200)
+    ap.add_argument("--config-warmup", type=int, default=20)
     return ap.parse_args()
 
 
@@ -138,12 +142,91 @@ def cpu_baseline(wl, inp, host_steps):
                       f"{out['total_committed']} tokens committed)"}
 
 
+def config_latencies(args):
+    """Single-step latency of each single-step workload (one JSON line each).
+
+    Every timed step starts from the same state (restored outside the timed
+    pair) and follows a 512 MB read that evicts the caches' contents, so the
+    KV prefix and logits come from HBM as in a real decoder. Reports the
+    median, p10 and p90 of the whole step and of the attention and entropy
+    calls, with the HBM rate of the algorithmic bytes at the median.
+    """
+    import numpy as np
+    import torch
+
+    from causal_streaming_decoding_amd import workloads as WL
+    from causal_streaming_decoding_amd.step import make_window_step, upload_step_inputs
+    from causal_streaming_decoding_amd.synth import make_step_inputs
+
+    dev = "cuda:0"
+    # evicting by reading leaves no dirty lines whose write-back would land
+    # inside the next timed step (a 512 MB write would leave up to the whole
+    # 256 MB infinity cache dirty)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MB
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+    hev = HipEvents(torch.cuda.current_stream().cuda_stream)
+    labels = ("step_start", "attn_start", "attn_end", "entropy_end", "step_end")
+    for wl in WL.ALL:
+        if wl.steps > 1:
+            continue  # the streaming loop is the default bench line
+        print(f"[bench] {wl.name}", file=sys.stderr, flush=True)
+        inp = make_step_inputs(wl)
+        st, q, k, v, logits, mpl = upload_step_inputs(wl, inp, dev)
+        step = make_window_step(wl, inp, dev, mpl)
+        snap = st.snapshot()
+        n = args.config_warmup + args.config_steps
+        ev = [{lab: hev.create() for lab in labels} for _ in range(n)]
+        for i in range(n):
+            st.restore(snap)
+            torch.sum(flush, dim=0, out=flush_sink)
+            e = ev[i]
+            hev.record(e["step_start"])
+            step.run(st, q, k, v, logits, mark=lambda lab, e=e: hev.record(e[lab]))
+            hev.record(e["step_end"])
+        torch.cuda.synchronize()
+        timed = ev[args.config_warmup:]
+        span = {name: np.array([hev.elapsed_ms(x[a], x[b]) for x in timed]) * 1e3
+                for name, (a, b) in {"step": ("step_start", "step_end"),
+                                     "attn": ("attn_start", "attn_end"),
+                                     "entropy": ("attn_end", "entropy_end")}.items()}
+        hev.destroy()
+        L = np.asarray(inp["prefix_len"], np.int64)
+        commits = step.commit_len.cpu().numpy()
+        b = step_bytes(wl, L, commits)
+        attn_bytes = b["kv"] + b["window"] + b["attn_out"] + b["commit"]
+
+        def stats(x):
+            return {"median": float(np.median(x)), "p10": float(np.percentile(x, 10)),
+                    "p90": float(np.percentile(x, 90))}
+
+        med = {k_: float(np.median(v_)) for k_, v_ in span.items()}
+        line = {
+            "workload": wl.name, "dtype": wl.dtype, "steps": args.config_steps,
+            "warmup": args.config_warmup, "unit": "us",
+            "step_us": stats(span["step"]), "attn_us": stats(span["attn"]),
+            "entropy_us": stats(span["entropy"]),
+            "attn_algorithmic_bytes": int(attn_bytes), "logits_bytes": int(b["logits"]),
+            "attn_hbm_gbps_at_median": attn_bytes / (med["attn"] * 1e-6) / 1e9,
+            "entropy_hbm_gbps_at_median": b["logits"] / (med["entropy"] * 1e-6) / 1e9,
+            "attn_plus_entropy_hbm_frac_at_median":
+                (attn_bytes + b["logits"]) / ((med["attn"] + med["entropy"]) * 1e-6) / 1e9
+                / HBM_PEAK_GBPS,
+            "data": "synthetic",
+        }
+        print(json.dumps(line), flush=True)
+        del st, q, k, v, logits, step
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build",
               file=sys.stderr)
         sys.exit(2)
+    if args.all_configs:
+        config_latencies(args)
+        return
 
     import numpy as np
     import torch

@@ -9,11 +9,12 @@
 // bf16 path (D = 128, page P = 16). One workgroup per (layer, sequence, kv
 // head, key-range split); each of its wavefronts owns one 16-row tile of the
 // group's M = W*g query rows (physical row p, query head h of the group). The
-// group's key pages stream through a 3-stage LDS ring, one page (16 keys, 8 KB
-// of K and V) per stage, filled by global->LDS DMA. A stage is refilled as soon
-// as every wave has finished reading it, so three pages are in flight while
-// the waves wait and two while they compute. Each key byte is read from HBM
-// once per workgroup.
+// group's key pages stream through an LDS ring, one page (16 keys, 8 KB of K
+// and V) per stage, filled by global->LDS DMA: 3 stages for 4-wave workgroups
+// (5 per CU), 7 for 8 waves and 15 for 16 waves (fewer per CU). A stage is
+// refilled as soon as every wave has finished reading it, so the whole ring is
+// in flight while the waves wait. Each key byte is read from HBM once per
+// workgroup.
 //
 //   S^T (16 keys x 16 rows)  = K (16 x 128) . Q^T        v_mfma_f32_16x16x32_bf16
 //   O^T (16 dims x 16 rows) += [V^T V^T] . [P_hi; P_lo]^T v_mfma_f32_16x16x32_bf16
@@ -55,9 +56,20 @@ constexpr int kPage = 16;
 constexpr int kMaxRows = 256;       // M = W*g rows: at most 16 wavefronts
 constexpr int kPageVecs = 512;      // 16-byte vectors of one page of one kv head (K 4 KB + V 4 KB)
 constexpr int kPartElems = 2048;    // bf16 elements of one 4 KB page part
-constexpr int kStages = 3;          // LDS ring depth (one 8 KB page per stage)
-constexpr int kAhead = kStages - 1; // pages in flight while one is computed
-constexpr int kWavesPerSimd = 5;    // register budget: 5 wavefronts per SIMD, 5 workgroups per CU
+constexpr int kNumCUs = 256;        // MI355X compute units
+
+// LDS ring (one 8 KB page per stage) per workgroup size. A CU holds 5
+// workgroups of 4 waves (registers: 5 wavefronts per SIMD), 2 of 8 or 1 of 16
+// (LDS); the ring depth keeps 10-15 pages (80-120 KB) in flight per CU in
+// every case.
+template <int NW>
+struct Ring {
+  // LDS caps the larger workgroups at 4 wavefronts per SIMD
+  static constexpr int kWavesPerSimd = NW == 4 ? 5 : 4;
+  static constexpr int kWgPerCu = NW == 4 ? 5 : (NW == 8 ? 2 : 1);
+  static constexpr int kStages = NW == 4 ? 3 : (NW == 8 ? 7 : 15);
+  static constexpr int kAhead = kStages - 1;  // pages in flight while one is computed
+};
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.f;
 
@@ -293,18 +305,19 @@ __device__ __forceinline__ void stage_release_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
-// Wait for the oldest in-flight stage when `behind` later stages (kDma DMAs
-// each) may stay in flight, then synchronise the workgroup.
-template <int kDma>
+// Wait for the oldest in-flight stage when `behind` (<= N) later stages,
+// kDma DMAs each, may stay in flight, then synchronise the workgroup. The
+// count must be an immediate, hence the chain over 0..N.
+template <int kDma, int N>
 __device__ __forceinline__ void stage_wait_behind(int behind) {
-  if (behind >= 3)
-    stage_wait_barrier<3 * kDma>();
-  else if (behind == 2)
-    stage_wait_barrier<2 * kDma>();
-  else if (behind == 1)
-    stage_wait_barrier<kDma>();
-  else
+  if constexpr (N == 0) {
     stage_wait_barrier<0>();
+  } else {
+    if (behind >= N)
+      stage_wait_barrier<N * kDma>();
+    else
+      stage_wait_behind<kDma, N - 1>(behind);
+  }
 }
 
 // Rotates a 16-byte slice pair of one row by RoPE: lo holds dims j0..j0+7,
@@ -363,9 +376,11 @@ __device__ __forceinline__ void append_committed(const AttnArgs& a, const Stage&
 // perm and rotated at its logical position as it is loaded.
 template <int NW, bool kRope>
 __global__ void __launch_bounds__(kWave * NW)
-__attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd)))
+__attribute__((amdgpu_waves_per_eu(Ring<NW>::kWavesPerSimd, Ring<NW>::kWavesPerSimd)))
 k_window_attn_bf16(AttnArgs a) {
   constexpr int kDma = DmaShape<NW>::kPerWave;  // DMA instructions per issuing thread per stage
+  constexpr int kStages = Ring<NW>::kStages;
+  constexpr int kAhead = Ring<NW>::kAhead;
   __shared__ Stage stage[kStages];
   __shared__ double s_omega[kRope ? kHeadDim / 2 : 1];
 
@@ -433,18 +448,20 @@ k_window_attn_bf16(AttnArgs a) {
   const uint16_t* kc_layer = a.kc + static_cast<size_t>(layer) * a.cache_layer_stride;
   const uint16_t* vc_layer = a.vc + static_cast<size_t>(layer) * a.cache_layer_stride;
   const int npg = pg_end - pg_begin;
-  // The first kAhead stages are always requested (page ids clamped to valid
-  // entries when the split has fewer pages; unused stages are simply not read),
-  // so the number of DMAs in flight here is a compile-time constant.
+  // The first min(kAhead, npg) pages are requested before the loop.
+  const int pro = min(kAhead, npg);
 #pragma unroll
   for (int j = 0; j < kAhead; ++j)
-    stage_dma<NW>(stage[j], wave, lane, min(pg_begin + j, pg_end - 1), bt, a.max_pages,
-                  a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
-  // Retire the query loads: only the DMAs issued after them may remain. Waves
-  // that issue no DMA (NW = 16) wait for everything first; that asm has no
+    if (j < pro)
+      stage_dma<NW>(stage[j], wave, lane, pg_begin + j, bt, a.max_pages, a.num_pages, a.Hkv, kvh,
+                    kc_layer, vc_layer);
+  // Retire the query loads: only the kAhead stages issued after them may
+  // remain. Waves that issue no DMA (NW = 16), and every wave when the split
+  // has fewer than kAhead pages, wait for everything first; that asm has no
   // register operands, so nothing touches the query registers before the
   // tied wait below.
-  if (wave >= DmaShape<NW>::kIssuers) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (wave >= DmaShape<NW>::kIssuers || pro < kAhead)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   asm volatile("s_waitcnt vmcnt(%4)"
                : "+v"(qv[0]), "+v"(qv[1]), "+v"(qv[2]), "+v"(qv[3])
                : "n"(kAhead * kDma));
@@ -470,15 +487,14 @@ k_window_attn_bf16(AttnArgs a) {
       stage_dma<NW>(stage[(i + kAhead) % kStages], wave, lane, pg + kAhead, bt, a.max_pages,
                     a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
     }
-    // requests issued after page i's: up to kAhead real pages, or the clamped
-    // dummy requests of the prologue when the split is shorter than kAhead
-    stage_wait_behind<kDma>(max(min(kAhead, npg - 1 - i), kAhead - 1 - i));
+    // pages requested after page i: up to kAhead, fewer near the end
+    stage_wait_behind<kDma, kAhead>(min(kAhead, npg - 1 - i));
     if (computes) attend_page(st, qr, stage[i % kStages], lane, L - pg * kPage, a.scale_log2);
   }
-  // The window reuses stage 0: every DMA - including the clamped dummy
-  // requests of the prologue when this split has fewer pages than kAhead, or
-  // none - must have landed before it is overwritten. The compiler does not
-  // see the asm DMAs, so a plain __syncthreads() would not wait for them.
+  // The window reuses stage 0: every DMA must have landed before it is
+  // overwritten (and none may be in flight when the workgroup ends). The
+  // compiler does not see the asm DMAs, so a plain __syncthreads() would not
+  // wait for them.
   stage_wait_barrier<0>();
 
   // ---- the window's own keys, causal over physical order -------------------
@@ -591,7 +607,12 @@ k_window_attn_bf16(AttnArgs a) {
 }
 
 // Merge of the per-split partials: out = sum_s O_s 2^(m_s - m) / sum_s l_s 2^(m_s - m).
-// One thread per (group, row, 4 dims).
+// One thread per (group, row, 4 dims), one pass over the splits in split
+// order with a running reference max; the partials are read kCombineBatch
+// splits at a time, all loads of a batch issued before any is used, so the
+// latency is paid once per batch rather than once per split.
+constexpr int kCombineBatch = 8;
+
 __global__ void __launch_bounds__(256)
 k_window_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                       uint16_t* __restrict__ out, int n_groups, int M, int n_splits, int B, int W,
@@ -603,24 +624,44 @@ k_window_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ 
   const int d4 = static_cast<int>(idx % quads);
   const int row = static_cast<int>((idx / quads) % M);
   const int group = static_cast<int>(idx / (static_cast<long long>(quads) * M));
-  float mmax = -INFINITY;
-  for (int s = 0; s < n_splits; ++s)
-    mmax = fmaxf(mmax, ws_ml[((static_cast<size_t>(group) * n_splits + s) * M + row) * 2]);
-  const float base = mmax == -INFINITY ? 0.f : mmax;
+  float m = -INFINITY, lsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float lsum = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const size_t part = static_cast<size_t>(group) * n_splits + s;
-    const float m = ws_ml[(part * M + row) * 2];
-    const float l = ws_ml[(part * M + row) * 2 + 1];
-    if (l == 0.f) continue;  // a split with no keys contributes nothing
-    const float w = __builtin_amdgcn_exp2f(m - base);
-    const float4 o = *reinterpret_cast<const float4*>(ws_o + (part * M + row) * kHeadDim + d4 * 4);
-    acc.x += o.x * w;
-    acc.y += o.y * w;
-    acc.z += o.z * w;
-    acc.w += o.w * w;
-    lsum += l * w;
+  for (int s0 = 0; s0 < n_splits; s0 += kCombineBatch) {
+    float2 ml[kCombineBatch];
+    float4 o[kCombineBatch];
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const int s = s0 + k;
+      const size_t part = (static_cast<size_t>(group) * n_splits + s) * M + row;
+      ml[k] = s < n_splits ? reinterpret_cast<const float2*>(ws_ml)[part]
+                           : make_float2(-INFINITY, 0.f);
+      o[k] = s < n_splits ? *reinterpret_cast<const float4*>(ws_o + part * kHeadDim + d4 * 4)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    // a split with no keys (l = 0, m = -inf) contributes nothing
+    float bm = m;
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k)
+      if (ml[k].y != 0.f) bm = fmaxf(bm, ml[k].x);
+    if (bm > m) {
+      const float r = __builtin_amdgcn_exp2f(m - bm);  // 0 while m = -inf
+      acc.x *= r;
+      acc.y *= r;
+      acc.z *= r;
+      acc.w *= r;
+      lsum *= r;
+      m = bm;
+    }
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      if (ml[k].y == 0.f) continue;
+      const float w = __builtin_amdgcn_exp2f(ml[k].x - m);
+      acc.x += o[k].x * w;
+      acc.y += o[k].y * w;
+      acc.z += o[k].z * w;
+      acc.w += o[k].w * w;
+      lsum += ml[k].y * w;
+    }
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   const int kvh = group % Hkv;
@@ -699,24 +740,44 @@ k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
     float sc = -INFINITY;
     if (key < nkeys) {
       float dot = 0.f;
+      // 16-byte loads, unrolled so that several are in flight at once
+      const float4* q4 = reinterpret_cast<const float4*>(qs);
       if (key < L) {
         const int pid = min(max(bt[key / kPage], 0), num_pages - 1);
-        const float* kp = kcl + (static_cast<size_t>(pid) * Hkv + kvh) * page_elems;
-        const int off = key % kPage;
-        for (int d = 0; d < D; ++d) dot += qs[d] * kp[((d >> 2) * kPage + off) * 4 + (d & 3)];
+        const float4* kp4 = reinterpret_cast<const float4*>(
+                                kcl + (static_cast<size_t>(pid) * Hkv + kvh) * page_elems) +
+                            key % kPage;
+#pragma unroll 4
+        for (int d4 = 0; d4 < D / 4; ++d4) {
+          const float4 kv = kp4[d4 * kPage], qv = q4[d4];
+          dot += qv.x * kv.x + qv.y * kv.y + qv.z * kv.z + qv.w * kv.w;
+        }
       } else if constexpr (kRope) {
         const int r = key - L;
-        const float* kr = k + ((lb * W + slot_of(r)) * Hkv + kvh) * D;
+        const float4* kr4 =
+            reinterpret_cast<const float4*>(k + ((lb * W + slot_of(r)) * Hkv + kvh) * D);
         const double tk = static_cast<double>(rp.pos[b * W + r]);
-        for (int j = 0; j < half; ++j) {
-          float c, sn;
-          rope_cos_sin(tk, rp.omega[j], c, sn);
-          const float k0 = kr[j], k1 = kr[j + half];
-          dot += qs[j] * (k0 * c - k1 * sn) + qs[j + half] * (k1 * c + k0 * sn);
+#pragma unroll 2
+        for (int j4 = 0; j4 < half / 4; ++j4) {
+          const float4 lo = kr4[j4], hi = kr4[j4 + half / 4];
+          const float4 ql = q4[j4], qh = q4[j4 + half / 4];
+          const float al[4] = {lo.x, lo.y, lo.z, lo.w}, ah[4] = {hi.x, hi.y, hi.z, hi.w};
+          const float bl[4] = {ql.x, ql.y, ql.z, ql.w}, bh[4] = {qh.x, qh.y, qh.z, qh.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float c, sn;
+            rope_cos_sin(tk, rp.omega[4 * j4 + e], c, sn);
+            dot += bl[e] * (al[e] * c - ah[e] * sn) + bh[e] * (ah[e] * c + al[e] * sn);
+          }
         }
       } else {
-        const float* kr = k + ((lb * W + (key - L)) * Hkv + kvh) * D;
-        for (int d = 0; d < D; ++d) dot += qs[d] * kr[d];
+        const float4* kr4 =
+            reinterpret_cast<const float4*>(k + ((lb * W + (key - L)) * Hkv + kvh) * D);
+#pragma unroll 4
+        for (int d4 = 0; d4 < D / 4; ++d4) {
+          const float4 kv = kr4[d4], qv = q4[d4];
+          dot += qv.x * kv.x + qv.y * kv.y + qv.z * kv.z + qv.w * kv.w;
+        }
       }
       sc = dot * scale_log2;
     }
@@ -774,11 +835,16 @@ static AttnPlan plan_bf16(int n_layers, int B, int W, int Hq, int Hkv, int max_p
   const int tiles = ceil_div(M, 16);
   pl.waves = tiles <= 4 ? 4 : (tiles <= 8 ? 8 : 16);
   const long long groups = 1LL * n_layers * B * Hkv;
-  // aim for >= 1024 workgroups (4 per CU) but keep >= 4 pages (64 keys) per split
+  // aim for one full round of workgroups (every CU holding as many as its
+  // registers allow) but keep >= 4 pages per split (8 for the deeper rings)
+  const int wg_per_cu = pl.waves == 4 ? Ring<4>::kWgPerCu
+                                      : (pl.waves == 8 ? Ring<8>::kWgPerCu : Ring<16>::kWgPerCu);
+  const long long target = 1LL * kNumCUs * wg_per_cu;
+  const int min_pages = pl.waves == 4 ? 4 : 8;
   const int npages = ceil_div(max(max_prefix_len, 1), kPage);
   int splits = 1;
-  if (groups < 1024) splits = static_cast<int>((1024 + groups - 1) / groups);
-  splits = max(1, min(splits, npages / 4));
+  if (groups < target) splits = static_cast<int>((target + groups - 1) / groups);
+  splits = max(1, min(splits, npages / min_pages));
   pl.n_splits = splits;
   if (splits > 1) {
     pl.ws_o_bytes = static_cast<size_t>(groups) * splits * M * kHeadDim * sizeof(float);

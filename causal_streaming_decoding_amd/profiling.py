@@ -13,8 +13,10 @@ is 1 GiB read and 1 GiB written. The window-attention record it writes holds a
 hash of the kernel's source files, so that a later reader can tell whether the
 counters still describe the kernel that is built.
 
-Usage::
+Usage (the second form summarises ``bench.py --all-configs``)::
 
+    python -m causal_streaming_decoding_amd.profiling configs --configs-jsonl <file> \\
+        --trace <dir> --out-md profiles/<name>.md
     python -m causal_streaming_decoding_amd.profiling \\
         --trace gpurun_out/prof_trace --fetch gpurun_out/prof_fetch \\
         --write gpurun_out/prof_write --bench-json gpurun_out/prof_bench.json \\
@@ -26,6 +28,7 @@ import csv
 import hashlib
 import json
 import os
+import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ATTN_SOURCES = ("csrc/attn.hip", "csrc/common.hpp")
@@ -137,7 +140,7 @@ def summarize(trace, fetch, write, bench_json, steps, out_md, out_traffic, comma
             continue
         lines.append(f"| `{n}` | {r / 1e6:.2f} | {w / 1e6:.2f} |")
     lines += ["", f"Window attention: algorithmic {alg / 1e6:.1f} MB per launch (KV prefix + window "
-              f"q/k/v read, output written); counted {(a_fetch + a_write) / 1e6:.1f} MB "
+              f"q/k/v read, output and committed rows written); counted {(a_fetch + a_write) / 1e6:.1f} MB "
               f"({(a_fetch + a_write) / alg:.3f} x)."]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -153,6 +156,44 @@ def summarize(trace, fetch, write, bench_json, steps, out_md, out_traffic, comma
         f.write(f"write_factor: {w_fac:.6f}\n")
         f.write(f"command_fetch: {command_fetch}\n")
         f.write(f"command_write: {command_write}\n")
+
+
+def summarize_configs(configs_jsonl, trace_dir, out_md, command_bench, command_trace):
+    """Single-step latencies of the other workloads (bench.py --all-configs) and
+    the kernel durations of a traced run of the same mode, per launch shape."""
+    import statistics
+
+    rows = [json.loads(ln) for ln in open(configs_jsonl) if ln.startswith("{")]
+    lines = ["# Single-step latencies of the parity workloads", "",
+             "MI355X (gfx950). Each timed step starts from the same state and follows a 512 MB "
+             "read that evicts the caches; times in microseconds (median, p10, p90 over the timed "
+             "steps). HBM rates are algorithmic bytes over the median. In the commands, `<repo>` "
+             "is the repository root.", "", "```", command_bench, "```", "",
+             "| workload | step median | p10 | p90 | attention | entropy+select | "
+             "attention GB/s | entropy GB/s |", "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(
+            f"| `{r['workload']}` | {r['step_us']['median']:.1f} | {r['step_us']['p10']:.1f} | "
+            f"{r['step_us']['p90']:.1f} | {r['attn_us']['median']:.1f} | "
+            f"{r['entropy_us']['median']:.1f} | {r['attn_hbm_gbps_at_median']:.0f} | "
+            f"{r['entropy_hbm_gbps_at_median']:.0f} |")
+    per = {}
+    with open(os.path.join(trace_dir, "run_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            n = short_name(r["Kernel_Name"])
+            if not n.startswith("wedlm::"):
+                continue
+            key = (n, int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1),
+                   int(r["Grid_Size_Y"]), int(r["Workgroup_Size_X"]))
+            per.setdefault(key, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines += ["", "## Kernel durations by launch shape", "", "```", command_trace, "```", "",
+              "| kernel | blocks x rows | threads | launches | median us |",
+              "|---|---|---|---|---|"]
+    for (n, gx, gy, wg), v in sorted(per.items(), key=lambda kv: -statistics.median(kv[1])):
+        lines.append(f"| `{n}` | {gx} x {gy} | {wg} | {len(v)} | {statistics.median(v):.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def read_traffic(path, workload, steps):
@@ -176,6 +217,17 @@ def read_traffic(path, workload, steps):
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "configs":
+        ap = argparse.ArgumentParser()
+        ap.add_argument("mode")
+        ap.add_argument("--configs-jsonl", required=True)
+        ap.add_argument("--trace", required=True)
+        ap.add_argument("--out-md", required=True)
+        ap.add_argument("--command-bench", default="")
+        ap.add_argument("--command-trace", default="")
+        a = ap.parse_args()
+        summarize_configs(a.configs_jsonl, a.trace, a.out_md, a.command_bench, a.command_trace)
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True)
     ap.add_argument("--fetch", required=True)

@@ -39,3 +39,22 @@ def test_committed_record_is_well_formed():
     write = float(rec["write_bytes_per_launch"])
     alg = float(rec["algorithmic_bytes_per_launch"])
     assert 0.9 < (fetch + write) / alg < 1.2
+
+
+def test_config_summary_from_files(tmp_path):
+    import json
+    (tmp_path / "trace").mkdir()
+    line = {"workload": "w", "step_us": {"median": 10.0, "p10": 9.0, "p90": 11.0},
+            "attn_us": {"median": 6.0}, "entropy_us": {"median": 3.0},
+            "attn_hbm_gbps_at_median": 100.0, "entropy_hbm_gbps_at_median": 50.0}
+    (tmp_path / "c.jsonl").write_text(json.dumps(line) + "\n")
+    hdr = "Kernel_Name,Grid_Size_X,Grid_Size_Y,Workgroup_Size_X,Start_Timestamp,End_Timestamp\n"
+    rows = ['"void wedlm::k_a<4>(int)",1024,1,256,0,5000', '"void wedlm::k_a<4>(int)",1024,1,256,0,7000',
+            '"other_kernel",64,1,64,0,1']
+    (tmp_path / "trace" / "run_kernel_trace.csv").write_text(hdr + "\n".join(rows) + "\n")
+    out = tmp_path / "o.md"
+    profiling.summarize_configs(str(tmp_path / "c.jsonl"), str(tmp_path / "trace"), str(out), "b", "t")
+    text = out.read_text()
+    assert "| `w` | 10.0 | 9.0 | 11.0 | 6.0 | 3.0 | 100 | 50 |" in text
+    assert "| `wedlm::k_a<4>` | 4 x 1 | 256 | 2 | 6.00 |" in text
+    assert "other_kernel" not in text

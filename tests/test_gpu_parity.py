@@ -85,6 +85,16 @@ def _variant(base, **kw):
                                        prefix=("uniform", 0, 45))),
     ("stream_shape_short", _variant(WL.QWEN3_8B_STREAM, name="edge_stream_layers", n_layers=3,
                                     B=4, V=3000, fill=("frac", 0.0, 1.0), steps=1)),
+    # 8-wave workgroups (128 query rows: 7-stage ring, 2 per CU), split key range
+    ("nw8_split", _variant(WL.QWEN3_8B_BS1, name="edge_nw8_split", W=32, prefix=("fixed", 3000),
+                           V=2048, B=2, fill=("frac", 0.3, 0.7))),
+    # 8-wave workgroups, no split (512 groups), short ragged prefixes
+    ("nw8_many_groups", _variant(WL.QWEN3_8B_STREAM, name="edge_nw8_layers", n_layers=8, B=8, W=32,
+                                 V=2048, fill=("frac", 0.0, 1.0), prefix=("uniform", 17, 900),
+                                 steps=1)),
+    # 16-wave workgroups with fewer pages per split than the 15-stage ring holds
+    ("nw16_short_splits", _variant(WL.QWEN25_7B_RAGGED, name="edge_nw16_short", B=2,
+                                   prefix=("uniform", 40, 130), V=2048)),
 ])
 def test_edge_cases(name, wl):
     _check(wl)

@@ -94,30 +94,39 @@ k_entropy_partial(const T* __restrict__ logits, int V, int chunk_elems, int n_ch
         if (i0 < end) vv[it].e[0] = z[i0];
       }
     }
+    // all of this pass's logits are in registers: first their max (and the
+    // vector where it first appears), then the sums against one reference
+    float mpass = kNegBig;
 #pragma unroll
     for (int it = 0; it < kEntIter; ++it) {
       const int i0 = base + (it * kEntThreads + threadIdx.x) * N;
-      if (i0 >= end) break;
-      float x[N];
+      if (i0 >= end) continue;  // (no break: the loop must unroll fully)
+      float mz = Elt<T>::load(&vv[it].e[0]);
 #pragma unroll
-      for (int e = 0; e < N; ++e) x[e] = Elt<T>::load(&vv[it].e[e]);
-      float mz = x[0];
-#pragma unroll
-      for (int e = 1; e < N; ++e) mz = fmaxf(mz, x[e]);
-      if (mz > m) {
-        best = i0;
-        best_raw = vv[it].raw;
+      for (int e = 1; e < N; ++e) mz = fmaxf(mz, Elt<T>::load(&vv[it].e[e]));
+      if (mz > mpass) {
+        mpass = mz;
+        if (mz > m) {
+          best = i0;
+          best_raw = vv[it].raw;
+        }
       }
-      const float mn = fmaxf(m, mz);
-      const float d = (m - mn) * kLog2eF;
+    }
+    if (mpass > m) {  // rescale the running sums to the new reference
+      const float d = (m - mpass) * kLog2eF;
       const float f = __builtin_amdgcn_exp2f(d);
       t = (t + d * s) * f;
       s = s * f;
-      m = mn;
-      const float mb = mn * kLog2eF;
+      m = mpass;
+    }
+    const float mb = m * kLog2eF;
+#pragma unroll
+    for (int it = 0; it < kEntIter; ++it) {
+      const int i0 = base + (it * kEntThreads + threadIdx.x) * N;
+      if (i0 >= end) continue;
 #pragma unroll
       for (int e = 0; e < N; ++e) {
-        const float u = fmaf(x[e], kLog2eF, -mb);
+        const float u = fmaf(Elt<T>::load(&vv[it].e[e]), kLog2eF, -mb);
         const float p = __builtin_amdgcn_exp2f(u);
         s += p;
         t = fmaf(p, u, t);

@@ -20,19 +20,17 @@
 //   O^T (16 dims x 16 rows) += [V^T V^T] . [P_hi; P_lo]^T v_mfma_f32_16x16x32_bf16
 //
 // P is split into a bf16 hi and lo part so that rounding the probabilities
-// costs no accuracy: the PV MFMA takes the 4 keys of a lane's hi parts and
-// the same 4 keys' lo parts in its 8 K slots, against the V rows duplicated.
+// costs no accuracy: the PV MFMA's 32 K slots take the 16 keys' hi parts and
+// then their lo parts, against the page's 16 V rows twice.
 //
 // Cache page layouts (16-byte vectors, contiguous per wave instruction):
 //   K page [Hkv][D/8][P][8]: 16-byte slices of the 16 keys side by side, so a
 //     page of one kv head is 4 KB contiguous and a DMA instruction moves 1 KB;
 //   V page [Hkv][D][P]: each value dimension's 16 keys contiguous (32 B), so a
-//     lane reads 4 consecutive keys of one dimension as one 8-byte vector.
-// The score MFMA leaves 4 consecutive keys of one query row in each lane,
-// which is both the P^T operand layout of the PV product and the key order of
-// that 8-byte V^T read: probabilities go from the softmax to the second MFMA
-// with no shuffle. Row max and row sum need two cross-lane steps (the 4 lanes
-// holding one row).
+//     lane reads 8 consecutive keys of one dimension as one 16-byte vector.
+// The score MFMA leaves 4 consecutive keys of one query row in each lane; two
+// row-swap permutes regroup them into 8-key runs for the PV product. Row max
+// and row sum need two cross-lane steps (the 4 lanes holding one row).
 //
 // When there are too few groups to fill the GPU, a group's pages are split
 // across workgroups; each split writes (max, sum, unnormalised O) and a combine
@@ -161,15 +159,36 @@ __device__ __forceinline__ float row_sum4(float x) {
   return c + d;
 }
 
+// Regroups the bf16 probability pairs for the PV product. On entry lane group
+// G (lanes 16G..16G+15) holds, for its query row, the hi parts (h01, h23) and
+// lo parts (l01, l23) of keys 4G..4G+3. On exit the four registers of group 0
+// hold the hi parts of keys 0..7, group 1 the hi parts of keys 8..15, group 2
+// the lo parts of keys 0..7 and group 3 the lo parts of keys 8..15: the B
+// operand whose K slots match a V^T operand holding 8 consecutive keys of one
+// value dimension (keys 8*(G & 1)..+7), one 16-byte LDS read with no copies.
+// The 32-lane swap moves the lo parts of groups 0-1 up and the hi parts of
+// groups 2-3 down; the 16-lane swap then pairs neighbouring groups. Two wait
+// states separate each VALU write from the permute that reads it.
+__device__ __forceinline__ void pv_regroup(uint32_t& h01, uint32_t& h23, uint32_t& l01,
+                                           uint32_t& l23) {
+  asm("s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %2\n\t"
+      "v_permlane32_swap_b32 %1, %3\n\t"
+      "s_nop 1\n\t"
+      "v_permlane16_swap_b32 %0, %2\n\t"
+      "v_permlane16_swap_b32 %1, %3"
+      : "+v"(h01), "+v"(h23), "+v"(l01), "+v"(l23));
+}
+
 // Scores, online softmax and PV for one 16-key stage.
 //
 // S^T = K Q^T (four v_mfma_f32_16x16x32_bf16 over the 128 dimensions) leaves
-// keys 4q..4q+3 of one query row in each lane - the B operand layout of the
-// v_mfma_f32_16x16x32_bf16 that forms O^T += V^T P^T (hi parts in K slots
-// 0-3, lo parts in 4-7), whose A operand is the 8 bytes holding the same 4
-// keys of one value dimension in the transposed V page, twice: no shuffle
-// between the two products. Row max and row sum take two row-swap permutes
-// (the 4 lanes holding a row).
+// keys 4q..4q+3 of one query row in each lane. After the probabilities are
+// split and regrouped (pv_regroup), the v_mfma_f32_16x16x32_bf16 that forms
+// O^T += V^T P^T takes in each lane 8 keys' hi or lo parts against the
+// 16 bytes holding the same 8 keys of one value dimension in the transposed V
+// page. Row max and row sum take two row-swap permutes (the 4 lanes holding a
+// row).
 //
 // Softmax: scores are scaled into log2 units inside one FMA. The reference
 // max m is raised only when a row's new max exceeds it by more than
@@ -214,17 +233,17 @@ __device__ __forceinline__ void attend_page(RowState& st, const bf16x8 (&qr)[4],
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -base));
   st.l += row_sum4((p[0] + p[1]) + (p[2] + p[3]));
-  const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
-  const uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
-  const uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
-  // K slots 0-3 of this lane: hi parts of keys 4*grp..+3; slots 4-7: lo parts.
+  uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
+  uint32_t l01 = pack_bf16x2(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+  uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+  pv_regroup(h01, h23, l01, l23);
   const u32x4 pb = {h01, h23, l01, l23};
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    // the same 4 keys of value dimension dt*16 + col against both halves
-    const u32x2 va = *reinterpret_cast<const u32x2*>(&sg.v[(dt * 16 + col) * kPage + grp * 4]);
-    const u32x4 a = {va.x, va.y, va.x, va.y};
-    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(pb), st.o[dt], 0, 0, 0);
+    // keys 8*(grp & 1) .. +7 of value dimension dt*16 + col: one 16-byte read
+    const u32x4 va =
+        *reinterpret_cast<const u32x4*>(&sg.v[(dt * 16 + col) * kPage + (grp & 1) * 8]);
+    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb), st.o[dt], 0, 0, 0);
   }
 }
 
@@ -389,13 +408,18 @@ k_window_attn_bf16(AttnArgs a) {
   const int wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
 
+  // Consecutive workgroups go to different XCDs (round robin). With the
+  // sequence as the fastest index after the split, each XCD streams every kv
+  // head of its sequences; with the kv head there (Hkv = 8), XCD x would read
+  // only the x-th 4 KB of every page record, which leaves HBM channels unevenly
+  // loaded when pages are allocated in order (measured 4.5 against 5.2 TB/s).
   int bid = blockIdx.x;
   const int split = bid % a.n_splits;
   bid /= a.n_splits;
-  const int kvh = bid % a.Hkv;
-  bid /= a.Hkv;
   const int b = bid % a.B;
-  const int layer = bid / a.B;
+  bid /= a.B;
+  const int kvh = bid % a.Hkv;
+  const int layer = bid / a.Hkv;
   const int group = (layer * a.B + b) * a.Hkv + kvh;
 
   const int L = min(max(a.prefix_len[b], 0), a.max_prefix_len);

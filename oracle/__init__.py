@@ -12,7 +12,8 @@ Sources (the pages this oracle is written from):
     (reorder filled before masks with logical positions kept, a causal forward
     over the window conditioned on the persistent KV cache, commit of the
     leftmost contiguous filled run, refill with masks, distance-penalised
-    entropy selection).
+    entropy selection; the forward pass's predictions come from a projection
+    of each slot's hidden state onto the vocabulary).
   * WeDLM review at sai.science, sections "Summary", "Weaknesses",
     "Reproducibility & code": RoPE keeps logical positions; the score equation
     is missing from the text; the entropy-threshold flag and the one-by-one
@@ -25,7 +26,8 @@ outputs are exact. The readings adopted where the pages are silent are listed
 in each function's docstring.
 
 Parity status:
-  * reorder, RoPE, attention, entropy: pinned (tests/test_oracle_*.py).
+  * reorder, RoPE, attention, entropy, vocabulary projection: pinned
+    (tests/test_oracle_*.py).
   * the select fallback (a step where no mask slot clears the threshold fills
     the single lowest-score mask slot): parity unpinned. The pages do not say
     what happens then; the rule is a reading, exercised by hand-worked cases
@@ -38,6 +40,7 @@ from .attention import window_attention_reordered, window_attention_masked, visi
 from .entropy import vocab_entropy_argmax
 from .select import select_slots
 from .commit import commit_and_refill, cache_slot_of
+from .lm_head import vocab_projection, lm_head_select
 from .step import window_step, stream_loop
 
 __all__ = [
@@ -51,6 +54,8 @@ __all__ = [
     "select_slots",
     "commit_and_refill",
     "cache_slot_of",
+    "vocab_projection",
+    "lm_head_select",
     "window_step",
     "stream_loop",
 ]

@@ -112,3 +112,27 @@ def test_page_offset_mistake_is_caught(monkeypatch):
     case = next(c for c in t_sel.CASES if c["name"] == "run_then_gap_commit_across_pages")
     with pytest.raises(AssertionError):
         t_sel.test_golden_case(case)
+
+
+def test_projection_transposed_is_caught(monkeypatch):
+    import tests.test_oracle_lm_head as t_lm
+
+    def transposed(hidden, w_vocab):
+        h = np.asarray(hidden, np.float64)
+        w = np.asarray(w_vocab, np.float64)
+        return h @ w[: h.shape[-1], : h.shape[-1]]  # rows taken for columns
+    monkeypatch.setattr(t_lm, "vocab_projection", transposed)
+    with pytest.raises((AssertionError, ValueError)):
+        t_lm.test_one_hot_hidden_selects_a_column()
+
+
+def test_projection_dropped_term_is_caught(monkeypatch):
+    import tests.test_oracle_lm_head as t_lm
+
+    def last_term_dropped(hidden, w_vocab):
+        h = np.asarray(hidden, np.float64)[..., :-1]
+        w = np.asarray(w_vocab, np.float64)[:, :-1]
+        return h @ w.T
+    monkeypatch.setattr(t_lm, "vocab_projection", last_term_dropped)
+    with pytest.raises(AssertionError):
+        t_lm.test_brute_force_small()

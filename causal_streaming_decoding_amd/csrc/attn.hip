@@ -11,13 +11,13 @@
 // group's M = W*g query rows (physical row p, query head h of the group). The
 // group's key pages stream through an LDS ring, one page (16 keys, 8 KB of K
 // and V) per stage, filled by global->LDS DMA: 3 stages for 4-wave workgroups
-// (5 per CU), 7 for 8 waves and 15 for 16 waves (fewer per CU). A stage is
-// refilled as soon as every wave has finished reading it, so the whole ring is
-// in flight while the waves wait. Each key byte is read from HBM once per
-// workgroup.
+// (5 per CU), 7 for 8 waves and 15 for 16 waves (fewer per CU). One barrier
+// per page both publishes it and frees the stage computed before it, which is
+// refilled at once: all but one stage are in flight while the waves compute.
+// Each key byte is read from HBM once per workgroup.
 //
-//   S^T (16 keys x 16 rows)  = K (16 x 128) . Q^T        v_mfma_f32_16x16x32_bf16
-//   O^T (16 dims x 16 rows) += [V^T V^T] . [P_hi; P_lo]^T v_mfma_f32_16x16x32_bf16
+//   S^T (16 keys x 16 rows)  = K (16 x 128) . Q^T         v_mfma_f32_16x16x32_bf16
+//   O^T (16 dims x 16 rows) += V^T (x2) . [P_hi; P_lo]^T  v_mfma_f32_16x16x32_bf16
 //
 // P is split into a bf16 hi and lo part so that rounding the probabilities
 // costs no accuracy: the PV MFMA's 32 K slots take the 16 keys' hi parts and
@@ -317,13 +317,6 @@ __device__ __forceinline__ void stage_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-// Every wave has finished reading the stages it computed: its LDS reads have
-// returned (lgkmcnt) before the workgroup synchronises, so a DMA issued after
-// this barrier cannot overwrite data that is still being read.
-__device__ __forceinline__ void stage_release_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
-}
-
 // Wait for the oldest in-flight stage when `behind` (<= N) later stages,
 // kDma DMAs each, may stay in flight, then synchronise the workgroup. The
 // count must be an immediate, hence the chain over 0..N.
@@ -499,20 +492,18 @@ k_window_attn_bf16(AttnArgs a) {
   for (int s = 0; s < 4; ++s) qr[s] = as_bf16x8(qv[s]);
 
   // Ring of kStages stages. The prologue requested pages 0 .. kAhead-1. At
-  // iteration i the stage that held page i-1 is refilled with page i+kAhead as
-  // soon as every wave has finished reading it (first barrier), before anyone
-  // waits for page i: kStages pages are in flight while the waves wait, kAhead
-  // while they compute. Each thread then waits for its own DMAs of page i and
-  // the second barrier makes every wave's part of page i visible.
+  // iteration i each thread waits for its own DMAs of page i and one barrier
+  // makes every wave's part visible; every wave has then also finished
+  // computing page i-1 (its LDS reads retired before it reached the barrier),
+  // so that stage is refilled with page i+kAhead right away: kAhead pages are
+  // in flight while the waves compute, one barrier per page.
   for (int i = 0; i < npg; ++i) {
     const int pg = pg_begin + i;
-    if (i + kAhead < npg) {
-      if (i > 0) stage_release_barrier();  // page i-1's stage is free
+    // pages requested after page i: up to kAhead-1, fewer near the end
+    stage_wait_behind<kDma, kAhead - 1>(min(kAhead - 1, npg - 1 - i));
+    if (i + kAhead < npg)
       stage_dma<NW>(stage[(i + kAhead) % kStages], wave, lane, pg + kAhead, bt, a.max_pages,
                     a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
-    }
-    // pages requested after page i: up to kAhead, fewer near the end
-    stage_wait_behind<kDma, kAhead>(min(kAhead, npg - 1 - i));
     if (computes) attend_page(st, qr, stage[i % kStages], lane, L - pg * kPage, a.scale_log2);
   }
   // The window reuses stage 0: every DMA must have landed before it is

@@ -91,6 +91,40 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// ---- softmax entropy partials ----------------------------------------------
+
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kLn2F = 0.6931471805599453f;
+// A start value below any finite logit that keeps (m_old - m_new) * log2e finite.
+constexpr float kNegBig = -1.0e30f;
+
+// Reduction state of softmax entropy over part of a row of logits z, in base
+// 2: m = max z, s = sum 2^u and t = sum u 2^u with u = (z - m) log2(e); idx is
+// the lowest index holding m. Entropy in nats is ln2 (log2 s - t / s).
+struct EntPartial {
+  float m, s, t;
+  int idx;
+};
+
+// a <- a (+) b: both sums are moved to the larger reference max by the exact
+// identity t' = (t + d s) 2^d, s' = s 2^d with d = (m_old - m_new) log2(e);
+// ties of the max keep the lower index.
+__device__ __forceinline__ void merge(EntPartial& a, const EntPartial& b) {
+  const float mn = fmaxf(a.m, b.m);
+  const float da = (a.m - mn) * kLog2eF, db = (b.m - mn) * kLog2eF;
+  const float fa = __builtin_amdgcn_exp2f(da), fb = __builtin_amdgcn_exp2f(db);
+  const float s = a.s * fa + b.s * fb;
+  const float t = (a.t + da * a.s) * fa + (b.t + db * b.s) * fb;
+  int idx;
+  if (a.m > b.m) idx = a.idx;
+  else if (b.m > a.m) idx = b.idx;
+  else idx = min(a.idx, b.idx);
+  a.m = mn;
+  a.s = s;
+  a.t = t;
+  a.idx = idx;
+}
+
 // ---- host helpers -----------------------------------------------------------
 
 inline int launch_status() {
@@ -112,5 +146,13 @@ int commit_rows_rope(int dtype, int n_layers, int B, int W, int Hkv, int D, int 
                      int num_pages, int max_pages, double theta, const int32_t* run_len,
                      const int32_t* prefix_len, const void* k_rows, const void* v_rows,
                      const int32_t* block_table, void* k_cache, void* v_cache, hipStream_t s);
+
+// Internal: the selection half of wedlm_entropy_select over n_chunks partials
+// per row ([B * W][n_chunks], in vocabulary order), enqueued on `s`. Defined
+// in entropy.hip.
+int launch_entropy_select(const EntPartial* part, int n_chunks, int B, int W,
+                          const uint8_t* filled, float lambda, float tau, int min_fill,
+                          float* entropy, float* score, int32_t* argmax_tok, uint8_t* selected,
+                          hipStream_t s);
 
 }  // namespace wedlm

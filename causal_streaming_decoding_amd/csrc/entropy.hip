@@ -25,31 +25,6 @@
 namespace wedlm {
 
 constexpr int kEntThreads = 256;
-constexpr float kLog2eF = 1.4426950408889634f;
-constexpr float kLn2F = 0.6931471805599453f;
-// A start value below any finite logit that keeps (m_old - m_new) * log2e finite.
-constexpr float kNegBig = -1.0e30f;
-
-struct EntPartial {
-  float m, s, t;
-  int idx;
-};
-
-__device__ __forceinline__ void merge(EntPartial& a, const EntPartial& b) {
-  const float mn = fmaxf(a.m, b.m);
-  const float da = (a.m - mn) * kLog2eF, db = (b.m - mn) * kLog2eF;
-  const float fa = __builtin_amdgcn_exp2f(da), fb = __builtin_amdgcn_exp2f(db);
-  const float s = a.s * fa + b.s * fb;
-  const float t = (a.t + da * a.s) * fa + (b.t + db * b.s) * fb;
-  int idx;
-  if (a.m > b.m) idx = a.idx;
-  else if (b.m > a.m) idx = b.idx;
-  else idx = min(a.idx, b.idx);
-  a.m = mn;
-  a.s = s;
-  a.t = t;
-  a.idx = idx;
-}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -216,6 +191,15 @@ k_entropy_select(const EntPartial* __restrict__ part, int n_chunks, int W,
   if (in_window) selected[b * W + i] = sel ? 1 : 0;
 }
 
+int launch_entropy_select(const EntPartial* part, int n_chunks, int B, int W,
+                          const uint8_t* filled, float lambda, float tau, int min_fill,
+                          float* entropy, float* score, int32_t* argmax_tok, uint8_t* selected,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(k_entropy_select, dim3(B), dim3(kWave), 0, s, part, n_chunks, W, filled,
+                     lambda, tau, min_fill, entropy, score, argmax_tok, selected);
+  return launch_status();
+}
+
 struct EntPlan {
   int chunk_elems, n_chunks;
   bool vec;
@@ -282,9 +266,8 @@ extern "C" int wedlm_entropy_select(int dtype, int B, int W, int V, const void* 
       hipLaunchKernelGGL((k_entropy_partial<float, false>), grid, dim3(kEntThreads), 0, s, z, V,
                          pl.chunk_elems, pl.n_chunks, part);
   }
-  int st = launch_status();
+  const int st = launch_status();
   if (st != WEDLM_OK) return st;
-  hipLaunchKernelGGL(k_entropy_select, dim3(B), dim3(kWave), 0, s, part, pl.n_chunks, W, filled,
-                     lambda, tau, min_fill, entropy, score, argmax_tok, selected);
-  return launch_status();
+  return launch_entropy_select(part, pl.n_chunks, B, W, filled, lambda, tau, min_fill, entropy,
+                               score, argmax_tok, selected, s);
 }

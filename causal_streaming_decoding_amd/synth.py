@@ -204,6 +204,35 @@ def stream_step_inputs(wl: Workload, step: int, device, seed=None):
     return q, k, v, logits
 
 
+def lm_head_inputs(B, W, hidden, V, device, seed=0, logit_sigma=2.0, spike=None):
+    """Inputs of the fused vocabulary projection + selection, drawn on ``device``.
+
+    One torch generator seeded with ``seed``, draws in this order: hidden
+    states [B, W, hidden] ~ N(0, 1); projection rows [V, hidden] ~
+    N(0, logit_sigma^2 / hidden), so that the logits have standard deviation
+    about ``logit_sigma`` like the logits workloads; filled flags [B, W], each
+    slot with probability 1/2; then, when ``spike = (lo, hi)``, for every slot a
+    uniform token t and a magnitude c ~ U[lo, hi], and the hidden state gets
+    (c / logit_sigma^2) times row t of the projection added (its logit then
+    rises by about c). Both float tensors are rounded once to bf16.
+
+    Returns (hidden bf16 [B, W, hidden], w_vocab bf16 [V, hidden], filled uint8 [B, W]).
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    h = torch.randn((B, W, hidden), generator=g, device=device, dtype=torch.float32)
+    w = torch.randn((V, hidden), generator=g, device=device, dtype=torch.float32)
+    w.mul_(logit_sigma / hidden ** 0.5)
+    filled = (torch.rand((B, W), generator=g, device=device) < 0.5).to(torch.uint8)
+    if spike is not None:
+        lo, hi = spike
+        tok = torch.randint(0, V, (B * W,), generator=g, device=device)
+        mag = torch.rand(B * W, generator=g, device=device) * (hi - lo) + lo
+        w_b = w.to(torch.bfloat16).to(torch.float32)  # the stored rows
+        h.view(B * W, hidden).add_(w_b[tok] * (mag / logit_sigma ** 2)[:, None])
+    return h.to(torch.bfloat16), w.to(torch.bfloat16), filled
+
+
 def to_f64(t):
     """Host float64 copy of a torch tensor or numpy array (exact for f32/bf16)."""
     if isinstance(t, torch.Tensor):

@@ -18,6 +18,8 @@
  * wedlm_commit_prefix_rope apply the RoPE of step 2 as they load the window,
  * so a step can run reorder -> attn_rope -> entropy_select -> commit_rope
  * without the separate RoPE pass and its physical-order copies.
+ * wedlm_lm_head_select fuses the vocabulary projection that produces the
+ * logits with step 4, so the logits are never written.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -218,6 +220,35 @@ int wedlm_entropy_select(int dtype, int B, int W, int V, const void* logits, con
                          float lambda, float tau, int min_fill, float* entropy, float* score,
                          int32_t* argmax_tok, uint8_t* selected, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace wedlm_lm_head_select needs (per-tile partial reductions). */
+size_t wedlm_lm_head_select_workspace_size(int dtype, int B, int W, int hidden, int V);
+
+/*
+ * wedlm_lm_head_select - vocabulary projection fused with wedlm_entropy_select.
+ * hyper.ai summary of WeDLM, "Method": the causal forward pass over the window
+ * produces the predictions that the distance-penalised entropy rule ranks; its
+ * last operation maps each slot's final hidden state to vocabulary logits.
+ *
+ * For every slot i of sequence b the logits are z = hidden[b][i][:] . w_vocab^T
+ * (z_v = sum_k hidden[b][i][k] * w_vocab[v][k], products of the bf16 inputs
+ * accumulated in fp32; no bias), and entropy, argmax, score and selected are
+ * then exactly those wedlm_entropy_select computes from z (same readings,
+ * same fp32 score arithmetic and threshold / floor rule). z itself is never
+ * stored.
+ *
+ *   hidden_states  [B][W][hidden] bf16, slot order, 16-byte aligned.
+ *   w_vocab        [V][hidden] bf16 (row v = vocabulary entry v), 16-byte aligned.
+ *   filled, lambda, tau, min_fill, entropy, score, argmax_tok, selected:
+ *                  as wedlm_entropy_select.
+ *   workspace >= wedlm_lm_head_select_workspace_size(...).
+ * dtype must be WEDLM_BF16 and hidden a multiple of 64 (else
+ * WEDLM_ERR_UNSUPPORTED); W <= WEDLM_MAX_WINDOW, B * W <= 65535.
+ */
+int wedlm_lm_head_select(int dtype, int B, int W, int hidden, int V, const void* hidden_states,
+                         const void* w_vocab, const uint8_t* filled, float lambda, float tau,
+                         int min_fill, float* entropy, float* score, int32_t* argmax_tok,
+                         uint8_t* selected, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * wedlm_commit_prefix - commit of the leading filled run, paged append, refill.

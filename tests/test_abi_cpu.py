@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(W.LIB_PATH),
 
 def test_exports_every_declared_function():
     declared = W.header_functions()
-    assert len(declared) == 11
+    assert len(declared) == 13
     lib = W.lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -31,7 +31,7 @@ def test_status_strings_and_version():
     assert "unsupported" in W.wedlm_status_string(-2)
     assert "workspace" in W.wedlm_status_string(-3)
     assert W.wedlm_abi_version() >> 16 == 1
-    assert W.wedlm_abi_version() & 0xffff >= 1  # fused RoPE entry points
+    assert W.wedlm_abi_version() & 0xffff >= 2  # fused RoPE and LM-head entry points
 
 
 def _raw(name, *args):
@@ -137,3 +137,33 @@ def test_layout_round_trip_cpu(dtype):
     page, off = int(table[t // P]), t % P
     assert torch.equal(kc[1, page, 2, 1, off], k[t, 2, X:2 * X])
     assert torch.equal(vc[1, page, 2, :, off], v[t, 2])
+
+
+def test_lm_head_validation_and_workspace():
+    ws = W.wedlm_lm_head_select_workspace_size
+    assert ws(W.WEDLM_BF16, 16, 16, 4096, 151936) > 0
+    assert ws(W.WEDLM_F32, 16, 16, 4096, 151936) == 0     # bf16 only
+    assert ws(W.WEDLM_BF16, 16, 16, 4000, 151936) == 0    # hidden % 64
+    assert ws(W.WEDLM_BF16, 16, 65, 4096, 151936) == 0    # W > 64
+    # more partials for more rows and a larger vocabulary
+    assert ws(W.WEDLM_BF16, 16, 16, 4096, 151936) > ws(W.WEDLM_BF16, 1, 16, 4096, 151936)
+    assert ws(W.WEDLM_BF16, 1, 16, 4096, 151936) > ws(W.WEDLM_BF16, 1, 16, 4096, 5000)
+    good = [W.WEDLM_BF16, 2, 8, 128, 1000, 16, 16, 1, 0.1, 1.0, 1, 1, 1, 1, 1, 1, 1 << 30, None]
+    a = list(good); a[0] = W.WEDLM_F32
+    assert _raw("wedlm_lm_head_select", *a) == -2
+    a = list(good); a[3] = 100
+    assert _raw("wedlm_lm_head_select", *a) == -2         # hidden % 64
+    a = list(good); a[1] = 0
+    assert _raw("wedlm_lm_head_select", *a) == -1
+    a = list(good); a[5] = None
+    assert _raw("wedlm_lm_head_select", *a) == -1         # null hidden states
+    a = list(good); a[6] = 8
+    assert _raw("wedlm_lm_head_select", *a) == -1         # misaligned w_vocab
+    a = list(good); a[10] = 2
+    assert _raw("wedlm_lm_head_select", *a) == -1         # min_fill
+    a = list(good); a[8] = float("nan")
+    assert _raw("wedlm_lm_head_select", *a) == -1
+    a = list(good); a[16] = 16
+    assert _raw("wedlm_lm_head_select", *a) == -3         # workspace too small
+    a = list(good); a[15] = None
+    assert _raw("wedlm_lm_head_select", *a) == -3

@@ -1,0 +1,129 @@
+"""Fused vocabulary projection + entropy selection against the oracle (GPU).
+
+The GPU computes the logits in fp32 from bf16 hidden states and projection
+rows and never stores them; the oracle forms them in float64 from the same
+stored values. Entropy |dH| <= 1e-3, argmax exact (a row whose two largest
+oracle logits lie within 1e-3 may take either, and is counted), score within
+the entropy bar (it is formed from the GPU's entropy), selection exact except
+for sequences the oracle flags as near ties. Shapes
+cover one, two and four 32-row blocks per workgroup, several row groups, a
+ragged last vocabulary tile and the full Qwen3-8B / Qwen2.5-7B projections
+(sampled sequences).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from causal_streaming_decoding_amd import wedlm as W
+from causal_streaming_decoding_amd.synth import lm_head_inputs, to_f64
+
+from .parity import ENTROPY_ATOL
+
+pytestmark = pytest.mark.gpu
+
+LAM, TAU = 0.1, 1.0
+
+
+def _gpu(B, Wn, hidden, V, h, w, filled, lam=LAM, tau=TAU, min_fill=1):
+    dev = h.device
+    ent = torch.empty((B, Wn), dtype=torch.float32, device=dev)
+    score = torch.empty_like(ent)
+    arg = torch.empty((B, Wn), dtype=torch.int32, device=dev)
+    sel = torch.empty((B, Wn), dtype=torch.uint8, device=dev)
+    nbytes = W.wedlm_lm_head_select_workspace_size(W.WEDLM_BF16, B, Wn, hidden, V)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    W.wedlm_lm_head_select(W.WEDLM_BF16, B, Wn, hidden, V, h, w, filled, lam, tau, min_fill, ent,
+                           score, arg, sel, ws, nbytes)
+    torch.cuda.synchronize()
+    return {"entropy": ent.cpu().numpy(), "score": score.cpu().numpy(),
+            "argmax": arg.cpu().numpy(), "selected": sel.cpu().numpy().astype(bool)}
+
+
+def _oracle_rows(h64, w, seqs):
+    """Oracle logits of the given sequences, the projection converted in slices."""
+    V = w.shape[0]
+    z = np.empty((len(seqs), h64.shape[1], V))
+    step = 16384
+    for v0 in range(0, V, step):
+        wb = to_f64(w[v0:v0 + step])
+        z[:, :, v0:v0 + step] = oracle.vocab_projection(h64[seqs], wb)
+    return z
+
+
+def _compare(gpu, h, w, filled, seqs, lam=LAM, tau=TAU, min_fill=1):
+    h64 = to_f64(h)
+    f = filled.cpu().numpy().astype(bool)
+    z = _oracle_rows(h64, w, seqs)
+    H, a = oracle.vocab_entropy_argmax(z)
+    near = 0
+    flags = 0
+    worst = 0.0
+    for j, b in enumerate(seqs):
+        dH = np.abs(gpu["entropy"][b] - H[j])
+        assert (dH <= ENTROPY_ATOL).all(), ("entropy", b, float(dH.max()))
+        for i in range(z.shape[1]):
+            ga = int(gpu["argmax"][b, i])
+            if ga != a[j, i]:
+                # only a near tie of the two largest logits may differ
+                assert z[j, i, ga] >= z[j, i].max() - 1e-3, ("argmax", b, i, ga, int(a[j, i]))
+                near += 1
+        r = oracle.select_slots(H[j], f[b], lam, tau, min_fill)
+        if r["flags"]:
+            flags += 1
+            continue
+        # the score carries the entropy's error; the decision must still agree
+        dS = np.abs(gpu["score"][b].astype(np.float64) - r["score"].astype(np.float64))
+        assert (dS <= ENTROPY_ATOL).all(), ("score", b, float(dS.max()))
+        assert np.array_equal(gpu["selected"][b], r["selected"]), ("selected", b)
+        worst = max(worst, float(dH.max()))
+    print(f"[lm_head] max |dH| {worst:.2e}, argmax near ties {near}, flagged sequences {flags}",
+          flush=True)
+    return near, flags
+
+
+@pytest.mark.parametrize("B,Wn,hidden,V,spike", [
+    (1, 16, 256, 5000, None),        # one 32-row block, ragged last vocabulary tile
+    (2, 32, 512, 4096, None),        # two blocks, exact tiles
+    (3, 32, 128, 3001, (16.0, 20.0)),  # four blocks, low-entropy slots (threshold fires)
+    (5, 40, 192, 2600, None),        # 200 rows: two row groups, the last ragged
+    (1, 1, 64, 1, None),             # one slot, one vocabulary entry, one chunk
+])
+def test_lm_head_small(B, Wn, hidden, V, spike):
+    print(f"[lm_head] B={B} W={Wn} hidden={hidden} V={V} spike={spike}", flush=True)
+    h, w, filled = lm_head_inputs(B, Wn, hidden, V, "cuda", seed=B + V, spike=spike)
+    gpu = _gpu(B, Wn, hidden, V, h, w, filled)
+    near, flags = _compare(gpu, h, w, filled, list(range(B)))
+    assert near <= 1
+    if spike is not None:
+        assert gpu["selected"].sum() > B  # the threshold fired beyond the one-per-sequence floor
+
+
+@pytest.mark.parametrize("B,Wn,hidden,V,seqs", [
+    (16, 16, 4096, 151936, [0, 9]),   # Qwen3-8B projection, 256 rows
+    (1, 16, 4096, 151936, [0]),       # one sequence, 16 rows
+    (16, 32, 3584, 152064, [3]),      # Qwen2.5-7B projection, 512 rows
+])
+def test_lm_head_full_vocab_sampled(B, Wn, hidden, V, seqs):
+    print(f"[lm_head] full B={B} W={Wn} hidden={hidden} V={V}", flush=True)
+    h, w, filled = lm_head_inputs(B, Wn, hidden, V, "cuda", seed=7)
+    gpu = _gpu(B, Wn, hidden, V, h, w, filled)
+    assert np.isfinite(gpu["entropy"]).all()
+    assert ((gpu["argmax"] >= 0) & (gpu["argmax"] < V)).all()
+    # a sequence with a mask slot selects at least one slot (floor rule)
+    f = filled.cpu().numpy().astype(bool)
+    for b in range(B):
+        assert gpu["selected"][b].any() == (~f[b]).any()
+        assert not (gpu["selected"][b] & f[b]).any()
+    near, _ = _compare(gpu, h, w, filled, seqs)
+    assert near <= 1
+
+
+def test_lm_head_deterministic():
+    B, Wn, hidden, V = 4, 32, 1024, 40000
+    h, w, filled = lm_head_inputs(B, Wn, hidden, V, "cuda", seed=11)
+    g1 = _gpu(B, Wn, hidden, V, h, w, filled)
+    g2 = _gpu(B, Wn, hidden, V, h, w, filled)
+    for k in g1:
+        assert np.array_equal(g1[k], g2[k]), k

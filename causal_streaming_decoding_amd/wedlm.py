@@ -42,6 +42,8 @@ _SIGNATURES = {
                                + [_c_size, _p]),
     "wedlm_commit_prefix_rope": (_c_int, [_c_int] * 9 + [_c_double] + [_p] * 13
                                  + [ctypes.c_int32, _p]),
+    "wedlm_lm_head_packed_size": (_c_size, [_c_int] * 3),
+    "wedlm_lm_head_pack": (_c_int, [_c_int] * 3 + [_p, _p, _p]),
     "wedlm_lm_head_select_workspace_size": (_c_size, [_c_int] * 5),
     "wedlm_lm_head_select": (_c_int, [_c_int] * 5 + [_p, _p, _p, _c_float, _c_float, _c_int]
                              + [_p] * 5 + [_c_size, _p]),
@@ -162,15 +164,24 @@ def wedlm_entropy_select(dtype, B, W, V, logits, filled, lam, tau, min_fill, ent
         workspace_bytes, _stream(stream)))
 
 
+def wedlm_lm_head_packed_size(dtype, hidden, V):
+    return lib().wedlm_lm_head_packed_size(dtype, hidden, V)
+
+
+def wedlm_lm_head_pack(dtype, hidden, V, w_vocab, w_packed, stream=None):
+    _check("wedlm_lm_head_pack", lib().wedlm_lm_head_pack(
+        dtype, hidden, V, _ptr(w_vocab), _ptr(w_packed), _stream(stream)))
+
+
 def wedlm_lm_head_select_workspace_size(dtype, B, W, hidden, V):
     return lib().wedlm_lm_head_select_workspace_size(dtype, B, W, hidden, V)
 
 
-def wedlm_lm_head_select(dtype, B, W, hidden, V, hidden_states, w_vocab, filled, lam, tau, min_fill,
+def wedlm_lm_head_select(dtype, B, W, hidden, V, hidden_states, w_packed, filled, lam, tau, min_fill,
                          entropy, score, argmax_tok, selected, workspace, workspace_bytes,
                          stream=None):
     _check("wedlm_lm_head_select", lib().wedlm_lm_head_select(
-        dtype, B, W, hidden, V, _ptr(hidden_states), _ptr(w_vocab), _ptr(filled), float(lam),
+        dtype, B, W, hidden, V, _ptr(hidden_states), _ptr(w_packed), _ptr(filled), float(lam),
         float(tau), int(min_fill), _ptr(entropy), _ptr(score), _ptr(argmax_tok), _ptr(selected),
         _ptr(workspace), workspace_bytes, _stream(stream)))
 

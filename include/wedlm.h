@@ -19,7 +19,8 @@
  * so a step can run reorder -> attn_rope -> entropy_select -> commit_rope
  * without the separate RoPE pass and its physical-order copies.
  * wedlm_lm_head_select fuses the vocabulary projection that produces the
- * logits with step 4, so the logits are never written.
+ * logits with step 4, so the logits are never written (wedlm_lm_head_pack lays
+ * the projection out for it once).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -221,6 +222,24 @@ int wedlm_entropy_select(int dtype, int B, int W, int V, const void* logits, con
                          int32_t* argmax_tok, uint8_t* selected, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Bytes of the packed projection wedlm_lm_head_pack writes (0 for an unsupported shape). */
+size_t wedlm_lm_head_packed_size(int dtype, int hidden, int V);
+
+/*
+ * wedlm_lm_head_pack - lays the vocabulary projection out for
+ * wedlm_lm_head_select (once per model: the weights do not change between
+ * steps). w_vocab [V][hidden] bf16 (row v = vocabulary entry v) is copied into
+ * 4 KB tiles: tile (b, c), at element offset (b * hidden / 64 + c) * 2048,
+ * holds rows 32b .. 32b+31 and hidden elements 64c .. 64c+63, ordered
+ * [ks][kg][row][8] with ks in 0..3, kg in 0..1, where the 8 elements are hidden
+ * 64c + 32kg + 8ks .. +7 of that row (the operand order of one MFMA K-step).
+ * Rows 32 * ceil(V / 32) > v >= V are zeros. w_packed holds
+ * wedlm_lm_head_packed_size bytes; both pointers 16-byte aligned.
+ * dtype WEDLM_BF16 and hidden a multiple of 256, else WEDLM_ERR_UNSUPPORTED.
+ */
+int wedlm_lm_head_pack(int dtype, int hidden, int V, const void* w_vocab, void* w_packed,
+                       void* stream);
+
 /* Bytes of workspace wedlm_lm_head_select needs (per-tile partial reductions). */
 size_t wedlm_lm_head_select_workspace_size(int dtype, int B, int W, int hidden, int V);
 
@@ -230,23 +249,23 @@ size_t wedlm_lm_head_select_workspace_size(int dtype, int B, int W, int hidden, 
  * produces the predictions that the distance-penalised entropy rule ranks; its
  * last operation maps each slot's final hidden state to vocabulary logits.
  *
- * For every slot i of sequence b the logits are z = hidden[b][i][:] . w_vocab^T
- * (z_v = sum_k hidden[b][i][k] * w_vocab[v][k], products of the bf16 inputs
+ * For every slot i of sequence b the logits are z = hidden[b][i][:] . w^T
+ * (z_v = sum_k hidden[b][i][k] * w[v][k], products of the bf16 inputs
  * accumulated in fp32; no bias), and entropy, argmax, score and selected are
  * then exactly those wedlm_entropy_select computes from z (same readings,
  * same fp32 score arithmetic and threshold / floor rule). z itself is never
  * stored.
  *
  *   hidden_states  [B][W][hidden] bf16, slot order, 16-byte aligned.
- *   w_vocab        [V][hidden] bf16 (row v = vocabulary entry v), 16-byte aligned.
+ *   w_packed       the projection w [V][hidden] as wedlm_lm_head_pack wrote it.
  *   filled, lambda, tau, min_fill, entropy, score, argmax_tok, selected:
  *                  as wedlm_entropy_select.
  *   workspace >= wedlm_lm_head_select_workspace_size(...).
- * dtype must be WEDLM_BF16 and hidden a multiple of 64 (else
+ * dtype must be WEDLM_BF16 and hidden a multiple of 256 (else
  * WEDLM_ERR_UNSUPPORTED); W <= WEDLM_MAX_WINDOW, B * W <= 65535.
  */
 int wedlm_lm_head_select(int dtype, int B, int W, int hidden, int V, const void* hidden_states,
-                         const void* w_vocab, const uint8_t* filled, float lambda, float tau,
+                         const void* w_packed, const uint8_t* filled, float lambda, float tau,
                          int min_fill, float* entropy, float* score, int32_t* argmax_tok,
                          uint8_t* selected, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(W.LIB_PATH),
 
 def test_exports_every_declared_function():
     declared = W.header_functions()
-    assert len(declared) == 13
+    assert len(declared) == 15
     lib = W.lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -143,22 +143,31 @@ def test_lm_head_validation_and_workspace():
     ws = W.wedlm_lm_head_select_workspace_size
     assert ws(W.WEDLM_BF16, 16, 16, 4096, 151936) > 0
     assert ws(W.WEDLM_F32, 16, 16, 4096, 151936) == 0     # bf16 only
-    assert ws(W.WEDLM_BF16, 16, 16, 4000, 151936) == 0    # hidden % 64
+    assert ws(W.WEDLM_BF16, 16, 16, 4000, 151936) == 0    # hidden % 256
+    assert ws(W.WEDLM_BF16, 16, 16, 4032, 151936) == 0
     assert ws(W.WEDLM_BF16, 16, 65, 4096, 151936) == 0    # W > 64
     # more partials for more rows and a larger vocabulary
     assert ws(W.WEDLM_BF16, 16, 16, 4096, 151936) > ws(W.WEDLM_BF16, 1, 16, 4096, 151936)
     assert ws(W.WEDLM_BF16, 1, 16, 4096, 151936) > ws(W.WEDLM_BF16, 1, 16, 4096, 5000)
-    good = [W.WEDLM_BF16, 2, 8, 128, 1000, 16, 16, 1, 0.1, 1.0, 1, 1, 1, 1, 1, 1, 1 << 30, None]
+    # packed projection: rows rounded up to 32
+    assert W.wedlm_lm_head_packed_size(W.WEDLM_BF16, 4096, 151936) == 151936 * 4096 * 2
+    assert W.wedlm_lm_head_packed_size(W.WEDLM_BF16, 256, 33) == 64 * 256 * 2
+    assert W.wedlm_lm_head_packed_size(W.WEDLM_BF16, 320, 33) == 0
+    assert _raw("wedlm_lm_head_pack", W.WEDLM_BF16, 320, 33, 16, 16, None) == -2
+    assert _raw("wedlm_lm_head_pack", W.WEDLM_BF16, 256, 0, 16, 16, None) == -1
+    assert _raw("wedlm_lm_head_pack", W.WEDLM_BF16, 256, 33, None, 16, None) == -1
+    assert _raw("wedlm_lm_head_pack", W.WEDLM_BF16, 256, 33, 16, 8, None) == -1
+    good = [W.WEDLM_BF16, 2, 8, 256, 1000, 16, 16, 1, 0.1, 1.0, 1, 1, 1, 1, 1, 1, 1 << 30, None]
     a = list(good); a[0] = W.WEDLM_F32
     assert _raw("wedlm_lm_head_select", *a) == -2
-    a = list(good); a[3] = 100
-    assert _raw("wedlm_lm_head_select", *a) == -2         # hidden % 64
+    a = list(good); a[3] = 320
+    assert _raw("wedlm_lm_head_select", *a) == -2         # hidden % 256
     a = list(good); a[1] = 0
     assert _raw("wedlm_lm_head_select", *a) == -1
     a = list(good); a[5] = None
     assert _raw("wedlm_lm_head_select", *a) == -1         # null hidden states
     a = list(good); a[6] = 8
-    assert _raw("wedlm_lm_head_select", *a) == -1         # misaligned w_vocab
+    assert _raw("wedlm_lm_head_select", *a) == -1         # misaligned packed projection
     a = list(good); a[10] = 2
     assert _raw("wedlm_lm_head_select", *a) == -1         # min_fill
     a = list(good); a[8] = float("nan")

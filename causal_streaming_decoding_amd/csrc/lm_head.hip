@@ -14,8 +14,9 @@
 // + r%4, so a row's softmax partial needs one swap of the two lane halves.
 //
 // Workgroup: 4 wavefronts, 256 vocabulary entries (64 per wavefront, two
-// 32-row A blocks) x up to 128 hidden rows (RB blocks of 32; more rows take
-// more workgroups, dispatched next to each other). The hidden dimension
+// 32-row A blocks) x up to 256 hidden rows (RB blocks of 32: the 256 rows'
+// accumulators fill the accumulation registers; more rows take more
+// workgroups, dispatched next to each other). The hidden dimension
 // streams in chunks of 64:
 //   - W, packed once by wedlm_lm_head_pack into 4 KB tiles (32 rows x 64, in
 //     MFMA operand order): each wavefront loads its own tiles straight into
@@ -46,7 +47,7 @@ constexpr int kLmKSteps = kLmKC / 16;                // MFMA K-steps per chunk
 constexpr int kLmTileElems = 32 * kLmKC;             // one packed W tile: 32 rows x 64 (4 KB)
 constexpr int kLmAhead = 3;                          // chunks requested ahead of the one computed
 constexpr int kLmStages = kLmAhead + 1;              // h ring stages and W register buffers
-constexpr int kLmMaxRB = 4;                          // 32-row blocks of hidden rows per workgroup
+constexpr int kLmMaxRB = 8;                          // 32-row blocks of hidden rows per workgroup
 
 __device__ __forceinline__ bf16x8_t as_bf16x8_t(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
 
@@ -320,7 +321,7 @@ struct LmPlan {
 
 static LmPlan plan_lm_head(int rows, int V) {
   LmPlan pl{};
-  pl.rb = rows <= 32 ? 1 : (rows <= 64 ? 2 : kLmMaxRB);
+  pl.rb = rows <= 32 ? 1 : (rows <= 64 ? 2 : (rows <= 128 ? 4 : kLmMaxRB));
   pl.row_groups = ceil_div(rows, 32 * pl.rb);
   pl.n_tiles = ceil_div(V, kLmVocabTile);
   // partial offsets stay 256-byte aligned
@@ -437,6 +438,7 @@ extern "C" int wedlm_lm_head_select(int dtype, int B, int W, int hidden, int V,
   switch (pl.rb) {
     case 1: hipLaunchKernelGGL(k_lm_head_partial<1>, grid, dim3(kLmThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL(k_lm_head_partial<2>, grid, dim3(kLmThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(k_lm_head_partial<4>, grid, dim3(kLmThreads), 0, s, a); break;
     default: hipLaunchKernelGGL(k_lm_head_partial<kLmMaxRB>, grid, dim3(kLmThreads), 0, s, a); break;
   }
   int st = launch_status();

@@ -102,6 +102,8 @@ def _compare(gpu, h, w, filled, seqs, lam=LAM, tau=TAU, min_fill=1):
     (4, 32, 1280, 2048, (6.0, 12.0)),  # five rotations of the chunk loop
     (2, 16, 1024, 700, None),        # a vocabulary smaller than three tiles
     (1, 5, 256, 33, None),           # a packed block that is mostly padding
+    (3, 60, 512, 3000, None),        # 180 rows: eight 32-row blocks, the last ragged
+    (6, 64, 256, 1000, (16.0, 20.0)),  # 384 rows: two workgroups of 256 and 128 rows
 ])
 def test_lm_head_small(B, Wn, hidden, V, spike):
     print(f"[lm_head] B={B} W={Wn} hidden={hidden} V={V} spike={spike}", flush=True)

@@ -46,6 +46,9 @@ def parse():
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--all-configs", action="store_true",
                     help="instead: single-step latency of every other workload, one JSON line each")
+    ap.add_argument("--lm-head", action="store_true",
+                    help="time the fused vocabulary projection + selection (one JSON line per shape)")
+    ap.add_argument("--lm-head-steps", type=int, default=50)
     ap.add_argument("--config-steps", type=int, default=200)
     ap.add_argument("--config-warmup", type=int, default=20)
     return ap.parse_args()
@@ -218,6 +221,112 @@ def config_latencies(args):
         torch.cuda.empty_cache()
 
 
+# (name, B, W, hidden, V): the projection of the streaming workload's window
+# rows (Qwen3-8B), one and four sequences of it, and the Qwen2.5-7B shape
+LM_HEAD_SHAPES = (
+    ("qwen3_8b_lm_head_bs16_W16", 16, 16, 4096, 151936),
+    ("qwen3_8b_lm_head_bs1_W16", 1, 16, 4096, 151936),
+    ("qwen3_8b_lm_head_bs4_W16", 4, 16, 4096, 151936),
+    ("qwen25_7b_lm_head_bs16_W32", 16, 32, 3584, 152064),
+)
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, vendor figure
+
+
+def lm_head_latencies(args):
+    """Fused vocabulary projection + entropy selection, one JSON line per shape.
+
+    The projection is packed once outside the timed region (model weights do
+    not change between steps). Each call is timed with HIP events on the
+    launch stream, back to back: the 1.2 GB projection does not fit in the
+    caches, so every call streams it from HBM. Algorithmic bytes = packed
+    projection + hidden states read once + outputs; flops = 2 rows hidden V.
+    The roofline is HBM when the intensity (flops per byte) is below the
+    bf16 ridge (2.5 PFLOP/s / 8 TB/s = 312), else MFMA. The oracle (float64
+    projection, entropy and selection) is timed on one sequence's rows.
+    """
+    import numpy as np
+    import torch
+
+    from causal_streaming_decoding_amd import wedlm as W
+    from causal_streaming_decoding_amd.synth import lm_head_inputs, to_f64
+
+    dev = "cuda:0"
+    hev = HipEvents(torch.cuda.current_stream().cuda_stream)
+    for name, B, Wn, hidden, V in LM_HEAD_SHAPES:
+        print(f"[bench] {name}", file=sys.stderr, flush=True)
+        h, w, filled = lm_head_inputs(B, Wn, hidden, V, dev, seed=0)
+        wp = torch.empty(W.wedlm_lm_head_packed_size(W.WEDLM_BF16, hidden, V) // 2,
+                         dtype=torch.bfloat16, device=dev)
+        W.wedlm_lm_head_pack(W.WEDLM_BF16, hidden, V, w, wp)
+        ent = torch.empty((B, Wn), dtype=torch.float32, device=dev)
+        score = torch.empty_like(ent)
+        arg = torch.empty((B, Wn), dtype=torch.int32, device=dev)
+        sel = torch.empty((B, Wn), dtype=torch.uint8, device=dev)
+        nb = W.wedlm_lm_head_select_workspace_size(W.WEDLM_BF16, B, Wn, hidden, V)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+        def call():
+            W.wedlm_lm_head_select(W.WEDLM_BF16, B, Wn, hidden, V, h, wp, filled, 0.1, 1.0, 1, ent,
+                                   score, arg, sel, ws, nb)
+        n_warm, n = 5, args.lm_head_steps
+        ev = [(hev.create(), hev.create()) for _ in range(n_warm + n)]
+        for a_, b_ in ev:
+            hev.record(a_)
+            call()
+            hev.record(b_)
+        torch.cuda.synchronize()
+        us = np.array([hev.elapsed_ms(a_, b_) for a_, b_ in ev[n_warm:]]) * 1e3
+        hev.destroy()
+        rows = B * Wn
+        byts = wp.numel() * 2 + h.numel() * 2 + rows * (4 + 4 + 4 + 1)
+        flops = 2.0 * rows * hidden * V
+        med = float(np.median(us))
+        intensity = flops / byts
+        ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+        if intensity < ridge:
+            roof = {"bound": "hbm", "achieved": byts / (med * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s"}
+        else:
+            roof = {"bound": "mfma", "achieved": flops / (med * 1e-6) / 1e12,
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = None
+        # oracle on the first sequence's rows (its W rows of logits)
+        import oracle
+        h64 = to_f64(h[:1])
+        t0 = time.perf_counter()
+        z = np.concatenate([oracle.vocab_projection(h64, to_f64(w[v0:v0 + 16384]))
+                            for v0 in range(0, V, 16384)], axis=-1)
+        H, _ = oracle.vocab_entropy_argmax(z)
+        oracle.select_slots(H[0], filled[0].cpu().numpy().astype(bool), 0.1, 1.0, 1)
+        cpu_s = time.perf_counter() - t0
+        line = {
+            "workload": name, "metric": "vocabulary projection + selection latency", "unit": "us",
+            "dtype": "bf16 (fp32 accumulation)", "rows": rows, "hidden": hidden, "V": V,
+            "steps": n, "warmup": n_warm,
+            "us": {"median": med, "p10": float(np.percentile(us, 10)),
+                   "p90": float(np.percentile(us, 90))},
+            "algorithmic_bytes": int(byts), "flops": flops, "intensity_flop_per_byte": intensity,
+            "hbm_gbps_at_median": byts / (med * 1e-6) / 1e9,
+            "tflops_at_median": flops / (med * 1e-6) / 1e12,
+            "roofline": roof,
+            "cpu_baseline": {"value": Wn / cpu_s, "unit": "rows/s", "kind": "oracle",
+                             "cores": len(os.sched_getaffinity(0)),
+                             "sample": f"one sequence's {Wn} rows: float64 projection, "
+                                       "entropy and selection (the projection converted to "
+                                       "float64 in slices, included)"},
+            "data": "synthetic",
+        }
+        print(json.dumps(line), flush=True)
+        del h, w, wp, ws
+        torch.cuda.empty_cache()
+    if args.calibrate_copy:
+        a = torch.empty(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -226,6 +335,9 @@ def main():
         sys.exit(2)
     if args.all_configs:
         config_latencies(args)
+        return
+    if args.lm_head:
+        lm_head_latencies(args)
         return
 
     import numpy as np

@@ -40,8 +40,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kLmThreads = 256;                      // 4 wavefronts
-constexpr int kLmVB = 2;                             // 32-row vocabulary blocks per wavefront
-constexpr int kLmVocabTile = 4 * kLmVB * 32;         // vocabulary entries per workgroup
+constexpr int kLmMaxVB = 2;                          // 32-row vocabulary blocks per wavefront (at most)
 constexpr int kLmKC = 64;                            // hidden elements per chunk
 constexpr int kLmKSteps = kLmKC / 16;                // MFMA K-steps per chunk
 constexpr int kLmTileElems = 32 * kLmKC;             // one packed W tile: 32 rows x 64 (4 KB)
@@ -100,12 +99,14 @@ __device__ __forceinline__ void wait_chunks_behind(int behind) {
   }
 }
 
-template <int RB>
+template <int RB, int VB>
 __global__ void __launch_bounds__(kLmThreads)
 k_lm_head_partial(LmArgs a) {
+  static_assert(VB == 1 || VB == 2, "vocabulary blocks per wavefront");
   constexpr int kTileRows = 32 * RB;
+  constexpr int kWaveVocab = 32 * VB;         // vocabulary entries per wavefront
   constexpr int kDmaH = RB;                   // h DMA instructions per wavefront per chunk (8 rows each)
-  constexpr int kPer = kLmVB * kLmKSteps + kDmaH;  // vector-memory operations per wavefront per chunk
+  constexpr int kPer = VB * kLmKSteps + kDmaH;  // vector-memory operations per wavefront per chunk
   constexpr int kStageElems = kTileRows * kLmKC;
   __shared__ uint16_t ring[kLmStages][kStageElems];  // hidden rows [row][64], swizzled
   __shared__ EntPartial red[4][kTileRows];
@@ -113,7 +114,7 @@ k_lm_head_partial(LmArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 31, kg = lane >> 5;
-  const int v_wg = blockIdx.y * kLmVocabTile;
+  const int v_wg = blockIdx.y * 4 * kWaveVocab;
   const int r0 = blockIdx.x * kTileRows;
   const int nk = a.hidden / kLmKC;  // a multiple of 4 on this path
 
@@ -121,10 +122,10 @@ k_lm_head_partial(LmArgs a) {
   // packed rows past V are zeros and their entries are masked at the end);
   // at K-step ks the lane reads 16 bytes at (ks*2 + kg)*32 + li of a tile,
   // so each load instruction reads 1 KB of contiguous memory
-  const uint16_t* wtile[kLmVB];
+  const uint16_t* wtile[VB];
 #pragma unroll
-  for (int vb = 0; vb < kLmVB; ++vb) {
-    const int blk = min((v_wg + wave * 64) / 32 + vb, a.v_blocks - 1);
+  for (int vb = 0; vb < VB; ++vb) {
+    const int blk = min((v_wg + wave * kWaveVocab) / 32 + vb, a.v_blocks - 1);
     wtile[vb] = a.w + static_cast<size_t>(blk) * nk * kLmTileElems + (kg * 32 + li) * 8;
   }
   // DMA sources: instruction j of this wavefront moves ring lines
@@ -142,14 +143,14 @@ k_lm_head_partial(LmArgs a) {
 #pragma unroll
   for (int ks = 0; ks < kLmKSteps; ++ks) hoff[ks] = li * kLmKC + h_swz(li, kg * 4 + ks) * 8;
 
-  typedef u32x4_t WBuf[kLmVB][kLmKSteps];
+  typedef u32x4_t WBuf[VB][kLmKSteps];
   WBuf wbuf[kLmStages];
   // chunk c's W loads (asm, waits explicit) then its h DMAs into ring stage c % 4
   auto issue = [&](int c, auto stage_c, WBuf& wb) {
     constexpr int T = decltype(stage_c)::value;
     const int k0 = c * kLmKC;
 #pragma unroll
-    for (int vb = 0; vb < kLmVB; ++vb)
+    for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
       for (int ks = 0; ks < kLmKSteps; ++ks)
         load16(wb[vb][ks], wtile[vb] + static_cast<size_t>(c) * kLmTileElems + ks * 512);
@@ -161,9 +162,9 @@ k_lm_head_partial(LmArgs a) {
                                            (j * 4 + wave) * 8 * kLmKC * 2));
     }
   };
-  f32x16 acc[kLmVB][RB];
+  f32x16 acc[VB][RB];
 #pragma unroll
-  for (int vb = 0; vb < kLmVB; ++vb)
+  for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -178,11 +179,17 @@ k_lm_head_partial(LmArgs a) {
     constexpr int S = decltype(s_c)::value;
     constexpr int kBehind = decltype(behind_c)::value;
     WBuf& wb = wbuf[S];
-    asm volatile("s_waitcnt vmcnt(%8) lgkmcnt(0)\n\ts_barrier"
-                 : "+v"(wb[0][0]), "+v"(wb[0][1]), "+v"(wb[0][2]), "+v"(wb[0][3]), "+v"(wb[1][0]),
-                   "+v"(wb[1][1]), "+v"(wb[1][2]), "+v"(wb[1][3])
-                 : "n"(kBehind * kPer)
-                 : "memory");
+    if constexpr (VB == 2)
+      asm volatile("s_waitcnt vmcnt(%8) lgkmcnt(0)\n\ts_barrier"
+                   : "+v"(wb[0][0]), "+v"(wb[0][1]), "+v"(wb[0][2]), "+v"(wb[0][3]),
+                     "+v"(wb[1][0]), "+v"(wb[1][1]), "+v"(wb[1][2]), "+v"(wb[1][3])
+                   : "n"(kBehind * kPer)
+                   : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%4) lgkmcnt(0)\n\ts_barrier"
+                   : "+v"(wb[0][0]), "+v"(wb[0][1]), "+v"(wb[0][2]), "+v"(wb[0][3])
+                   : "n"(kBehind * kPer)
+                   : "memory");
     if constexpr (decltype(issue_c)::value)
       issue(c + kLmAhead, std::integral_constant<int, (S + kLmAhead) % kLmStages>{},
             wbuf[(S + kLmAhead) % kLmStages]);
@@ -203,7 +210,7 @@ k_lm_head_partial(LmArgs a) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int vb = 0; vb < kLmVB; ++vb)
+        for (int vb = 0; vb < VB; ++vb)
           acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               as_bf16x8_t(wb[vb][ks]), as_bf16x8_t(hb[ks & 1][rb]), acc[vb][rb], 0, 0, 0);
     }
@@ -242,10 +249,10 @@ k_lm_head_partial(LmArgs a) {
   for (int rb = 0; rb < RB; ++rb) {
     EntPartial p{kNegBig, 0.f, 0.f, 0x7fffffff};
 #pragma unroll
-    for (int vb = 0; vb < kLmVB; ++vb)
+    for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int v = v_wg + wave * 64 + vb * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
+        const int v = v_wg + wave * kWaveVocab + vb * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
         const float z = acc[vb][rb][r];
         if (v < a.V && (z > p.m || (z == p.m && v < p.idx))) {
           p.m = z;
@@ -254,10 +261,10 @@ k_lm_head_partial(LmArgs a) {
       }
     const float mb = p.m * kLog2eF;
 #pragma unroll
-    for (int vb = 0; vb < kLmVB; ++vb)
+    for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int v = v_wg + wave * 64 + vb * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
+        const int v = v_wg + wave * kWaveVocab + vb * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
         const float u = fmaf(acc[vb][rb][r], kLog2eF, -mb);
         const float e = v < a.V ? __builtin_amdgcn_exp2f(u) : 0.f;
         p.s += e;
@@ -315,15 +322,18 @@ k_entropy_merge_rows(const EntPartial* __restrict__ part, int n_tiles, EntPartia
 }
 
 struct LmPlan {
-  int rb, n_tiles, row_groups;
+  int rb, vb, n_tiles, row_groups;
   size_t part_bytes, merged_bytes;
 };
 
 static LmPlan plan_lm_head(int rows, int V) {
   LmPlan pl{};
   pl.rb = rows <= 32 ? 1 : (rows <= 64 ? 2 : (rows <= 128 ? 4 : kLmMaxRB));
+  // two blocks per wavefront: one block (twice the tiles, a smaller last
+  // round) measured slower for 256 and 512 rows
+  pl.vb = kLmMaxVB;
   pl.row_groups = ceil_div(rows, 32 * pl.rb);
-  pl.n_tiles = ceil_div(V, kLmVocabTile);
+  pl.n_tiles = ceil_div(V, 4 * 32 * pl.vb);
   // partial offsets stay 256-byte aligned
   pl.part_bytes = (static_cast<size_t>(rows) * pl.n_tiles * sizeof(EntPartial) + 255) & ~size_t(255);
   pl.merged_bytes = static_cast<size_t>(rows) * sizeof(EntPartial);
@@ -335,7 +345,7 @@ static int validate_shape(int dtype, int hidden, int V) {
   if (!valid_dtype(dtype)) return WEDLM_ERR_UNSUPPORTED;
   if (hidden <= 0 || V <= 0) return WEDLM_ERR_INVALID;
   if (dtype != WEDLM_BF16 || hidden % (kLmKC * kLmStages) != 0) return WEDLM_ERR_UNSUPPORTED;
-  if (ceil_div(V, kLmVocabTile) > 65535 || 1LL * ceil_div(V, 32) * 32 * hidden > (1LL << 40))
+  if (ceil_div(V, 4 * 32) > 65535 || 1LL * ceil_div(V, 32) * 32 * hidden > (1LL << 40))
     return WEDLM_ERR_UNSUPPORTED;
   return WEDLM_OK;
 }
@@ -435,12 +445,11 @@ extern "C" int wedlm_lm_head_select(int dtype, int B, int W, int hidden, int V,
   a.n_tiles = pl.n_tiles;
   a.v_blocks = ceil_div(V, 32);
   const dim3 grid(pl.row_groups, pl.n_tiles);
-  switch (pl.rb) {
-    case 1: hipLaunchKernelGGL(k_lm_head_partial<1>, grid, dim3(kLmThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_lm_head_partial<2>, grid, dim3(kLmThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(k_lm_head_partial<4>, grid, dim3(kLmThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_lm_head_partial<kLmMaxRB>, grid, dim3(kLmThreads), 0, s, a); break;
-  }
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(kLmThreads), 0, s, a); };
+  if (pl.rb == 1) go(k_lm_head_partial<1, 2>);
+  else if (pl.rb == 2) go(k_lm_head_partial<2, 2>);
+  else if (pl.rb == 4) go(k_lm_head_partial<4, 2>);
+  else go(k_lm_head_partial<8, 2>);
   int st = launch_status();
   if (st != WEDLM_OK) return st;
   hipLaunchKernelGGL(k_entropy_merge_rows, dim3(rows), dim3(kLmThreads), 0, s, part, pl.n_tiles,

@@ -13,7 +13,8 @@ is 1 GiB read and 1 GiB written. The window-attention record it writes holds a
 hash of the kernel's source files, so that a later reader can tell whether the
 counters still describe the kernel that is built.
 
-Usage (the second form summarises ``bench.py --all-configs``)::
+Usage (the second form summarises ``bench.py --all-configs``, the third
+``bench.py --lm-head``)::
 
     python -m causal_streaming_decoding_amd.profiling configs --configs-jsonl <file> \\
         --trace <dir> --out-md profiles/<name>.md
@@ -21,6 +22,8 @@ Usage (the second form summarises ``bench.py --all-configs``)::
         --trace gpurun_out/prof_trace --fetch gpurun_out/prof_fetch \\
         --write gpurun_out/prof_write --bench-json gpurun_out/prof_bench.json \\
         --steps 256 --out-md profiles/<name>.md --out-traffic profiles/<name>_traffic.txt
+    python -m causal_streaming_decoding_amd.profiling lmhead --bench-jsonl <file> \\
+        --trace <dir> --fetch <dir> --write <dir> --out-md profiles/<name>.md
 """
 
 import argparse
@@ -196,6 +199,72 @@ def summarize_configs(configs_jsonl, trace_dir, out_md, command_bench, command_t
         f.write("\n".join(lines) + "\n")
 
 
+def _dispatch_runs(csv_path, name_prefix, value_key, counter=None):
+    """Runs of consecutive dispatches of one kernel with the same (name, grid),
+    in dispatch order: [(name, grid, [values])]."""
+    with open(csv_path) as f:
+        rows = list(csv.DictReader(f))
+    if counter is not None:
+        rows = [r for r in rows if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    runs = []
+    for r in rows:
+        n = short_name(r["Kernel_Name"])
+        if not n.startswith(name_prefix):
+            continue
+        key = (n, int(r["Grid_Size"]) if "Grid_Size" in r else int(r["Grid_Size_X"]))
+        v = value_key(r)
+        if runs and runs[-1][0] == key:
+            runs[-1][1].append(v)
+        else:
+            runs.append((key, [v]))
+    return [(k[0], k[1], v) for k, v in runs]
+
+
+def summarize_lm_head(bench_jsonl, trace, fetch, write, out_md, command_bench, command_trace,
+                      command_fetch, command_write):
+    """Vocabulary projection: per shape, the partial-reduction kernel's trace
+    duration and calibrated HBM bytes against its algorithmic bytes."""
+    import statistics
+
+    lines_in = [json.loads(ln) for ln in open(bench_jsonl) if ln.startswith("{")]
+    kern = "wedlm::k_lm_head_partial"
+    dur = _dispatch_runs(os.path.join(trace, "run_kernel_trace.csv"), kern,
+                         lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    _, f_cal = counter_values(fetch, "FETCH_SIZE")
+    _, w_cal = counter_values(write, "WRITE_SIZE")
+    f_fac, w_fac = f_cal / CALIBRATION_KIB, w_cal / CALIBRATION_KIB
+    fet = _dispatch_runs(os.path.join(fetch, "run_counter_collection.csv"), kern,
+                         lambda r: float(r["Counter_Value"]), "FETCH_SIZE")
+    wri = _dispatch_runs(os.path.join(write, "run_counter_collection.csv"), kern,
+                         lambda r: float(r["Counter_Value"]), "WRITE_SIZE")
+    if not (len(dur) == len(fet) == len(wri) == len(lines_in)):
+        raise SystemExit(f"shape runs do not line up: {len(dur)} {len(fet)} {len(wri)} {len(lines_in)}")
+    out = ["# Fused vocabulary projection + selection", "",
+           "MI355X (gfx950). One row per shape of `bench.py --lm-head`: the bench's HIP-event "
+           "median of the whole call (projection kernel, partial merge, selection), the trace "
+           "median of the projection kernel `k_lm_head_partial` alone, and that kernel's HBM "
+           "bytes from the counters (calibrated by a 1 GiB copy, mean over the timed calls). "
+           "In the commands, `<repo>` is the repository root.", "",
+           "```", command_bench, command_trace, command_fetch, command_write, "```", "",
+           f"Calibration: FETCH_SIZE factor {f_fac:.4f}, WRITE_SIZE factor {w_fac:.4f}.", "",
+           "| shape | rows x hidden x V | call median us | kernel | kernel median us | "
+           "algorithmic MB | read MB | written MB | counted / algorithmic | roofline |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for ln, (name, grid, d), (_, _, fv), (_, _, wv) in zip(lines_in, dur, fet, wri):
+        rd = statistics.mean(fv[-ln["steps"]:]) * 1024.0 / f_fac
+        wr = statistics.mean(wv[-ln["steps"]:]) * 1024.0 / w_fac
+        alg = ln["algorithmic_bytes"]
+        roof = ln["roofline"]
+        out.append(
+            f"| `{ln['workload']}` | {ln['rows']} x {ln['hidden']} x {ln['V']} | "
+            f"{ln['us']['median']:.1f} | `{name}` ({grid // 256} row groups) | "
+            f"{statistics.median(d[-ln['steps']:]):.1f} | {alg / 1e6:.1f} | {rd / 1e6:.1f} | "
+            f"{wr / 1e6:.2f} | {(rd + wr) / alg:.3f} | {roof['bound']} {roof['frac'] * 100:.1f} % |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(out) + "\n")
+
+
 def read_traffic(path, workload, steps):
     """Counted HBM bytes per attention launch, or None when the record does not apply.
 
@@ -217,6 +286,20 @@ def read_traffic(path, workload, steps):
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "lmhead":
+        ap = argparse.ArgumentParser()
+        ap.add_argument("mode")
+        ap.add_argument("--bench-jsonl", required=True)
+        ap.add_argument("--trace", required=True)
+        ap.add_argument("--fetch", required=True)
+        ap.add_argument("--write", required=True)
+        ap.add_argument("--out-md", required=True)
+        for k in ("bench", "trace", "fetch", "write"):
+            ap.add_argument(f"--command-{k}", default="")
+        a = ap.parse_args()
+        summarize_lm_head(a.bench_jsonl, a.trace, a.fetch, a.write, a.out_md, a.command_bench,
+                          a.command_trace, a.command_fetch, a.command_write)
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "configs":
         ap = argparse.ArgumentParser()
         ap.add_argument("mode")

@@ -39,7 +39,7 @@ from .rope import rope_frequencies, rope_rotate
 from .attention import window_attention_reordered, window_attention_masked, visible_mask
 from .entropy import vocab_entropy_argmax
 from .select import select_slots
-from .commit import commit_and_refill, cache_slot_of
+from .commit import commit_and_refill, cache_slot_of, commit_count
 from .lm_head import vocab_projection, lm_head_select
 from .step import window_step, stream_loop
 
@@ -54,6 +54,7 @@ __all__ = [
     "select_slots",
     "commit_and_refill",
     "cache_slot_of",
+    "commit_count",
     "vocab_projection",
     "lm_head_select",
     "window_step",

@@ -21,7 +21,7 @@ from .commit import commit_and_refill
 
 def window_step(filled, tokens, prefix_len, q, k, v, k_cache, v_cache, logits, block_table,
                 theta, lam, tau, page_size, min_fill=1, mask_id=-1, layers=None, scale=None,
-                override_selected=None, store=None):
+                override_selected=None, store=None, commit_rule="stream"):
     """One window step for a batch of sequences and n_layers independent layers.
 
     Args:
@@ -40,6 +40,8 @@ def window_step(filled, tokens, prefix_len, q, k, v, k_cache, v_cache, logits, b
         rotated window rows are stored through it before they are attended to
         and committed: the rows a bf16 cache receives are bf16 values. The
         returned q_phys / k_phys / v_phys stay unrounded.
+      commit_rule: "stream" (commit the leading filled run) or "block" (commit
+        the window only once it is entirely filled); see ``commit_count``.
 
     Returns a dict of float64 / int64 numpy results (see keys below).
     """
@@ -116,7 +118,7 @@ def window_step(filled, tokens, prefix_len, q, k, v, k_cache, v_cache, logits, b
     new_len = np.empty_like(prefix_len)
     for b in range(B):
         c = commit_and_refill(tokens[b], filled[b], prefix_len[b], out["run"][b], out["selected"][b],
-                              a[b], block_table[b], page_size, mask_id)
+                              a[b], block_table[b], page_size, mask_id, rule=commit_rule)
         out["commit_len"][b] = c["commit_len"]
         out["cache_slot"][b] = c["cache_slot"]
         out["committed"].append(c["committed"])
@@ -149,7 +151,7 @@ class _Growable:
 
 def stream_loop(filled, tokens, prefix_len, k_cache, v_cache, block_table, steps, inputs_for_step,
                 theta, lam, tau, page_size, min_fill=1, mask_id=-1, attend=None, track_layers=(),
-                override_selected=None, on_step=None, store=None):
+                override_selected=None, on_step=None, store=None, commit_rule="stream"):
     """Run the streaming decoder for ``steps`` window steps.
 
     Args:
@@ -164,6 +166,8 @@ def stream_loop(filled, tokens, prefix_len, k_cache, v_cache, block_table, steps
       on_step(s, result) is called after each step with window_step's result.
       store: as in ``window_step``; committed rows enter the tracked caches
         through it too.
+      commit_rule: as in ``window_step`` ("block" gives the stop-and-wait
+        decoder on the same steps).
 
     Returns dict with per-step commit lengths [steps, B], the final state and
     the total committed tokens.
@@ -193,7 +197,7 @@ def stream_loop(filled, tokens, prefix_len, k_cache, v_cache, block_table, steps
             ov = (lambda b, sel, _s=s: override_selected(_s, b, sel))
         r = window_step(filled, tokens, prefix_len, q, k, v, kc, vc, logits, block_table, theta, lam,
                         tau, page_size, min_fill, mask_id, layers=layers, override_selected=ov,
-                        store=store)
+                        store=store, commit_rule=commit_rule)
         keep = store if store is not None else (lambda x: x)
         for layer in track_layers:
             for b in range(len(prefix_len)):

@@ -156,3 +156,46 @@ def test_stream_loop_progresses_with_floor_rule():
     commits = out["commit_len"].sum(axis=0)
     assert np.array_equal(out["filled"].sum(axis=1), steps - commits)
     assert (commits >= steps - W).all()
+
+
+def test_block_rule_commits_only_whole_windows():
+    from oracle import commit_count
+    assert [commit_count(r, 4, "stream") for r in range(5)] == [0, 1, 2, 3, 4]
+    assert [commit_count(r, 4, "block") for r in range(5)] == [0, 0, 0, 0, 4]
+    with pytest.raises(ValueError):
+        commit_count(1, 4, "other")
+    table = np.arange(8)
+    # three of four slots filled: nothing is cached, the fills stay in the window
+    c = commit_and_refill([5, 6, 7, -1], [1, 1, 1, 0], 16, 3, [0, 0, 0, 1], [0, 0, 0, 9], table,
+                          PAGE, rule="block")
+    assert c["commit_len"] == 0 and c["prefix_len"] == 16
+    assert c["filled"].tolist() == [True] * 4 and c["tokens"].tolist() == [5, 6, 7, 9]
+    assert (c["cache_slot"] == -1).all()
+    # a full window: cached at once, replaced by four masks
+    c = commit_and_refill([5, 6, 7, 9], [1, 1, 1, 1], 16, 4, [0, 0, 0, 0], [0, 0, 0, 0], table,
+                          PAGE, rule="block")
+    assert c["commit_len"] == 4 and c["prefix_len"] == 20
+    assert c["committed"].tolist() == [5, 6, 7, 9]
+    assert not c["filled"].any() and (c["tokens"] == -1).all()
+    assert c["cache_slot"].tolist() == [16 + j for j in range(4)]  # page 1 of an identity table
+
+
+def test_stream_loop_block_rule():
+    # stop-and-wait: every commit is 0 or W, and with one fill per step (tau = -inf)
+    # a window is cached every W steps
+    steps = 3 * 8
+    d = _small_stream(2, steps)
+    B, W, L0 = d["B"], d["W"], d["L0"]
+    out = stream_loop(np.zeros((B, W), bool), np.full((B, W), -1), np.full(B, L0), d["k_cache"],
+                      d["v_cache"], d["table"], steps, lambda s: d["per_step"][s], d["theta"],
+                      lam=0.1, tau=float("-inf"), page_size=PAGE, commit_rule="block")
+    c = out["commit_len"]
+    assert set(np.unique(c).tolist()) <= {0, W}
+    # fills at steps 0..W-1 complete the first window; the step whose forward
+    # sees it full commits it and has no mask left to predict (the pipeline
+    # bubble of block decoding), so windows are cached every W + 1 steps
+    commit_steps = [s for s in range(steps) if s >= W and (s - W) % (W + 1) == 0]
+    expect = np.zeros_like(c)
+    expect[commit_steps] = W
+    assert np.array_equal(c, expect)
+    assert np.array_equal(out["prefix_len"], np.full(B, L0 + W * len(commit_steps)))

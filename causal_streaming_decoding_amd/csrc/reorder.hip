@@ -8,7 +8,10 @@
 // one 64-bit mask; a slot's physical index is then a popcount of the flags
 // below it (filled slots) or n_obs plus the popcount of the masks below it
 // (mask slots), which is the stable partition. The leading filled run, used by
-// the commit, is the count of trailing ones of the ballot.
+// the commit, is the count of trailing ones of the ballot. Under the block
+// rule (the stop-and-wait baseline that the same summary contrasts with
+// streaming: a block is cached only once finalised) the run counts only when
+// it covers the whole window, and is 0 otherwise.
 #include "common.hpp"
 
 namespace wedlm {
@@ -16,7 +19,7 @@ namespace wedlm {
 constexpr int kReorderWaves = 4;
 
 __global__ void __launch_bounds__(kWave * kReorderWaves)
-k_window_reorder(int B, int W, const uint8_t* __restrict__ filled,
+k_window_reorder(int B, int W, int block_rule, const uint8_t* __restrict__ filled,
                  const int32_t* __restrict__ prefix_len, int32_t* __restrict__ perm,
                  int32_t* __restrict__ inv_perm, int32_t* __restrict__ pos,
                  int32_t* __restrict__ n_obs, int32_t* __restrict__ run_len) {
@@ -41,22 +44,39 @@ k_window_reorder(int B, int W, const uint8_t* __restrict__ filled,
     n_obs[b] = nobs;
     // lanes >= W contribute 0 bits, so the first zero is at most W
     const uint64_t zeros = ~fm;
-    run_len[b] = zeros == 0 ? kWave : __builtin_ctzll(zeros);
+    const int run = zeros == 0 ? kWave : __builtin_ctzll(zeros);
+    run_len[b] = block_rule ? (run == W ? W : 0) : run;
   }
 }
 
 }  // namespace wedlm
 
-extern "C" int wedlm_window_reorder(int B, int W, const uint8_t* filled, const int32_t* prefix_len,
-                                    int32_t* perm, int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
-                                    int32_t* run_len, void* stream) {
+static int launch_reorder(int B, int W, int block_rule, const uint8_t* filled,
+                          const int32_t* prefix_len, int32_t* perm, int32_t* inv_perm, int32_t* pos,
+                          int32_t* n_obs, int32_t* run_len, void* stream) {
   using namespace wedlm;
   if (B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW) return WEDLM_ERR_INVALID;
   if (!filled || !prefix_len || !perm || !inv_perm || !pos || !n_obs || !run_len)
     return WEDLM_ERR_INVALID;
   const int blocks = ceil_div(B, kReorderWaves);
   hipLaunchKernelGGL(k_window_reorder, dim3(blocks), dim3(kWave * kReorderWaves), 0,
-                     as_stream(stream), B, W, filled, prefix_len, perm, inv_perm, pos, n_obs,
-                     run_len);
+                     as_stream(stream), B, W, block_rule, filled, prefix_len, perm, inv_perm, pos,
+                     n_obs, run_len);
   return launch_status();
+}
+
+extern "C" int wedlm_window_reorder(int B, int W, const uint8_t* filled, const int32_t* prefix_len,
+                                    int32_t* perm, int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
+                                    int32_t* run_len, void* stream) {
+  return launch_reorder(B, W, 0, filled, prefix_len, perm, inv_perm, pos, n_obs, run_len, stream);
+}
+
+extern "C" int wedlm_window_reorder_rule(int B, int W, int commit_rule, const uint8_t* filled,
+                                         const int32_t* prefix_len, int32_t* perm,
+                                         int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
+                                         int32_t* run_len, void* stream) {
+  if (commit_rule != WEDLM_COMMIT_STREAM && commit_rule != WEDLM_COMMIT_BLOCK)
+    return WEDLM_ERR_INVALID;
+  return launch_reorder(B, W, commit_rule == WEDLM_COMMIT_BLOCK ? 1 : 0, filled, prefix_len, perm,
+                        inv_perm, pos, n_obs, run_len, stream);
 }

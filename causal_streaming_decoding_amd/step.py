@@ -43,7 +43,7 @@ class WindowStep:
 
     def __init__(self, n_layers, B, W, Hq, Hkv, D, V, page_size, num_pages, max_pages, dtype,
                  device, max_prefix_len, theta, lam, tau, min_fill=1, mask_id=-1, scale=None,
-                 fused_rope=True):
+                 fused_rope=True, commit_rule=W_.COMMIT_STREAM):
         self.n_layers, self.B, self.W, self.Hq, self.Hkv, self.D, self.V = (
             n_layers, B, W, Hq, Hkv, D, V)
         self.page_size, self.num_pages, self.max_pages = page_size, num_pages, max_pages
@@ -53,6 +53,8 @@ class WindowStep:
         self.scale = scale if scale is not None else D ** -0.5
         self.max_prefix_len = max_prefix_len
         self.fused_rope = fused_rope
+        # COMMIT_STREAM: the leading filled run; COMMIT_BLOCK: the whole window once filled
+        self.commit_rule = commit_rule
         # fused path: the attention call appends the committed rows (else the
         # commit call writes them itself)
         self.fused_append = True
@@ -89,8 +91,9 @@ class WindowStep:
 
     # -- the five calls -------------------------------------------------------
     def reorder(self, st, stream=None):
-        W_.wedlm_window_reorder(self.B, self.W, st.filled, st.prefix_len, self.perm, self.inv,
-                                self.pos, self.n_obs, self.run_len, stream)
+        W_.wedlm_window_reorder_rule(self.B, self.W, self.commit_rule, st.filled, st.prefix_len,
+                                     self.perm, self.inv, self.pos, self.n_obs, self.run_len,
+                                     stream)
 
     def rope(self, q, k, v, stream=None):
         W_.wedlm_rope_logical(self.dt, self.n_layers, self.B, self.W, self.Hq, self.Hkv, self.D,
@@ -209,11 +212,13 @@ def upload_step_inputs(wl, inp, device):
     return st, q, k, v, logits, int(inp["prefix_len"].max())
 
 
-def make_window_step(wl, inp, device, max_prefix_len, fused_rope=True):
-    """WindowStep sized for a workload and its inputs."""
+def make_window_step(wl, inp, device, max_prefix_len, fused_rope=True, commit_rule=None):
+    """WindowStep sized for a workload and its inputs (streaming commits unless
+    ``commit_rule`` says otherwise)."""
     from .synth import torch_dtype
 
     return WindowStep(wl.n_layers, wl.B, wl.W, wl.Hq, wl.Hkv, wl.D, wl.V, wl.page_size,
                       inp["num_pages"], inp["block_table"].shape[1], torch_dtype(wl), device,
                       max_prefix_len, wl.theta, wl.lam, wl.tau, wl.min_fill, wl.mask_id,
-                      fused_rope=fused_rope)
+                      fused_rope=fused_rope,
+                      commit_rule=W_.COMMIT_STREAM if commit_rule is None else commit_rule)

@@ -30,6 +30,7 @@ _SIGNATURES = {
     "wedlm_status_string": (ctypes.c_char_p, [_c_int]),
     "wedlm_abi_version": (_c_int, []),
     "wedlm_window_reorder": (_c_int, [_c_int, _c_int, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "wedlm_window_reorder_rule": (_c_int, [_c_int, _c_int, _c_int, _p, _p, _p, _p, _p, _p, _p, _p]),
     "wedlm_rope_logical": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_double,
                                     _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "wedlm_window_attn_workspace_size": (_c_size, [_c_int] * 9),
@@ -128,6 +129,17 @@ def wedlm_window_reorder(B, W, filled, prefix_len, perm, inv_perm, pos, n_obs, r
     _check("wedlm_window_reorder", lib().wedlm_window_reorder(
         B, W, _ptr(filled), _ptr(prefix_len), _ptr(perm), _ptr(inv_perm), _ptr(pos), _ptr(n_obs),
         _ptr(run_len), _stream(stream)))
+
+
+COMMIT_STREAM = 0
+COMMIT_BLOCK = 1
+
+
+def wedlm_window_reorder_rule(B, W, commit_rule, filled, prefix_len, perm, inv_perm, pos, n_obs,
+                              run_len, stream=None):
+    _check("wedlm_window_reorder_rule", lib().wedlm_window_reorder_rule(
+        B, W, commit_rule, _ptr(filled), _ptr(prefix_len), _ptr(perm), _ptr(inv_perm), _ptr(pos),
+        _ptr(n_obs), _ptr(run_len), _stream(stream)))
 
 
 def wedlm_rope_logical(dtype, n_layers, B, W, Hq, Hkv, D, theta, q, k, v, perm, pos, q_phys, k_phys,

@@ -78,6 +78,12 @@ enum wedlm_dtype { WEDLM_F32 = 0, WEDLM_BF16 = 1 };
 /* Largest window the kernels accept (one 64-lane wavefront per sequence). */
 #define WEDLM_MAX_WINDOW 64
 
+/* Commit rules of wedlm_window_reorder_rule. */
+enum wedlm_commit_rule {
+  WEDLM_COMMIT_STREAM = 0, /* the leftmost contiguous filled run (streaming decoding) */
+  WEDLM_COMMIT_BLOCK = 1   /* the whole window once every slot is filled, else nothing */
+};
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* wedlm_status_string(int status);
 
@@ -102,6 +108,22 @@ int wedlm_abi_version(void);
 int wedlm_window_reorder(int B, int W, const uint8_t* filled, const int32_t* prefix_len,
                          int32_t* perm, int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
                          int32_t* run_len, void* stream);
+
+/*
+ * wedlm_window_reorder_rule - wedlm_window_reorder with a choice of commit rule
+ * for run_len (everything else identical). hyper.ai summary of WeDLM,
+ * "Method", contrasts streaming with block decoding, where a block is cached
+ * only once it is entirely finalised; sai.science review, "Reproducibility &
+ * code": the released engine has no block-wise decoder.
+ *   WEDLM_COMMIT_STREAM: run_len = the leading filled run (as wedlm_window_reorder);
+ *   WEDLM_COMMIT_BLOCK:  run_len = W when every slot is filled, else 0, so the
+ *     commit caches the whole window at once and refills it with W masks
+ *     (stop-and-wait decoding on the same kernels).
+ * Another commit_rule value returns WEDLM_ERR_INVALID.
+ */
+int wedlm_window_reorder_rule(int B, int W, int commit_rule, const uint8_t* filled,
+                              const int32_t* prefix_len, int32_t* perm, int32_t* inv_perm,
+                              int32_t* pos, int32_t* n_obs, int32_t* run_len, void* stream);
 
 /*
  * wedlm_rope_logical - rotary embedding at logical positions, gathered into

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(W.LIB_PATH),
 
 def test_exports_every_declared_function():
     declared = W.header_functions()
-    assert len(declared) == 15
+    assert len(declared) == 16
     lib = W.lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -31,7 +31,7 @@ def test_status_strings_and_version():
     assert "unsupported" in W.wedlm_status_string(-2)
     assert "workspace" in W.wedlm_status_string(-3)
     assert W.wedlm_abi_version() >> 16 == 1
-    assert W.wedlm_abi_version() & 0xffff >= 2  # fused RoPE and LM-head entry points
+    assert W.wedlm_abi_version() & 0xffff >= 3  # fused RoPE, LM head, commit rules
 
 
 def _raw(name, *args):
@@ -39,6 +39,10 @@ def _raw(name, *args):
 
 
 def test_reorder_validation():
+    assert _raw("wedlm_window_reorder_rule", 1, 8, 2, 1, 1, 1, 1, 1, 1, 1, None) == -1  # rule
+    assert _raw("wedlm_window_reorder_rule", 1, 8, -1, 1, 1, 1, 1, 1, 1, 1, None) == -1
+    assert _raw("wedlm_window_reorder_rule", 0, 8, 1, 1, 1, 1, 1, 1, 1, 1, None) == -1
+    assert _raw("wedlm_window_reorder_rule", 1, 8, 0, None, 1, 1, 1, 1, 1, 1, None) == -1
     assert _raw("wedlm_window_reorder", 0, 8, 1, 1, 1, 1, 1, 1, 1, None) == -1
     assert _raw("wedlm_window_reorder", 1, 65, 1, 1, 1, 1, 1, 1, 1, None) == -1
     assert _raw("wedlm_window_reorder", 1, 8, None, 1, 1, 1, 1, 1, 1, None) == -1

@@ -17,6 +17,8 @@ import torch
 import oracle
 from causal_streaming_decoding_amd import layout
 from causal_streaming_decoding_amd import workloads as WL
+from causal_streaming_decoding_amd.decode_stats import decode_counters
+from causal_streaming_decoding_amd.wedlm import COMMIT_BLOCK, COMMIT_STREAM
 from causal_streaming_decoding_amd.step import make_window_step, upload_step_inputs
 from causal_streaming_decoding_amd.synth import make_step_inputs, stream_step_inputs, to_f64
 
@@ -25,21 +27,25 @@ from .parity import ATTN_ATOL, ATTN_RTOL, ENTROPY_ATOL, stored_pair_bound, stora
 pytestmark = pytest.mark.gpu
 
 
-def _run_stream(wl, steps, sampled_layers, attend_steps):
-    print(f"[stream] {wl.name} steps={steps} layers={sampled_layers}", flush=True)
+def _run_stream(wl, steps, sampled_layers, attend_steps, commit_rule="stream"):
+    print(f"[stream] {wl.name} steps={steps} layers={sampled_layers} tau={wl.tau} "
+          f"rule={commit_rule}", flush=True)
     dev = "cuda"
     inp = make_step_inputs(wl, steps=wl.steps)
     st, _, _, _, _, L0 = upload_step_inputs(wl, inp, dev)
-    step = make_window_step(wl, inp, dev, L0 + wl.W * steps)
+    rule = {"stream": COMMIT_STREAM, "block": COMMIT_BLOCK}[commit_rule]
+    step = make_window_step(wl, inp, dev, L0 + wl.W * steps, commit_rule=rule)
     gpu_log, host_inputs = [], []
     for s in range(steps):
         q, k, v, logits = stream_step_inputs(wl, s, dev)
         mpl = L0 + wl.W * s
+        rec_prefix_in = st.prefix_len.cpu().numpy()
         step.run(st, q, k, v, logits, max_prefix_len=mpl)
         torch.cuda.synchronize()
         rec = {key: getattr(step, key).cpu().numpy() for key in
                ("perm", "inv", "pos", "run_len", "entropy", "argmax", "selected", "commit_len",
                 "cache_slot")}
+        rec["prefix_len_in"] = rec_prefix_in
         rec["tokens"] = st.tokens.cpu().numpy()
         rec["filled"] = st.filled.cpu().numpy()
         rec["prefix_len"] = st.prefix_len.cpu().numpy()
@@ -67,13 +73,16 @@ def _run_stream(wl, steps, sampled_layers, attend_steps):
         attend=lambda s: range(len(sampled_layers)) if s in attend_steps else [],
         track_layers=range(len(sampled_layers)),
         override_selected=lambda s, b, sel: gpu_log[s]["selected"][b].astype(bool),
-        on_step=lambda s, r: ref_log.append(r), store=storage_rounding(wl.dtype))
+        on_step=lambda s, r: ref_log.append(r), store=storage_rounding(wl.dtype),
+        commit_rule=commit_rule)
 
     flags = 0
     for s in range(steps):
         g, r = gpu_log[s], ref_log[s]
         assert np.array_equal(g["perm"], r["perm"]), ("perm", s)
-        assert np.array_equal(g["run_len"], r["run"]), ("run", s)
+        # the reorder reports the commit rule's count (the raw run when streaming)
+        expect_run = [oracle.commit_count(x, wl.W, commit_rule) for x in r["run"]]
+        assert np.array_equal(g["run_len"], expect_run), ("run", s)
         assert (np.abs(g["entropy"] - r["entropy"]) <= ENTROPY_ATOL).all(), ("entropy", s)
         assert np.array_equal(g["argmax"], r["argmax"]), ("argmax", s)
         flagged = {b for b, _, _ in r["flags"]}
@@ -101,9 +110,16 @@ def _run_stream(wl, steps, sampled_layers, attend_steps):
         assert np.array_equal(vr, ref_v), ("cache v", i, b)
     total = int(sum(g["commit_len"].sum() for g in gpu_log))
     longest = int(max(g["commit_len"].max() for g in gpu_log))
+    # the decoding counters of the two runs agree exactly
+    cg = decode_counters([{"prefix_len_in": g["prefix_len_in"], "selected": g["selected"],
+                           "commit_len": g["commit_len"]} for g in gpu_log], wl.W)
+    cr = decode_counters([{"prefix_len_in": r["prefix_len_in"], "selected": r["selected"],
+                           "commit_len": r["commit_len"]} for r in ref_log], wl.W)
+    assert cg == cr, (cg, cr)
     print(f"[stream] {wl.name}: {steps} steps ok, committed {total}, longest commit {longest}, "
-          f"flags {flags}", flush=True)
-    return total, longest
+          f"flags {flags}, p_cache {cg['p_cache']}, tokens/forward {cg['tokens_per_forward']:.3f}",
+          flush=True)
+    return total, longest, cg
 
 
 def test_stream_full_shape_first_steps():
@@ -114,5 +130,32 @@ def test_stream_low_entropy_multi_commit():
     # big spikes make the threshold fire, so runs longer than one token are committed
     wl = dataclasses.replace(WL.QWEN3_8B_STREAM, name="stream_low_entropy", n_layers=4, B=8,
                              V=30000, spike=("prob", 0.9, 16.0, 20.0))
-    _, longest = _run_stream(wl, steps=24, sampled_layers=[0, 3], attend_steps={3, 23})
+    _, longest, _ = _run_stream(wl, steps=24, sampled_layers=[0, 3], attend_steps={3, 23})
     assert longest > 1  # multi-token commits happened
+
+
+def test_stream_one_by_one_mode():
+    # threshold None of the released engine: tau = -inf, one fill per step
+    wl = dataclasses.replace(WL.QWEN3_8B_STREAM, name="stream_one_by_one", n_layers=4, B=8,
+                             tau=float("-inf"))
+    _, longest, c = _run_stream(wl, steps=24, sampled_layers=[1], attend_steps={5})
+    assert c["predictions_per_forward"] <= 1.0
+
+
+def test_stream_block_rule():
+    # stop-and-wait on the same kernels: whole windows are cached, W + 1 steps apart
+    wl = dataclasses.replace(WL.QWEN3_8B_STREAM, name="stream_block", n_layers=4, B=8,
+                             tau=float("-inf"))
+    _, longest, c = _run_stream(wl, steps=3 * (wl.W + 1), sampled_layers=[0, 2],
+                                attend_steps={0, wl.W, wl.W + 1}, commit_rule="block")
+    assert longest == wl.W
+    assert set(c["delay_histogram"]) == set(range(1, wl.W + 1))
+
+
+def test_stream_block_rule_low_entropy():
+    # threshold fills several slots per step: a window completes sooner
+    wl = dataclasses.replace(WL.QWEN3_8B_STREAM, name="stream_block_low_entropy", n_layers=4,
+                             B=8, V=30000, spike=("prob", 0.9, 16.0, 20.0))
+    _, longest, c = _run_stream(wl, steps=24, sampled_layers=[3], attend_steps={7},
+                                commit_rule="block")
+    assert longest == wl.W

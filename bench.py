@@ -49,6 +49,10 @@ def parse():
     ap.add_argument("--lm-head", action="store_true",
                     help="time the fused vocabulary projection + selection (one JSON line per shape)")
     ap.add_argument("--lm-head-steps", type=int, default=50)
+    ap.add_argument("--decode-modes", action="store_true",
+                    help="streaming vs one-by-one vs block-wise decoding on the same kernels "
+                         "(one JSON line per mode and logit regime)")
+    ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--config-steps", type=int, default=200)
     ap.add_argument("--config-warmup", type=int, default=20)
     return ap.parse_args()
@@ -327,6 +331,92 @@ def lm_head_latencies(args):
         torch.cuda.synchronize()
 
 
+def decode_modes(args):
+    """Streaming, one-by-one and block-wise decoding of the streaming workload.
+
+    Modes (all on the same kernels, from the same start state and inputs):
+    streaming (the workload's threshold, leading-run commits), one-by-one
+    (threshold -inf: the single lowest-score mask per step, leading-run
+    commits) and block-wise stop-and-wait (the workload's threshold, the
+    window is committed only once entirely filled). Two logit regimes: the
+    workload's own logits, and a low-entropy variant (spike probability 0.9,
+    magnitude U[16, 20]) where the threshold fills several slots per step.
+    Each mode is timed over --decode-steps window steps (steps/s, committed
+    tokens/s), then replayed untimed from the same start to read its decoding
+    counters (tokens and predictions per forward, p_cache, commit delay).
+    """
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    from causal_streaming_decoding_amd import wedlm as Wd
+    from causal_streaming_decoding_amd import workloads as WL
+    from causal_streaming_decoding_amd.decode_stats import decode_counters
+    from causal_streaming_decoding_amd.step import make_window_step, upload_step_inputs
+    from causal_streaming_decoding_amd.synth import make_step_inputs, stream_step_inputs
+
+    dev = "cuda:0"
+    K = args.decode_steps
+    base = WL.BY_NAME[args.workload]
+    regimes = (("workload_logits", base),
+               ("low_entropy_logits", dataclasses.replace(base, spike=("prob", 0.9, 16.0, 20.0))))
+    modes = (("streaming", Wd.COMMIT_STREAM, None), ("one_by_one", Wd.COMMIT_STREAM, float("-inf")),
+             ("block_wise", Wd.COMMIT_BLOCK, None))
+    for regime, wl0 in regimes:
+        print(f"[bench] {regime}: building inputs ({K} steps)", file=sys.stderr, flush=True)
+        inp = make_step_inputs(wl0, steps=K)
+        ins = [stream_step_inputs(wl0, s, dev) for s in range(K)]
+        for mode, rule, tau in modes:
+            wl = wl0 if tau is None else dataclasses.replace(wl0, tau=tau)
+            st, _, _, _, _, L0 = upload_step_inputs(wl, inp, dev)
+            step = make_window_step(wl, inp, dev, L0 + wl.W * K, commit_rule=rule)
+            commit_log = torch.zeros((K, wl.B), dtype=torch.int32, device=dev)
+            snap = st.snapshot()
+            for s in range(min(8, K)):  # warm-up
+                q, k, v, logits = ins[s]
+                step.run(st, q, k, v, logits, max_prefix_len=L0 + wl.W * s)
+            torch.cuda.synchronize()
+            st.restore(snap)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for s in range(K):
+                q, k, v, logits = ins[s]
+                step.run(st, q, k, v, logits, max_prefix_len=L0 + wl.W * s,
+                         commit_len=commit_log[s])
+            torch.cuda.synchronize()
+            elapsed = time.perf_counter() - t0
+            committed = int(commit_log.sum().item())
+            # untimed replay from the same start: per-step records for the counters
+            st.restore(snap)
+            recs = []
+            for s in range(K):
+                q, k, v, logits = ins[s]
+                L_in = st.prefix_len.cpu().numpy()
+                step.run(st, q, k, v, logits, max_prefix_len=L0 + wl.W * s)
+                recs.append({"prefix_len_in": L_in,
+                             "selected": step.selected.cpu().numpy().astype(bool),
+                             "commit_len": step.commit_len.cpu().numpy()})
+            c = decode_counters(recs, wl.W)
+            assert c["committed"] == committed  # the replay took the timed run's path
+            line = {
+                "workload": base.name, "mode": mode, "logits": regime, "steps": K,
+                "tau": wl.tau, "lambda": wl.lam,
+                "window_steps_per_s": K / elapsed, "ms_per_step": elapsed / K * 1e3,
+                "committed_tokens_per_s": committed / elapsed,
+                "tokens_per_forward": c["tokens_per_forward"],
+                "predictions_per_forward": c["predictions_per_forward"],
+                "p_cache": c["p_cache"], "mean_commit_delay": c["mean_commit_delay"],
+                "delay_histogram": {str(k_): v_ for k_, v_ in c["delay_histogram"].items()},
+                "data": "synthetic",
+            }
+            print(json.dumps(line), flush=True)
+            del st, step, commit_log
+            torch.cuda.empty_cache()
+        del ins
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -338,6 +428,9 @@ def main():
         return
     if args.lm_head:
         lm_head_latencies(args)
+        return
+    if args.decode_modes:
+        decode_modes(args)
         return
 
     import numpy as np

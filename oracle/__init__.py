@@ -26,8 +26,8 @@ outputs are exact. The readings adopted where the pages are silent are listed
 in each function's docstring.
 
 Parity status:
-  * reorder, RoPE, attention, entropy, vocabulary projection: pinned
-    (tests/test_oracle_*.py).
+  * reorder, RoPE, attention, entropy, vocabulary projection, dual-stream
+    attention: pinned (tests/test_oracle_*.py).
   * the select fallback (a step where no mask slot clears the threshold fills
     the single lowest-score mask slot): parity unpinned. The pages do not say
     what happens then; the rule is a reading, exercised by hand-worked cases
@@ -41,6 +41,7 @@ from .entropy import vocab_entropy_argmax
 from .select import select_slots
 from .commit import commit_and_refill, cache_slot_of, commit_count
 from .lm_head import vocab_projection, lm_head_select
+from .dual_stream import dual_stream_attention
 from .step import window_step, stream_loop
 
 __all__ = [
@@ -56,6 +57,7 @@ __all__ = [
     "cache_slot_of",
     "commit_count",
     "vocab_projection",
+    "dual_stream_attention",
     "lm_head_select",
     "window_step",
     "stream_loop",

@@ -136,3 +136,32 @@ def test_projection_dropped_term_is_caught(monkeypatch):
     monkeypatch.setattr(t_lm, "vocab_projection", last_term_dropped)
     with pytest.raises(AssertionError):
         t_lm.test_brute_force_small()
+
+
+def test_dual_stream_own_block_memory_leak_is_caught(monkeypatch):
+    import oracle.dual_stream as ds
+    import tests.test_oracle_dual_stream as t_ds
+    orig = ds.dual_stream_visibility
+
+    def leaky(filled, block):
+        vis = orig(filled, block)
+        N = len(filled)
+        for t in range(N):
+            j0 = (t // block) * block
+            vis[N + t, j0:min(j0 + block, N)] = True  # the clean copy of its own block
+        return vis
+    monkeypatch.setattr(ds, "dual_stream_visibility", leaky)
+    with pytest.raises(AssertionError):
+        t_ds.test_no_leakage()
+
+
+def test_dual_stream_masks_first_is_caught(monkeypatch):
+    import oracle.dual_stream as ds
+    import tests.test_oracle_dual_stream as t_ds
+    orig = ds.block_rank
+
+    def masks_first(filled, block):
+        return orig(~np.asarray(filled, bool), block)
+    monkeypatch.setattr(ds, "block_rank", masks_first)
+    with pytest.raises(AssertionError):
+        t_ds.test_mask_form_equals_reordered_form()

@@ -53,6 +53,8 @@ def parse():
                     help="streaming vs one-by-one vs block-wise decoding on the same kernels "
                          "(one JSON line per mode and logit regime)")
     ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--dual-stream", action="store_true",
+                    help="time the dual-stream masking attention forward (one JSON line per block size)")
     ap.add_argument("--config-steps", type=int, default=200)
     ap.add_argument("--config-warmup", type=int, default=20)
     return ap.parse_args()
@@ -417,6 +419,73 @@ def decode_modes(args):
         torch.cuda.empty_cache()
 
 
+def dual_stream_latencies(args):
+    """Dual-stream masking attention forward of one layer, one JSON line per
+    block size: 4 samples x 4096 positions, Qwen3-8B heads (32 / 8, D = 128),
+    bf16, half of the prediction stream observed. Timed with HIP events around
+    the whole forward (memory rows into the cache, both attentions, both
+    reorders), 20 calls after 3 warm-up calls. Algorithmic bytes: both
+    streams' q / k / v read and outputs written once, the memory rows written
+    to the cache and read back once (every block re-reads its prefix, but a
+    sample's memory rows - 16 MB - stay in the caches, so the re-reads are
+    not HBM traffic; they are reported separately). Flops: QK and PV over
+    each block's visible keys. The roofline is the one the intensity selects
+    (MFMA for these shapes).
+    """
+    import numpy as np
+    import torch
+
+    from causal_streaming_decoding_amd.dual_stream import DualStreamAttention
+
+    dev = "cuda:0"
+    S, N, Hq, Hkv, D, theta = 4, 4096, 32, 8, 128, 1e6
+    g = torch.Generator(device=dev).manual_seed(0)
+    r = lambda h: torch.randn((S, N, h, D), generator=g, device=dev).to(torch.bfloat16)
+    qm, km, vm, qp, kp, vp = r(Hq), r(Hkv), r(Hkv), r(Hq), r(Hkv), r(Hkv)
+    filled = (torch.rand((S, N), generator=g, device=dev) < 0.5).to(torch.uint8)
+    hev = HipEvents(torch.cuda.current_stream().cuda_stream)
+    for Bk in (16, 32, 64):
+        ds = DualStreamAttention(S, N, Bk, Hq, Hkv, D, theta, torch.bfloat16, dev)
+        ev = [(hev.create(), hev.create()) for _ in range(23)]
+        for a_, b_ in ev:
+            hev.record(a_)
+            ds.forward(qm, km, vm, qp, kp, vp, filled)
+            hev.record(b_)
+        torch.cuda.synchronize()
+        us = np.array([hev.elapsed_ms(a_, b_) for a_, b_ in ev[3:]]) * 1e3
+        hev.destroy()
+        nb = N // Bk
+        row = Hkv * D * 2                                   # bytes of one position's k (or v)
+        prefix_reads = 2 * S * sum(j * Bk for j in range(nb)) * 2 * row
+        byts = 2 * S * N * (Hq * D * 2 * 2 + 2 * row) + 2 * S * N * 2 * row
+        flops = 2 * S * Hq * D * 2 * sum(Bk * (j * Bk + (Bk + 1) / 2) for j in range(nb))
+        med = float(np.median(us))
+        ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+        if flops / byts < ridge:
+            roof = {"bound": "hbm", "achieved": byts / (med * 1e-6) / 1e9, "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s"}
+        else:
+            roof = {"bound": "mfma", "achieved": flops / (med * 1e-6) / 1e12,
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = None
+        line = {
+            "workload": f"dual_stream_S{S}_N{N}_Bk{Bk}_qwen3_8b_heads",
+            "metric": "dual-stream attention forward latency", "unit": "us", "dtype": "bf16",
+            "us": {"median": med, "p10": float(np.percentile(us, 10)),
+                   "p90": float(np.percentile(us, 90))},
+            "tokens_per_s": 2 * S * N / (med * 1e-6),
+            "algorithmic_bytes": int(byts), "prefix_rereads_bytes": int(prefix_reads),
+            "flops": flops, "intensity_flop_per_byte": flops / byts,
+            "roofline": roof,
+            "tflops_at_median": flops / (med * 1e-6) / 1e12,
+            "data": "synthetic",
+        }
+        print(json.dumps(line), flush=True)
+        del ds
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -431,6 +500,9 @@ def main():
         return
     if args.decode_modes:
         decode_modes(args)
+        return
+    if args.dual_stream:
+        dual_stream_latencies(args)
         return
 
     import numpy as np

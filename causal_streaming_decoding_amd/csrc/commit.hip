@@ -13,7 +13,7 @@
 //   k_commit_state one wavefront per sequence: cache slots, window shift with
 //                  the new fills, mask refill, prefix_len += c. It runs after
 //                  the copies (same stream), which read the old prefix_len.
-#include "common.hpp"
+#include "window_ops.hpp"
 
 #include <cmath>
 #include <type_traits>
@@ -21,12 +21,6 @@
 namespace wedlm {
 
 constexpr int kCommitThreads = 256;
-
-__device__ __forceinline__ int commit_length(int run, int L, int W, int max_pages, int P) {
-  int c = min(max(run, 0), W);
-  const int room = max(max_pages * P - L, 0);
-  return min(c, room);
-}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -155,40 +149,19 @@ k_commit_state(int W, int P, int num_pages, int max_pages, const int32_t* __rest
                int32_t mask_id) {
   const int b = blockIdx.x;
   const int i = threadIdx.x;
-  const bool in_window = i < W;
-  const int L = max(prefix_len[b], 0);
-  const int c = commit_length(run_len[b], L, W, max_pages, P);
-  int f = 0, tok = mask_id;
-  if (in_window) {
+  bool f = false, sel = false;
+  int tok = mask_id, am = 0;
+  if (i < W) {
     const int row = b * W + i;
-    const bool sel = selected[row] != 0;
-    f = (filled[row] != 0 || sel) ? 1 : 0;
-    tok = sel ? argmax_tok[row] : tokens[row];
+    f = filled[row] != 0;
+    tok = tokens[row];
+    sel = selected[row] != 0;
+    am = argmax_tok[row];
   }
-  // every lane has read its slot; shift left by c within the wavefront
-  const int src = i + c;
-  const int f_in = __shfl(f, src < kWave ? src : 0, kWave);
-  const int t_in = __shfl(tok, src < kWave ? src : 0, kWave);
-  if (in_window) {
-    const int row = b * W + i;
-    const bool keep = src < W;
-    filled[row] = keep ? static_cast<uint8_t>(f_in) : static_cast<uint8_t>(0);
-    tokens[row] = keep ? t_in : mask_id;
-    int slot = -1;
-    if (i < c) {
-      const int t = L + i;
-      const int pid = min(max(block_table[static_cast<size_t>(b) * max_pages + t / P], 0),
-                          num_pages - 1);
-      slot = pid * P + t % P;
-    }
-    cache_slot[row] = slot;
-  }
-  if (i == 0) {
-    commit_len[b] = c;
-    prefix_len[b] = L + c;
-  }
+  bool f_new;
+  wave_commit_state(b, W, i, P, num_pages, max_pages, run_len[b], f, tok, sel, am, block_table,
+                    tokens, filled, prefix_len, commit_len, cache_slot, mask_id, f_new);
 }
-
 
 }  // namespace wedlm
 

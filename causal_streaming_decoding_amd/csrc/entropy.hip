@@ -20,7 +20,9 @@
 //   row to (m, s, t, argmax) in the workspace.
 // k_entropy_select: one wavefront per sequence merges the chunks of its W
 //   rows, forms entropy and score, and applies the threshold / floor rule.
-#include "common.hpp"
+// k_step_tail: the same selection followed by the window-state commit and the
+//   next step's reorder, in one wavefront per sequence.
+#include "window_ops.hpp"
 
 namespace wedlm {
 
@@ -144,51 +146,46 @@ k_entropy_select(const EntPartial* __restrict__ part, int n_chunks, int W,
                  int32_t* __restrict__ argmax_tok, uint8_t* __restrict__ selected) {
   const int b = blockIdx.x;
   const int i = threadIdx.x;
-  const bool in_window = i < W;
-  float sc = INFINITY;
-  bool cand = false;
-  if (in_window) {
-    const int row = b * W + i;
-    const EntPartial* pr = part + static_cast<size_t>(row) * n_chunks;
-    EntPartial acc = pr[0];
-    // partials are loaded 8 at a time so that their latencies overlap, and
-    // merged in chunk order
-    for (int c0 = 1; c0 < n_chunks; c0 += 8) {
-      EntPartial buf[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (c0 + k < n_chunks) buf[k] = pr[c0 + k];
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (c0 + k < n_chunks) merge(acc, buf[k]);
-    }
-    const float H = kLn2F * (log2f(acc.s) - acc.t / acc.s);
-    // product rounded, then the sum: no fused multiply-add
-    sc = __fadd_rn(H, __fmul_rn(lambda, static_cast<float>(i)));
-    entropy[row] = H;
-    score[row] = sc;
-    argmax_tok[row] = acc.idx;
-    cand = filled[row] == 0;
+  const bool cand = i < W && filled[b * W + i] == 0;
+  int am;
+  wave_select(part, n_chunks, b, W, i, cand, lambda, tau, min_fill, entropy, score, argmax_tok,
+              selected, am);
+}
+
+// Step tail, one wavefront per sequence: selection from the entropy partials,
+// the commit of this step's run (the rows are already in the cache) with the
+// window shift and refill, and the next step's reorder of the new window -
+// the same three operations as k_entropy_select, k_commit_state and
+// k_window_reorder in one launch. run_len is read as this step's run and
+// overwritten with the next step's.
+__global__ void __launch_bounds__(kWave)
+k_step_tail(const EntPartial* __restrict__ part, int n_chunks, int W, float lambda, float tau,
+            int min_fill, int P, int num_pages, int max_pages, int block_rule,
+            const int32_t* __restrict__ block_table, int32_t* __restrict__ tokens,
+            uint8_t* __restrict__ filled, int32_t* __restrict__ prefix_len,
+            int32_t* __restrict__ run_len, int32_t* __restrict__ commit_len,
+            int32_t* __restrict__ cache_slot, int32_t mask_id, float* __restrict__ entropy,
+            float* __restrict__ score, int32_t* __restrict__ argmax_tok,
+            uint8_t* __restrict__ selected, int32_t* __restrict__ perm,
+            int32_t* __restrict__ inv_perm, int32_t* __restrict__ pos,
+            int32_t* __restrict__ n_obs) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  bool f = false;
+  int tok = mask_id;
+  if (i < W) {
+    f = filled[b * W + i] != 0;
+    tok = tokens[b * W + i];
   }
-  bool sel = cand && sc < tau;
-  const uint64_t any_sel = __ballot(sel);
-  const uint64_t any_cand = __ballot(cand);
-  if (any_sel == 0 && any_cand != 0 && min_fill == 1) {
-    // lowest score among candidates, lowest slot on equal scores
-    float best = cand ? sc : INFINITY;
-    int who = cand ? i : kWave;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ob = __shfl_xor(best, off, kWave);
-      const int ow = __shfl_xor(who, off, kWave);
-      if (ob < best || (ob == best && ow < who)) {
-        best = ob;
-        who = ow;
-      }
-    }
-    sel = (i == who);
-  }
-  if (in_window) selected[b * W + i] = sel ? 1 : 0;
+  const int run = run_len[b];
+  int am;
+  const bool sel = wave_select(part, n_chunks, b, W, i, i < W && !f, lambda, tau, min_fill,
+                               entropy, score, argmax_tok, selected, am);
+  bool f_new;
+  const int L_new = wave_commit_state(b, W, i, P, num_pages, max_pages, run, f, tok, sel, am,
+                                      block_table, tokens, filled, prefix_len, commit_len,
+                                      cache_slot, mask_id, f_new);
+  wave_reorder(b, W, i, f_new, L_new, block_rule, perm, inv_perm, pos, n_obs, run_len);
 }
 
 int launch_entropy_select(const EntPartial* part, int n_chunks, int B, int W,
@@ -222,6 +219,28 @@ static EntPlan plan_entropy(int dtype, int B, int W, int V) {
 
 using namespace wedlm;
 
+static void launch_entropy_partials(int dtype, int B, int W, int V, const void* logits,
+                                    const EntPlan& pl, EntPartial* part, hipStream_t s) {
+  const dim3 grid(pl.n_chunks, B * W);
+  if (dtype == WEDLM_BF16) {
+    const uint16_t* z = static_cast<const uint16_t*>(logits);
+    if (pl.vec)
+      hipLaunchKernelGGL((k_entropy_partial<uint16_t, true>), grid, dim3(kEntThreads), 0, s, z, V,
+                         pl.chunk_elems, pl.n_chunks, part);
+    else
+      hipLaunchKernelGGL((k_entropy_partial<uint16_t, false>), grid, dim3(kEntThreads), 0, s, z, V,
+                         pl.chunk_elems, pl.n_chunks, part);
+  } else {
+    const float* z = static_cast<const float*>(logits);
+    if (pl.vec)
+      hipLaunchKernelGGL((k_entropy_partial<float, true>), grid, dim3(kEntThreads), 0, s, z, V,
+                         pl.chunk_elems, pl.n_chunks, part);
+    else
+      hipLaunchKernelGGL((k_entropy_partial<float, false>), grid, dim3(kEntThreads), 0, s, z, V,
+                         pl.chunk_elems, pl.n_chunks, part);
+  }
+}
+
 extern "C" size_t wedlm_entropy_select_workspace_size(int dtype, int B, int W, int V) {
   if (!valid_dtype(dtype) || B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW || V <= 0) return 0;
   const EntPlan pl = plan_entropy(dtype, B, W, V);
@@ -248,26 +267,46 @@ extern "C" int wedlm_entropy_select(int dtype, int B, int W, int V, const void* 
     return WEDLM_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
   EntPartial* part = static_cast<EntPartial*>(workspace);
-  const dim3 grid(pl.n_chunks, B * W);
-  if (dtype == WEDLM_BF16) {
-    const uint16_t* z = static_cast<const uint16_t*>(logits);
-    if (pl.vec)
-      hipLaunchKernelGGL((k_entropy_partial<uint16_t, true>), grid, dim3(kEntThreads), 0, s, z, V,
-                         pl.chunk_elems, pl.n_chunks, part);
-    else
-      hipLaunchKernelGGL((k_entropy_partial<uint16_t, false>), grid, dim3(kEntThreads), 0, s, z, V,
-                         pl.chunk_elems, pl.n_chunks, part);
-  } else {
-    const float* z = static_cast<const float*>(logits);
-    if (pl.vec)
-      hipLaunchKernelGGL((k_entropy_partial<float, true>), grid, dim3(kEntThreads), 0, s, z, V,
-                         pl.chunk_elems, pl.n_chunks, part);
-    else
-      hipLaunchKernelGGL((k_entropy_partial<float, false>), grid, dim3(kEntThreads), 0, s, z, V,
-                         pl.chunk_elems, pl.n_chunks, part);
-  }
+  launch_entropy_partials(dtype, B, W, V, logits, pl, part, s);
   const int st = launch_status();
   if (st != WEDLM_OK) return st;
   return launch_entropy_select(part, pl.n_chunks, B, W, filled, lambda, tau, min_fill, entropy,
                                score, argmax_tok, selected, s);
+}
+
+extern "C" int wedlm_select_commit_reorder(
+    int dtype, int B, int W, int V, const void* logits, float lambda, float tau, int min_fill,
+    int page_size, int num_pages, int max_pages, int commit_rule, const int32_t* block_table,
+    int32_t* run_len, int32_t* tokens, uint8_t* filled, int32_t* prefix_len, int32_t* commit_len,
+    int32_t* cache_slot, int32_t mask_id, float* entropy, float* score, int32_t* argmax_tok,
+    uint8_t* selected, int32_t* perm, int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return WEDLM_ERR_UNSUPPORTED;
+  if (B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW || V <= 0) return WEDLM_ERR_INVALID;
+  if (min_fill != 0 && min_fill != 1) return WEDLM_ERR_INVALID;
+  if (lambda != lambda || tau != tau) return WEDLM_ERR_INVALID;  // NaN
+  if (commit_rule != WEDLM_COMMIT_STREAM && commit_rule != WEDLM_COMMIT_BLOCK)
+    return WEDLM_ERR_INVALID;
+  if (page_size <= 0 || num_pages <= 0 || max_pages <= 0) return WEDLM_ERR_INVALID;
+  if (page_size != 16) return WEDLM_ERR_UNSUPPORTED;
+  if (!logits || !block_table || !run_len || !tokens || !filled || !prefix_len || !commit_len ||
+      !cache_slot || !entropy || !score || !argmax_tok || !selected || !perm || !inv_perm ||
+      !pos || !n_obs)
+    return WEDLM_ERR_INVALID;
+  if (1LL * B * W > 65535) return WEDLM_ERR_UNSUPPORTED;
+  EntPlan pl = plan_entropy(dtype, B, W, V);
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) pl.vec = false;
+  const size_t need = static_cast<size_t>(B) * W * pl.n_chunks * sizeof(EntPartial);
+  if (workspace == nullptr || workspace_bytes < need) return WEDLM_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  EntPartial* part = static_cast<EntPartial*>(workspace);
+  launch_entropy_partials(dtype, B, W, V, logits, pl, part, s);
+  const int st = launch_status();
+  if (st != WEDLM_OK) return st;
+  hipLaunchKernelGGL(k_step_tail, dim3(B), dim3(kWave), 0, s, part, pl.n_chunks, W, lambda, tau,
+                     min_fill, page_size, num_pages, max_pages,
+                     commit_rule == WEDLM_COMMIT_BLOCK ? 1 : 0, block_table, tokens, filled,
+                     prefix_len, run_len, commit_len, cache_slot, mask_id, entropy, score,
+                     argmax_tok, selected, perm, inv_perm, pos, n_obs);
+  return launch_status();
 }

@@ -12,7 +12,7 @@
 // rule (the stop-and-wait baseline that the same summary contrasts with
 // streaming: a block is cached only once finalised) the run counts only when
 // it covers the whole window, and is 0 otherwise.
-#include "common.hpp"
+#include "window_ops.hpp"
 
 namespace wedlm {
 
@@ -26,27 +26,9 @@ k_window_reorder(int B, int W, int block_rule, const uint8_t* __restrict__ fille
   const int lane = threadIdx.x & (kWave - 1);
   const int b = blockIdx.x * kReorderWaves + (threadIdx.x >> 6);
   if (b >= B) return;  // uniform per wavefront
-  const bool in_window = lane < W;
-  const bool f = in_window && filled[b * W + lane] != 0;
-  const uint64_t fm = __ballot(f);
-  const uint64_t window = (W == kWave) ? ~0ull : ((1ull << W) - 1ull);
-  const uint64_t mm = ~fm & window;
-  const uint64_t below = (1ull << lane) - 1ull;  // lane < 64, so the shift is defined
-  const int nobs = __popcll(fm);
-  const int phys = f ? __popcll(fm & below) : nobs + __popcll(mm & below);
-  const int L = max(prefix_len[b], 0);
-  if (in_window) {
-    inv_perm[b * W + lane] = phys;
-    perm[b * W + phys] = lane;
-    pos[b * W + phys] = L + lane;
-  }
-  if (lane == 0) {
-    n_obs[b] = nobs;
-    // lanes >= W contribute 0 bits, so the first zero is at most W
-    const uint64_t zeros = ~fm;
-    const int run = zeros == 0 ? kWave : __builtin_ctzll(zeros);
-    run_len[b] = block_rule ? (run == W ? W : 0) : run;
-  }
+  const bool f = lane < W && filled[b * W + lane] != 0;
+  wave_reorder(b, W, lane, f, max(prefix_len[b], 0), block_rule, perm, inv_perm, pos, n_obs,
+               run_len);
 }
 
 }  // namespace wedlm

@@ -116,7 +116,8 @@ def summarize(trace, fetch, write, bench_json, steps, out_md, out_traffic, comma
     attn = next(n for n, *_ in stats if ATTN_KERNEL in n)
     a_fetch = per_launch(fetch_kib, attn, f_fac)
     a_write = per_launch(write_kib, attn, w_fac)
-    alg = roof["algorithmic_bytes_per_launch"]
+    # the counters cover every timed launch; the events a uniform sample of them
+    alg = roof.get("algorithmic_bytes_per_launch_all_steps", roof["algorithmic_bytes_per_launch"])
     trace_avg = next(t[2] for t in stats if t[0] == attn)
 
     lines = [f"# Window step kernels: {bench['config']['workload']}", "",

@@ -7,12 +7,15 @@ forward's projections and logits are inputs (synthetic), so one step is:
 reorder -> RoPE at logical positions -> window attention -> entropy/select ->
 commit. With ``fused_rope`` (the default) the RoPE step runs inside the
 attention and commit calls (wedlm_window_attn_rope, wedlm_commit_prefix_rope)
-instead of as its own pass over the window. Device buffers are allocated once;
-``run`` only enqueues kernels and never synchronises, so steps can be chained
-or timed back to back.
+instead of as its own pass over the window. With ``fused_tail`` the selection,
+the window-state commit and the next step's reorder run as one call
+(wedlm_select_commit_reorder), so a chain of steps is one reorder followed by
+(attention, tail) pairs. Device buffers are allocated once; ``run`` only
+enqueues kernels and never synchronises, so steps can be chained or timed back
+to back.
 """
 
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 
 import torch
 
@@ -28,6 +31,10 @@ class StreamState:
     block_table: torch.Tensor  # [B, max_pages] int32
     k_cache: torch.Tensor      # [nl, num_pages, Hkv, D/X, P, X]
     v_cache: torch.Tensor      # [nl, num_pages, Hkv, D, P]
+    # the WindowStep whose perm / pos / run_len hold the reorder of this
+    # window as it stands (set by the fused tail); code that edits the window
+    # by hand sets it to None so that the next step reorders first
+    ordered_by: object = field(default=None, compare=False, repr=False)
 
     def snapshot(self):
         return (self.tokens.clone(), self.filled.clone(), self.prefix_len.clone())
@@ -36,6 +43,7 @@ class StreamState:
         self.tokens.copy_(snap[0])
         self.filled.copy_(snap[1])
         self.prefix_len.copy_(snap[2])
+        self.ordered_by = None
 
 
 class WindowStep:
@@ -43,7 +51,7 @@ class WindowStep:
 
     def __init__(self, n_layers, B, W, Hq, Hkv, D, V, page_size, num_pages, max_pages, dtype,
                  device, max_prefix_len, theta, lam, tau, min_fill=1, mask_id=-1, scale=None,
-                 fused_rope=True, commit_rule=W_.COMMIT_STREAM):
+                 fused_rope=True, commit_rule=W_.COMMIT_STREAM, fused_tail=False):
         self.n_layers, self.B, self.W, self.Hq, self.Hkv, self.D, self.V = (
             n_layers, B, W, Hq, Hkv, D, V)
         self.page_size, self.num_pages, self.max_pages = page_size, num_pages, max_pages
@@ -58,6 +66,9 @@ class WindowStep:
         # fused path: the attention call appends the committed rows (else the
         # commit call writes them itself)
         self.fused_append = True
+        # selection + state commit + next reorder in one call (needs fused_rope
+        # and fused_append: the rows must be in the cache before the tail)
+        self.fused_tail = fused_tail
         i32 = dict(dtype=torch.int32, device=device)
         self.perm = torch.empty((B, W), **i32)
         self.inv = torch.empty((B, W), **i32)
@@ -94,6 +105,11 @@ class WindowStep:
         W_.wedlm_window_reorder_rule(self.B, self.W, self.commit_rule, st.filled, st.prefix_len,
                                      self.perm, self.inv, self.pos, self.n_obs, self.run_len,
                                      stream)
+        st.ordered_by = self
+
+    def ordered(self, st):
+        """Whether perm / pos / run_len already hold the reorder of ``st``."""
+        return st.ordered_by is self
 
     def rope(self, q, k, v, stream=None):
         W_.wedlm_rope_logical(self.dt, self.n_layers, self.B, self.W, self.Hq, self.Hkv, self.D,
@@ -142,6 +158,18 @@ class WindowStep:
                                     self.commit_len if commit_len is None else commit_len,
                                     self.cache_slot, self.mask_id, stream)
 
+    def select_commit_reorder(self, st, logits, commit_len=None, stream=None):
+        """Fused tail: selection, window-state commit (rows already appended)
+        and the reorder of the refreshed window for the next step."""
+        W_.wedlm_select_commit_reorder(
+            self.dt, self.B, self.W, self.V, logits, self.lam, self.tau, self.min_fill,
+            self.page_size, self.num_pages, self.max_pages, self.commit_rule, st.block_table,
+            self.run_len, st.tokens, st.filled, st.prefix_len,
+            self.commit_len if commit_len is None else commit_len, self.cache_slot, self.mask_id,
+            self.entropy, self.score, self.argmax, self.selected, self.perm, self.inv, self.pos,
+            self.n_obs, self.ent_ws, self.ent_ws_bytes, stream)
+        st.ordered_by = self
+
     def commit(self, st, commit_len=None, stream=None):
         W_.wedlm_commit_prefix(self.dt, self.n_layers, self.B, self.W, self.Hkv, self.D,
                                self.page_size, self.num_pages, self.max_pages, self.run_len,
@@ -156,9 +184,17 @@ class WindowStep:
 
         ``mark``: optional callable invoked with "attn_start", "attn_end" (also
         the start of entropy/select) and "entropy_end" at those points of the
-        launch sequence, e.g. to record timing events on ``stream``.
+        launch sequence, e.g. to record timing events on ``stream``. With the
+        fused tail "entropy_end" follows the whole tail (selection, state
+        commit and the next reorder).
+
+        With the fused tail, perm / inv / pos / n_obs / run_len hold the next
+        step's order when ``run`` returns (the order this step used is what
+        they held before it, or what its own first reorder wrote).
         """
-        self.reorder(st, stream)
+        tail = self.fused_tail and self.fused_rope and self.fused_append
+        if not (tail and self.ordered(st)):
+            self.reorder(st, stream)
         if not self.fused_rope:
             self.rope(q, k, v, stream)
         if mark is not None:
@@ -169,9 +205,16 @@ class WindowStep:
             self.attn(st, max_prefix_len, stream)
         if mark is not None:
             mark("attn_end")
+        if tail:
+            self.select_commit_reorder(st, logits, commit_len, stream)
+            if mark is not None:
+                mark("entropy_end")
+            return
         self.entropy_select(st, logits, stream)
         if mark is not None:
             mark("entropy_end")
+        # the commit below changes the window without reordering it
+        st.ordered_by = None
         if self.fused_rope and self.fused_append:
             # the committed rows were appended by attn_rope: window state only
             self.commit_rope(st, None, None, commit_len, stream)
@@ -212,7 +255,8 @@ def upload_step_inputs(wl, inp, device):
     return st, q, k, v, logits, int(inp["prefix_len"].max())
 
 
-def make_window_step(wl, inp, device, max_prefix_len, fused_rope=True, commit_rule=None):
+def make_window_step(wl, inp, device, max_prefix_len, fused_rope=True, commit_rule=None,
+                     fused_tail=False):
     """WindowStep sized for a workload and its inputs (streaming commits unless
     ``commit_rule`` says otherwise)."""
     from .synth import torch_dtype
@@ -221,4 +265,5 @@ def make_window_step(wl, inp, device, max_prefix_len, fused_rope=True, commit_ru
                       inp["num_pages"], inp["block_table"].shape[1], torch_dtype(wl), device,
                       max_prefix_len, wl.theta, wl.lam, wl.tau, wl.min_fill, wl.mask_id,
                       fused_rope=fused_rope,
-                      commit_rule=W_.COMMIT_STREAM if commit_rule is None else commit_rule)
+                      commit_rule=W_.COMMIT_STREAM if commit_rule is None else commit_rule,
+                      fused_tail=fused_tail)

@@ -20,7 +20,9 @@
  * without the separate RoPE pass and its physical-order copies.
  * wedlm_lm_head_select fuses the vocabulary projection that produces the
  * logits with step 4, so the logits are never written (wedlm_lm_head_pack lays
- * the projection out for it once).
+ * the projection out for it once). wedlm_select_commit_reorder runs step 4,
+ * the window-state half of step 5 and the next step's step 1 as one tail, so
+ * steps chain as reorder -> (attn_rope -> select_commit_reorder) repeated.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -343,6 +345,44 @@ int wedlm_commit_prefix_rope(int dtype, int n_layers, int B, int W, int Hkv, int
                              void* v_cache, int32_t* tokens, uint8_t* filled,
                              int32_t* prefix_len, int32_t* commit_len, int32_t* cache_slot,
                              int32_t mask_id, void* stream);
+
+/*
+ * wedlm_select_commit_reorder - the step's tail in one call: entropy and
+ * selection (wedlm_entropy_select), the window-state half of the commit
+ * (wedlm_commit_prefix_rope with k = v = NULL) and the next step's reorder
+ * (wedlm_window_reorder_rule) of the refreshed window. hyper.ai summary of
+ * WeDLM, "Method": after the forward the decoder fills positions by the
+ * distance-penalised entropy rule, commits the leftmost filled run, appends
+ * masks, and the next forward starts from the window reordered again.
+ *
+ * Results are bitwise those of the three calls in that order on the same
+ * inputs: entropy, score, argmax_tok, selected as wedlm_entropy_select;
+ * tokens, filled, prefix_len, commit_len, cache_slot as the commit (with c
+ * from this step's run_len, clamped as there); then perm, inv_perm, pos,
+ * n_obs and run_len of the new window as wedlm_window_reorder_rule under
+ * commit_rule.
+ *
+ * The committed rows must already be in the cache: the step's
+ * wedlm_window_attn_rope ran with commit_run = run_len. run_len is in/out:
+ * read as this step's run (from the reorder that ordered this step's
+ * window), overwritten with the next step's. The perm / pos the step's
+ * attention read are overwritten too, so the call must follow that attention
+ * on the same stream (it always does when both are on one stream).
+ *   logits [B][W][V] (dtype), 16-byte aligned for the vector path.
+ *   block_table [B][max_pages]; page_size must be 16 (else
+ *   WEDLM_ERR_UNSUPPORTED). Other arguments and layouts as in the three calls.
+ *   workspace >= wedlm_entropy_select_workspace_size(dtype, B, W, V).
+ * B * W <= 65535; W <= WEDLM_MAX_WINDOW.
+ */
+int wedlm_select_commit_reorder(int dtype, int B, int W, int V, const void* logits, float lambda,
+                                float tau, int min_fill, int page_size, int num_pages,
+                                int max_pages, int commit_rule, const int32_t* block_table,
+                                int32_t* run_len, int32_t* tokens, uint8_t* filled,
+                                int32_t* prefix_len, int32_t* commit_len, int32_t* cache_slot,
+                                int32_t mask_id, float* entropy, float* score,
+                                int32_t* argmax_tok, uint8_t* selected, int32_t* perm,
+                                int32_t* inv_perm, int32_t* pos, int32_t* n_obs, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(W.LIB_PATH),
 
 def test_exports_every_declared_function():
     declared = W.header_functions()
-    assert len(declared) == 16
+    assert len(declared) == 17
     lib = W.lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -31,7 +31,7 @@ def test_status_strings_and_version():
     assert "unsupported" in W.wedlm_status_string(-2)
     assert "workspace" in W.wedlm_status_string(-3)
     assert W.wedlm_abi_version() >> 16 == 1
-    assert W.wedlm_abi_version() & 0xffff >= 3  # fused RoPE, LM head, commit rules
+    assert W.wedlm_abi_version() & 0xffff >= 4  # fused RoPE, LM head, commit rules, step tail
 
 
 def _raw(name, *args):
@@ -110,6 +110,29 @@ def test_entropy_validation_and_workspace():
     assert _raw("wedlm_entropy_select", *a) == -1
     a = list(args); a[7] = float("nan")
     assert _raw("wedlm_entropy_select", *a) == -1
+
+
+def test_step_tail_validation():
+    # dtype B W V logits lam tau min_fill P num_pages max_pages rule, 7 state pointers,
+    # mask id, 8 output pointers, workspace, bytes, stream
+    args = ([1, 16, 16, 151936, 16, 0.1, 1.0, 1, 16, 100, 10, 0] + [1] * 7 + [-1] + [1] * 8
+            + [None, 0, None])
+    assert _raw("wedlm_select_commit_reorder", *args) == -3   # no workspace
+    a = list(args); a[11] = 2
+    assert _raw("wedlm_select_commit_reorder", *a) == -1      # commit rule
+    a = list(args); a[7] = 2
+    assert _raw("wedlm_select_commit_reorder", *a) == -1      # min_fill
+    a = list(args); a[6] = float("nan")
+    assert _raw("wedlm_select_commit_reorder", *a) == -1
+    a = list(args); a[8] = 8
+    assert _raw("wedlm_select_commit_reorder", *a) == -2      # pages of 16 positions only
+    a = list(args); a[2] = 65
+    assert _raw("wedlm_select_commit_reorder", *a) == -1
+    for i in (4, 12, 13, 14, 15, 16, 17, 18, 20, 21, 22, 23, 24, 25, 26, 27):
+        a = list(args); a[i] = None
+        assert _raw("wedlm_select_commit_reorder", *a) == -1, i
+    a = list(args); a[1] = 4096
+    assert _raw("wedlm_select_commit_reorder", *a) == -2      # B * W above 65535
 
 
 def test_commit_validation():

@@ -27,24 +27,35 @@ from .parity import ATTN_ATOL, ATTN_RTOL, ENTROPY_ATOL, stored_pair_bound, stora
 pytestmark = pytest.mark.gpu
 
 
-def _run_stream(wl, steps, sampled_layers, attend_steps, commit_rule="stream"):
+ORDER_KEYS = ("perm", "inv", "pos", "run_len")
+
+
+def _run_stream(wl, steps, sampled_layers, attend_steps, commit_rule="stream", fused_tail=False):
     print(f"[stream] {wl.name} steps={steps} layers={sampled_layers} tau={wl.tau} "
-          f"rule={commit_rule}", flush=True)
+          f"rule={commit_rule} fused_tail={fused_tail}", flush=True)
     dev = "cuda"
     inp = make_step_inputs(wl, steps=wl.steps)
     st, _, _, _, _, L0 = upload_step_inputs(wl, inp, dev)
     rule = {"stream": COMMIT_STREAM, "block": COMMIT_BLOCK}[commit_rule]
-    step = make_window_step(wl, inp, dev, L0 + wl.W * steps, commit_rule=rule)
+    step = make_window_step(wl, inp, dev, L0 + wl.W * steps, commit_rule=rule,
+                            fused_tail=fused_tail)
+    if fused_tail:
+        # the first step's order; every later one is written by the previous tail
+        step.reorder(st)
     gpu_log, host_inputs = [], []
     for s in range(steps):
         q, k, v, logits = stream_step_inputs(wl, s, dev)
         mpl = L0 + wl.W * s
         rec_prefix_in = st.prefix_len.cpu().numpy()
+        # the order a step attends with: before the call under the fused tail
+        # (which leaves the next step's order behind), after it otherwise
+        order = {key: getattr(step, key).cpu().numpy() for key in ORDER_KEYS}
         step.run(st, q, k, v, logits, max_prefix_len=mpl)
         torch.cuda.synchronize()
         rec = {key: getattr(step, key).cpu().numpy() for key in
-               ("perm", "inv", "pos", "run_len", "entropy", "argmax", "selected", "commit_len",
-                "cache_slot")}
+               ORDER_KEYS + ("entropy", "argmax", "selected", "commit_len", "cache_slot")}
+        if fused_tail:
+            rec.update(order)
         rec["prefix_len_in"] = rec_prefix_in
         rec["tokens"] = st.tokens.cpu().numpy()
         rec["filled"] = st.filled.cpu().numpy()
@@ -158,4 +169,21 @@ def test_stream_block_rule_low_entropy():
                              B=8, V=30000, spike=("prob", 0.9, 16.0, 20.0))
     _, longest, c = _run_stream(wl, steps=24, sampled_layers=[3], attend_steps={7},
                                 commit_rule="block")
+    assert longest == wl.W
+
+
+def test_stream_fused_tail():
+    # selection + state commit + next reorder as one call, against the oracle
+    wl = dataclasses.replace(WL.QWEN3_8B_STREAM, name="stream_fused_tail", n_layers=4, B=8,
+                             V=30000, spike=("prob", 0.9, 16.0, 20.0))
+    _, longest, _ = _run_stream(wl, steps=24, sampled_layers=[0, 3], attend_steps={0, 1, 23},
+                                fused_tail=True)
+    assert longest > 1
+
+
+def test_stream_fused_tail_block_rule():
+    wl = dataclasses.replace(WL.QWEN3_8B_STREAM, name="stream_fused_tail_block", n_layers=4,
+                             B=8, tau=float("-inf"))
+    _, longest, _ = _run_stream(wl, steps=2 * (wl.W + 1), sampled_layers=[1],
+                                attend_steps={wl.W}, commit_rule="block", fused_tail=True)
     assert longest == wl.W

@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--dual-stream", action="store_true",
                     help="time the dual-stream masking attention forward (one JSON line per block size)")
+    ap.add_argument("--read-bw", action="store_true",
+                    help="HBM read-rate probe (plain streaming read and random 4 KB blocks, the "
+                         "paged cache's pattern) as context for the roofline fractions")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record the attention / entropy timing events on every n-th timed "
                          "step (each record idles the GPU for a few microseconds)")
@@ -493,6 +496,55 @@ def dual_stream_latencies(args):
         torch.cuda.empty_cache()
 
 
+def read_bandwidth(args):
+    """Achievable HBM read rate on this GPU (one JSON line): the library's read
+    probe over 8 GiB as a plain stream and as 4 KB blocks in a random order,
+    each at several grid sizes (best reported), plus a torch device copy."""
+    import torch
+
+    from causal_streaming_decoding_amd import wedlm as Wd
+
+    dev = "cuda:0"
+    nbytes = 8 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    n_blk = nbytes // 4096
+    gen = torch.Generator(device="cpu").manual_seed(0)
+    order = torch.randperm(n_blk, generator=gen).to(torch.int32).to(dev)
+    grids = (1024, 2048, 4096, 8192)
+    sink = torch.empty(max(grids) * 256, dtype=torch.int32, device=dev)
+    reps = 10
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    by_grid = {}
+    for kind, blocks in (("stream", None), ("paged_4k", order)):
+        for grid in grids:
+            t = timed(lambda: Wd.wedlm_read_probe(src, nbytes, blocks, n_blk, sink, grid))
+            by_grid[f"{kind}_grid{grid}"] = nbytes / t / 1e9
+    half = nbytes // 2
+    a, b = src[:half], torch.empty(half, dtype=torch.uint8, device=dev)
+    t_copy = timed(lambda: b.copy_(a))
+    best = {k: max(v for g, v in by_grid.items() if g.startswith(k + "_")) for k in
+            ("stream", "paged_4k")}
+    print(json.dumps({
+        "metric": "achievable HBM read GB/s (probe)", "bytes": nbytes,
+        "stream_read_gbps": best["stream"], "paged_4k_read_gbps": best["paged_4k"],
+        "copy_read_plus_write_gbps": 2 * half / t_copy / 1e9,
+        "peak_gbps": HBM_PEAK_GBPS, "stream_frac": best["stream"] / HBM_PEAK_GBPS,
+        "paged_4k_frac": best["paged_4k"] / HBM_PEAK_GBPS,
+        "by_grid": by_grid}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -510,6 +562,9 @@ def main():
         return
     if args.dual_stream:
         dual_stream_latencies(args)
+        return
+    if args.read_bw:
+        read_bandwidth(args)
         return
 
     import numpy as np

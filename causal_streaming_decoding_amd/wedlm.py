@@ -48,6 +48,7 @@ _SIGNATURES = {
     "wedlm_lm_head_select_workspace_size": (_c_size, [_c_int] * 5),
     "wedlm_lm_head_select": (_c_int, [_c_int] * 5 + [_p, _p, _p, _c_float, _c_float, _c_int]
                              + [_p] * 5 + [_c_size, _p]),
+    "wedlm_read_probe": (_c_int, [_p, _c_size, _p, _c_int, _p, _c_int, _p]),
     "wedlm_select_commit_reorder": (_c_int, [_c_int] * 4 + [_p, _c_float, _c_float] + [_c_int] * 5
                                     + [_p] * 7 + [ctypes.c_int32] + [_p] * 9 + [_c_size, _p]),
 }
@@ -243,3 +244,9 @@ def wedlm_select_commit_reorder(dtype, B, W, V, logits, lam, tau, min_fill, page
         _ptr(prefix_len), _ptr(commit_len), _ptr(cache_slot), int(mask_id), _ptr(entropy),
         _ptr(score), _ptr(argmax_tok), _ptr(selected), _ptr(perm), _ptr(inv_perm), _ptr(pos),
         _ptr(n_obs), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def wedlm_read_probe(src, nbytes, block_order, n_blocks, sink, grid, stream=None):
+    _check("wedlm_read_probe", lib().wedlm_read_probe(
+        _ptr(src), nbytes, _ptr(block_order), int(n_blocks), _ptr(sink), int(grid),
+        _stream(stream)))

@@ -384,6 +384,24 @@ int wedlm_select_commit_reorder(int dtype, int B, int W, int V, const void* logi
                                 int32_t* inv_perm, int32_t* pos, int32_t* n_obs, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * wedlm_read_probe - HBM read-rate probe, a measurement aid beside the step
+ * (not a step of the method): the rate this GPU reaches on a plain streaming
+ * read and on the paged cache's pattern gives the step kernels' roofline
+ * fractions their context.
+ *
+ * block_order == NULL: reads all of src[0 .. bytes) once as 16-byte vectors
+ *   (grid-stride, non-temporal).
+ * block_order != NULL: reads n_blocks 4 KB blocks of src, block
+ *   block_order[j] for j = 0 .. n_blocks-1 (entries clamped to the
+ *   bytes / 4096 blocks src holds), one wavefront per block at a time.
+ * src 16-byte aligned, bytes >= 16; sink holds grid * 256 uint32 (one
+ * xor-fold per thread, written so that no read is dead code);
+ * 0 < grid <= 2^20. Enqueues one kernel on stream.
+ */
+int wedlm_read_probe(const void* src, size_t bytes, const int32_t* block_order, int n_blocks,
+                     uint32_t* sink, int grid, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(W.LIB_PATH),
 
 def test_exports_every_declared_function():
     declared = W.header_functions()
-    assert len(declared) == 17
+    assert len(declared) == 18
     lib = W.lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -133,6 +133,16 @@ def test_step_tail_validation():
         assert _raw("wedlm_select_commit_reorder", *a) == -1, i
     a = list(args); a[1] = 4096
     assert _raw("wedlm_select_commit_reorder", *a) == -2      # B * W above 65535
+
+
+def test_read_probe_validation():
+    assert _raw("wedlm_read_probe", None, 4096, None, 0, 16, 1, None) == -1
+    assert _raw("wedlm_read_probe", 16, 4096, None, 0, None, 1, None) == -1
+    assert _raw("wedlm_read_probe", 16, 4096, None, 0, 16, 0, None) == -1
+    assert _raw("wedlm_read_probe", 17, 4096, None, 0, 16, 1, None) == -1    # misaligned
+    assert _raw("wedlm_read_probe", 16, 8, None, 0, 16, 1, None) == -1
+    assert _raw("wedlm_read_probe", 16, 4096, 16, 0, 16, 1, None) == -1      # no blocks
+    assert _raw("wedlm_read_probe", 16, 2048, 16, 4, 16, 1, None) == -1      # src under 4 KB
 
 
 def test_commit_validation():

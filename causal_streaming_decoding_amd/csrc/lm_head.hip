@@ -47,6 +47,7 @@ constexpr int kLmTileElems = 32 * kLmKC;             // one packed W tile: 32 ro
 constexpr int kLmAhead = 3;                          // chunks requested ahead of the one computed
 constexpr int kLmStages = kLmAhead + 1;              // h ring stages and W register buffers
 constexpr int kLmMaxRB = 8;                          // 32-row blocks of hidden rows per workgroup
+constexpr int kNumXcds = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
 
 __device__ __forceinline__ bf16x8_t as_bf16x8_t(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
 
@@ -77,7 +78,7 @@ struct LmArgs {
   const uint16_t* h;   // [rows][hidden]
   const uint16_t* w;   // packed: [v_blocks][hidden / 64][4 K-steps][2][32 rows][8]
   EntPartial* part;    // [rows][n_tiles]
-  int rows, hidden, V, n_tiles, v_blocks;
+  int rows, hidden, V, n_tiles, v_blocks, row_groups;
 };
 
 template <int N>
@@ -114,8 +115,17 @@ k_lm_head_partial(LmArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 31, kg = lane >> 5;
-  const int v_wg = blockIdx.y * 4 * kWaveVocab;
-  const int r0 = blockIdx.x * kTileRows;
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id; the row
+  // groups of one vocabulary tile are given ids on the same XCD, one after
+  // the other, so they run together and share the tile's projection through
+  // that XCD's L2 (with one row group this is the identity).
+  const int xcd = blockIdx.x % kNumXcds;
+  const int slot = blockIdx.x / kNumXcds;
+  const int tile = (slot / a.row_groups) * kNumXcds + xcd;
+  const int rg = slot % a.row_groups;
+  if (tile >= a.n_tiles) return;  // padding of the last round of 8 tiles (whole workgroup)
+  const int v_wg = tile * 4 * kWaveVocab;
+  const int r0 = rg * kTileRows;
   const int nk = a.hidden / kLmKC;  // a multiple of 4 on this path
 
   // this lane's W: the packed tiles of its two 32-row vocabulary blocks (the
@@ -289,7 +299,7 @@ k_lm_head_partial(LmArgs a) {
     EntPartial p = red[0][tid];
 #pragma unroll
     for (int w = 1; w < 4; ++w) merge(p, red[w][tid]);
-    a.part[static_cast<size_t>(r0 + tid) * a.n_tiles + blockIdx.y] = p;
+    a.part[static_cast<size_t>(r0 + tid) * a.n_tiles + tile] = p;
   }
 }
 
@@ -328,7 +338,10 @@ struct LmPlan {
 
 static LmPlan plan_lm_head(int rows, int V) {
   LmPlan pl{};
-  pl.rb = rows <= 32 ? 1 : (rows <= 64 ? 2 : (rows <= 128 ? 4 : kLmMaxRB));
+  // up to 256 rows: groups of at most 128 rows (two groups on one XCD share
+  // each tile through L2: 434 against 450 us for one 256-row group at 256
+  // rows); above that 256-row groups (four 128-row groups measured slower)
+  pl.rb = rows <= 32 ? 1 : (rows <= 64 ? 2 : (rows <= 256 ? 4 : kLmMaxRB));
   // two blocks per wavefront: one block (twice the tiles, a smaller last
   // round) measured slower for 256 and 512 rows
   pl.vb = kLmMaxVB;
@@ -444,7 +457,8 @@ extern "C" int wedlm_lm_head_select(int dtype, int B, int W, int hidden, int V,
   a.V = V;
   a.n_tiles = pl.n_tiles;
   a.v_blocks = ceil_div(V, 32);
-  const dim3 grid(pl.row_groups, pl.n_tiles);
+  a.row_groups = pl.row_groups;
+  const dim3 grid(pl.row_groups * ceil_div(pl.n_tiles, kNumXcds) * kNumXcds);
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(kLmThreads), 0, s, a); };
   if (pl.rb == 1) go(k_lm_head_partial<1, 2>);
   else if (pl.rb == 2) go(k_lm_head_partial<2, 2>);

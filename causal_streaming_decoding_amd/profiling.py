@@ -253,13 +253,16 @@ def summarize_lm_head(bench_jsonl, trace, fetch, write, out_md, command_bench, c
            "algorithmic MB | read MB | written MB | counted / algorithmic | roofline |",
            "|---|---|---|---|---|---|---|---|---|---|"]
     for ln, (name, grid, d), (_, _, fv), (_, _, wv) in zip(lines_in, dur, fet, wri):
+        # the kernel's first template argument is its 32-row blocks per workgroup
+        rb = int(name.split("<", 1)[1].split(",", 1)[0])
+        groups = -(-ln["rows"] // (32 * rb))
         rd = statistics.mean(fv[-ln["steps"]:]) * 1024.0 / f_fac
         wr = statistics.mean(wv[-ln["steps"]:]) * 1024.0 / w_fac
         alg = ln["algorithmic_bytes"]
         roof = ln["roofline"]
         out.append(
             f"| `{ln['workload']}` | {ln['rows']} x {ln['hidden']} x {ln['V']} | "
-            f"{ln['us']['median']:.1f} | `{name}` ({grid // 256} row groups) | "
+            f"{ln['us']['median']:.1f} | `{name}` ({groups} row groups) | "
             f"{statistics.median(d[-ln['steps']:]):.1f} | {alg / 1e6:.1f} | {rd / 1e6:.1f} | "
             f"{wr / 1e6:.2f} | {(rd + wr) / alg:.3f} | {roof['bound']} {roof['frac'] * 100:.1f} % |")
     with open(out_md, "w") as f:

@@ -34,9 +34,12 @@
 //
 // When there are too few groups to fill the GPU, a group's pages are split
 // across workgroups; each split writes (max, sum, unnormalised O) and a combine
-// kernel merges them. The window's own keys are processed by the last split
-// with the causal rule (row p sees window rows 0..p), staged into LDS in the
-// same page layout.
+// kernel merges them. The splits follow the live prefix lengths: each
+// (layer, kv head) gets a fixed number of workgroups, and each sequence as
+// many of them as its pages need, so a ragged batch's longest sequence is not
+// the long pole (find_split). The window's own keys are processed by the last
+// split with the causal rule (row p sees window rows 0..p), staged into LDS in
+// the same page layout.
 #include "common.hpp"
 
 #include <cmath>
@@ -81,10 +84,15 @@ struct AttnArgs {
   const int32_t* block_table;
   const int32_t* prefix_len;
   uint16_t* out;       // [nl][B][W][Hq][D]
-  float* ws_o;         // [groups][splits][M][D]
-  float* ws_ml;        // [groups][splits][M][2]
+  // split partials, one slot per workgroup: slot = (layer*Hkv + kvh)*cols + j
+  float* ws_o;         // [n_layers*Hkv*cols][M][D]
+  float* ws_ml;        // [n_layers*Hkv*cols][M][2]
+  int2* ws_plan;       // [groups]: first slot and number of splits of each group
   int B, W, Hq, Hkv, g, M;
-  int num_pages, max_pages, max_prefix_len, n_splits;
+  int num_pages, max_pages, max_prefix_len;
+  int cols;            // workgroups per (layer, kv head): B, or S > B when split
+  int split;           // key ranges split across workgroups (partials + combine)
+  int min_pages;       // no split takes fewer pages than this (unless it is all there is)
   long long cache_layer_stride;  // elements per layer of one cache
   float scale_log2;
   // RoPE fused into the loads (else unused): physical row -> slot, logical
@@ -387,6 +395,87 @@ __device__ __forceinline__ void append_committed(const AttnArgs& a, const Stage&
   }
 }
 
+// ---- key-range splits of a ragged batch ----------------------------------
+// In split mode each (layer, kv head) column has S = cols workgroups. The
+// work of sequence b is u_b = its prefix pages + its window's 16-key chunks
+// (the last split also attends to the window). With a split size of K units,
+// sequence b takes ceil(u_b / K) consecutive workgroups of the column, split s
+// covering pages [s K, (s+1) K) of its prefix. K is the smallest value, not
+// below min_pages, for which the sequences' split counts fit in S: it lies in
+// [ceil(P / S), ceil((P - B) / (S - B))] with P = sum u_b, and the upper end
+// always fits (ceil(u/K) <= (u - 1)/K + 1 for u >= 1), so a binary search over
+// that interval finds it. Every wave of the workgroup evaluates this with the
+// same inputs and gets the same wave-uniform result; workgroups past the last
+// split return at once.
+struct SplitSlot {
+  int b;        // sequence, or -1 when this workgroup has no split
+  int split;    // index of this split within its sequence
+  int n_split;  // splits of the sequence
+  int first;    // workgroup index (within the column) of the sequence's split 0
+  int K;        // units per split
+};
+
+__device__ __forceinline__ int seq_units(const AttnArgs& a, int b) {
+  const int L = min(max(a.prefix_len[b], 0), a.max_prefix_len);
+  return (L + kPage - 1) / kPage + (a.W + kPage - 1) / kPage;
+}
+
+__device__ __forceinline__ long long wave_sum_ll(long long x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+// sum over sequences of ceil(u_b / K) (K = 1 gives sum u_b)
+__device__ __forceinline__ long long split_total(const AttnArgs& a, int K, int lane) {
+  long long n = 0;
+  for (int b0 = 0; b0 < a.B; b0 += kWave) {
+    const int b = b0 + lane;
+    const unsigned u = b < a.B ? static_cast<unsigned>(seq_units(a, b)) : 0u;
+    n += wave_sum_ll(static_cast<long long>((u + K - 1) / static_cast<unsigned>(K)));
+  }
+  return n;
+}
+
+__device__ SplitSlot find_split(const AttnArgs& a, int j, int lane) {
+  const long long S = a.cols, Bn = a.B;  // S > B in split mode
+  const long long P = split_total(a, 1, lane);
+  long long lo = max(static_cast<long long>(a.min_pages), (P + S - 1) / S);
+  long long hi = max(lo, (P - Bn + (S - Bn) - 1) / (S - Bn));
+  while (lo < hi) {
+    const long long mid = (lo + hi) / 2;
+    if (split_total(a, static_cast<int>(mid), lane) <= S)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  const int K = static_cast<int>(lo);
+  SplitSlot r{-1, 0, 1, 0, K};
+  long long base = 0;  // workgroups taken by the sequences before this chunk
+  for (int b0 = 0; b0 < a.B; b0 += kWave) {
+    const int b = b0 + lane;
+    const int n = b < a.B ? (seq_units(a, b) + K - 1) / K : 0;
+    int incl = n;  // inclusive prefix sum over the chunk's lanes
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int t = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += t;
+    }
+    const long long lo_j = base + incl - n;
+    const unsigned long long hit = __ballot(n > 0 && j >= lo_j && j < base + incl);
+    if (hit) {
+      const int src = __ffsll(static_cast<long long>(hit)) - 1;
+      r.b = b0 + src;
+      r.first = static_cast<int>(base) + __shfl(incl - n, src, kWave);
+      r.n_split = __shfl(n, src, kWave);
+      r.split = j - r.first;
+      return r;
+    }
+    base += __shfl(incl, kWave - 1, kWave);
+  }
+  return r;
+}
+
 // NW wavefronts per workgroup, one 16-row tile each. kRope: q, k, v are in
 // slot order before RoPE; each query row and window key is gathered through
 // perm and rotated at its logical position as it is loaded.
@@ -411,20 +500,29 @@ k_window_attn_bf16(AttnArgs a) {
   // only the x-th 4 KB of every page record, which leaves HBM channels unevenly
   // loaded when pages are allocated in order (measured 4.5 against 5.2 TB/s).
   int bid = blockIdx.x;
-  const int split = bid % a.n_splits;
-  bid /= a.n_splits;
-  const int b = bid % a.B;
-  bid /= a.B;
+  const int j = bid % a.cols;  // sequence, or (sequence, split) in split mode
+  bid /= a.cols;
   const int kvh = bid % a.Hkv;
   const int layer = bid / a.Hkv;
+  int b = j, split = 0, n_split = 1, K = 0;
+  if (a.split) {
+    const SplitSlot sl = find_split(a, j, lane);
+    if (sl.b < 0) return;  // every wave of the workgroup takes this branch
+    b = __builtin_amdgcn_readfirstlane(sl.b);
+    split = __builtin_amdgcn_readfirstlane(sl.split);
+    n_split = __builtin_amdgcn_readfirstlane(sl.n_split);
+    K = __builtin_amdgcn_readfirstlane(sl.K);
+  }
   const int group = (layer * a.B + b) * a.Hkv + kvh;
+  const size_t slot = static_cast<size_t>(layer * a.Hkv + kvh) * a.cols + j;
 
   const int L = min(max(a.prefix_len[b], 0), a.max_prefix_len);
   const int npages = (L + kPage - 1) / kPage;
-  const int per_split = (npages + a.n_splits - 1) / a.n_splits;
-  const int pg_begin = min(npages, split * per_split);
-  const int pg_end = min(npages, pg_begin + per_split);
-  const bool with_window = split == a.n_splits - 1;
+  const int pg_begin = a.split ? min(npages, split * K) : 0;
+  const int pg_end = a.split ? min(npages, pg_begin + K) : npages;
+  const bool with_window = split == n_split - 1;
+  if (a.split && split == 0 && tid == 0)
+    a.ws_plan[group] = make_int2(static_cast<int>(slot), n_split);
 
   // ---- this wave's 16 query rows (B operand of S^T = K Q^T) ---------------
   // Loaded through asm, before the first pages' DMAs, and retired below with
@@ -601,7 +699,7 @@ k_window_attn_bf16(AttnArgs a) {
   // ---- write out ------------------------------------------------------------
   mfma_result_guard(st.o);
   if (!row_ok) return;
-  if (a.n_splits == 1) {
+  if (!a.split) {
     const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
     uint16_t* orow = a.out + ((lb * a.W + prow) * a.Hq + kvh * a.g + hh) * kHeadDim;
 #pragma unroll
@@ -611,14 +709,13 @@ k_window_attn_bf16(AttnArgs a) {
       *reinterpret_cast<u32x2*>(orow + dt * 16 + grp * 4) = w;
     }
   } else {
-    const size_t part = static_cast<size_t>(group) * a.n_splits + split;
-    float* o = a.ws_o + (part * a.M + row) * kHeadDim;
+    float* o = a.ws_o + (slot * a.M + row) * kHeadDim;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
       *reinterpret_cast<float4*>(o + dt * 16 + grp * 4) =
           make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
     if (grp == 0) {
-      float* ml = a.ws_ml + (part * a.M + row) * 2;
+      float* ml = a.ws_ml + (slot * a.M + row) * 2;
       ml[0] = st.m;
       ml[1] = st.l;
     }
@@ -626,16 +723,17 @@ k_window_attn_bf16(AttnArgs a) {
 }
 
 // Merge of the per-split partials: out = sum_s O_s 2^(m_s - m) / sum_s l_s 2^(m_s - m).
-// One thread per (group, row, 4 dims), one pass over the splits in split
-// order with a running reference max; the partials are read kCombineBatch
+// One thread per (group, row, 4 dims), one pass over the group's splits (the
+// plan entry its split 0 wrote: first slot, count) in split order with a
+// running reference max; the partials are read kCombineBatch
 // splits at a time, all loads of a batch issued before any is used, so the
 // latency is paid once per batch rather than once per split.
 constexpr int kCombineBatch = 8;
 
 __global__ void __launch_bounds__(256)
 k_window_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
-                      uint16_t* __restrict__ out, int n_groups, int M, int n_splits, int B, int W,
-                      int Hq, int Hkv, int g) {
+                      const int2* __restrict__ ws_plan, uint16_t* __restrict__ out, int n_groups,
+                      int M, int W, int Hq, int Hkv, int g) {
   const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int quads = kHeadDim / 4;
   const long long total = static_cast<long long>(n_groups) * M * quads;
@@ -643,6 +741,8 @@ k_window_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ 
   const int d4 = static_cast<int>(idx % quads);
   const int row = static_cast<int>((idx / quads) % M);
   const int group = static_cast<int>(idx / (static_cast<long long>(quads) * M));
+  const int2 plan = ws_plan[group];
+  const int n_splits = plan.y;
   float m = -INFINITY, lsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < n_splits; s0 += kCombineBatch) {
@@ -651,7 +751,7 @@ k_window_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ 
 #pragma unroll
     for (int k = 0; k < kCombineBatch; ++k) {
       const int s = s0 + k;
-      const size_t part = (static_cast<size_t>(group) * n_splits + s) * M + row;
+      const size_t part = (static_cast<size_t>(plan.x) + s) * M + row;
       ml[k] = s < n_splits ? reinterpret_cast<const float2*>(ws_ml)[part]
                            : make_float2(-INFINITY, 0.f);
       o[k] = s < n_splits ? *reinterpret_cast<const float4*>(ws_o + part * kHeadDim + d4 * 4)
@@ -842,9 +942,11 @@ k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
 
 // ---- launch planning -------------------------------------------------------
 struct AttnPlan {
-  int n_splits;
+  int cols;   // workgroups per (layer, kv head)
+  bool split;
+  int min_pages;
   int waves;  // wavefronts per workgroup: 4, 8 or 16 (one 16-row tile each)
-  size_t ws_o_bytes, ws_ml_bytes;
+  size_t ws_o_bytes, ws_ml_bytes, ws_plan_bytes;
 };
 
 static AttnPlan plan_bf16(int n_layers, int B, int W, int Hq, int Hkv, int max_prefix_len) {
@@ -854,20 +956,31 @@ static AttnPlan plan_bf16(int n_layers, int B, int W, int Hq, int Hkv, int max_p
   const int tiles = ceil_div(M, 16);
   pl.waves = tiles <= 4 ? 4 : (tiles <= 8 ? 8 : 16);
   const long long groups = 1LL * n_layers * B * Hkv;
+  const long long columns = 1LL * n_layers * Hkv;
   // aim for one full round of workgroups (every CU holding as many as its
-  // registers allow) but keep >= 4 pages per split (8 for the deeper rings)
+  // registers allow) but keep >= 4 pages per split (8 for the deeper rings);
+  // how the column's workgroups are shared out follows the live prefix
+  // lengths on the device (find_split)
   const int wg_per_cu = pl.waves == 4 ? Ring<4>::kWgPerCu
                                       : (pl.waves == 8 ? Ring<8>::kWgPerCu : Ring<16>::kWgPerCu);
   const long long target = 1LL * kNumCUs * wg_per_cu;
-  const int min_pages = pl.waves == 4 ? 4 : 8;
+  pl.min_pages = pl.waves == 4 ? 4 : 8;
   const int npages = ceil_div(max(max_prefix_len, 1), kPage);
-  int splits = 1;
-  if (groups < target) splits = static_cast<int>((target + groups - 1) / groups);
-  splits = max(1, min(splits, npages / min_pages));
-  pl.n_splits = splits;
-  if (splits > 1) {
-    pl.ws_o_bytes = static_cast<size_t>(groups) * splits * M * kHeadDim * sizeof(float);
-    pl.ws_ml_bytes = static_cast<size_t>(groups) * splits * M * 2 * sizeof(float);
+  pl.cols = B;
+  pl.split = false;
+  if (groups < target) {
+    long long S = (target + columns - 1) / columns;
+    S = std::min(S, 1LL * B * max(1, npages / pl.min_pages));
+    if (S > B) {
+      pl.cols = static_cast<int>(S);
+      pl.split = true;
+    }
+  }
+  if (pl.split) {
+    const size_t slots = static_cast<size_t>(columns) * pl.cols;
+    pl.ws_o_bytes = slots * M * kHeadDim * sizeof(float);
+    pl.ws_ml_bytes = slots * M * 2 * sizeof(float);
+    pl.ws_plan_bytes = static_cast<size_t>(groups) * sizeof(int2);
   }
   return pl;
 }
@@ -899,7 +1012,7 @@ extern "C" size_t wedlm_window_attn_workspace_size(int dtype, int n_layers, int 
     return 0;
   if (dtype != WEDLM_BF16) return 0;
   const AttnPlan pl = plan_bf16(n_layers, B, W, Hq, Hkv, max_prefix_len);
-  return pl.ws_o_bytes + pl.ws_ml_bytes;
+  return pl.ws_o_bytes + pl.ws_ml_bytes + pl.ws_plan_bytes;
 }
 
 // Shared by both entry points; `rope` selects the fused-RoPE kernels (q, k, v
@@ -955,7 +1068,7 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
                             const_cast<void*>(k_cache), const_cast<void*>(v_cache), s);
   }
   const AttnPlan pl = plan_bf16(n_layers, B, W, Hq, Hkv, max_prefix_len);
-  const size_t need = pl.ws_o_bytes + pl.ws_ml_bytes;
+  const size_t need = pl.ws_o_bytes + pl.ws_ml_bytes + pl.ws_plan_bytes;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return WEDLM_ERR_WORKSPACE;
   AttnArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -968,6 +1081,9 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   a.out = static_cast<uint16_t*>(out_phys);
   a.ws_o = need ? static_cast<float*>(workspace) : nullptr;
   a.ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_o_bytes) : nullptr;
+  a.ws_plan = need ? reinterpret_cast<int2*>(static_cast<char*>(workspace) + pl.ws_o_bytes +
+                                             pl.ws_ml_bytes)
+                   : nullptr;
   a.B = B;
   a.W = W;
   a.Hq = Hq;
@@ -977,7 +1093,9 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   a.num_pages = num_pages;
   a.max_pages = max_pages;
   a.max_prefix_len = max_prefix_len;
-  a.n_splits = pl.n_splits;
+  a.cols = pl.cols;
+  a.split = pl.split ? 1 : 0;
+  a.min_pages = pl.min_pages;
   a.cache_layer_stride = cache_layer_stride;
   a.scale_log2 = scale_log2;
   a.perm = perm;
@@ -987,7 +1105,7 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   a.kc_w = commit_run ? static_cast<uint16_t*>(const_cast<void*>(k_cache)) : nullptr;
   a.vc_w = commit_run ? static_cast<uint16_t*>(const_cast<void*>(v_cache)) : nullptr;
   const long long groups = 1LL * n_layers * B * Hkv;
-  const long long blocks = groups * pl.n_splits;
+  const long long blocks = 1LL * n_layers * Hkv * pl.cols;
   if (blocks > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
   const dim3 grid(static_cast<unsigned>(blocks));
   auto go = [&](auto kernel, int waves) {
@@ -1000,11 +1118,11 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   else
     rope ? go(k_window_attn_bf16<16, true>, 16) : go(k_window_attn_bf16<16, false>, 16);
   st = launch_status();
-  if (st != WEDLM_OK || pl.n_splits == 1) return st;
+  if (st != WEDLM_OK || !pl.split) return st;
   const long long threads = groups * a.M * (kHeadDim / 4);
   hipLaunchKernelGGL(k_window_attn_combine, dim3(static_cast<unsigned>((threads + 255) / 256)),
-                     dim3(256), 0, s, a.ws_o, a.ws_ml, a.out, static_cast<int>(groups), a.M,
-                     pl.n_splits, B, W, Hq, Hkv, a.g);
+                     dim3(256), 0, s, a.ws_o, a.ws_ml, a.ws_plan, a.out, static_cast<int>(groups),
+                     a.M, W, Hq, Hkv, a.g);
   return launch_status();
 }
 

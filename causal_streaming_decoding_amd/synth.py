@@ -7,7 +7,8 @@ path (through ``layout.py``) and the CPU oracle consume what it returns.
 
 Recipe (host side, ``numpy.random.default_rng(seed)`` = PCG64), draws in this
 fixed order:
-  1. prefix length of each sequence (fixed, or uniform integers in [lo, hi]);
+  1. prefix length of each sequence (fixed, uniform integers in [lo, hi], or
+     an explicit list);
   2. a random permutation of the page pool, dealt out to the sequences in
      order, each getting enough pages for its prefix plus ``W * steps``
      positions (every step commits at most W tokens);
@@ -57,6 +58,11 @@ def _prefix_lengths(wl, rng):
         return np.full(wl.B, int(wl.prefix[1]), dtype=np.int64)
     if kind == "uniform":
         return rng.integers(wl.prefix[1], wl.prefix[2] + 1, size=wl.B).astype(np.int64)
+    if kind == "list":  # explicit per-sequence lengths (no draw)
+        lengths = np.asarray(wl.prefix[1], dtype=np.int64)
+        if lengths.shape != (wl.B,):
+            raise ValueError("prefix list needs one length per sequence")
+        return lengths
     raise ValueError(kind)
 
 

@@ -24,7 +24,7 @@ class Workload:
     V: int
     lam: float
     tau: float
-    prefix: tuple           # ("fixed", L) or ("uniform", lo, hi) inclusive, per sequence
+    prefix: tuple           # ("fixed", L), ("uniform", lo, hi) inclusive, or ("list", (L_0, ..))
     fill: tuple             # ("count", n) | ("frac", lo, hi) one draw | ("frac_per_seq", lo, hi) | ("none",)
     spike: tuple            # ("slots", n, mag) | ("all_uniform", lo, hi) | ("prob", p, lo, hi) | ("none",)
     steps: int = 1          # window steps of one run (the streaming loop runs many)

@@ -150,7 +150,11 @@ int wedlm_rope_logical(int dtype, int n_layers, int B, int W, int Hq, int Hkv, i
 /*
  * Bytes of workspace wedlm_window_attn needs for these sizes. max_prefix_len is
  * a host-side upper bound of every prefix_len[b]. Returns 0 when no workspace is
- * needed (no key-range split) and also for invalid sizes.
+ * needed (no key-range split) and also for invalid sizes. When the key ranges
+ * are split (too few (layer, sequence, kv head) groups to fill the GPU), how
+ * the workgroups are shared out between the sequences follows the prefix_len
+ * values on the device at launch time, so the size depends only on the host
+ * sizes and no host synchronisation is needed.
  */
 size_t wedlm_window_attn_workspace_size(int dtype, int n_layers, int B, int W, int Hq, int Hkv,
                                         int D, int page_size, int max_prefix_len);

@@ -95,6 +95,15 @@ def _variant(base, **kw):
     # 16-wave workgroups with fewer pages per split than the 15-stage ring holds
     ("nw16_short_splits", _variant(WL.QWEN25_7B_RAGGED, name="edge_nw16_short", B=2,
                                    prefix=("uniform", 40, 130), V=2048)),
+    # split plan over very uneven prefixes: empty, one key, one page, a long one
+    ("split_plan_extremes", _variant(WL.QWEN25_7B_RAGGED, name="edge_split_extremes", B=6,
+                                     prefix=("list", (0, 1, 4000, 16, 2047, 33)), V=2048)),
+    # 8-wave workgroups, split plan with a sequence that has no prefix at all
+    ("split_plan_nw8", _variant(WL.QWEN3_8B_BS1, name="edge_split_nw8", W=32, B=3,
+                                prefix=("list", (3000, 5, 0)), V=2048, fill=("frac", 0.3, 0.7))),
+    # 4-wave workgroups, 40 sequences sharing 160 workgroups per kv head
+    ("split_plan_many_seqs", _variant(WL.QWEN3_8B_BS1, name="edge_split_many", B=40,
+                                      prefix=("uniform", 0, 1500), V=1024)),
 ])
 def test_edge_cases(name, wl):
     _check(wl)

@@ -69,7 +69,10 @@ struct Ring {
   static constexpr int kWavesPerSimd = NW == 4 ? 5 : 4;
   static constexpr int kWgPerCu = NW == 4 ? 5 : (NW == 8 ? 2 : 1);
   static constexpr int kStages = NW == 4 ? 3 : (NW == 8 ? 7 : 15);
-  static constexpr int kAhead = kStages - 1;  // pages in flight while one is computed
+  // The deep rings advance two pages per barrier (attend_pages2): the waves
+  // compute two stages while the others are in flight.
+  static constexpr bool kPair = NW >= 8;
+  static constexpr int kAhead = kStages - (kPair ? 2 : 1);  // pages in flight during compute
 };
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.f;
@@ -255,6 +258,72 @@ __device__ __forceinline__ void attend_page(RowState& st, const bf16x8 (&qr)[4],
   }
 }
 
+// P^T for the PV product of one page from a lane's 4 probabilities (hi and lo
+// bf16 parts, regrouped as in attend_page), then O^T += V^T P^T over the page.
+__device__ __forceinline__ void pv_page(RowState& st, const Stage& sg, int col, int grp,
+                                        float p0, float p1, float p2, float p3) {
+  uint32_t h01 = pack_bf16x2(p0, p1), h23 = pack_bf16x2(p2, p3);
+  uint32_t l01 = pack_bf16x2(p0 - bf16_lo(h01), p1 - bf16_hi(h01));
+  uint32_t l23 = pack_bf16x2(p2 - bf16_lo(h23), p3 - bf16_hi(h23));
+  pv_regroup(h01, h23, l01, l23);
+  const u32x4 pb = {h01, h23, l01, l23};
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const u32x4 va =
+        *reinterpret_cast<const u32x4*>(&sg.v[(dt * 16 + col) * kPage + (grp & 1) * 8]);
+    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb), st.o[dt], 0, 0, 0);
+  }
+}
+
+// Two 16-key stages at once (the deep rings): the two score products are
+// independent MFMA chains, and the row max, the rescale decision and the row
+// sum are taken once over the pair's 32 keys. Otherwise as attend_page; the
+// PV products are accumulated in page order.
+__device__ __forceinline__ void attend_pages2(RowState& st, const bf16x8 (&qr)[4],
+                                              const Stage& s0, const Stage& s1, int lane,
+                                              int lim0, int lim1, float scale_log2) {
+  const int col = lane & 15, grp = lane >> 4;
+  f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const u32x4 ka = *reinterpret_cast<const u32x4*>(&s0.k[s * 512 + lane * 8]);
+    const u32x4 kb = *reinterpret_cast<const u32x4*>(&s1.k[s * 512 + lane * 8]);
+    sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qr[s], sa, 0, 0, 0);
+    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb), qr[s], sb, 0, 0, 0);
+  }
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sa), "+v"(sb));  // as mfma_result_guard
+  float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+  if (lim0 < kPage) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (grp * 4 + i >= lim0) x[i] = -INFINITY;
+  }
+  if (lim1 < kPage) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (grp * 4 + i >= lim1) x[4 + i] = -INFINITY;
+  }
+  const float m8 = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  const float mc = row_max4(m8) * scale_log2;
+  const bool raise = mc > st.m + kRescaleLog2;
+  if (__ballot(raise)) {
+    const float m_new = raise ? mc : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 when st.m = -inf
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.o[dt] *= alpha;
+    st.m = m_new;
+  }
+  const float base = st.m == -INFINITY ? 0.f : st.m;
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -base));
+  st.l += row_sum4(((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+  pv_page(st, s0, col, grp, p[0], p[1], p[2], p[3]);
+  pv_page(st, s1, col, grp, p[4], p[5], p[6], p[7]);
+}
+
 // Asynchronous page staging: global -> LDS DMA (global_load_lds_dwordx4).
 // Each instruction moves 64 lanes x 16 B = 1 KB: lane l's 16 bytes land at
 // M0 + 16 l in LDS. A stage is 512 vectors (K then V of one page); wavefront w
@@ -264,20 +333,35 @@ __device__ __forceinline__ void attend_page(RowState& st, const bf16x8 (&qr)[4],
 // conservative vmcnt waits before every LDS read of the ring; the waits are
 // explicit (stage_wait_barrier) and counted per thread in issue order.
 // M0 is a reserved register: it is saved and restored around the DMA.
-// The loads carry the non-temporal hint (nt): every cache byte is read once
-// per step, so it should not displace other lines on its way through the
-// caches; on the 36-layer streaming shape this took the launch from 5.1 to
-// 5.5 TB/s (the scope bits sc0 / sc1 on top of it changed nothing).
+// kNt: the loads carry the non-temporal hint (nt). When every page is read
+// once per launch (each sequence owns its pages, as in decoding), the pages
+// should not displace other lines on their way through the caches: on the
+// 36-layer streaming shape this took the launch from 5.1 to 5.5 TB/s (the
+// scope bits sc0 / sc1 on top of it changed nothing). When block-table rows
+// share pages (the dual-stream forward: every block of a sample reads the
+// sample's memory rows), the re-reads hit in the caches only without the
+// hint (2.9 against 2.3 ms for the 16-key-block forward).
+template <bool kNt>
 __device__ __forceinline__ void lds_dma_16(const void* gptr, uint32_t lds_byte_addr) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off nt\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gptr), "s"(lds_byte_addr)
-      : "memory");
+  if constexpr (kNt)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_byte_addr)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_byte_addr)
+        : "memory");
 }
 
 // A wave-uniform block-table entry through the scalar cache (read only).
@@ -299,7 +383,7 @@ struct DmaShape {
   static constexpr int kIssuers = kPageVecs / (kWave * kPerWave);  // waves that issue
 };
 
-template <int NW>
+template <int NW, bool kNt>
 __device__ __forceinline__ void stage_dma(Stage& sg, int wave, int lane, int pg, const int32_t* bt,
                                           int max_pages, int num_pages, int Hkv, int kvh,
                                           const uint16_t* kc_layer, const uint16_t* vc_layer) {
@@ -317,7 +401,7 @@ __device__ __forceinline__ void stage_dma(Stage& sg, int wave, int lane, int pg,
   for (int i = 0; i < S::kPerWave; ++i) {
     const int v0 = (i * S::kIssuers + wave) * kWave;  // first vector (wave-uniform)
     const uint16_t* base = (v0 < 256 ? kc_layer + off : vc_layer + off - 256 * 8);
-    lds_dma_16(base + (v0 + lane) * 8, __builtin_amdgcn_readfirstlane(lds_base + v0 * 16));
+    lds_dma_16<kNt>(base + (v0 + lane) * 8, __builtin_amdgcn_readfirstlane(lds_base + v0 * 16));
   }
 }
 
@@ -479,7 +563,7 @@ __device__ SplitSlot find_split(const AttnArgs& a, int j, int lane) {
 // NW wavefronts per workgroup, one 16-row tile each. kRope: q, k, v are in
 // slot order before RoPE; each query row and window key is gathered through
 // perm and rotated at its logical position as it is loaded.
-template <int NW, bool kRope>
+template <int NW, bool kRope, bool kNt>
 __global__ void __launch_bounds__(kWave * NW)
 __attribute__((amdgpu_waves_per_eu(Ring<NW>::kWavesPerSimd, Ring<NW>::kWavesPerSimd)))
 k_window_attn_bf16(AttnArgs a) {
@@ -572,7 +656,7 @@ k_window_attn_bf16(AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < kAhead; ++j)
     if (j < pro)
-      stage_dma<NW>(stage[j], wave, lane, pg_begin + j, bt, a.max_pages, a.num_pages, a.Hkv, kvh,
+      stage_dma<NW, kNt>(stage[j], wave, lane, pg_begin + j, bt, a.max_pages, a.num_pages, a.Hkv, kvh,
                     kc_layer, vc_layer);
   // Retire the query loads: only the kAhead stages issued after them may
   // remain. Waves that issue no DMA (NW = 16), and every wave when the split
@@ -599,12 +683,32 @@ k_window_attn_bf16(AttnArgs a) {
   // computing page i-1 (its LDS reads retired before it reached the barrier),
   // so that stage is refilled with page i+kAhead right away: kAhead pages are
   // in flight while the waves compute, one barrier per page.
-  for (int i = 0; i < npg; ++i) {
+  // The deep rings (kPair) take pages i and i+1 per barrier and refill the two
+  // stages computed before them (kAhead = kStages - 2); an odd last page is
+  // taken alone.
+  int i0 = 0;
+  if constexpr (Ring<NW>::kPair) {
+    for (; i0 + 1 < npg; i0 += 2) {
+      const int pg = pg_begin + i0;
+      // pages requested after page i0+1: up to kAhead-2, fewer near the end
+      stage_wait_behind<kDma, kAhead - 2>(min(kAhead - 2, npg - 2 - i0));
+      if (i0 + kAhead < npg)
+        stage_dma<NW, kNt>(stage[(i0 + kAhead) % kStages], wave, lane, pg + kAhead, bt, a.max_pages,
+                      a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
+      if (i0 + kAhead + 1 < npg)
+        stage_dma<NW, kNt>(stage[(i0 + kAhead + 1) % kStages], wave, lane, pg + kAhead + 1, bt,
+                      a.max_pages, a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
+      if (computes)
+        attend_pages2(st, qr, stage[i0 % kStages], stage[(i0 + 1) % kStages], lane,
+                      L - pg * kPage, L - (pg + 1) * kPage, a.scale_log2);
+    }
+  }
+  for (int i = i0; i < npg; ++i) {
     const int pg = pg_begin + i;
     // pages requested after page i: up to kAhead-1, fewer near the end
     stage_wait_behind<kDma, kAhead - 1>(min(kAhead - 1, npg - 1 - i));
     if (i + kAhead < npg)
-      stage_dma<NW>(stage[(i + kAhead) % kStages], wave, lane, pg + kAhead, bt, a.max_pages,
+      stage_dma<NW, kNt>(stage[(i + kAhead) % kStages], wave, lane, pg + kAhead, bt, a.max_pages,
                     a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
     if (computes) attend_page(st, qr, stage[i % kStages], lane, L - pg * kPage, a.scale_log2);
   }
@@ -1111,12 +1215,20 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   auto go = [&](auto kernel, int waves) {
     hipLaunchKernelGGL(kernel, grid, dim3(kWave * waves), 0, s, a);
   };
+  // Pages are certainly read more than once per launch when the block table
+  // holds more page references than there are pages (rows share pages); then
+  // the DMA keeps the default cache policy, otherwise it streams (kNt).
+  const bool nt = 1LL * B * ceil_div(max(max_prefix_len, 1), kPage) <= num_pages;
+  auto pick = [&](auto k_nt, auto k_cached, int waves) { nt ? go(k_nt, waves) : go(k_cached, waves); };
   if (pl.waves == 4)
-    rope ? go(k_window_attn_bf16<4, true>, 4) : go(k_window_attn_bf16<4, false>, 4);
+    rope ? pick(k_window_attn_bf16<4, true, true>, k_window_attn_bf16<4, true, false>, 4)
+         : pick(k_window_attn_bf16<4, false, true>, k_window_attn_bf16<4, false, false>, 4);
   else if (pl.waves == 8)
-    rope ? go(k_window_attn_bf16<8, true>, 8) : go(k_window_attn_bf16<8, false>, 8);
+    rope ? pick(k_window_attn_bf16<8, true, true>, k_window_attn_bf16<8, true, false>, 8)
+         : pick(k_window_attn_bf16<8, false, true>, k_window_attn_bf16<8, false, false>, 8);
   else
-    rope ? go(k_window_attn_bf16<16, true>, 16) : go(k_window_attn_bf16<16, false>, 16);
+    rope ? pick(k_window_attn_bf16<16, true, true>, k_window_attn_bf16<16, true, false>, 16)
+         : pick(k_window_attn_bf16<16, false, true>, k_window_attn_bf16<16, false, false>, 16);
   st = launch_status();
   if (st != WEDLM_OK || !pl.split) return st;
   const long long threads = groups * a.M * (kHeadDim / 4);

@@ -190,7 +190,9 @@ def config_latencies(args):
         print(f"[bench] {wl.name}", file=sys.stderr, flush=True)
         inp = make_step_inputs(wl)
         st, q, k, v, logits, mpl = upload_step_inputs(wl, inp, dev)
-        step = make_window_step(wl, inp, dev, mpl)
+        # the launch sequence of the streaming loop: the selection, state commit
+        # and next reorder run as one tail call after the entropy pass
+        step = make_window_step(wl, inp, dev, mpl, fused_tail=True)
         snap = st.snapshot()
         n = args.config_warmup + args.config_steps
         ev = [{lab: hev.create() for lab in labels} for _ in range(n)]

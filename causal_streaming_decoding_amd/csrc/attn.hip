@@ -10,11 +10,12 @@
 // head, key-range split); each of its wavefronts owns one 16-row tile of the
 // group's M = W*g query rows (physical row p, query head h of the group). The
 // group's key pages stream through an LDS ring, one page (16 keys, 8 KB of K
-// and V) per stage, filled by global->LDS DMA: 3 stages for 4-wave workgroups
-// (5 per CU), 7 for 8 waves and 15 for 16 waves (fewer per CU). One barrier
-// per page both publishes it and frees the stage computed before it, which is
-// refilled at once: all but one stage are in flight while the waves compute.
-// Each key byte is read from HBM once per workgroup.
+// and V) per stage, filled by global->LDS DMA: 4 stages for 4-wave workgroups
+// (4 per CU), 7 for 8 waves and 15 for 16 waves (fewer per CU). The waves take
+// two pages per barrier; the barrier both publishes them and frees the two
+// stages computed before them, which are refilled at once: all but two stages
+// are in flight while the waves compute. Each key byte is read from HBM once
+// per workgroup.
 //
 //   S^T (16 keys x 16 rows)  = K (16 x 128) . Q^T         v_mfma_f32_16x16x32_bf16
 //   O^T (16 dims x 16 rows) += V^T (x2) . [P_hi; P_lo]^T  v_mfma_f32_16x16x32_bf16
@@ -59,19 +60,21 @@ constexpr int kPageVecs = 512;      // 16-byte vectors of one page of one kv hea
 constexpr int kPartElems = 2048;    // bf16 elements of one 4 KB page part
 constexpr int kNumCUs = 256;        // MI355X compute units
 
-// LDS ring (one 8 KB page per stage) per workgroup size. A CU holds 5
-// workgroups of 4 waves (registers: 5 wavefronts per SIMD), 2 of 8 or 1 of 16
-// (LDS); the ring depth keeps 10-15 pages (80-120 KB) in flight per CU in
-// every case.
+// LDS ring (one 8 KB page per stage) per workgroup size. A CU holds 4
+// workgroups of 4 waves, 2 of 8 or 1 of 16 (4 wavefronts per SIMD in every
+// case); the ring keeps 8-13 pages (64-104 KB) in flight per CU while the
+// waves compute. Every ring advances two pages per barrier (attend_pages2):
+// against one page per barrier with 3 stages at 5 workgroups per CU, this
+// took the 36-layer streaming launch from 5.49 to 5.64 TB/s and the
+// dual-stream forward with 16-key blocks from 2.31 to 2.16 ms (5 workgroups
+// per CU with 4 stages, the RoPE frequencies kept in a free stage, and 3 per
+// CU with 6 stages both measured slower on those shapes).
 template <int NW>
 struct Ring {
-  // LDS caps the larger workgroups at 4 wavefronts per SIMD
-  static constexpr int kWavesPerSimd = NW == 4 ? 5 : 4;
-  static constexpr int kWgPerCu = NW == 4 ? 5 : (NW == 8 ? 2 : 1);
-  static constexpr int kStages = NW == 4 ? 3 : (NW == 8 ? 7 : 15);
-  // The deep rings advance two pages per barrier (attend_pages2): the waves
-  // compute two stages while the others are in flight.
-  static constexpr bool kPair = NW >= 8;
+  static constexpr int kWavesPerSimd = 4;
+  static constexpr int kWgPerCu = NW == 4 ? 4 : (NW == 8 ? 2 : 1);
+  static constexpr int kStages = NW == 4 ? 4 : (NW == 8 ? 7 : 15);
+  static constexpr bool kPair = true;
   static constexpr int kAhead = kStages - (kPair ? 2 : 1);  // pages in flight during compute
 };
 constexpr float kLog2e = 1.4426950408889634f;
@@ -1128,9 +1131,10 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
                        const int32_t* perm, const int32_t* pos, const void* k_cache,
                        const void* v_cache, const int32_t* block_table, const int32_t* prefix_len,
                        const int32_t* commit_run, void* out_phys, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       size_t workspace_bytes, int flags, void* stream) {
   int st = validate_attn(dtype, n_layers, B, W, Hq, Hkv, D, page_size, max_prefix_len);
   if (st != WEDLM_OK) return st;
+  if ((flags & ~WEDLM_ATTN_SHARED_PAGES) != 0) return WEDLM_ERR_INVALID;
   if (num_pages <= 0 || max_pages <= 0 || static_cast<long long>(max_pages) * page_size <
                                                static_cast<long long>(max_prefix_len))
     return WEDLM_ERR_INVALID;
@@ -1215,10 +1219,9 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   auto go = [&](auto kernel, int waves) {
     hipLaunchKernelGGL(kernel, grid, dim3(kWave * waves), 0, s, a);
   };
-  // Pages are certainly read more than once per launch when the block table
-  // holds more page references than there are pages (rows share pages); then
+  // Pages that several rows share are read more than once per launch: then
   // the DMA keeps the default cache policy, otherwise it streams (kNt).
-  const bool nt = 1LL * B * ceil_div(max(max_prefix_len, 1), kPage) <= num_pages;
+  const bool nt = (flags & WEDLM_ATTN_SHARED_PAGES) == 0;
   auto pick = [&](auto k_nt, auto k_cached, int waves) { nt ? go(k_nt, waves) : go(k_cached, waves); };
   if (pl.waves == 4)
     rope ? pick(k_window_attn_bf16<4, true, true>, k_window_attn_bf16<4, true, false>, 4)
@@ -1244,11 +1247,11 @@ extern "C" int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, 
                                  const void* v_phys, const void* k_cache, const void* v_cache,
                                  const int32_t* block_table, const int32_t* prefix_len,
                                  void* out_phys, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+                                 int flags, void* stream) {
   return launch_attn(false, dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages,
                      max_prefix_len, scale, 0.0, q_phys, k_phys, v_phys, nullptr, nullptr, k_cache,
                      v_cache, block_table, prefix_len, nullptr, out_phys, workspace,
-                     workspace_bytes, stream);
+                     workspace_bytes, flags, stream);
 }
 
 extern "C" int wedlm_window_attn_rope(int dtype, int n_layers, int B, int W, int Hq, int Hkv,
@@ -1258,9 +1261,9 @@ extern "C" int wedlm_window_attn_rope(int dtype, int n_layers, int B, int W, int
                                       const int32_t* pos, void* k_cache, void* v_cache,
                                       const int32_t* block_table, const int32_t* prefix_len,
                                       const int32_t* commit_run, void* out_phys, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+                                      size_t workspace_bytes, int flags, void* stream) {
   return launch_attn(true, dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages,
                      max_prefix_len, scale, theta, q, k, v, perm, pos, k_cache, v_cache,
                      block_table, prefix_len, commit_run, out_phys, workspace, workspace_bytes,
-                     stream);
+                     flags, stream);
 }

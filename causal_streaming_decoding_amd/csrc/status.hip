@@ -12,4 +12,4 @@ extern "C" const char* wedlm_status_string(int status) {
   }
 }
 
-extern "C" int wedlm_abi_version(void) { return (1 << 16) | 4; }
+extern "C" int wedlm_abi_version(void) { return (1 << 16) | 5; }

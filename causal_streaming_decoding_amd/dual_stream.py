@@ -93,7 +93,8 @@ class DualStreamAttention:
                                   self.num_pages, self.max_pages, self.N - self.Bk, self.scale,
                                   self.theta, q, k, v, o["perm"], o["pos"], self.k_cache,
                                   self.v_cache, self.block_table, self.prefix_len, None, out,
-                                  self.ws if self.ws_bytes else None, self.ws_bytes, stream)
+                                  self.ws if self.ws_bytes else None, self.ws_bytes,
+                                  flags=W_.WEDLM_ATTN_SHARED_PAGES, stream=stream)
 
     def forward(self, q_mem, k_mem, v_mem, q_pred, k_pred, v_pred, filled, stream=None):
         """q_* [S, N, Hq, D], k_* / v_* [S, N, Hkv, D] (slot order, before RoPE),

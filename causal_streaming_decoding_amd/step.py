@@ -130,7 +130,7 @@ class WindowStep:
                              self.page_size, self.num_pages, self.max_pages, mpl, self.scale,
                              self.q_phys, self.k_phys, self.v_phys, st.k_cache, st.v_cache,
                              st.block_table, st.prefix_len, self.out_phys, self.attn_ws,
-                             self.attn_ws_bytes, stream)
+                             self.attn_ws_bytes, stream=stream)
 
     def attn_rope(self, st, q, k, v, max_prefix_len=None, stream=None, append=True):
         """Attention with RoPE fused; ``append`` also writes the rows the commit
@@ -141,7 +141,7 @@ class WindowStep:
                                   self.scale, self.theta, q, k, v, self.perm, self.pos,
                                   st.k_cache, st.v_cache, st.block_table, st.prefix_len,
                                   self.run_len if append else None, self.out_phys, self.attn_ws,
-                                  self.attn_ws_bytes, stream)
+                                  self.attn_ws_bytes, stream=stream)
 
     def entropy_select(self, st, logits, stream=None):
         W_.wedlm_entropy_select(self.dt, self.B, self.W, self.V, logits, st.filled, self.lam,

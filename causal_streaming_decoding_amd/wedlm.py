@@ -20,6 +20,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "wedlm.h")
 
 WEDLM_F32 = 0
 WEDLM_BF16 = 1
+WEDLM_ATTN_SHARED_PAGES = 1  # attention flag: rows of the block table share pages
 MAX_WINDOW = 64
 
 _c_int, _c_size, _c_float, _c_double, _p = (ctypes.c_int, ctypes.c_size_t, ctypes.c_float,
@@ -34,13 +35,13 @@ _SIGNATURES = {
     "wedlm_rope_logical": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_double,
                                     _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "wedlm_window_attn_workspace_size": (_c_size, [_c_int] * 9),
-    "wedlm_window_attn": (_c_int, [_c_int] * 11 + [_c_float] + [_p] * 9 + [_c_size, _p]),
+    "wedlm_window_attn": (_c_int, [_c_int] * 11 + [_c_float] + [_p] * 9 + [_c_size, _c_int, _p]),
     "wedlm_entropy_select_workspace_size": (_c_size, [_c_int] * 4),
     "wedlm_entropy_select": (_c_int, [_c_int] * 4 + [_p, _p, _c_float, _c_float, _c_int] + [_p] * 5
                              + [_c_size, _p]),
     "wedlm_commit_prefix": (_c_int, [_c_int] * 9 + [_p] * 13 + [ctypes.c_int32, _p]),
     "wedlm_window_attn_rope": (_c_int, [_c_int] * 11 + [_c_float, _c_double] + [_p] * 12
-                               + [_c_size, _p]),
+                               + [_c_size, _c_int, _p]),
     "wedlm_commit_prefix_rope": (_c_int, [_c_int] * 9 + [_c_double] + [_p] * 13
                                  + [ctypes.c_int32, _p]),
     "wedlm_lm_head_packed_size": (_c_size, [_c_int] * 3),
@@ -159,12 +160,12 @@ def wedlm_window_attn_workspace_size(dtype, n_layers, B, W, Hq, Hkv, D, page_siz
 
 def wedlm_window_attn(dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages,
                       max_prefix_len, scale, q_phys, k_phys, v_phys, k_cache, v_cache, block_table,
-                      prefix_len, out_phys, workspace, workspace_bytes, stream=None):
+                      prefix_len, out_phys, workspace, workspace_bytes, flags=0, stream=None):
     _check("wedlm_window_attn", lib().wedlm_window_attn(
         dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages, max_prefix_len,
         float(scale), _ptr(q_phys), _ptr(k_phys), _ptr(v_phys), _ptr(k_cache), _ptr(v_cache),
         _ptr(block_table), _ptr(prefix_len), _ptr(out_phys), _ptr(workspace), workspace_bytes,
-        _stream(stream)))
+        flags, _stream(stream)))
 
 
 def wedlm_entropy_select_workspace_size(dtype, B, W, V):
@@ -214,12 +215,12 @@ def wedlm_commit_prefix(dtype, n_layers, B, W, Hkv, D, page_size, num_pages, max
 def wedlm_window_attn_rope(dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages,
                            max_prefix_len, scale, theta, q, k, v, perm, pos, k_cache, v_cache,
                            block_table, prefix_len, commit_run, out_phys, workspace,
-                           workspace_bytes, stream=None):
+                           workspace_bytes, flags=0, stream=None):
     _check("wedlm_window_attn_rope", lib().wedlm_window_attn_rope(
         dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages, max_prefix_len,
         float(scale), float(theta), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(pos),
         _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(prefix_len), _ptr(commit_run),
-        _ptr(out_phys), _ptr(workspace), workspace_bytes, _stream(stream)))
+        _ptr(out_phys), _ptr(workspace), workspace_bytes, flags, _stream(stream)))
 
 
 def wedlm_commit_prefix_rope(dtype, n_layers, B, W, Hkv, D, page_size, num_pages, max_pages, theta,

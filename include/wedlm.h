@@ -77,6 +77,11 @@ enum wedlm_status {
 /* Element types. */
 enum wedlm_dtype { WEDLM_F32 = 0, WEDLM_BF16 = 1 };
 
+/* flags of wedlm_window_attn / wedlm_window_attn_rope */
+enum wedlm_attn_flags {
+  WEDLM_ATTN_SHARED_PAGES = 1 /* rows of block_table reference the same pages */
+};
+
 /* Largest window the kernels accept (one 64-lane wavefront per sequence). */
 #define WEDLM_MAX_WINDOW 64
 
@@ -180,12 +185,21 @@ size_t wedlm_window_attn_workspace_size(int dtype, int n_layers, int B, int W, i
  * D == 128; f32 needs D even and <= 256. workspace: at least
  * wedlm_window_attn_workspace_size(...) bytes (may be NULL if that is 0).
  * Block-table entries are clamped to [0, num_pages).
+ * flags: 0 when every page is referenced by one row of block_table (each
+ * sequence owns its pages, as in decoding): each page is then read once per
+ * launch and the bf16 path loads it with the non-temporal cache hint.
+ * WEDLM_ATTN_SHARED_PAGES when rows share pages (a shared prefix; the
+ * dual-stream forward, where every block of a sample reads the sample's
+ * memory rows): the loads keep the default cache policy so that the re-reads
+ * hit in the caches. Results are identical either way; any other bit is
+ * WEDLM_ERR_INVALID.
  */
 int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D, int page_size,
                       int num_pages, int max_pages, int max_prefix_len, float scale,
                       const void* q_phys, const void* k_phys, const void* v_phys, const void* k_cache,
                       const void* v_cache, const int32_t* block_table, const int32_t* prefix_len,
-                      void* out_phys, void* workspace, size_t workspace_bytes, void* stream);
+                      void* out_phys, void* workspace, size_t workspace_bytes, int flags,
+                      void* stream);
 
 /*
  * wedlm_window_attn_rope - wedlm_window_attn with the RoPE step fused into its
@@ -200,7 +214,7 @@ int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv, in
  * evaluated in fp32 (error ~1e-7), the rotation done in fp32 and rounded once
  * to the element type before the products, as with wedlm_rope_logical.
  * No q_phys / k_phys / v_phys is written. All other arguments, layouts, sizes,
- * workspace and errors are those of wedlm_window_attn; theta > 0.
+ * workspace, flags and errors are those of wedlm_window_attn; theta > 0.
  *
  * commit_run (device [B], may be NULL): when given, the call also performs the
  * cache half of the commit (hyper.ai summary, "Method": the leftmost filled
@@ -219,7 +233,7 @@ int wedlm_window_attn_rope(int dtype, int n_layers, int B, int W, int Hq, int Hk
                            const int32_t* perm, const int32_t* pos, void* k_cache, void* v_cache,
                            const int32_t* block_table, const int32_t* prefix_len,
                            const int32_t* commit_run, void* out_phys, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           size_t workspace_bytes, int flags, void* stream);
 
 /* Bytes of workspace wedlm_entropy_select needs (per-chunk partial reductions). */
 size_t wedlm_entropy_select_workspace_size(int dtype, int B, int W, int V);

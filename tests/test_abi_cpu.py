@@ -31,7 +31,8 @@ def test_status_strings_and_version():
     assert "unsupported" in W.wedlm_status_string(-2)
     assert "workspace" in W.wedlm_status_string(-3)
     assert W.wedlm_abi_version() >> 16 == 1
-    assert W.wedlm_abi_version() & 0xffff >= 4  # fused RoPE, LM head, commit rules, step tail
+    assert W.wedlm_abi_version() & 0xffff >= 5  # fused RoPE, LM head, commit rules, step tail,
+    #                                               attention flags
 
 
 def _raw(name, *args):
@@ -63,8 +64,10 @@ def test_rope_validation():
 def test_attn_validation_and_workspace():
     # bf16 needs D = 128; page size 16 only; rows W*g <= 256
     assert W.wedlm_window_attn_workspace_size(1, 1, 1, 16, 32, 8, 64, 16, 2048) == 0
-    base = [1, 1, 4, 16, 32, 8, 128, 16, 8196, 2049, 32768, 0.088] + [1] * 9 + [0, None]
+    base = [1, 1, 4, 16, 32, 8, 128, 16, 8196, 2049, 32768, 0.088] + [1] * 9 + [0, 0, None]
     assert _raw("wedlm_window_attn", *base) == -3        # split planned, no workspace
+    a = list(base); a[-2] = 2
+    assert _raw("wedlm_window_attn", *a) == -1           # unknown flag bit
     need = W.wedlm_window_attn_workspace_size(1, 1, 4, 16, 32, 8, 128, 16, 32768)
     assert need > 0
     a = list(base); a[6] = 64
@@ -81,8 +84,10 @@ def test_attn_validation_and_workspace():
 
 def test_fused_rope_entry_points_validate():
     # wedlm_window_attn_rope: same checks as wedlm_window_attn plus theta, perm, pos
-    base = [1, 1, 4, 16, 32, 8, 128, 16, 8196, 2049, 32768, 0.088, 1e6] + [1] * 12 + [0, None]
+    base = [1, 1, 4, 16, 32, 8, 128, 16, 8196, 2049, 32768, 0.088, 1e6] + [1] * 12 + [0, 0, None]
     assert _raw("wedlm_window_attn_rope", *base) == -3    # split planned, no workspace
+    a = list(base); a[-2] = 1 << 5
+    assert _raw("wedlm_window_attn_rope", *a) == -1       # unknown flag bit
     a = list(base); a[12] = 0.0
     assert _raw("wedlm_window_attn_rope", *a) == -1       # theta must be > 0
     a = list(base); a[16] = None

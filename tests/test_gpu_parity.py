@@ -154,3 +154,31 @@ def test_invalid_host_arguments_raise():
     u = torch.zeros(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(W.WedlmError):
         W.wedlm_window_reorder(1, 65, u, t, t, t, t, t, t)
+
+
+@pytest.mark.parametrize("wl", [
+    _variant(WL.QWEN3_8B_BS1, name="flags_nw4", B=3, V=2048, prefix=("uniform", 100, 900)),
+    _variant(WL.QWEN25_7B_RAGGED, name="flags_nw16", B=3, V=2048, prefix=("uniform", 100, 900)),
+])
+def test_cache_policy_flag_bitwise_same(wl):
+    """The shared-pages flag only changes the cache hint of the page loads:
+    outputs with and without it are bitwise equal."""
+    from causal_streaming_decoding_amd import wedlm as W_
+    from causal_streaming_decoding_amd.step import make_window_step, upload_step_inputs
+
+    print(f"[parity] {wl.name}", flush=True)
+    inp = make_step_inputs(wl)
+    st, q, k, v, _, mpl = upload_step_inputs(wl, inp, "cuda:0")
+    step = make_window_step(wl, inp, "cuda:0", mpl)
+    step.reorder(st, None)
+    outs = []
+    for flags in (0, W_.WEDLM_ATTN_SHARED_PAGES):
+        out = torch.empty_like(step.out_phys)
+        W_.wedlm_window_attn_rope(step.dt, step.n_layers, step.B, step.W, step.Hq, step.Hkv,
+                                  step.D, step.page_size, step.num_pages, step.max_pages, mpl,
+                                  step.scale, step.theta, q, k, v, step.perm, step.pos,
+                                  st.k_cache, st.v_cache, st.block_table, st.prefix_len, None,
+                                  out, step.attn_ws, step.attn_ws_bytes, flags=flags)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])

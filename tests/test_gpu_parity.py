@@ -104,6 +104,9 @@ def _variant(base, **kw):
     # 4-wave workgroups, 40 sequences sharing 160 workgroups per kv head
     ("split_plan_many_seqs", _variant(WL.QWEN3_8B_BS1, name="edge_split_many", B=40,
                                       prefix=("uniform", 0, 1500), V=1024)),
+    # more sequences than one wavefront's lanes: the plan scans them in chunks
+    ("split_plan_100_seqs", _variant(WL.QWEN3_8B_BS1, name="edge_split_100", B=100,
+                                     prefix=("uniform", 0, 300), V=512)),
 ])
 def test_edge_cases(name, wl):
     _check(wl)

@@ -40,8 +40,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="qwen3_8b_36L_bs16_L1024_W16_stream256")
-    ap.add_argument("--cpu-baseline-steps", type=int, default=1,
-                    help="window steps of the oracle timed on the host (0 disables)")
+    ap.add_argument("--cpu-baseline-steps", type=int, default=2,
+                    help="window steps of the oracle timed on the host (0 disables; one step of "
+                         "the streaming workload is ~8 s of fp64 work on 16 host cores)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--all-configs", action="store_true",

@@ -7,11 +7,12 @@
 // prior art; this kernel is written for CDNA4 from scratch.
 //
 // bf16 path (D = 128, page P = 16). One workgroup per (layer, sequence, kv
-// head, key-range split); each of its wavefronts owns one 16-row tile of the
-// group's M = W*g query rows (physical row p, query head h of the group). The
+// head, key-range split) - two when the group has more than 8 row tiles, each
+// taking half of the rows; each wavefront owns one 16-row tile of the group's
+// M = W*g query rows (physical row p, query head h of the group). The
 // group's key pages stream through an LDS ring, one page (16 keys, 8 KB of K
 // and V) per stage, filled by global->LDS DMA: 4 stages for 4-wave workgroups
-// (4 per CU), 7 for 8 waves and 15 for 16 waves (fewer per CU). The waves take
+// (4 per CU) and 7 for 8 waves (2 per CU). The waves take
 // two pages per barrier; the barrier both publishes them and frees the two
 // stages computed before them, which are refilled at once: all but two stages
 // are in flight while the waves compute. Each key byte is read from HBM once
@@ -55,15 +56,15 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
-constexpr int kMaxRows = 256;       // M = W*g rows: at most 16 wavefronts
+constexpr int kMaxRows = 256;       // M = W*g rows: at most two 8-wave workgroups
 constexpr int kPageVecs = 512;      // 16-byte vectors of one page of one kv head (K 4 KB + V 4 KB)
 constexpr int kPartElems = 2048;    // bf16 elements of one 4 KB page part
 constexpr int kNumCUs = 256;        // MI355X compute units
+constexpr int kNumXcds = 8;         // MI355X: 8 XCDs of 32 CUs, workgroups dealt round-robin
 
 // LDS ring (one 8 KB page per stage) per workgroup size. A CU holds 4
-// workgroups of 4 waves, 2 of 8 or 1 of 16 (4 wavefronts per SIMD in every
-// case); the ring keeps 8-13 pages (64-104 KB) in flight per CU while the
-// waves compute. Every ring advances two pages per barrier (attend_pages2):
+// workgroups of 4 waves or 2 of 8 (4 wavefronts per SIMD either way); the
+// ring keeps 8-10 pages (64-80 KB) in flight per CU while the waves compute. Every ring advances two pages per barrier (attend_pages2):
 // against one page per barrier with 3 stages at 5 workgroups per CU, this
 // took the 36-layer streaming launch from 5.49 to 5.64 TB/s and the
 // dual-stream forward with 16-key blocks from 2.31 to 2.16 ms (5 workgroups
@@ -71,9 +72,10 @@ constexpr int kNumCUs = 256;        // MI355X compute units
 // CU with 6 stages both measured slower on those shapes).
 template <int NW>
 struct Ring {
+  static_assert(NW == 4 || NW == 8, "4- or 8-wave workgroups");
   static constexpr int kWavesPerSimd = 4;
-  static constexpr int kWgPerCu = NW == 4 ? 4 : (NW == 8 ? 2 : 1);
-  static constexpr int kStages = NW == 4 ? 4 : (NW == 8 ? 7 : 15);
+  static constexpr int kWgPerCu = NW == 4 ? 4 : 2;
+  static constexpr int kStages = NW == 4 ? 4 : 7;
   static constexpr bool kPair = true;
   static constexpr int kAhead = kStages - (kPair ? 2 : 1);  // pages in flight during compute
 };
@@ -96,7 +98,10 @@ struct AttnArgs {
   int2* ws_plan;       // [groups]: first slot and number of splits of each group
   int B, W, Hq, Hkv, g, M;
   int num_pages, max_pages, max_prefix_len;
-  int cols;            // workgroups per (layer, kv head): B, or S > B when split
+  int cols;            // work units per (layer, kv head): B, or S > B when split
+  int parts;           // workgroups per work unit, each taking part_rows of the M rows
+  int part_rows;
+  long long units;     // n_layers * Hkv * cols
   int split;           // key ranges split across workgroups (partials + combine)
   int min_pages;       // no split takes fewer pages than this (unless it is all there is)
   long long cache_layer_stride;  // elements per layer of one cache
@@ -330,8 +335,8 @@ __device__ __forceinline__ void attend_pages2(RowState& st, const bf16x8 (&qr)[4
 // Asynchronous page staging: global -> LDS DMA (global_load_lds_dwordx4).
 // Each instruction moves 64 lanes x 16 B = 1 KB: lane l's 16 bytes land at
 // M0 + 16 l in LDS. A stage is 512 vectors (K then V of one page); wavefront w
-// issues instructions for vectors (i*NW + w)*64 .. +63, and wavefronts past the
-// eighth issue none when NW = 16.
+// issues instructions for vectors (i*NW + w)*64 .. +63 (two each for 4 waves,
+// one each for 8).
 // The DMA is issued from inline asm so that the compiler does not add its own
 // conservative vmcnt waits before every LDS read of the ring; the waits are
 // explicit (stage_wait_barrier) and counted per thread in issue order.
@@ -587,6 +592,16 @@ k_window_attn_bf16(AttnArgs a) {
   // only the x-th 4 KB of every page record, which leaves HBM channels unevenly
   // loaded when pages are allocated in order (measured 4.5 against 5.2 TB/s).
   int bid = blockIdx.x;
+  int part = 0;
+  if (a.parts > 1) {
+    // the row parts of one work unit are kNumXcds ids apart: same XCD, dispatched
+    // together, so the second reads the unit's pages from that XCD's L2
+    const int xcd = bid % kNumXcds;
+    const int rest = bid / kNumXcds;
+    part = rest % a.parts;
+    bid = (rest / a.parts) * kNumXcds + xcd;
+    if (bid >= a.units) return;  // padding of the last XCD round
+  }
   const int j = bid % a.cols;  // sequence, or (sequence, split) in split mode
   bid /= a.cols;
   const int kvh = bid % a.Hkv;
@@ -608,7 +623,7 @@ k_window_attn_bf16(AttnArgs a) {
   const int pg_begin = a.split ? min(npages, split * K) : 0;
   const int pg_end = a.split ? min(npages, pg_begin + K) : npages;
   const bool with_window = split == n_split - 1;
-  if (a.split && split == 0 && tid == 0)
+  if (a.split && split == 0 && part == 0 && tid == 0)
     a.ws_plan[group] = make_int2(static_cast<int>(slot), n_split);
 
   // ---- this wave's 16 query rows (B operand of S^T = K Q^T) ---------------
@@ -616,8 +631,9 @@ k_window_attn_bf16(AttnArgs a) {
   // an explicit vmcnt that lets those DMAs stay in flight. (Rows past M read
   // row 0 of the group - valid memory - and are never stored.)
   const size_t lb = static_cast<size_t>(layer) * a.B + b;
-  const int row = wave * 16 + col;
-  const bool row_ok = row < a.M;
+  const int row0 = part * a.part_rows;  // first row of this workgroup's part
+  const int row = row0 + wave * 16 + col;
+  const bool row_ok = row < a.M && wave * 16 < a.part_rows;
   const int prow = row / a.g, hh = row % a.g;
   int qslot = row_ok ? prow : 0;  // window row holding this query row
   int qpos = 0;
@@ -647,7 +663,8 @@ k_window_attn_bf16(AttnArgs a) {
   st.l = 0.f;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bool computes = wave * 16 < a.M;  // waves past the last row tile only move data
+  // waves past the part's last row tile only move data
+  const bool computes = wave * 16 < a.part_rows && row0 + wave * 16 < a.M;
 
   // ---- paged prefix: pages through the LDS ring ----------------------------
   const int32_t* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
@@ -662,7 +679,7 @@ k_window_attn_bf16(AttnArgs a) {
       stage_dma<NW, kNt>(stage[j], wave, lane, pg_begin + j, bt, a.max_pages, a.num_pages, a.Hkv, kvh,
                     kc_layer, vc_layer);
   // Retire the query loads: only the kAhead stages issued after them may
-  // remain. Waves that issue no DMA (NW = 16), and every wave when the split
+  // remain. Waves that issue no DMA (none with 4 or 8 waves), and every wave when the split
   // has fewer than kAhead pages, wait for everything first; that asm has no
   // register operands, so nothing touches the query registers before the
   // tied wait below.
@@ -793,7 +810,8 @@ k_window_attn_bf16(AttnArgs a) {
       }
       __syncthreads();
       if constexpr (kRope) {
-        if (a.commit_run != nullptr) append_committed(a, sg, bt, b, layer, kvh, kw0, tid, kWave * NW);
+        if (a.commit_run != nullptr && part == 0)
+          append_committed(a, sg, bt, b, layer, kvh, kw0, tid, kWave * NW);
       }
       if (computes) {
         const int lim = min(a.W, prow + 1) - kw0;  // window key kw0 + kk visible iff kk < lim
@@ -1049,7 +1067,9 @@ k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
 
 // ---- launch planning -------------------------------------------------------
 struct AttnPlan {
-  int cols;   // workgroups per (layer, kv head)
+  int cols;   // work units per (layer, kv head)
+  int parts;  // workgroups per work unit (row parts)
+  int part_rows;
   bool split;
   int min_pages;
   int waves;  // wavefronts per workgroup: 4, 8 or 16 (one 16-row tile each)
@@ -1061,16 +1081,21 @@ static AttnPlan plan_bf16(int n_layers, int B, int W, int Hq, int Hkv, int max_p
   const int g = Hq / Hkv;
   const int M = W * g;
   const int tiles = ceil_div(M, 16);
-  pl.waves = tiles <= 4 ? 4 : (tiles <= 8 ? 8 : 16);
+  // more than 8 row tiles: two 8-wave workgroups per work unit, each with half
+  // of the rows (one 16-wave workgroup per CU measured slower: 3.13 against
+  // 2.65 ms for the dual-stream forward with 64-key blocks, equal for the
+  // g = 7, W = 32 decoding shape)
+  pl.waves = tiles <= 4 ? 4 : 8;
+  pl.parts = tiles > 8 ? 2 : 1;
+  pl.part_rows = ceil_div(tiles, pl.parts) * 16;
   const long long groups = 1LL * n_layers * B * Hkv;
   const long long columns = 1LL * n_layers * Hkv;
   // aim for one full round of workgroups (every CU holding as many as its
   // registers allow) but keep >= 4 pages per split (8 for the deeper rings);
   // how the column's workgroups are shared out follows the live prefix
   // lengths on the device (find_split)
-  const int wg_per_cu = pl.waves == 4 ? Ring<4>::kWgPerCu
-                                      : (pl.waves == 8 ? Ring<8>::kWgPerCu : Ring<16>::kWgPerCu);
-  const long long target = 1LL * kNumCUs * wg_per_cu;
+  const int wg_per_cu = pl.waves == 4 ? Ring<4>::kWgPerCu : Ring<8>::kWgPerCu;
+  const long long target = 1LL * kNumCUs * wg_per_cu / pl.parts;  // work units per round
   pl.min_pages = pl.waves == 4 ? 4 : 8;
   const int npages = ceil_div(max(max_prefix_len, 1), kPage);
   pl.cols = B;
@@ -1202,6 +1227,9 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   a.max_pages = max_pages;
   a.max_prefix_len = max_prefix_len;
   a.cols = pl.cols;
+  a.parts = pl.parts;
+  a.part_rows = pl.part_rows;
+  a.units = 1LL * n_layers * Hkv * pl.cols;
   a.split = pl.split ? 1 : 0;
   a.min_pages = pl.min_pages;
   a.cache_layer_stride = cache_layer_stride;
@@ -1213,7 +1241,8 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   a.kc_w = commit_run ? static_cast<uint16_t*>(const_cast<void*>(k_cache)) : nullptr;
   a.vc_w = commit_run ? static_cast<uint16_t*>(const_cast<void*>(v_cache)) : nullptr;
   const long long groups = 1LL * n_layers * B * Hkv;
-  const long long blocks = 1LL * n_layers * Hkv * pl.cols;
+  const long long blocks =
+      pl.parts == 1 ? a.units : (a.units + kNumXcds - 1) / kNumXcds * kNumXcds * pl.parts;
   if (blocks > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
   const dim3 grid(static_cast<unsigned>(blocks));
   auto go = [&](auto kernel, int waves) {
@@ -1226,12 +1255,9 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   if (pl.waves == 4)
     rope ? pick(k_window_attn_bf16<4, true, true>, k_window_attn_bf16<4, true, false>, 4)
          : pick(k_window_attn_bf16<4, false, true>, k_window_attn_bf16<4, false, false>, 4);
-  else if (pl.waves == 8)
+  else
     rope ? pick(k_window_attn_bf16<8, true, true>, k_window_attn_bf16<8, true, false>, 8)
          : pick(k_window_attn_bf16<8, false, true>, k_window_attn_bf16<8, false, false>, 8);
-  else
-    rope ? pick(k_window_attn_bf16<16, true, true>, k_window_attn_bf16<16, true, false>, 16)
-         : pick(k_window_attn_bf16<16, false, true>, k_window_attn_bf16<16, false, false>, 16);
   st = launch_status();
   if (st != WEDLM_OK || !pl.split) return st;
   const long long threads = groups * a.M * (kHeadDim / 4);

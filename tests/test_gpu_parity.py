@@ -92,8 +92,8 @@ def _variant(base, **kw):
     ("nw8_many_groups", _variant(WL.QWEN3_8B_STREAM, name="edge_nw8_layers", n_layers=8, B=8, W=32,
                                  V=2048, fill=("frac", 0.0, 1.0), prefix=("uniform", 17, 900),
                                  steps=1)),
-    # 16-wave workgroups with fewer pages per split than the 15-stage ring holds
-    ("nw16_short_splits", _variant(WL.QWEN25_7B_RAGGED, name="edge_nw16_short", B=2,
+    # 224 rows: two 8-wave row parts per work unit, splits shorter than the 7-stage ring
+    ("rowparts_short_splits", _variant(WL.QWEN25_7B_RAGGED, name="edge_rowparts_short", B=2,
                                    prefix=("uniform", 40, 130), V=2048)),
     # split plan over very uneven prefixes: empty, one key, one page, a long one
     ("split_plan_extremes", _variant(WL.QWEN25_7B_RAGGED, name="edge_split_extremes", B=6,
@@ -161,11 +161,12 @@ def test_invalid_host_arguments_raise():
 
 @pytest.mark.parametrize("wl", [
     _variant(WL.QWEN3_8B_BS1, name="flags_nw4", B=3, V=2048, prefix=("uniform", 100, 900)),
-    _variant(WL.QWEN25_7B_RAGGED, name="flags_nw16", B=3, V=2048, prefix=("uniform", 100, 900)),
+    _variant(WL.QWEN25_7B_RAGGED, name="flags_rowparts", B=3, V=2048, prefix=("uniform", 100, 900)),
 ])
 def test_cache_policy_flag_bitwise_same(wl):
     """The shared-pages flag only changes the cache hint of the page loads:
-    outputs with and without it are bitwise equal."""
+    outputs with and without it are bitwise equal (4-wave workgroups, and two
+    8-wave row parts per work unit)."""
     from causal_streaming_decoding_amd import wedlm as W_
     from causal_streaming_decoding_amd.step import make_window_step, upload_step_inputs
 

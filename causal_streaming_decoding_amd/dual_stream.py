@@ -16,7 +16,11 @@ the library's calls with one "sequence" per (sample, block):
      memory block's rotated keys and values into a paged cache (one 16-token
      page list per sample, shared by all its blocks' block-table rows);
   2. wedlm_window_attn_rope over the memory blocks: causal attention of the
-     memory stream (block j over the memory prefix plus itself);
+     memory stream (block j over the memory prefix plus itself). The memory
+     stream's attention is plain causal attention over the whole sequence, so
+     its result does not depend on the block size: it runs in 16-key windows
+     whatever Bk is (the fastest window shape of the attention kernel), and
+     its output, in identity order, has the same layout as Bk-key blocks;
   3. wedlm_window_reorder of the prediction stream's observed flags, then
      wedlm_window_attn_rope over the prediction blocks against the same
      memory prefix.
@@ -33,12 +37,37 @@ from . import wedlm as W_
 PAGE = 16
 
 
+class _Blocks:
+    """One stream's windows: S samples of N positions in blocks of W, block j
+    at logical positions j*W .. over a prefix of the sample's first j*W
+    memory positions (one window per (sample, block))."""
+
+    def __init__(self, S, N, W, Hq, Hkv, D, dt, dtype, device, block_pages):
+        i32 = dict(dtype=torch.int32, device=device)
+        self.W, self.nb = W, N // W
+        self.Bp = S * self.nb
+        j = torch.arange(self.nb, **i32)
+        self.prefix_len = (j * W).repeat(S).contiguous()
+        self.block_table = block_pages.expand(S, self.nb, block_pages.shape[-1]).reshape(
+            self.Bp, -1).contiguous()
+        self.all_obs = torch.ones((self.Bp, W), dtype=torch.uint8, device=device)
+        self.order = {k: torch.empty(sh, **i32) for k, sh in (
+            ("perm", (self.Bp, W)), ("inv", (self.Bp, W)), ("pos", (self.Bp, W)),
+            ("n_obs", (self.Bp,)), ("run", (self.Bp,)))}
+        self.out = torch.empty((1, self.Bp, W, Hq, D), dtype=dtype, device=device)
+        self.ws_bytes = W_.wedlm_window_attn_workspace_size(dt, 1, self.Bp, W, Hq, Hkv, D, PAGE,
+                                                            N - W)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
+
+
 class DualStreamAttention:
     """Buffers and launches of one dual-stream attention layer for fixed shapes.
 
     S samples of N positions, blocks of Bk (N % Bk == 0, N % 16 == 0), bf16
     (D = 128) or f32 projections [S, N, H, D] of both streams.
     """
+
+    MEMORY_WINDOW = 16
 
     def __init__(self, S, N, Bk, Hq, Hkv, D, theta, dtype, device, scale=None):
         if N % Bk or N % PAGE or not (1 <= Bk <= W_.MAX_WINDOW):
@@ -47,53 +76,48 @@ class DualStreamAttention:
         self.theta = theta
         self.dt = W_.dtype_code(dtype)
         self.scale = D ** -0.5 if scale is None else scale
-        self.nb = N // Bk
-        self.Bp = S * self.nb                      # one window per (sample, block)
         self.max_pages = N // PAGE
         self.num_pages = S * self.max_pages
         i32 = dict(dtype=torch.int32, device=device)
-        j = torch.arange(self.nb, **i32)
-        self.prefix_len = (j * Bk).repeat(S).contiguous()
+        # one page list per sample, shared by the block-table rows of all its blocks
         pages = torch.arange(self.num_pages, **i32).view(S, 1, self.max_pages)
-        self.block_table = pages.expand(S, self.nb, self.max_pages).reshape(self.Bp, -1).contiguous()
+        self.mem_blocks = _Blocks(S, N, self.MEMORY_WINDOW, Hq, Hkv, D, self.dt, dtype, device,
+                                  pages)
+        self.pred_blocks = _Blocks(S, N, Bk, Hq, Hkv, D, self.dt, dtype, device, pages)
+        self.mem, self.pred = self.mem_blocks.order, self.pred_blocks.order
         X = 16 // torch.tensor([], dtype=dtype).element_size()
         self.k_cache = torch.empty((1, self.num_pages, Hkv, D // X, PAGE, X), dtype=dtype,
                                    device=device)
         self.v_cache = torch.empty((1, self.num_pages, Hkv, D, PAGE), dtype=dtype, device=device)
-        self.all_obs = torch.ones((self.Bp, Bk), dtype=torch.uint8, device=device)
+        # scratch window state for the commit call over the memory windows (its
+        # state half is not used)
+        m = self.mem_blocks
+        self.tokens = torch.empty((m.Bp, m.W), **i32)
+        self.filled_scratch = torch.empty((m.Bp, m.W), dtype=torch.uint8, device=device)
+        self.len_scratch = torch.empty((m.Bp,), **i32)
+        self.commit_len = torch.empty((m.Bp,), **i32)
+        self.cache_slot = torch.empty((m.Bp, m.W), **i32)
+        self.selected = torch.zeros((m.Bp, m.W), dtype=torch.uint8, device=device)
+        self.argmax = torch.zeros((m.Bp, m.W), **i32)
+        # the memory stream's output in Bk-key blocks: the same memory (identity order)
+        self.out_mem = m.out.view(1, S * N // Bk, Bk, Hq, D)
+        self.out_pred = self.pred_blocks.out
 
-        def order():
-            return {k: torch.empty(s, **i32) for k, s in (
-                ("perm", (self.Bp, Bk)), ("inv", (self.Bp, Bk)), ("pos", (self.Bp, Bk)),
-                ("n_obs", (self.Bp,)), ("run", (self.Bp,)))}
-        self.mem, self.pred = order(), order()
-        # scratch window state for the commit call (its state half is not used)
-        self.tokens = torch.empty((self.Bp, Bk), **i32)
-        self.filled_scratch = torch.empty((self.Bp, Bk), dtype=torch.uint8, device=device)
-        self.len_scratch = torch.empty((self.Bp,), **i32)
-        self.commit_len = torch.empty((self.Bp,), **i32)
-        self.cache_slot = torch.empty((self.Bp, Bk), **i32)
-        self.selected = torch.zeros((self.Bp, Bk), dtype=torch.uint8, device=device)
-        self.argmax = torch.zeros((self.Bp, Bk), **i32)
-        self.out_mem = torch.empty((1, self.Bp, Bk, Hq, D), dtype=dtype, device=device)
-        self.out_pred = torch.empty_like(self.out_mem)
-        self.ws_bytes = W_.wedlm_window_attn_workspace_size(self.dt, 1, self.Bp, Bk, Hq, Hkv, D,
-                                                            PAGE, N - Bk)
-        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=device)
+    def _view(self, x, H, blk):
+        return x.reshape(1, blk.Bp, blk.W, H, self.D)
 
-    def _view(self, x, H):
-        return x.reshape(1, self.Bp, self.Bk, H, self.D)
-
-    def _reorder(self, filled, o, stream):
-        W_.wedlm_window_reorder(self.Bp, self.Bk, filled, self.prefix_len, o["perm"], o["inv"],
+    def _reorder(self, filled, blk, stream):
+        o = blk.order
+        W_.wedlm_window_reorder(blk.Bp, blk.W, filled, blk.prefix_len, o["perm"], o["inv"],
                                 o["pos"], o["n_obs"], o["run"], stream)
 
-    def _attend(self, q, k, v, o, out, stream):
-        W_.wedlm_window_attn_rope(self.dt, 1, self.Bp, self.Bk, self.Hq, self.Hkv, self.D, PAGE,
-                                  self.num_pages, self.max_pages, self.N - self.Bk, self.scale,
+    def _attend(self, q, k, v, blk, stream):
+        o = blk.order
+        W_.wedlm_window_attn_rope(self.dt, 1, blk.Bp, blk.W, self.Hq, self.Hkv, self.D, PAGE,
+                                  self.num_pages, self.max_pages, self.N - blk.W, self.scale,
                                   self.theta, q, k, v, o["perm"], o["pos"], self.k_cache,
-                                  self.v_cache, self.block_table, self.prefix_len, None, out,
-                                  self.ws if self.ws_bytes else None, self.ws_bytes,
+                                  self.v_cache, blk.block_table, blk.prefix_len, None, blk.out,
+                                  blk.ws if blk.ws_bytes else None, blk.ws_bytes,
                                   flags=W_.WEDLM_ATTN_SHARED_PAGES, stream=stream)
 
     def forward(self, q_mem, k_mem, v_mem, q_pred, k_pred, v_pred, filled, stream=None):
@@ -104,20 +128,23 @@ class DualStreamAttention:
         rows in physical order (the memory stream's is its slot order);
         ``self.pred["inv"]`` maps a prediction slot to its physical row.
         """
-        qm, km, vm = self._view(q_mem, self.Hq), self._view(k_mem, self.Hkv), self._view(v_mem, self.Hkv)
-        qp, kp, vp = self._view(q_pred, self.Hq), self._view(k_pred, self.Hkv), self._view(v_pred, self.Hkv)
+        m, p = self.mem_blocks, self.pred_blocks
+        qm, km, vm = (self._view(q_mem, self.Hq, m), self._view(k_mem, self.Hkv, m),
+                      self._view(v_mem, self.Hkv, m))
+        qp, kp, vp = (self._view(q_pred, self.Hq, p), self._view(k_pred, self.Hkv, p),
+                      self._view(v_pred, self.Hkv, p))
         # 1. the memory stream's rotated keys and values into the paged cache
-        self._reorder(self.all_obs, self.mem, stream)
-        self.filled_scratch.copy_(self.all_obs)
-        self.len_scratch.copy_(self.prefix_len)
-        W_.wedlm_commit_prefix_rope(self.dt, 1, self.Bp, self.Bk, self.Hkv, self.D, PAGE,
-                                    self.num_pages, self.max_pages, self.theta, self.mem["run"],
-                                    self.selected, self.argmax, km, vm, self.block_table,
+        self._reorder(m.all_obs, m, stream)
+        self.filled_scratch.copy_(m.all_obs)
+        self.len_scratch.copy_(m.prefix_len)
+        W_.wedlm_commit_prefix_rope(self.dt, 1, m.Bp, m.W, self.Hkv, self.D, PAGE,
+                                    self.num_pages, self.max_pages, self.theta, m.order["run"],
+                                    self.selected, self.argmax, km, vm, m.block_table,
                                     self.k_cache, self.v_cache, self.tokens, self.filled_scratch,
                                     self.len_scratch, self.commit_len, self.cache_slot, -1, stream)
-        # 2. memory stream: causal over the memory prefix and its own block
-        self._attend(qm, km, vm, self.mem, self.out_mem, stream)
+        # 2. memory stream: causal over the memory prefix and its own window
+        self._attend(qm, km, vm, m, stream)
         # 3. prediction stream: reordered blocks over the memory prefix
-        self._reorder(filled.reshape(self.Bp, self.Bk), self.pred, stream)
-        self._attend(qp, kp, vp, self.pred, self.out_pred, stream)
+        self._reorder(filled.reshape(p.Bp, p.W), p, stream)
+        self._attend(qp, kp, vp, p, stream)
         return self.out_mem, self.out_pred

@@ -1091,12 +1091,14 @@ static AttnPlan plan_bf16(int n_layers, int B, int W, int Hq, int Hkv, int max_p
   const long long groups = 1LL * n_layers * B * Hkv;
   const long long columns = 1LL * n_layers * Hkv;
   // aim for one full round of workgroups (every CU holding as many as its
-  // registers allow) but keep >= 4 pages per split (8 for the deeper rings);
+  // registers allow) but keep >= 8 pages per split (4 measured slower where it
+  // mattered: the bs1, L = 2048 step took 43.0 against 38.6 us, its combine
+  // merging twice as many partials);
   // how the column's workgroups are shared out follows the live prefix
   // lengths on the device (find_split)
   const int wg_per_cu = pl.waves == 4 ? Ring<4>::kWgPerCu : Ring<8>::kWgPerCu;
   const long long target = 1LL * kNumCUs * wg_per_cu / pl.parts;  // work units per round
-  pl.min_pages = pl.waves == 4 ? 4 : 8;
+  pl.min_pages = 8;
   const int npages = ceil_div(max(max_prefix_len, 1), kPage);
   pl.cols = B;
   pl.split = false;

@@ -6,13 +6,13 @@
 // and PagedAttention's block table (mlsanity.com page, "Builds on") are the
 // prior art; this kernel is written for CDNA4 from scratch.
 //
-// bf16 path (D = 128, page P = 16). One workgroup per (layer, sequence, kv
-// head, key-range split) - two when the group has more than 8 row tiles, each
-// taking half of the rows; each wavefront owns one 16-row tile of the group's
-// M = W*g query rows (physical row p, query head h of the group). The
+// bf16 path (D = 128, page P = 16). One workgroup of 4 wavefronts per (layer,
+// sequence, kv head, key-range split, part of 4 row tiles); each wavefront
+// owns one 16-row tile of the group's M = W*g query rows (physical row p,
+// query head h of the group), and the parts of one group run on one XCD. The
 // group's key pages stream through an LDS ring, one page (16 keys, 8 KB of K
-// and V) per stage, filled by global->LDS DMA: 4 stages for 4-wave workgroups
-// (4 per CU) and 7 for 8 waves (2 per CU). The waves take
+// and V) per stage, filled by global->LDS DMA: 4 stages, 4 workgroups per CU.
+// The waves take
 // two pages per barrier; the barrier both publishes them and frees the two
 // stages computed before them, which are refilled at once: all but two stages
 // are in flight while the waves compute. Each key byte is read from HBM once
@@ -63,8 +63,10 @@ constexpr int kNumCUs = 256;        // MI355X compute units
 constexpr int kNumXcds = 8;         // MI355X: 8 XCDs of 32 CUs, workgroups dealt round-robin
 
 // LDS ring (one 8 KB page per stage) per workgroup size. A CU holds 4
-// workgroups of 4 waves or 2 of 8 (4 wavefronts per SIMD either way); the
-// ring keeps 8-10 pages (64-80 KB) in flight per CU while the waves compute. Every ring advances two pages per barrier (attend_pages2):
+// workgroups of 4 waves (4 wavefronts per SIMD); the ring keeps 8 pages
+// (64 KB) in flight per CU while the waves compute. The launches use 4-wave
+// workgroups only; the 8-wave configuration (2 per CU, 7 stages) is kept as a
+// measured alternative. Every ring advances two pages per barrier (attend_pages2):
 // against one page per barrier with 3 stages at 5 workgroups per CU, this
 // took the 36-layer streaming launch from 5.49 to 5.64 TB/s and the
 // dual-stream forward with 16-key blocks from 2.31 to 2.16 ms (5 workgroups
@@ -1081,12 +1083,14 @@ static AttnPlan plan_bf16(int n_layers, int B, int W, int Hq, int Hkv, int max_p
   const int g = Hq / Hkv;
   const int M = W * g;
   const int tiles = ceil_div(M, 16);
-  // more than 8 row tiles: two 8-wave workgroups per work unit, each with half
-  // of the rows (one 16-wave workgroup per CU measured slower: 3.13 against
-  // 2.65 ms for the dual-stream forward with 64-key blocks, equal for the
-  // g = 7, W = 32 decoding shape)
-  pl.waves = tiles <= 4 ? 4 : 8;
-  pl.parts = tiles > 8 ? 2 : 1;
+  // more than 4 row tiles: one 4-wave workgroup per 4 tiles of the work unit
+  // (row parts on one XCD). Larger workgroups measured slower: for the
+  // dual-stream prediction blocks, 2.36 / 2.37 ms with one 8-wave workgroup
+  // (32-key blocks) or two (64-key blocks) against 2.18 / 2.22 ms, and 3.13 ms
+  // with one 16-wave workgroup (64-key blocks); the g = 7, W = 32 decoding
+  // shape is within 2 % either way.
+  pl.waves = 4;
+  pl.parts = ceil_div(tiles, 4);
   pl.part_rows = ceil_div(tiles, pl.parts) * 16;
   const long long groups = 1LL * n_layers * B * Hkv;
   const long long columns = 1LL * n_layers * Hkv;
@@ -1096,7 +1100,7 @@ static AttnPlan plan_bf16(int n_layers, int B, int W, int Hq, int Hkv, int max_p
   // merging twice as many partials);
   // how the column's workgroups are shared out follows the live prefix
   // lengths on the device (find_split)
-  const int wg_per_cu = pl.waves == 4 ? Ring<4>::kWgPerCu : Ring<8>::kWgPerCu;
+  const int wg_per_cu = Ring<4>::kWgPerCu;
   const long long target = 1LL * kNumCUs * wg_per_cu / pl.parts;  // work units per round
   pl.min_pages = 8;
   const int npages = ceil_div(max(max_prefix_len, 1), kPage);
@@ -1254,12 +1258,8 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   // the DMA keeps the default cache policy, otherwise it streams (kNt).
   const bool nt = (flags & WEDLM_ATTN_SHARED_PAGES) == 0;
   auto pick = [&](auto k_nt, auto k_cached, int waves) { nt ? go(k_nt, waves) : go(k_cached, waves); };
-  if (pl.waves == 4)
-    rope ? pick(k_window_attn_bf16<4, true, true>, k_window_attn_bf16<4, true, false>, 4)
-         : pick(k_window_attn_bf16<4, false, true>, k_window_attn_bf16<4, false, false>, 4);
-  else
-    rope ? pick(k_window_attn_bf16<8, true, true>, k_window_attn_bf16<8, true, false>, 8)
-         : pick(k_window_attn_bf16<8, false, true>, k_window_attn_bf16<8, false, false>, 8);
+  rope ? pick(k_window_attn_bf16<4, true, true>, k_window_attn_bf16<4, true, false>, pl.waves)
+       : pick(k_window_attn_bf16<4, false, true>, k_window_attn_bf16<4, false, false>, pl.waves);
   st = launch_status();
   if (st != WEDLM_OK || !pl.split) return st;
   const long long threads = groups * a.M * (kHeadDim / 4);

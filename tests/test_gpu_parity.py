@@ -85,20 +85,20 @@ def _variant(base, **kw):
                                        prefix=("uniform", 0, 45))),
     ("stream_shape_short", _variant(WL.QWEN3_8B_STREAM, name="edge_stream_layers", n_layers=3,
                                     B=4, V=3000, fill=("frac", 0.0, 1.0), steps=1)),
-    # 8-wave workgroups (128 query rows: 7-stage ring, 2 per CU), split key range
+    # 128 query rows: two 4-wave row parts per work unit, split key range
     ("nw8_split", _variant(WL.QWEN3_8B_BS1, name="edge_nw8_split", W=32, prefix=("fixed", 3000),
                            V=2048, B=2, fill=("frac", 0.3, 0.7))),
-    # 8-wave workgroups, no split (512 groups), short ragged prefixes
+    # 128 query rows in two row parts, no split (512 groups), short ragged prefixes
     ("nw8_many_groups", _variant(WL.QWEN3_8B_STREAM, name="edge_nw8_layers", n_layers=8, B=8, W=32,
                                  V=2048, fill=("frac", 0.0, 1.0), prefix=("uniform", 17, 900),
                                  steps=1)),
-    # 224 rows: two 8-wave row parts per work unit, splits shorter than the 7-stage ring
+    # 224 rows: four 4-wave row parts per work unit, short splits
     ("rowparts_short_splits", _variant(WL.QWEN25_7B_RAGGED, name="edge_rowparts_short", B=2,
                                    prefix=("uniform", 40, 130), V=2048)),
     # split plan over very uneven prefixes: empty, one key, one page, a long one
     ("split_plan_extremes", _variant(WL.QWEN25_7B_RAGGED, name="edge_split_extremes", B=6,
                                      prefix=("list", (0, 1, 4000, 16, 2047, 33)), V=2048)),
-    # 8-wave workgroups, split plan with a sequence that has no prefix at all
+    # two row parts, split plan with a sequence that has no prefix at all
     ("split_plan_nw8", _variant(WL.QWEN3_8B_BS1, name="edge_split_nw8", W=32, B=3,
                                 prefix=("list", (3000, 5, 0)), V=2048, fill=("frac", 0.3, 0.7))),
     # 4-wave workgroups, 40 sequences sharing 160 workgroups per kv head
@@ -165,8 +165,8 @@ def test_invalid_host_arguments_raise():
 ])
 def test_cache_policy_flag_bitwise_same(wl):
     """The shared-pages flag only changes the cache hint of the page loads:
-    outputs with and without it are bitwise equal (4-wave workgroups, and two
-    8-wave row parts per work unit)."""
+    outputs with and without it are bitwise equal (one 4-wave workgroup per
+    work unit, and four row parts per work unit)."""
     from causal_streaming_decoding_amd import wedlm as W_
     from causal_streaming_decoding_amd.step import make_window_step, upload_step_inputs
 

@@ -56,7 +56,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
-constexpr int kMaxRows = 256;       // M = W*g rows: at most two 8-wave workgroups
+constexpr int kMaxRows = 256;       // M = W*g rows: at most four 4-wave row parts
 constexpr int kPageVecs = 512;      // 16-byte vectors of one page of one kv head (K 4 KB + V 4 KB)
 constexpr int kPartElems = 2048;    // bf16 elements of one 4 KB page part
 constexpr int kNumCUs = 256;        // MI355X compute units

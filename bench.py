@@ -551,7 +551,7 @@ def read_bandwidth(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build",
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported",
               file=sys.stderr)
         sys.exit(2)
     if args.all_configs:

@@ -19,8 +19,8 @@ Usage (the second form summarises ``bench.py --all-configs``, the third
     python -m causal_streaming_decoding_amd.profiling configs --configs-jsonl <file> \\
         --trace <dir> --out-md profiles/<name>.md
     python -m causal_streaming_decoding_amd.profiling \\
-        --trace gpurun_out/prof_trace --fetch gpurun_out/prof_fetch \\
-        --write gpurun_out/prof_write --bench-json gpurun_out/prof_bench.json \\
+        --trace <out>/prof_trace --fetch <out>/prof_fetch \\
+        --write <out>/prof_write --bench-json <out>/prof_bench.json \\
         --steps 256 --out-md profiles/<name>.md --out-traffic profiles/<name>_traffic.txt
     python -m causal_streaming_decoding_amd.profiling lmhead --bench-jsonl <file> \\
         --trace <dir> --fetch <dir> --write <dir> --out-md profiles/<name>.md

@@ -69,7 +69,7 @@ extern "C" {
 enum wedlm_status {
   WEDLM_OK = 0,
   WEDLM_ERR_INVALID = -1,     /* null pointer, size <= 0, Hq % Hkv != 0, W > 64, ... */
-  WEDLM_ERR_UNSUPPORTED = -2, /* a shape or dtype this build has no kernel for     */
+  WEDLM_ERR_UNSUPPORTED = -2, /* a shape or dtype the library has no kernel for   */
   WEDLM_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required    */
   WEDLM_ERR_HIP = -4          /* the HIP runtime reported an error at launch        */
 };

@@ -28,6 +28,7 @@ pytestmark = pytest.mark.gpu
     (3, 128, 16, 4, 4, "all"),         # MHA; prediction stream fully observed
     (1, 128, 16, 8, 2, "none"),        # prediction stream fully masked
     (1, 1024, 16, 8, 2, "random"),     # 64 blocks: prefixes up to 1008
+    (2, 128, 8, 8, 2, "random"),       # blocks smaller than the memory stream's 16-key windows
 ])
 def test_dual_stream_parity(S, N, Bk, Hq, Hkv, fill):
     print(f"[dual] S={S} N={N} Bk={Bk} Hq={Hq} Hkv={Hkv} fill={fill}", flush=True)

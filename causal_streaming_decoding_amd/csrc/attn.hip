@@ -1035,26 +1035,43 @@ k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
     m = m_new;
 #pragma unroll
     for (int i = 0; i < kF32MaxD / kWave; ++i) o[i] *= alpha;
+    // PV over this step's keys, kPvBatch keys at a time: the batch's values
+    // are all requested before any is used (one key at a time left a chain of
+    // dependent block-table and value loads per key), then accumulated in key
+    // order.
+    constexpr int kPvBatch = 8;
     const int nk = min(kWave, nkeys - k0);
-    for (int j = 0; j < nk; ++j) {
-      const float pj = __shfl(pk, j, kWave);
-      const int kj = k0 + j;
-      if (kj < L) {
-        const int pid = min(max(bt[kj / kPage], 0), num_pages - 1);
-        const float* vp = vcl + (static_cast<size_t>(pid) * Hkv + kvh) * page_elems;
-        const int off = kj % kPage;
+    for (int j0 = 0; j0 < nk; j0 += kPvBatch) {
+      float pj[kPvBatch];
+      float vv[kPvBatch][kF32MaxD / kWave];
+#pragma unroll
+      for (int u = 0; u < kPvBatch; ++u) {
+        const int j = j0 + u;
+        pj[u] = __shfl(pk, min(j, kWave - 1), kWave);
+        const int kj = k0 + j;
+        const float* src = nullptr;
+        int stride = 1;
+        if (j < nk) {
+          if (kj < L) {
+            const int pid = min(max(bt[kj / kPage], 0), num_pages - 1);
+            src = vcl + (static_cast<size_t>(pid) * Hkv + kvh) * page_elems + kj % kPage;
+            stride = kPage;
+          } else {
+            src = v + ((lb * W + slot_of(kj - L)) * Hkv + kvh) * D;
+          }
+        }
 #pragma unroll
         for (int i = 0; i < kF32MaxD / kWave; ++i) {
           const int d = lane + i * kWave;
-          if (d < D) o[i] += pj * vp[d * kPage + off];
+          vv[u][i] = (src != nullptr && d < D) ? src[d * stride] : 0.f;
         }
-      } else {
-        const float* vr = v + ((lb * W + slot_of(kj - L)) * Hkv + kvh) * D;
+      }
 #pragma unroll
-        for (int i = 0; i < kF32MaxD / kWave; ++i) {
-          const int d = lane + i * kWave;
-          if (d < D) o[i] += pj * vr[d];
-        }
+      for (int u = 0; u < kPvBatch; ++u) {
+        if (j0 + u >= nk) break;
+#pragma unroll
+        for (int i = 0; i < kF32MaxD / kWave; ++i)
+          if (lane + i * kWave < D) o[i] += pj[u] * vv[u][i];
       }
     }
   }

@@ -201,6 +201,20 @@ __device__ __forceinline__ void pv_regroup(uint32_t& h01, uint32_t& h23, uint32_
       : "+v"(h01), "+v"(h23), "+v"(l01), "+v"(l23));
 }
 
+// Keys past a partial last prefix page have p = 0, but 0 * NaN and 0 * Inf are
+// NaN in the PV product: cache positions a sequence has not written yet may
+// hold any bits. On such a page (lim < 16, wave-uniform) the V operand's
+// elements of keys >= lim are cleared. A lane holds keys 8*(grp & 1) .. +7 of
+// one value dimension, two keys per 32-bit word.
+__device__ __forceinline__ u32x4 v_key_mask(int lim, int grp) {
+  const int nv = min(max(lim - (grp & 1) * 8, 0), 8);  // valid keys of this lane's 8
+  u32x4 m;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    m[w] = (2 * w < nv ? 0x0000ffffu : 0u) | (2 * w + 1 < nv ? 0xffff0000u : 0u);
+  return m;
+}
+
 // Scores, online softmax and PV for one 16-key stage.
 //
 // S^T = K Q^T (four v_mfma_f32_16x16x32_bf16 over the 128 dimensions) leaves
@@ -220,8 +234,13 @@ __device__ __forceinline__ void pv_regroup(uint32_t& h01, uint32_t& h23, uint32_
 //
 // P enters the PV product as a bf16 pair hi + lo (hi = RNE(p), lo = RNE(p - hi)),
 // so the probabilities carry ~16 mantissa bits instead of bf16's 8.
+//
+// lim: keys kk < lim of the stage are visible to this lane's row. vlim: keys
+// kk >= vlim (wave-uniform) are cleared from the V operand as well; a prefix
+// page passes vlim = lim, a window chunk kPage (its rows are window inputs, or
+// zero past W).
 __device__ __forceinline__ void attend_page(RowState& st, const bf16x8 (&qr)[4], const Stage& sg,
-                                            int lane, int lim, float scale_log2) {
+                                            int lane, int lim, int vlim, float scale_log2) {
   const int col = lane & 15, grp = lane >> 4;
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -259,6 +278,16 @@ __device__ __forceinline__ void attend_page(RowState& st, const bf16x8 (&qr)[4],
   uint32_t l23 = pack_bf16x2(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
   pv_regroup(h01, h23, l01, l23);
   const u32x4 pb = {h01, h23, l01, l23};
+  if (vlim < kPage) {
+    const u32x4 vm = v_key_mask(vlim, grp);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const u32x4 va =
+          *reinterpret_cast<const u32x4*>(&sg.v[(dt * 16 + col) * kPage + (grp & 1) * 8]) & vm;
+      st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb), st.o[dt], 0, 0, 0);
+    }
+    return;
+  }
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     // keys 8*(grp & 1) .. +7 of value dimension dt*16 + col: one 16-byte read
@@ -269,14 +298,25 @@ __device__ __forceinline__ void attend_page(RowState& st, const bf16x8 (&qr)[4],
 }
 
 // P^T for the PV product of one page from a lane's 4 probabilities (hi and lo
-// bf16 parts, regrouped as in attend_page), then O^T += V^T P^T over the page.
+// bf16 parts, regrouped as in attend_page), then O^T += V^T P^T over the page;
+// V elements of keys >= vlim are cleared (a partial last prefix page).
 __device__ __forceinline__ void pv_page(RowState& st, const Stage& sg, int col, int grp,
-                                        float p0, float p1, float p2, float p3) {
+                                        float p0, float p1, float p2, float p3, int vlim) {
   uint32_t h01 = pack_bf16x2(p0, p1), h23 = pack_bf16x2(p2, p3);
   uint32_t l01 = pack_bf16x2(p0 - bf16_lo(h01), p1 - bf16_hi(h01));
   uint32_t l23 = pack_bf16x2(p2 - bf16_lo(h23), p3 - bf16_hi(h23));
   pv_regroup(h01, h23, l01, l23);
   const u32x4 pb = {h01, h23, l01, l23};
+  if (vlim < kPage) {
+    const u32x4 vm = v_key_mask(vlim, grp);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const u32x4 va =
+          *reinterpret_cast<const u32x4*>(&sg.v[(dt * 16 + col) * kPage + (grp & 1) * 8]) & vm;
+      st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb), st.o[dt], 0, 0, 0);
+    }
+    return;
+  }
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     const u32x4 va =
@@ -330,8 +370,8 @@ __device__ __forceinline__ void attend_pages2(RowState& st, const bf16x8 (&qr)[4
 #pragma unroll
   for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], scale_log2, -base));
   st.l += row_sum4(((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-  pv_page(st, s0, col, grp, p[0], p[1], p[2], p[3]);
-  pv_page(st, s1, col, grp, p[4], p[5], p[6], p[7]);
+  pv_page(st, s0, col, grp, p[0], p[1], p[2], p[3], lim0);
+  pv_page(st, s1, col, grp, p[4], p[5], p[6], p[7], lim1);
 }
 
 // Asynchronous page staging: global -> LDS DMA (global_load_lds_dwordx4).
@@ -732,7 +772,8 @@ k_window_attn_bf16(AttnArgs a) {
     if (i + kAhead < npg)
       stage_dma<NW, kNt>(stage[(i + kAhead) % kStages], wave, lane, pg + kAhead, bt, a.max_pages,
                     a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
-    if (computes) attend_page(st, qr, stage[i % kStages], lane, L - pg * kPage, a.scale_log2);
+    if (computes)
+      attend_page(st, qr, stage[i % kStages], lane, L - pg * kPage, L - pg * kPage, a.scale_log2);
   }
   // The window reuses stage 0: every DMA must have landed before it is
   // overwritten (and none may be in flight when the workgroup ends). The
@@ -817,7 +858,7 @@ k_window_attn_bf16(AttnArgs a) {
       }
       if (computes) {
         const int lim = min(a.W, prow + 1) - kw0;  // window key kw0 + kk visible iff kk < lim
-        attend_page(st, qr, sg, lane, lim, a.scale_log2);
+        attend_page(st, qr, sg, lane, lim, kPage, a.scale_log2);
       }
       __syncthreads();
     }
@@ -1189,6 +1230,9 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   if (!q || !k || !v || !k_cache || !v_cache || !block_table || !prefix_len || !out_phys)
     return WEDLM_ERR_INVALID;
   if (rope && (!perm || !pos || !(theta > 0.0) || D % 2 != 0)) return WEDLM_ERR_INVALID;
+  // the fused f32 kernel rotates window keys four dimension pairs at a time
+  // (float4 halves), as the f32 commit does
+  if (rope && dtype == WEDLM_F32 && D % 8 != 0) return WEDLM_ERR_UNSUPPORTED;
   if (!(scale > 0.f)) return WEDLM_ERR_INVALID;
   hipStream_t s = as_stream(stream);
   const long long cache_layer_stride = 1LL * num_pages * Hkv * D * page_size;

@@ -182,7 +182,10 @@ size_t wedlm_window_attn_workspace_size(int dtype, int n_layers, int B, int W, i
  *      [0, max_prefix_len]).
  * out: out_phys [n_layers][B][W][Hq][D], physical order.
  * Host sizes: page_size P in {16}; max_prefix_len <= max_pages * P; bf16 needs
- * D == 128; f32 needs D even and <= 256. workspace: at least
+ * D == 128; f32 needs D a multiple of 4 and <= 256 (WEDLM_ERR_UNSUPPORTED
+ * otherwise). Cache positions at or past prefix_len[b] in a sequence's last
+ * page may hold any bits, NaN and Inf included: they never reach the output.
+ * workspace: at least
  * wedlm_window_attn_workspace_size(...) bytes (may be NULL if that is 0).
  * Block-table entries are clamped to [0, num_pages).
  * flags: 0 when every page is referenced by one row of block_table (each
@@ -214,7 +217,8 @@ int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv, in
  * evaluated in fp32 (error ~1e-7), the rotation done in fp32 and rounded once
  * to the element type before the products, as with wedlm_rope_logical.
  * No q_phys / k_phys / v_phys is written. All other arguments, layouts, sizes,
- * workspace, flags and errors are those of wedlm_window_attn; theta > 0.
+ * workspace, flags and errors are those of wedlm_window_attn; theta > 0; the
+ * f32 path needs D a multiple of 8 (WEDLM_ERR_UNSUPPORTED otherwise).
  *
  * commit_run (device [B], may be NULL): when given, the call also performs the
  * cache half of the commit (hyper.ai summary, "Method": the leftmost filled

@@ -10,20 +10,38 @@ vocabulary id among equal maxima (greedy decoding instead of the evaluation's
 temperature sampling, which would need a shared random stream).
 """
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 
-def vocab_entropy_argmax(logits):
+def vocab_entropy_argmax(logits, workers=1):
     """Entropy (nats) and argmax of softmax(logits) along the last axis.
 
     Args:
       logits: float array [..., V] (promoted to float64; -inf entries allowed
               as long as every row has a finite maximum).
+      workers: rows are independent; with workers > 1 they are dealt out in
+              contiguous chunks to that many threads (each row's arithmetic is
+              unchanged, so the result is the same bit for bit).
 
     Returns (entropy float64 [...], argmax int64 [...]):
       p = softmax(z), H = -sum_v p_v ln p_v (terms with p_v = 0 count 0),
       argmax = lowest v with z_v = max z.
     """
+    z = np.asarray(logits)
+    if workers > 1 and z.ndim > 1 and z.shape[-1] > 0:
+        rows = z.reshape(-1, z.shape[-1])
+        chunks = np.array_split(np.arange(rows.shape[0]), min(workers, rows.shape[0]))
+        with ThreadPoolExecutor(len(chunks)) as pool:
+            parts = list(pool.map(lambda c: _rows_entropy_argmax(rows[c[0]: c[-1] + 1]), chunks))
+        H = np.concatenate([h for h, _ in parts]).reshape(z.shape[:-1])
+        a = np.concatenate([x for _, x in parts]).reshape(z.shape[:-1])
+        return H, a
+    return _rows_entropy_argmax(z)
+
+
+def _rows_entropy_argmax(logits):
     z = np.asarray(logits, dtype=np.float64)
     m = z.max(axis=-1, keepdims=True)
     shifted = z - m

@@ -28,11 +28,13 @@ def vocab_projection(hidden, w_vocab):
     return h @ w.T
 
 
-def lm_head_select(hidden, w_vocab, filled, lam, tau, min_fill=1):
+def lm_head_select(hidden, w_vocab, filled, lam, tau, min_fill=1, adopt=None):
     """Entropy, argmax and selection of every slot from its hidden state.
 
     Args:
       hidden:  [B, W, hidden]; w_vocab: [V, hidden]; filled: [B, W] bool.
+      adopt: optional [B, W] bool, another implementation's selections, taken
+        only by flagged near-tie decisions (``select_slots``).
 
     Returns dict: entropy [B, W] float64, argmax [B, W] int64, logits
     [B, W, V] float64, and per sequence the ``select_slots`` result
@@ -41,5 +43,6 @@ def lm_head_select(hidden, w_vocab, filled, lam, tau, min_fill=1):
     z = vocab_projection(hidden, w_vocab)
     H, a = vocab_entropy_argmax(z)
     f = np.asarray(filled, dtype=bool)
-    sel = [select_slots(H[b], f[b], lam, tau, min_fill) for b in range(H.shape[0])]
+    sel = [select_slots(H[b], f[b], lam, tau, min_fill,
+                        adopt=None if adopt is None else adopt[b]) for b in range(H.shape[0])]
     return {"entropy": H, "argmax": a, "logits": z, "select": sel}

@@ -17,15 +17,15 @@ Readings (none of this is printed on the pages):
     the lowest score is filled (lowest slot on equal scores). PARITY UNPINNED:
     the pages never state what a step does when nothing clears the threshold;
     this is the one-token rule of their one-by-one mode applied as a floor.
-  * the fill decision is taken in float32 arithmetic: the kernel's precision,
-    as the pages name none. The float64 margins are reported as flags when a
-    decision is within ``tie_eps`` of flipping.
+  * every score and decision is float64, the definition itself. A decision
+    whose float64 margin is under ``tie_eps`` is reported as a flag: another
+    implementation that rounds differently may take it the other way.
 """
 
 import numpy as np
 
 
-def select_slots(entropy, filled, lam, tau, min_fill=1, tie_eps=1e-4):
+def select_slots(entropy, filled, lam, tau, min_fill=1, tie_eps=1e-4, adopt=None):
     """Choose the mask slots to fill in one window.
 
     Args:
@@ -34,9 +34,16 @@ def select_slots(entropy, filled, lam, tau, min_fill=1, tie_eps=1e-4):
       lam, tau: penalty weight and threshold.
       min_fill: 1 to fill the lowest-score mask slot when none clears tau.
       tie_eps: margin under which a decision is flagged as a near tie.
+      adopt: optional [W] bool, another implementation's selection for this
+        window. Only flagged decisions take it: a threshold comparison of
+        slot i within tie_eps of tau takes adopt[i]; when the floor rule's
+        lowest score has runners-up within tie_eps, the floor slot is the one
+        of those tied candidates that adopt selects (when it selects exactly
+        one). Every other decision is the oracle's own, so a caller comparing
+        the two selections slot by slot still sees any unflagged difference.
 
     Returns dict:
-      score     [W] float32  (H + lam * i, float32 arithmetic),
+      score     [W] float64 (H + lam * i),
       selected  [W] bool,
       fallback  bool, the floor rule decided the step,
       flags     list of (kind, slot) near-tie flags.
@@ -44,27 +51,28 @@ def select_slots(entropy, filled, lam, tau, min_fill=1, tie_eps=1e-4):
     H = np.asarray(entropy, dtype=np.float64)
     f = np.asarray(filled, dtype=bool)
     W = H.shape[0]
-    lam32 = np.float32(lam)
-    tau32 = np.float32(tau)
-    idx32 = np.arange(W, dtype=np.float32)
-    # two separate float32 roundings: the product, then the sum
-    score = (H.astype(np.float32) + (lam32 * idx32).astype(np.float32)).astype(np.float32)
-    score64 = H + float(lam) * np.arange(W, dtype=np.float64)
+    score = H + float(lam) * np.arange(W, dtype=np.float64)
+    adopt = None if adopt is None else np.asarray(adopt, dtype=bool)
 
     candidates = [i for i in range(W) if not f[i]]
     selected = np.zeros(W, dtype=bool)
     flags = []
     for i in candidates:
-        if score[i] < tau32:
-            selected[i] = True
-        if abs(score64[i] - float(tau)) < tie_eps:
+        take = bool(score[i] < tau)
+        if abs(score[i] - float(tau)) < tie_eps:
             flags.append(("threshold", i))
+            if adopt is not None:
+                take = bool(adopt[i])
+        selected[i] = take
     fallback = False
     if not selected.any() and candidates and min_fill == 1:
         best = min(candidates, key=lambda i: (score[i], i))
+        tied = [i for i in candidates if i != best and abs(score[i] - score[best]) < tie_eps]
+        flags.extend(("fallback", i) for i in tied)
+        if tied and adopt is not None:
+            chosen = [i for i in [best] + tied if adopt[i]]
+            if len(chosen) == 1:
+                best = chosen[0]
         selected[best] = True
         fallback = True
-        for i in candidates:
-            if i != best and abs(score64[i] - score64[best]) < tie_eps:
-                flags.append(("fallback", i))
     return {"score": score, "selected": selected, "fallback": fallback, "flags": flags}

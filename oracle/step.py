@@ -21,7 +21,7 @@ from .commit import commit_and_refill
 
 def window_step(filled, tokens, prefix_len, q, k, v, k_cache, v_cache, logits, block_table,
                 theta, lam, tau, page_size, min_fill=1, mask_id=-1, layers=None, scale=None,
-                override_selected=None, store=None, commit_rule="stream"):
+                adopt_selected=None, store=None, commit_rule="stream", workers=1):
     """One window step for a batch of sequences and n_layers independent layers.
 
     Args:
@@ -33,8 +33,9 @@ def window_step(filled, tokens, prefix_len, q, k, v, k_cache, v_cache, logits, b
       logits [B, W, V]: slot order.
       block_table [B, max_pages]: page ids per sequence.
       layers: layer indices whose attention is computed (default: all).
-      override_selected: optional callable(b, selection_dict) -> [W] bool used
-        to adopt another decision for a flagged near tie.
+      adopt_selected: optional callable(b) -> [W] bool, another
+        implementation's selection for sequence b; only the flagged near-tie
+        decisions take it (``select_slots``' ``adopt``).
       store: optional callable mapping a float64 array to the values a storage
         type holds (e.g. one round-to-nearest-even to bf16). When given, the
         rotated window rows are stored through it before they are attended to
@@ -42,6 +43,7 @@ def window_step(filled, tokens, prefix_len, q, k, v, k_cache, v_cache, logits, b
         returned q_phys / k_phys / v_phys stay unrounded.
       commit_rule: "stream" (commit the leading filled run) or "block" (commit
         the window only once it is entirely filled); see ``commit_count``.
+      workers: threads for the entropy's independent rows (same result).
 
     Returns a dict of float64 / int64 numpy results (see keys below).
     """
@@ -93,21 +95,18 @@ def window_step(filled, tokens, prefix_len, q, k, v, k_cache, v_cache, logits, b
         attn[layer] = o
     out["attn_out_phys"] = attn
 
-    H, a = vocab_entropy_argmax(logits)
+    H, a = vocab_entropy_argmax(logits, workers=workers)
     out["entropy"], out["argmax"] = H, a
-    out["score"] = np.zeros((B, W), np.float32)
+    out["score"] = np.zeros((B, W), np.float64)
     out["selected"] = np.zeros((B, W), bool)
     out["fallback"] = np.zeros(B, bool)
     out["flags"] = []
     for b in range(B):
-        s = select_slots(H[b], filled[b], lam, tau, min_fill)
-        sel = s["selected"]
-        if s["flags"]:
-            out["flags"].extend((b, kind, i) for kind, i in s["flags"])
-            if override_selected is not None:
-                sel = np.asarray(override_selected(b, s), dtype=bool)
+        other = None if adopt_selected is None else adopt_selected(b)
+        s = select_slots(H[b], filled[b], lam, tau, min_fill, adopt=other)
+        out["flags"].extend((b, kind, i) for kind, i in s["flags"])
         out["score"][b] = s["score"]
-        out["selected"][b] = sel
+        out["selected"][b] = s["selected"]
         out["fallback"][b] = s["fallback"]
 
     out["commit_len"] = np.zeros(B, np.int64)
@@ -151,7 +150,7 @@ class _Growable:
 
 def stream_loop(filled, tokens, prefix_len, k_cache, v_cache, block_table, steps, inputs_for_step,
                 theta, lam, tau, page_size, min_fill=1, mask_id=-1, attend=None, track_layers=(),
-                override_selected=None, on_step=None, store=None, commit_rule="stream"):
+                adopt_selected=None, on_step=None, store=None, commit_rule="stream", workers=1):
     """Run the streaming decoder for ``steps`` window steps.
 
     Args:
@@ -162,12 +161,14 @@ def stream_loop(filled, tokens, prefix_len, k_cache, v_cache, block_table, steps
         ``window_step``.
       attend(s) -> layers whose attention to compute at step s (default none);
         they must be tracked layers.
-      override_selected(s, b, selection) -> [W] bool for flagged near ties.
+      adopt_selected(s, b) -> [W] bool: another implementation's selection at
+        step s, taken only by flagged near-tie decisions.
       on_step(s, result) is called after each step with window_step's result.
       store: as in ``window_step``; committed rows enter the tracked caches
         through it too.
       commit_rule: as in ``window_step`` ("block" gives the stop-and-wait
         decoder on the same steps).
+      workers: as in ``window_step``.
 
     Returns dict with per-step commit lengths [steps, B], the final state and
     the total committed tokens.
@@ -193,11 +194,11 @@ def stream_loop(filled, tokens, prefix_len, k_cache, v_cache, block_table, steps
             kc[layer] = [g.view() for g in caches[layer][0]]
             vc[layer] = [g.view() for g in caches[layer][1]]
         ov = None
-        if override_selected is not None:
-            ov = (lambda b, sel, _s=s: override_selected(_s, b, sel))
+        if adopt_selected is not None:
+            ov = (lambda b, _s=s: adopt_selected(_s, b))
         r = window_step(filled, tokens, prefix_len, q, k, v, kc, vc, logits, block_table, theta, lam,
-                        tau, page_size, min_fill, mask_id, layers=layers, override_selected=ov,
-                        store=store, commit_rule=commit_rule)
+                        tau, page_size, min_fill, mask_id, layers=layers, adopt_selected=ov,
+                        store=store, commit_rule=commit_rule, workers=workers)
         keep = store if store is not None else (lambda x: x)
         for layer in track_layers:
             for b in range(len(prefix_len)):

@@ -78,6 +78,21 @@ def test_attn_validation_and_workspace():
     assert _raw("wedlm_window_attn", *a) == -1
     a = list(base); a[3] = 64; a[4] = 64; a[5] = 8       # 64 * 8 rows > 256
     assert _raw("wedlm_window_attn", *a) == -2
+
+
+def test_attn_rope_f32_needs_d_multiple_of_8():
+    # f32 fused RoPE rotates window keys in float4 halves: D % 8 == 4 is
+    # rejected before any launch (the separate f32 attention takes D % 4 == 0)
+    def rope_args(D):
+        return [0, 1, 1, 8, 2, 1, D, 16, 4, 4, 40, 0.1, 1e4] + [1] * 12 + [0, 0, None]
+    assert _raw("wedlm_window_attn_rope", *rope_args(68)) == -2
+    assert _raw("wedlm_window_attn_rope", *rope_args(12)) == -2
+    base = [0, 1, 1, 8, 2, 1, 68, 16, 4, 4, 40, 0.1] + [1] * 9 + [0, 0, None]
+    # the unfused f32 path has no such limit: with D = 68 it gets past validation
+    # (a -2 here would mean the limit leaked into it); a null output stops it
+    # before any launch
+    a = list(base); a[19] = None
+    assert _raw("wedlm_window_attn", *a) == -1
     # a c5-sized call needs no split workspace
     assert W.wedlm_window_attn_workspace_size(1, 36, 16, 16, 32, 8, 128, 16, 1024) == 0
 

@@ -2,14 +2,15 @@
 
 The GPU computes the logits in fp32 from bf16 hidden states and projection
 rows and never stores them; the oracle forms them in float64 from the same
-stored values. Entropy |dH| <= 1e-3, argmax exact (a row whose two largest
-oracle logits lie within 1e-3 may take either, and is counted), score within
-the entropy bar (it is formed from the GPU's entropy), selection exact except
-for sequences the oracle flags as near ties. Shapes
-cover one, two and four 32-row blocks per workgroup, several row groups, a
-ragged last vocabulary tile and packed block, one to many rotations of the
-chunk loop and the full Qwen3-8B / Qwen2.5-7B projections (sampled
-sequences). The packed layout is checked element by element against its
+stored values. Entropy |dH| <= 1e-3; argmax exact, except that a row whose
+GPU argmax lies within 1e-4 of the oracle's largest logit is a flagged near
+tie (counted and reported); score within the entropy bar (it is formed from
+the GPU's entropy); selection exact on every slot, a decision the oracle flags
+as a near tie (within 1e-4) taking the GPU's choice for that comparison only.
+Shapes cover one, two and four 32-row blocks per workgroup, several row
+groups, a ragged last vocabulary tile and packed block, one to many rotations
+of the chunk loop and the full Qwen3-8B / Qwen2.5-7B projections (every
+sequence). The packed layout is checked element by element against its
 documented index formula.
 """
 
@@ -26,6 +27,7 @@ from .parity import ENTROPY_ATOL
 pytestmark = pytest.mark.gpu
 
 LAM, TAU = 0.1, 1.0
+TIE = 1e-4  # the near-tie band of the stated parity bar
 
 
 def _pack(hidden, V, w):
@@ -66,7 +68,7 @@ def _compare(gpu, h, w, filled, seqs, lam=LAM, tau=TAU, min_fill=1):
     h64 = to_f64(h)
     f = filled.cpu().numpy().astype(bool)
     z = _oracle_rows(h64, w, seqs)
-    H, a = oracle.vocab_entropy_argmax(z)
+    H, a = oracle.vocab_entropy_argmax(z, workers=8)
     near = 0
     flags = 0
     worst = 0.0
@@ -76,20 +78,20 @@ def _compare(gpu, h, w, filled, seqs, lam=LAM, tau=TAU, min_fill=1):
         for i in range(z.shape[1]):
             ga = int(gpu["argmax"][b, i])
             if ga != a[j, i]:
-                # only a near tie of the two largest logits may differ
-                assert z[j, i, ga] >= z[j, i].max() - 1e-3, ("argmax", b, i, ga, int(a[j, i]))
+                # a flagged near tie: the GPU's token is within the band of the maximum
+                assert 0 <= ga < z.shape[2], ("argmax", b, i, ga)
+                assert z[j, i, ga] > z[j, i].max() - TIE, ("argmax", b, i, ga, int(a[j, i]))
                 near += 1
-        r = oracle.select_slots(H[j], f[b], lam, tau, min_fill)
-        if r["flags"]:
-            flags += 1
-            continue
-        # the score carries the entropy's error; the decision must still agree
-        dS = np.abs(gpu["score"][b].astype(np.float64) - r["score"].astype(np.float64))
+        r = oracle.select_slots(H[j], f[b], lam, tau, min_fill, tie_eps=TIE,
+                                adopt=gpu["selected"][b])
+        flags += len(r["flags"])
+        # the score carries the entropy's error; every decision must still agree
+        dS = np.abs(gpu["score"][b].astype(np.float64) - r["score"])
         assert (dS <= ENTROPY_ATOL).all(), ("score", b, float(dS.max()))
         assert np.array_equal(gpu["selected"][b], r["selected"]), ("selected", b)
         worst = max(worst, float(dH.max()))
-    print(f"[lm_head] max |dH| {worst:.2e}, argmax near ties {near}, flagged sequences {flags}",
-          flush=True)
+    print(f"[lm_head] {len(seqs)} sequences: max |dH| {worst:.2e}, argmax near ties (< {TIE}) "
+          f"{near}, flagged selection decisions {flags}", flush=True)
     return near, flags
 
 
@@ -109,18 +111,17 @@ def test_lm_head_small(B, Wn, hidden, V, spike):
     print(f"[lm_head] B={B} W={Wn} hidden={hidden} V={V} spike={spike}", flush=True)
     h, w, filled = lm_head_inputs(B, Wn, hidden, V, "cuda", seed=B + V, spike=spike)
     gpu = _gpu(B, Wn, hidden, V, h, w, filled)
-    near, flags = _compare(gpu, h, w, filled, list(range(B)))
-    assert near <= 1
+    _compare(gpu, h, w, filled, list(range(B)))
     if spike is not None and spike[0] >= 16.0:
         assert gpu["selected"].sum() > B  # the threshold fired beyond the one-per-sequence floor
 
 
-@pytest.mark.parametrize("B,Wn,hidden,V,seqs", [
-    (16, 16, 4096, 151936, [0, 9]),   # Qwen3-8B projection, 256 rows
-    (1, 16, 4096, 151936, [0]),       # one sequence, 16 rows
-    (16, 32, 3584, 152064, [3]),      # Qwen2.5-7B projection, 512 rows
+@pytest.mark.parametrize("B,Wn,hidden,V", [
+    (16, 16, 4096, 151936),   # Qwen3-8B projection, 256 rows
+    (1, 16, 4096, 151936),    # one sequence, 16 rows
+    (16, 32, 3584, 152064),   # Qwen2.5-7B projection, 512 rows
 ])
-def test_lm_head_full_vocab_sampled(B, Wn, hidden, V, seqs):
+def test_lm_head_full_vocab(B, Wn, hidden, V):
     print(f"[lm_head] full B={B} W={Wn} hidden={hidden} V={V}", flush=True)
     h, w, filled = lm_head_inputs(B, Wn, hidden, V, "cuda", seed=7)
     gpu = _gpu(B, Wn, hidden, V, h, w, filled)
@@ -131,8 +132,8 @@ def test_lm_head_full_vocab_sampled(B, Wn, hidden, V, seqs):
     for b in range(B):
         assert gpu["selected"][b].any() == (~f[b]).any()
         assert not (gpu["selected"][b] & f[b]).any()
-    near, _ = _compare(gpu, h, w, filled, seqs)
-    assert near <= 1
+    # every sequence (float64 logits of all rows: up to ~620 MB on the host)
+    _compare(gpu, h, w, filled, list(range(B)))
 
 
 def test_lm_head_deterministic():

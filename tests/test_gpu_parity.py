@@ -112,6 +112,29 @@ def test_edge_cases(name, wl):
     _check(wl)
 
 
+@pytest.mark.parametrize("wl", [
+    # one sequence per page count: splits, a ragged last page, 4 row tiles
+    _variant(WL.QWEN3_8B_BS1, name="poison_bs1", B=3, prefix=("list", (77, 2047, 1000)), V=2048),
+    # 224 rows in row parts, ragged prefixes over split key ranges
+    _variant(WL.QWEN25_7B_RAGGED, name="poison_gqa7", B=4, prefix=("uniform", 1, 900), V=2048),
+    # no split (many groups)
+    _variant(WL.QWEN3_8B_STREAM, name="poison_layers", n_layers=6, B=6, V=2048,
+             fill=("frac", 0.0, 1.0), prefix=("uniform", 17, 500), steps=1),
+    _variant(WL.TINY_FP32, name="poison_fp32", B=3, prefix=("list", (40, 3, 17))),
+], ids=lambda w: w.name)
+def test_non_finite_page_tails_never_reach_the_output(wl):
+    # cache positions a sequence has not written (past prefix_len in its last
+    # page) hold NaN / Inf: both step forms still match the oracle
+    print(f"[parity] {wl.name}: NaN / Inf page tails", flush=True)
+    inp = make_step_inputs(wl)
+    gpu = gpu_step(wl, inp, poison=True)
+    fused = gpu_step(wl, inp, fused_rope=True, poison=True)
+    ref = oracle_step(wl, inp, gpu=gpu)
+    for out in (gpu, fused):
+        assert np.isfinite(out["attn_out_phys"]).all()
+        compare_step(wl, out, ref)
+
+
 def test_deterministic_bitwise():
     wl = _variant(WL.QWEN25_7B_RAGGED, name="determinism", B=4, V=20000)
     inp = make_step_inputs(wl)

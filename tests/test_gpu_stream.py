@@ -1,14 +1,17 @@
 """Streaming loop at the full 36-layer, BS=16 Qwen3-8B shape against the oracle (GPU).
 
-The GPU runs every layer of every step; the oracle replays the same steps on
-host copies of the same inputs. Every step's reorder, entropies, argmax,
-selection, commit lengths, cache slots and window state are compared; the
-attention output and the committed cache rows are compared on sampled layers
-(the oracle tracks only those layers' caches). Flagged near ties adopt the
-GPU's choice, as in the single-step tests.
+The GPU runs every layer of every step; the oracle replays the same steps in
+lockstep on host copies of the same inputs (each step's inputs are dropped
+once both sides have used them, so the whole 256-step loop fits in memory).
+Every step's reorder, entropies, argmax, selection, commit lengths, cache
+slots and window state are compared; the attention output and the committed
+cache rows are compared on sampled layers (the oracle tracks only those
+layers' caches). A flagged near-tie decision takes the GPU's choice for that
+comparison only; every slot of every selection is compared.
 """
 
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -28,9 +31,23 @@ pytestmark = pytest.mark.gpu
 
 
 ORDER_KEYS = ("perm", "inv", "pos", "run_len")
+# host threads for the oracle's entropy rows (the machine's CPU share)
+WORKERS = min(16, len(os.sched_getaffinity(0)))
 
 
-def _run_stream(wl, steps, sampled_layers, attend_steps, commit_rule="stream", fused_tail=False):
+def _to_host_f32(t):
+    """Exact float32 host copy of a bf16 / f32 device tensor (half the bytes of f64)."""
+    return t.detach().cpu().to(torch.float32).numpy()
+
+
+def _run_stream(wl, steps, sampled_layers, attend_steps, commit_rule="stream", fused_tail=False,
+                attend_after_len=None, progress_every=0):
+    """Run ``steps`` window steps on the GPU and in the oracle in lockstep.
+
+    attend_steps: steps whose attention is compared on the sampled layers;
+    attend_after_len: also the first step at which every sequence's prefix
+    has reached that length (e.g. just after the first page crossing).
+    """
     print(f"[stream] {wl.name} steps={steps} layers={sampled_layers} tau={wl.tau} "
           f"rule={commit_rule} fused_tail={fused_tail}", flush=True)
     dev = "cuda"
@@ -42,11 +59,18 @@ def _run_stream(wl, steps, sampled_layers, attend_steps, commit_rule="stream", f
     if fused_tail:
         # the first step's order; every later one is written by the previous tail
         step.reorder(st)
-    gpu_log, host_inputs = [], []
-    for s in range(steps):
+    gpu_log = []
+    attended = []
+    state = {"crossed": attend_after_len is None}
+
+    def gpu_step(s):
+        """Runs GPU step s; returns the host inputs of the oracle's step s."""
         q, k, v, logits = stream_step_inputs(wl, s, dev)
         mpl = L0 + wl.W * s
         rec_prefix_in = st.prefix_len.cpu().numpy()
+        attend = s in attend_steps
+        if not state["crossed"] and rec_prefix_in.min() >= attend_after_len:
+            state["crossed"] = attend = True
         # the order a step attends with: before the call under the fused tail
         # (which leaves the next step's order behind), after it otherwise
         order = {key: getattr(step, key).cpu().numpy() for key in ORDER_KEYS}
@@ -60,47 +84,26 @@ def _run_stream(wl, steps, sampled_layers, attend_steps, commit_rule="stream", f
         rec["tokens"] = st.tokens.cpu().numpy()
         rec["filled"] = st.filled.cpu().numpy()
         rec["prefix_len"] = st.prefix_len.cpu().numpy()
-        if s in attend_steps:
+        if attend:
             rec["attn"] = {i: to_f64(step.out_phys[l]) for i, l in enumerate(sampled_layers)}
+            attended.append((s, int(rec_prefix_in.min())))
         gpu_log.append(rec)
-        host_inputs.append((to_f64(q[sampled_layers]), to_f64(k[sampled_layers]),
-                            to_f64(v[sampled_layers]), to_f64(logits)))
-    # committed rows of the sampled layers, read back from the pages
-    final_len = st.prefix_len.cpu().numpy()
-    gpu_rows = {}
-    for i, l in enumerate(sampled_layers):
-        for b in range(wl.B):
-            n = int(final_len[b]) - int(inp["prefix_len"][b])
-            kr, vr = layout.read_rows(st.k_cache, st.v_cache, l, st.block_table[b].cpu(),
-                                      int(inp["prefix_len"][b]), n)
-            gpu_rows[(i, b)] = (to_f64(kr), to_f64(vr))
+        return (_to_host_f32(q[sampled_layers]), _to_host_f32(k[sampled_layers]),
+                _to_host_f32(v[sampled_layers]), _to_host_f32(logits))
 
-    ref_log = []
-    kc = [[np.asarray(x, np.float64) for x in inp["k_cache"][l]] for l in sampled_layers]
-    vc = [[np.asarray(x, np.float64) for x in inp["v_cache"][l]] for l in sampled_layers]
-    out = oracle.stream_loop(
-        inp["filled"], inp["tokens"], inp["prefix_len"], kc, vc, inp["block_table"], steps,
-        lambda s: host_inputs[s], wl.theta, wl.lam, wl.tau, wl.page_size, wl.min_fill, wl.mask_id,
-        attend=lambda s: range(len(sampled_layers)) if s in attend_steps else [],
-        track_layers=range(len(sampled_layers)),
-        override_selected=lambda s, b, sel: gpu_log[s]["selected"][b].astype(bool),
-        on_step=lambda s, r: ref_log.append(r), store=storage_rounding(wl.dtype),
-        commit_rule=commit_rule)
+    flags = [0]
 
-    flags = 0
-    for s in range(steps):
-        g, r = gpu_log[s], ref_log[s]
+    def compare(s, r):
+        g = gpu_log[s]
         assert np.array_equal(g["perm"], r["perm"]), ("perm", s)
         # the reorder reports the commit rule's count (the raw run when streaming)
         expect_run = [oracle.commit_count(x, wl.W, commit_rule) for x in r["run"]]
         assert np.array_equal(g["run_len"], expect_run), ("run", s)
         assert (np.abs(g["entropy"] - r["entropy"]) <= ENTROPY_ATOL).all(), ("entropy", s)
         assert np.array_equal(g["argmax"], r["argmax"]), ("argmax", s)
-        flagged = {b for b, _, _ in r["flags"]}
-        flags += len(r["flags"])
-        for b in range(wl.B):
-            if b not in flagged:
-                assert np.array_equal(g["selected"][b].astype(bool), r["selected"][b]), ("sel", s, b)
+        flags[0] += len(r["flags"])
+        # every slot: a flagged decision already took the GPU's choice
+        assert np.array_equal(g["selected"].astype(bool), r["selected"]), ("sel", s)
         assert np.array_equal(g["commit_len"], r["commit_len"]), ("commit_len", s)
         assert np.array_equal(g["cache_slot"], r["cache_slot"]), ("cache_slot", s)
         assert np.array_equal(g["tokens"], r["tokens"]), ("tokens", s)
@@ -111,29 +114,74 @@ def _run_stream(wl, steps, sampled_layers, attend_steps, commit_rule="stream", f
                 err = np.abs(g["attn"][i] - r["attn_out_phys"][i])
                 ok = err <= ATTN_ATOL + ATTN_RTOL * np.abs(r["attn_out_phys"][i])
                 assert ok.all(), ("attn", s, i, float(err.max()))
-    for (i, b), (kr, vr) in gpu_rows.items():
-        L = int(inp["prefix_len"][b])
-        ref_k = out["caches"][i][0][b][L:]
-        ref_v = out["caches"][i][1][b][L:]
-        assert kr.shape == ref_k.shape
-        # the oracle's cache holds its rows as stored (rounded once), like the GPU's
-        assert (np.abs(kr - ref_k) <= stored_pair_bound(ref_k, wl.dtype)).all(), ("cache k", i, b)
-        assert np.array_equal(vr, ref_v), ("cache v", i, b)
+            del g["attn"]
+        # keep only what the decoding counters need
+        ref_log.append({"prefix_len_in": r["prefix_len_in"], "selected": r["selected"],
+                        "commit_len": r["commit_len"]})
+        if progress_every and (s + 1) % progress_every == 0:
+            print(f"[stream] {wl.name}: step {s + 1}/{steps} ok, prefix "
+                  f"{int(r['prefix_len'].min())}..{int(r['prefix_len'].max())}", flush=True)
+
+    ref_log = []
+    kc = [[np.asarray(x, np.float64) for x in inp["k_cache"][l]] for l in sampled_layers]
+    vc = [[np.asarray(x, np.float64) for x in inp["v_cache"][l]] for l in sampled_layers]
+    init_len = np.asarray(inp["prefix_len"]).copy()
+    del inp["k_cache"], inp["v_cache"]
+
+    def attend(s):
+        return range(len(sampled_layers)) if "attn" in gpu_log[s] else []
+
+    out = oracle.stream_loop(
+        inp["filled"], inp["tokens"], inp["prefix_len"], kc, vc, inp["block_table"], steps,
+        gpu_step, wl.theta, wl.lam, wl.tau, wl.page_size, wl.min_fill, wl.mask_id,
+        attend=attend, track_layers=range(len(sampled_layers)),
+        adopt_selected=lambda s, b: gpu_log[s]["selected"][b].astype(bool),
+        on_step=compare, store=storage_rounding(wl.dtype), commit_rule=commit_rule,
+        workers=WORKERS)
+    del kc, vc
+    assert state["crossed"], "no step reached the requested prefix length"
+
+    # committed rows of the sampled layers, read back from the pages
+    final_len = st.prefix_len.cpu().numpy()
+    for i, l in enumerate(sampled_layers):
+        for b in range(wl.B):
+            L = int(init_len[b])
+            n = int(final_len[b]) - L
+            kr, vr = layout.read_rows(st.k_cache, st.v_cache, l, st.block_table[b].cpu(), L, n)
+            kr, vr = to_f64(kr), to_f64(vr)
+            ref_k = out["caches"][i][0][b][L:]
+            ref_v = out["caches"][i][1][b][L:]
+            assert kr.shape == ref_k.shape
+            # the oracle's cache holds its rows as stored (rounded once), like the GPU's
+            assert (np.abs(kr - ref_k) <= stored_pair_bound(ref_k, wl.dtype)).all(), ("cache k", i, b)
+            assert np.array_equal(vr, ref_v), ("cache v", i, b)
     total = int(sum(g["commit_len"].sum() for g in gpu_log))
     longest = int(max(g["commit_len"].max() for g in gpu_log))
     # the decoding counters of the two runs agree exactly
     cg = decode_counters([{"prefix_len_in": g["prefix_len_in"], "selected": g["selected"],
                            "commit_len": g["commit_len"]} for g in gpu_log], wl.W)
-    cr = decode_counters([{"prefix_len_in": r["prefix_len_in"], "selected": r["selected"],
-                           "commit_len": r["commit_len"]} for r in ref_log], wl.W)
+    cr = decode_counters(ref_log, wl.W)
     assert cg == cr, (cg, cr)
     print(f"[stream] {wl.name}: {steps} steps ok, committed {total}, longest commit {longest}, "
-          f"flags {flags}, p_cache {cg['p_cache']}, tokens/forward {cg['tokens_per_forward']:.3f}",
-          flush=True)
+          f"flags {flags[0]}, attention checked at (step, min prefix) {attended}, "
+          f"p_cache {cg['p_cache']}, tokens/forward {cg['tokens_per_forward']:.3f}", flush=True)
     return total, longest, cg
 
 
-def test_stream_full_shape_first_steps():
+@pytest.mark.timeout(900)
+def test_stream_full_shape_all_steps_fused_tail():
+    # the loop bench.py times: 36 layers, 16 sequences, vocabulary 151936, all
+    # 256 steps with the fused tail; attention on three layers at the first
+    # steps, just after every sequence's first page crossing (prefix 1040),
+    # spread over the run and at the last step
+    wl = WL.QWEN3_8B_STREAM
+    _run_stream(wl, steps=wl.steps, sampled_layers=[0, 17, 35],
+                attend_steps={0, 1, 64, 128, 192, wl.steps - 1}, fused_tail=True,
+                attend_after_len=wl.prefix[1] + wl.page_size, progress_every=32)
+
+
+def test_stream_full_shape_separate_tail_first_steps():
+    # the same loop with the three separate calls after the entropy pass
     _run_stream(WL.QWEN3_8B_STREAM, steps=12, sampled_layers=[0, 17, 35], attend_steps={0, 5, 11})
 
 

@@ -83,3 +83,13 @@ def test_argmax_lowest_index_on_ties():
     z = np.array([[1.0, 3.0, 3.0, 2.0], [5.0, 5.0, 5.0, 5.0], [0.0, -1.0, 0.0, 0.0]])
     _, a = vocab_entropy_argmax(z)
     assert a.tolist() == [1, 0, 0]
+
+
+def test_threaded_rows_are_bitwise_the_same():
+    # rows are independent: dealing them to threads changes no bit
+    z = np.random.default_rng(5).normal(0, 2, size=(7, 3, 4099))
+    z[2, 1, 17] += 30.0
+    H1, a1 = vocab_entropy_argmax(z)
+    for workers in (2, 5, 64):
+        H, a = vocab_entropy_argmax(z, workers=workers)
+        assert np.array_equal(H, H1) and np.array_equal(a, a1)

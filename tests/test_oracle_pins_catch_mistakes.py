@@ -95,8 +95,8 @@ def test_missing_scale_is_caught(monkeypatch):
 def test_penalty_sign_mistake_is_caught(monkeypatch):
     orig = select_mod.select_slots
 
-    def minus_penalty(entropy, filled, lam, tau, min_fill=1, tie_eps=1e-4):
-        return orig(entropy, filled, -lam, tau, min_fill, tie_eps)
+    def minus_penalty(entropy, filled, lam, tau, min_fill=1, tie_eps=1e-4, adopt=None):
+        return orig(entropy, filled, -lam, tau, min_fill, tie_eps, adopt)
     monkeypatch.setattr(t_sel, "select_slots", minus_penalty)
     case = next(c for c in t_sel.CASES if c["name"] == "distance_penalty_orders_slots")
     with pytest.raises(AssertionError):

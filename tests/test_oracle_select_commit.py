@@ -56,6 +56,48 @@ def test_tie_flags():
     assert s["flags"] == []
 
 
+def test_scores_and_decisions_are_float64():
+    # 1 - 2^-40 clears tau = 1 in float64; the float32 rounding of the same
+    # score would be exactly 1.0 and would not (strict comparison)
+    h = 1.0 - 2.0 ** -40
+    s = select_slots([h, 9.0], [False, False], 0.0, 1.0, 1)
+    assert s["score"].dtype == np.float64 and s["score"][0] == h
+    assert s["selected"].tolist() == [True, False] and not s["fallback"]
+    assert ("threshold", 0) in s["flags"]
+
+
+def test_adopt_takes_only_flagged_threshold_decisions():
+    # slot 0's score is within 1e-4 of tau: flagged, so the other side's
+    # decision for it is taken; slot 1 is far from every boundary
+    H = [1.00005, 5.0]
+    own = select_slots(H, [False, False], 0.0, 1.0, 1)
+    assert own["selected"].tolist() == [True, False] and own["fallback"]  # floor rule
+    s = select_slots(H, [False, False], 0.0, 1.0, 1, adopt=[True, False])
+    assert s["selected"].tolist() == [True, False] and not s["fallback"]  # adopted threshold
+    # an unflagged difference is not adopted: the caller's slot-by-slot
+    # comparison will see it
+    s = select_slots(H, [False, False], 0.0, 1.0, 1, adopt=[False, True])
+    assert s["selected"].tolist() == [True, False]
+    # far from the threshold nothing is adopted
+    s = select_slots([0.2, 3.0], [False, False], 0.1, 1.0, 1, adopt=[False, True])
+    assert s["selected"].tolist() == [True, False] and s["flags"] == []
+
+
+def test_adopt_floor_rule_tie():
+    # floor rule: slots 1 and 2 score 3.0 and 3.00005 (a near tie), slot 3 far above
+    H = [0.0, 2.9, 2.80005, 9.0]
+    f = [True, False, False, False]
+    own = select_slots(H, f, 0.1, 1.0, 1)
+    assert own["selected"].tolist() == [False, True, False, False]
+    assert own["flags"] == [("fallback", 2)]
+    s = select_slots(H, f, 0.1, 1.0, 1, adopt=[False, False, True, False])
+    assert s["selected"].tolist() == [False, False, True, False]
+    # a pick outside the tied set, or two picks, leave the oracle's own choice
+    for other in ([False, False, False, True], [False, True, True, False]):
+        s = select_slots(H, f, 0.1, 1.0, 1, adopt=other)
+        assert s["selected"].tolist() == [False, True, False, False]
+
+
 def test_commit_rejects_a_wrong_run():
     with pytest.raises(ValueError):
         commit_and_refill([1, -1], [True, False], 0, 2, [False, False], [0, 0], [0], 16)

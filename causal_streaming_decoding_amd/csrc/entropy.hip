@@ -22,7 +22,11 @@
 //   rows, forms entropy and score, and applies the threshold / floor rule.
 // k_step_tail: the same selection followed by the window-state commit and the
 //   next step's reorder, in one wavefront per sequence.
+// wedlm_entropy_select_noalloc runs the same two kernels with the chunk
+// partials in a fixed device array instead of a caller workspace.
 #include "window_ops.hpp"
+
+#include <mutex>
 
 namespace wedlm {
 
@@ -247,11 +251,11 @@ extern "C" size_t wedlm_entropy_select_workspace_size(int dtype, int B, int W, i
   return static_cast<size_t>(B) * W * pl.n_chunks * sizeof(EntPartial);
 }
 
-extern "C" int wedlm_entropy_select(int dtype, int B, int W, int V, const void* logits,
-                                    const uint8_t* filled, float lambda, float tau, int min_fill,
-                                    float* entropy, float* score, int32_t* argmax_tok,
-                                    uint8_t* selected, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+// Host-side checks shared by wedlm_entropy_select and its workspace-free form.
+static int validate_entropy_select(int dtype, int B, int W, int V, const void* logits,
+                                   const uint8_t* filled, float lambda, float tau, int min_fill,
+                                   const float* entropy, const float* score,
+                                   const int32_t* argmax_tok, const uint8_t* selected) {
   if (!valid_dtype(dtype)) return WEDLM_ERR_UNSUPPORTED;
   if (B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW || V <= 0) return WEDLM_ERR_INVALID;
   if (min_fill != 0 && min_fill != 1) return WEDLM_ERR_INVALID;
@@ -259,19 +263,88 @@ extern "C" int wedlm_entropy_select(int dtype, int B, int W, int V, const void* 
   if (!logits || !filled || !entropy || !score || !argmax_tok || !selected)
     return WEDLM_ERR_INVALID;
   if (1LL * B * W > 65535) return WEDLM_ERR_UNSUPPORTED;
+  return WEDLM_OK;
+}
+
+// The chunk-partial pass into `part`, then the per-sequence selection.
+static int run_entropy_select(int dtype, int B, int W, int V, const void* logits, EntPlan pl,
+                              EntPartial* part, const uint8_t* filled, float lambda, float tau,
+                              int min_fill, float* entropy, float* score, int32_t* argmax_tok,
+                              uint8_t* selected, hipStream_t s) {
+  launch_entropy_partials(dtype, B, W, V, logits, pl, part, s);
+  const int st = launch_status();
+  if (st != WEDLM_OK) return st;
+  return launch_entropy_select(part, pl.n_chunks, B, W, filled, lambda, tau, min_fill, entropy,
+                               score, argmax_tok, selected, s);
+}
+
+extern "C" int wedlm_entropy_select(int dtype, int B, int W, int V, const void* logits,
+                                    const uint8_t* filled, float lambda, float tau, int min_fill,
+                                    float* entropy, float* score, int32_t* argmax_tok,
+                                    uint8_t* selected, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  const int v = validate_entropy_select(dtype, B, W, V, logits, filled, lambda, tau, min_fill,
+                                        entropy, score, argmax_tok, selected);
+  if (v != WEDLM_OK) return v;
   EntPlan pl = plan_entropy(dtype, B, W, V);
   if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) pl.vec = false;
   const size_t need = static_cast<size_t>(B) * W * pl.n_chunks * sizeof(EntPartial);
   if (need > wedlm_entropy_select_workspace_size(dtype, B, W, V) ||
       workspace == nullptr || workspace_bytes < need)
     return WEDLM_ERR_WORKSPACE;
-  hipStream_t s = as_stream(stream);
-  EntPartial* part = static_cast<EntPartial*>(workspace);
-  launch_entropy_partials(dtype, B, W, V, logits, pl, part, s);
-  const int st = launch_status();
-  if (st != WEDLM_OK) return st;
-  return launch_entropy_select(part, pl.n_chunks, B, W, filled, lambda, tau, min_fill, entropy,
-                               score, argmax_tok, selected, s);
+  return run_entropy_select(dtype, B, W, V, logits, pl, static_cast<EntPartial*>(workspace),
+                            filled, lambda, tau, min_fill, entropy, score, argmax_tok, selected,
+                            as_stream(stream));
+}
+
+// ---- workspace-free form ------------------------------------------------------
+// The chunk partials go to a fixed array in device memory that the library
+// owns: each GPU the library runs on holds its own copy (allocated with the
+// code object, kept until the process ends). Host code never uses the array's
+// name as an address (in host code it is a stand-in, not a device pointer):
+// its device address is looked up once per device, with that device current,
+// and kept.
+static __device__ __align__(256) unsigned char scratch[WEDLM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of this device's scratch array (nullptr on a HIP error).
+static void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+extern "C" int wedlm_entropy_select_noalloc(int dtype, int B, int W, int V, const void* logits,
+                                            const uint8_t* filled, float lambda, float tau,
+                                            int min_fill, float* entropy, float* score,
+                                            int32_t* argmax_tok, uint8_t* selected,
+                                            void* stream) {
+  const int v = validate_entropy_select(dtype, B, W, V, logits, filled, lambda, tau, min_fill,
+                                        entropy, score, argmax_tok, selected);
+  if (v != WEDLM_OK) return v;
+  EntPlan pl = plan_entropy(dtype, B, W, V);
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) pl.vec = false;
+  const size_t need = static_cast<size_t>(B) * W * pl.n_chunks * sizeof(EntPartial);
+  if (need > WEDLM_NOALLOC_SCRATCH_BYTES) return WEDLM_ERR_SCRATCH_LIMIT;
+  void* part = scratch_on_current_device();
+  if (part == nullptr) return WEDLM_ERR_HIP;
+  // every partial is written by the chunk pass before the selection reads it:
+  // nothing has to start cleared
+  return run_entropy_select(dtype, B, W, V, logits, pl, static_cast<EntPartial*>(part), filled,
+                            lambda, tau, min_fill, entropy, score, argmax_tok, selected,
+                            as_stream(stream));
 }
 
 extern "C" int wedlm_select_commit_reorder(

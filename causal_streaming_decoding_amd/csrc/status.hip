@@ -8,8 +8,10 @@ extern "C" const char* wedlm_status_string(int status) {
     case WEDLM_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case WEDLM_ERR_WORKSPACE: return "workspace missing or too small";
     case WEDLM_ERR_HIP: return "HIP launch error";
+    case WEDLM_ERR_SCRATCH_LIMIT:
+      return "sizes need more than the library's fixed scratch (use the workspace form)";
     default: return "unknown status";
   }
 }
 
-extern "C" int wedlm_abi_version(void) { return (1 << 16) | 5; }
+extern "C" int wedlm_abi_version(void) { return (1 << 16) | 6; }

@@ -39,6 +39,8 @@ _SIGNATURES = {
     "wedlm_entropy_select_workspace_size": (_c_size, [_c_int] * 4),
     "wedlm_entropy_select": (_c_int, [_c_int] * 4 + [_p, _p, _c_float, _c_float, _c_int] + [_p] * 5
                              + [_c_size, _p]),
+    "wedlm_entropy_select_noalloc": (_c_int, [_c_int] * 4 + [_p, _p, _c_float, _c_float, _c_int]
+                                     + [_p] * 5),
     "wedlm_commit_prefix": (_c_int, [_c_int] * 9 + [_p] * 13 + [ctypes.c_int32, _p]),
     "wedlm_window_attn_rope": (_c_int, [_c_int] * 11 + [_c_float, _c_double] + [_p] * 12
                                + [_c_size, _c_int, _p]),
@@ -178,6 +180,13 @@ def wedlm_entropy_select(dtype, B, W, V, logits, filled, lam, tau, min_fill, ent
         dtype, B, W, V, _ptr(logits), _ptr(filled), float(lam), float(tau), int(min_fill),
         _ptr(entropy), _ptr(score), _ptr(argmax_tok), _ptr(selected), _ptr(workspace),
         workspace_bytes, _stream(stream)))
+
+
+def wedlm_entropy_select_noalloc(dtype, B, W, V, logits, filled, lam, tau, min_fill, entropy,
+                                 score, argmax_tok, selected, stream=None):
+    _check("wedlm_entropy_select_noalloc", lib().wedlm_entropy_select_noalloc(
+        dtype, B, W, V, _ptr(logits), _ptr(filled), float(lam), float(tau), int(min_fill),
+        _ptr(entropy), _ptr(score), _ptr(argmax_tok), _ptr(selected), _stream(stream)))
 
 
 def wedlm_lm_head_packed_size(dtype, hidden, V):

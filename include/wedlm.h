@@ -71,7 +71,8 @@ enum wedlm_status {
   WEDLM_ERR_INVALID = -1,     /* null pointer, size <= 0, Hq % Hkv != 0, W > 64, ... */
   WEDLM_ERR_UNSUPPORTED = -2, /* a shape or dtype the library has no kernel for   */
   WEDLM_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required    */
-  WEDLM_ERR_HIP = -4          /* the HIP runtime reported an error at launch        */
+  WEDLM_ERR_HIP = -4,         /* the HIP runtime reported an error at launch        */
+  WEDLM_ERR_SCRATCH_LIMIT = -5 /* sizes exceed the fixed scratch of a *_noalloc call */
 };
 
 /* Element types. */
@@ -267,6 +268,36 @@ int wedlm_entropy_select(int dtype, int B, int W, int V, const void* logits, con
                          float lambda, float tau, int min_fill, float* entropy, float* score,
                          int32_t* argmax_tok, uint8_t* selected, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Size of the fixed device scratch of wedlm_entropy_select_noalloc (per GPU). */
+#define WEDLM_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/*
+ * wedlm_entropy_select_noalloc - wedlm_entropy_select without a workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same operation, arguments (minus workspace / workspace_bytes), layouts,
+ * results (bitwise those of wedlm_entropy_select on the same inputs) and
+ * errors as wedlm_entropy_select. The per-chunk partial reductions go to a
+ * fixed array in device memory that the library owns: WEDLM_NOALLOC_SCRATCH_BYTES
+ * (4 MiB) on every GPU the library runs on, held until the process ends. Sizes
+ * whose partials need more - wedlm_entropy_select_workspace_size(dtype, B, W, V)
+ * above 4 MiB, e.g. B * W rows of a 152k vocabulary beyond about 26k rows -
+ * return WEDLM_ERR_SCRATCH_LIMIT before anything is enqueued. The call
+ * allocates and frees nothing (the array's device address is looked up once
+ * per device, on the first call with that device current; a failure there
+ * returns WEDLM_ERR_HIP).
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (different streams, or other host threads) race and may return
+ * wrong results; calls ordered on one stream are safe. Nothing in the array
+ * has to start cleared: each call writes every partial before reading it.
+ */
+int wedlm_entropy_select_noalloc(int dtype, int B, int W, int V, const void* logits,
+                                 const uint8_t* filled, float lambda, float tau, int min_fill,
+                                 float* entropy, float* score, int32_t* argmax_tok,
+                                 uint8_t* selected, void* stream);
 
 /* Bytes of the packed projection wedlm_lm_head_pack writes (0 for an unsupported shape). */
 size_t wedlm_lm_head_packed_size(int dtype, int hidden, int V);

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(W.LIB_PATH),
 
 def test_exports_every_declared_function():
     declared = W.header_functions()
-    assert len(declared) == 18
+    assert len(declared) == 19
     lib = W.lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -31,8 +31,9 @@ def test_status_strings_and_version():
     assert "unsupported" in W.wedlm_status_string(-2)
     assert "workspace" in W.wedlm_status_string(-3)
     assert W.wedlm_abi_version() >> 16 == 1
-    assert W.wedlm_abi_version() & 0xffff >= 5  # fused RoPE, LM head, commit rules, step tail,
-    #                                               attention flags
+    assert W.wedlm_abi_version() & 0xffff >= 6  # fused RoPE, LM head, commit rules, step tail,
+    #                                               attention flags, workspace-free selection
+    assert "scratch" in W.wedlm_status_string(-5)
 
 
 def _raw(name, *args):
@@ -233,3 +234,19 @@ def test_lm_head_validation_and_workspace():
     assert _raw("wedlm_lm_head_select", *a) == -3         # workspace too small
     a = list(good); a[15] = None
     assert _raw("wedlm_lm_head_select", *a) == -3
+
+
+def test_entropy_select_noalloc_validation():
+    # host checks come before the scratch lookup: none of these touches a GPU
+    args = [1, 16, 16, 151936, 1, 1, 0.1, 1.0, 1, 1, 1, 1, 1, None]
+    a = list(args); a[4] = None
+    assert _raw("wedlm_entropy_select_noalloc", *a) == -1      # null logits
+    a = list(args); a[8] = 2
+    assert _raw("wedlm_entropy_select_noalloc", *a) == -1      # min_fill
+    a = list(args); a[0] = 9
+    assert _raw("wedlm_entropy_select_noalloc", *a) == -2      # dtype
+    # partials beyond the fixed 4 MiB scratch: refused with its own status
+    big = W.wedlm_entropy_select_workspace_size(1, 1000, 64, 151936)
+    assert big > 4 << 20
+    a = list(args); a[1] = 1000; a[2] = 64
+    assert _raw("wedlm_entropy_select_noalloc", *a) == -5

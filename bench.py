@@ -67,6 +67,11 @@ def parse():
                          "instead of the fused tail")
     ap.add_argument("--config-steps", type=int, default=200)
     ap.add_argument("--config-warmup", type=int, default=20)
+    ap.add_argument("--only", default=None,
+                    help="with --all-configs: time only this workload (e.g. to trace it alone)")
+    ap.add_argument("--reps", type=int, default=3,
+                    help="timed repetitions of the --steps steps, each from the same start "
+                         "state (restored from a snapshot between them); the median is reported")
     return ap.parse_args()
 
 
@@ -161,14 +166,41 @@ def cpu_baseline(wl, inp, host_steps):
                       f"{out['total_committed']} tokens committed)"}
 
 
+def entropy_report(entropy, filled, score, tau):
+    """Histogram of the slot entropies (nats, unit bins) and how often the
+    threshold fires among mask slots: the logits' regime, from the kernels'
+    own output."""
+    import numpy as np
+
+    H = np.asarray(entropy, np.float64).ravel()
+    mask = ~np.asarray(filled, bool).ravel()
+    sc = np.asarray(score, np.float64).ravel()
+    top = int(np.ceil(max(float(H.max()), 1.0)))
+    counts, edges = np.histogram(H, bins=np.arange(0, top + 1))
+    return {"unit": "nats", "bins": [f"[{int(a)},{int(b)})" for a, b in zip(edges[:-1], edges[1:])],
+            "counts": counts.tolist(), "slots": int(H.size), "min": float(H.min()),
+            "median": float(np.median(H)), "max": float(H.max()),
+            "mask_slots": int(mask.sum()),
+            "mask_slots_below_tau": int((sc[mask] < tau).sum())}
+
+
 def config_latencies(args):
     """Single-step latency of each single-step workload (one JSON line each).
 
     Every timed step starts from the same state (restored outside the timed
     pair) and follows a 512 MB read that evicts the caches' contents, so the
-    KV prefix and logits come from HBM as in a real decoder. Reports the
-    median, p10 and p90 of the whole step and of the attention and entropy
-    calls, with the HBM rate of the algorithmic bytes at the median.
+    KV prefix and logits come from HBM as in a real decoder. The step is the
+    streaming loop's launch sequence (reorder, attention with fused RoPE and
+    append, split combine where split, entropy pass, fused tail), captured
+    once as a HIP graph and replayed between two timing events: nothing else
+    sits between the step's kernels. Reported: the median, p10 and p90 of the
+    replayed step; the same step launched eagerly (one host call per kernel);
+    and, from an eager pass with timing events between the kernels, the
+    attention and entropy + tail segments (each event record adds a few
+    microseconds of idle GPU, so these are upper bounds of the kernels; the
+    kernel trace gives their own durations). HBM rates use the algorithmic
+    bytes over the segment medians. The slot entropies of the step are
+    reported as a histogram.
     """
     import numpy as np
     import torch
@@ -185,9 +217,12 @@ def config_latencies(args):
     flush_sink = torch.empty((), dtype=torch.float32, device=dev)
     hev = HipEvents(torch.cuda.current_stream().cuda_stream)
     labels = ("step_start", "attn_start", "attn_end", "entropy_end", "step_end")
+    n = args.config_warmup + args.config_steps
     for wl in WL.ALL:
         if wl.steps > 1:
             continue  # the streaming loop is the default bench line
+        if args.only is not None and wl.name != args.only:
+            continue
         print(f"[bench] {wl.name}", file=sys.stderr, flush=True)
         inp = make_step_inputs(wl)
         st, q, k, v, logits, mpl = upload_step_inputs(wl, inp, dev)
@@ -195,47 +230,60 @@ def config_latencies(args):
         # and next reorder run as one tail call after the entropy pass
         step = make_window_step(wl, inp, dev, mpl, fused_tail=True)
         snap = st.snapshot()
-        n = args.config_warmup + args.config_steps
-        ev = [{lab: hev.create() for lab in labels} for _ in range(n)]
-        for i in range(n):
-            st.restore(snap)
-            torch.sum(flush, dim=0, out=flush_sink)
-            e = ev[i]
-            hev.record(e["step_start"])
-            step.run(st, q, k, v, logits, mark=lambda lab, e=e: hev.record(e[lab]))
-            hev.record(e["step_end"])
-        torch.cuda.synchronize()
-        timed = ev[args.config_warmup:]
-        span = {name: np.array([hev.elapsed_ms(x[a], x[b]) for x in timed]) * 1e3
-                for name, (a, b) in {"step": ("step_start", "step_end"),
-                                     "attn": ("attn_start", "attn_end"),
-                                     "entropy": ("attn_end", "entropy_end")}.items()}
-        hev.destroy()
+        graph = step.capture(st, q, k, v, logits)
+
+        def timed(launch, marks):
+            ev = [{lab: hev.create() for lab in labels} for _ in range(n)]
+            for i in range(n):
+                st.restore(snap)
+                torch.sum(flush, dim=0, out=flush_sink)
+                e = ev[i]
+                hev.record(e["step_start"])
+                launch((lambda lab, e=e: hev.record(e[lab])) if marks else None)
+                hev.record(e["step_end"])
+            torch.cuda.synchronize()
+            out = {}
+            spans = {"step": ("step_start", "step_end")}
+            if marks:
+                spans.update(attn=("attn_start", "attn_end"), entropy=("attn_end", "entropy_end"))
+            for name, (a, b) in spans.items():
+                out[name] = np.array([hev.elapsed_ms(x[a], x[b]) for x in ev[args.config_warmup:]]) * 1e3
+            hev.destroy()
+            return out
+
+        g_span = timed(lambda mark: graph.replay(), False)
+        e_span = timed(lambda mark: step.run(st, q, k, v, logits), False)
+        m_span = timed(lambda mark: step.run(st, q, k, v, logits, mark=mark), True)
         L = np.asarray(inp["prefix_len"], np.int64)
         commits = step.commit_len.cpu().numpy()
         b = step_bytes(wl, L, commits)
         attn_bytes = b["kv"] + b["window"] + b["attn_out"] + b["commit"]
+        ent = entropy_report(step.entropy.cpu().numpy(), inp["filled"], step.score.cpu().numpy(),
+                             wl.tau)
 
         def stats(x):
             return {"median": float(np.median(x)), "p10": float(np.percentile(x, 10)),
                     "p90": float(np.percentile(x, 90))}
 
-        med = {k_: float(np.median(v_)) for k_, v_ in span.items()}
+        med = {k_: float(np.median(v_)) for k_, v_ in m_span.items()}
+        step_bytes_total = sum(b.values())
         line = {
             "workload": wl.name, "dtype": wl.dtype, "steps": args.config_steps,
             "warmup": args.config_warmup, "unit": "us",
-            "step_us": stats(span["step"]), "attn_us": stats(span["attn"]),
-            "entropy_us": stats(span["entropy"]),
+            "step_us": stats(g_span["step"]), "step_launch": "one HIP graph replay",
+            "eager_step_us": stats(e_span["step"]),
+            "attn_segment_us": stats(m_span["attn"]),
+            "entropy_tail_segment_us": stats(m_span["entropy"]),
+            "step_algorithmic_bytes": int(step_bytes_total),
+            "step_hbm_gbps_at_median": step_bytes_total / (float(np.median(g_span["step"])) * 1e-6) / 1e9,
             "attn_algorithmic_bytes": int(attn_bytes), "logits_bytes": int(b["logits"]),
-            "attn_hbm_gbps_at_median": attn_bytes / (med["attn"] * 1e-6) / 1e9,
-            "entropy_hbm_gbps_at_median": b["logits"] / (med["entropy"] * 1e-6) / 1e9,
-            "attn_plus_entropy_hbm_frac_at_median":
-                (attn_bytes + b["logits"]) / ((med["attn"] + med["entropy"]) * 1e-6) / 1e9
-                / HBM_PEAK_GBPS,
+            "attn_hbm_gbps_at_segment_median": attn_bytes / (med["attn"] * 1e-6) / 1e9,
+            "entropy_hbm_gbps_at_segment_median": b["logits"] / (med["entropy"] * 1e-6) / 1e9,
+            "entropy_histogram": ent,
             "data": "synthetic",
         }
         print(json.dumps(line), flush=True)
-        del st, q, k, v, logits, step
+        del st, q, k, v, logits, step, graph
         torch.cuda.empty_cache()
 
 
@@ -595,8 +643,6 @@ def main():
         q, k, v, logits = ins[s]
         step.run(st, q, k, v, logits, max_prefix_len=L0 + wl.W * s, commit_len=commit_log[s])
     torch.cuda.synchronize()
-    st.restore(snap)
-    commit_log.zero_()
     # the library launches on the stream it is given; None is the null stream,
     # which is torch's current stream here
     hev = HipEvents(torch.cuda.current_stream().cuda_stream)
@@ -605,26 +651,49 @@ def main():
     # record costs GPU idle time, which would otherwise be part of every step
     every = max(args.event_every, 1)
     sampled = list(range(0, K, every))
-    ev = {s: {lab: hev.create() for lab in labels} for s in sampled}
-    torch.cuda.synchronize()
+    reps = max(args.reps, 1)
+    elapsed_reps, attn_ms, ent_ms, commits_reps = [], [], [], []
+    for r in range(reps):
+        st.restore(snap)
+        commit_log.zero_()
+        ev = {s: {lab: hev.create() for lab in labels} for s in sampled}
+        torch.cuda.synchronize()
+        print(f"[bench] timing {K} steps (repetition {r + 1} of {reps})", file=sys.stderr,
+              flush=True)
+        t0 = time.perf_counter()
+        for s in range(K):
+            q, k, v, logits = ins[s % n_inputs]
+            mark = (lambda lab, e=ev[s]: hev.record(e[lab])) if s in ev else None
+            step.run(st, q, k, v, logits, max_prefix_len=L0 + wl.W * s, commit_len=commit_log[s],
+                     mark=mark)
+        torch.cuda.synchronize()
+        elapsed_reps.append(time.perf_counter() - t0)
+        attn_ms += [hev.elapsed_ms(ev[s]["attn_start"], ev[s]["attn_end"]) for s in sampled]
+        ent_ms += [hev.elapsed_ms(ev[s]["attn_end"], ev[s]["entropy_end"]) for s in sampled]
+        hev.destroy()
+        commits_reps.append(commit_log[:K].cpu().numpy().astype(np.int64))
+    for c in commits_reps[1:]:
+        if not np.array_equal(c, commits_reps[0]):
+            raise RuntimeError("repetitions from the same state committed different tokens")
+    elapsed = float(np.median(elapsed_reps))
+    attn_ms = np.array(attn_ms)
+    ent_ms = np.array(ent_ms)
+    commits = commits_reps[0]
 
-    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
+    # untimed replay of the same steps for the logits' entropy regime
+    st.restore(snap)
+    ent_all, score_all, filled_all = [], [], []
     for s in range(K):
         q, k, v, logits = ins[s % n_inputs]
-        mark = (lambda lab, e=ev[s]: hev.record(e[lab])) if s in ev else None
-        step.run(st, q, k, v, logits, max_prefix_len=L0 + wl.W * s, commit_len=commit_log[s],
-                 mark=mark)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+        filled_all.append(st.filled.cpu().numpy().astype(bool))
+        step.run(st, q, k, v, logits, max_prefix_len=L0 + wl.W * s)
+        ent_all.append(step.entropy.cpu().numpy())
+        score_all.append(step.score.cpu().numpy())
+    ent_hist = entropy_report(np.stack(ent_all), np.stack(filled_all), np.stack(score_all), wl.tau)
 
-    commits = commit_log[:K].cpu().numpy().astype(np.int64)
-    attn_ms = np.array([hev.elapsed_ms(ev[s]["attn_start"], ev[s]["attn_end"]) for s in sampled])
-    ent_ms = np.array([hev.elapsed_ms(ev[s]["attn_end"], ev[s]["entropy_end"]) for s in sampled])
-    hev.destroy()
     L = np.asarray(inp["prefix_len"], np.int64).copy()
     tot = {"kv": 0, "window": 0, "attn_out": 0, "commit": 0, "logits": 0}
-    attn_bytes = ent_bytes = 0    # over the sampled steps
+    attn_bytes = ent_bytes = 0    # over the sampled steps of one repetition
     attn_bytes_all = 0            # over every timed step (as the byte counters see them)
     for s in range(K):
         b = step_bytes(wl, L, commits[s])
@@ -632,16 +701,19 @@ def main():
             tot[key] += b[key]
         a = b["kv"] + b["window"] + b["attn_out"] + b["commit"]
         attn_bytes_all += a
-        if s in ev:
+        if s in sampled:
             attn_bytes += a
             ent_bytes += b["logits"]
         L += commits[s]
+    attn_bytes *= reps  # the event samples of every repetition
+    ent_bytes *= reps
     total_bytes = sum(tot.values())
     committed = int(commits.sum())
     attn_gbps = attn_bytes / (attn_ms.sum() * 1e-3) / 1e9
     ent_gbps = ent_bytes / (ent_ms.sum() * 1e-3) / 1e9
     both_gbps = (attn_bytes + ent_bytes) / ((attn_ms.sum() + ent_ms.sum()) * 1e-3) / 1e9
     step_gbps = total_bytes / elapsed / 1e9
+    alg_per_launch = attn_bytes / (len(sampled) * reps)
 
     if args.calibrate_copy:
         a = torch.empty(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
@@ -650,7 +722,10 @@ def main():
         torch.cuda.synchronize()
 
     from causal_streaming_decoding_amd.profiling import read_traffic
-    traffic = read_traffic(os.path.join(ROOT, "profiles", TRAFFIC_RECORD), wl.name, K)
+    ratio = read_traffic(os.path.join(ROOT, "profiles", TRAFFIC_RECORD), wl.name)
+    # counted bytes per launch = the recorded counted / algorithmic ratio times
+    # this run's algorithmic bytes per launch (null once the kernel changed)
+    traffic = None if ratio is None else ratio * alg_per_launch
 
     cpu = None
     if args.cpu_baseline_steps > 0:
@@ -677,6 +752,9 @@ def main():
                    "initial_prefix": int(L0), "page_size": wl.page_size,
                    "step_tail": "separate" if args.separate_tail else "fused",
                    "parallelism": "single GPU"},
+        "timing": f"median of {reps} repetitions of steps 0..{K - 1} from the start state "
+                  f"(window-steps/s per repetition: "
+                  f"{', '.join(f'{K / e:.1f}' for e in elapsed_reps)})",
         "committed_tokens": committed,
         "committed_tokens_per_s": committed / elapsed,
         "step_hbm_gbps": step_gbps,
@@ -685,12 +763,15 @@ def main():
         "attn_plus_entropy_hbm_frac": both_gbps / HBM_PEAK_GBPS,
         "entropy_hbm_gbps": ent_gbps,
         "bytes_per_step_avg": {k_: v_ / K for k_, v_ in tot.items()},
+        "entropy_histogram": ent_hist,
         "roofline": {"kernel": "k_window_attn_bf16", "bound": "hbm", "achieved": attn_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": attn_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic, "avg_launch_ms": float(attn_ms.mean()),
-                     "algorithmic_bytes_per_launch": attn_bytes / len(sampled),
+                     "traffic": traffic, "traffic_over_algorithmic": ratio,
+                     "avg_launch_ms": float(attn_ms.mean()),
+                     "algorithmic_bytes_per_launch": alg_per_launch,
                      "algorithmic_bytes_per_launch_all_steps": attn_bytes_all / K,
-                     "timed_launches": f"{len(sampled)} of {K} (every {every}th step)"},
+                     "timed_launches": f"{len(sampled)} of {K} (every {every}th step) in each "
+                                       f"of {reps} repetitions"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

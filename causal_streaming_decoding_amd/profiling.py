@@ -17,7 +17,7 @@ Usage (the second form summarises ``bench.py --all-configs``, the third
 ``bench.py --lm-head``)::
 
     python -m causal_streaming_decoding_amd.profiling configs --configs-jsonl <file> \\
-        --trace <dir> --out-md profiles/<name>.md
+        --trace <workload>=<dir> [--trace ...] --out-md profiles/<name>.md
     python -m causal_streaming_decoding_amd.profiling \\
         --trace <out>/prof_trace --fetch <out>/prof_fetch \\
         --write <out>/prof_write --bench-json <out>/prof_bench.json \\
@@ -156,46 +156,65 @@ def summarize(trace, fetch, write, bench_json, steps, out_md, out_traffic, comma
         f.write(f"fetch_bytes_per_launch: {a_fetch:.0f}\n")
         f.write(f"write_bytes_per_launch: {a_write:.0f}\n")
         f.write(f"algorithmic_bytes_per_launch: {alg:.0f}\n")
+        f.write(f"counted_over_algorithmic: {(a_fetch + a_write) / alg:.4f}\n")
         f.write(f"fetch_factor: {f_fac:.6f}\n")
         f.write(f"write_factor: {w_fac:.6f}\n")
         f.write(f"command_fetch: {command_fetch}\n")
         f.write(f"command_write: {command_write}\n")
 
 
-def summarize_configs(configs_jsonl, trace_dir, out_md, command_bench, command_trace):
-    """Single-step latencies of the other workloads (bench.py --all-configs) and
-    the kernel durations of a traced run of the same mode, per launch shape."""
+def summarize_configs(configs_jsonl, traces, out_md, command_bench, command_trace):
+    """Single-step latencies of the other workloads (bench.py --all-configs) and,
+    per workload, the kernel durations of a traced run of that workload alone
+    (``traces``: [(workload, trace dir)]; ``command_trace`` may hold a
+    ``{workload}`` placeholder)."""
     import statistics
 
     rows = [json.loads(ln) for ln in open(configs_jsonl) if ln.startswith("{")]
     lines = ["# Single-step latencies of the parity workloads", "",
              "MI355X (gfx950). Each timed step starts from the same state and follows a 512 MB "
              "read that evicts the caches; times in microseconds (median, p10, p90 over the timed "
-             "steps). HBM rates are algorithmic bytes over the median. In the commands, `<repo>` "
-             "is the repository root.", "", "```", command_bench, "```", "",
-             "| workload | step median | p10 | p90 | attention | entropy+select | "
-             "attention GB/s | entropy GB/s |", "|---|---|---|---|---|---|---|---|"]
+             "steps). *graph*: the step captured once as a HIP graph and replayed between two "
+             "timing events (nothing else between its kernels); *eager*: the same launches as one "
+             "host call each. The attention and entropy + tail segments come from an eager pass "
+             "with timing events between the kernels (each record idles the GPU a few "
+             "microseconds: upper bounds); HBM rates are algorithmic bytes over those medians. "
+             "H: slot entropies in nats (min / median), and the mask slots whose score clears the "
+             "threshold. In the commands, `<repo>` is the repository root.", "",
+             "```", command_bench, "```", "",
+             "| workload | graph step median | p10 | p90 | eager step | attention segment | "
+             "entropy + tail segment | step GB/s | attention GB/s | entropy GB/s | H min / median "
+             "| mask slots below tau |", "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
+        h = r["entropy_histogram"]
         lines.append(
             f"| `{r['workload']}` | {r['step_us']['median']:.1f} | {r['step_us']['p10']:.1f} | "
-            f"{r['step_us']['p90']:.1f} | {r['attn_us']['median']:.1f} | "
-            f"{r['entropy_us']['median']:.1f} | {r['attn_hbm_gbps_at_median']:.0f} | "
-            f"{r['entropy_hbm_gbps_at_median']:.0f} |")
-    per = {}
-    with open(os.path.join(trace_dir, "run_kernel_trace.csv")) as f:
-        for r in csv.DictReader(f):
-            n = short_name(r["Kernel_Name"])
-            if not n.startswith("wedlm::"):
-                continue
-            key = (n, int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1),
-                   int(r["Grid_Size_Y"]), int(r["Workgroup_Size_X"]))
-            per.setdefault(key, []).append(
-                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    lines += ["", "## Kernel durations by launch shape", "", "```", command_trace, "```", "",
-              "| kernel | blocks x rows | threads | launches | median us |",
-              "|---|---|---|---|---|"]
-    for (n, gx, gy, wg), v in sorted(per.items(), key=lambda kv: -statistics.median(kv[1])):
-        lines.append(f"| `{n}` | {gx} x {gy} | {wg} | {len(v)} | {statistics.median(v):.2f} |")
+            f"{r['step_us']['p90']:.1f} | {r['eager_step_us']['median']:.1f} | "
+            f"{r['attn_segment_us']['median']:.1f} | {r['entropy_tail_segment_us']['median']:.1f} | "
+            f"{r['step_hbm_gbps_at_median']:.0f} | {r['attn_hbm_gbps_at_segment_median']:.0f} | "
+            f"{r['entropy_hbm_gbps_at_segment_median']:.0f} | {h['min']:.2f} / {h['median']:.2f} | "
+            f"{h['mask_slots_below_tau']} of {h['mask_slots']} |")
+    lines += ["", "Entropy histograms (unit bins, nats): "]
+    for r in rows:
+        h = r["entropy_histogram"]
+        nz = [f"{b} {c}" for b, c in zip(h["bins"], h["counts"]) if c]
+        lines.append(f"* `{r['workload']}`: " + ", ".join(nz))
+    lines += ["", "## Kernel durations per workload", "", "```", command_trace, "```"]
+    for workload, trace_dir in traces:
+        per = {}
+        with open(os.path.join(trace_dir, "run_kernel_trace.csv")) as f:
+            for r in csv.DictReader(f):
+                n = short_name(r["Kernel_Name"])
+                if not n.startswith("wedlm::"):
+                    continue
+                key = (n, int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1),
+                       int(r["Grid_Size_Y"]), int(r["Workgroup_Size_X"]))
+                per.setdefault(key, []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines += ["", f"`{workload}`", "", "| kernel | blocks x rows | threads | launches | median us |",
+                  "|---|---|---|---|---|"]
+        for (n, gx, gy, wg), v in sorted(per.items(), key=lambda kv: -statistics.median(kv[1])):
+            lines.append(f"| `{n}` | {gx} x {gy} | {wg} | {len(v)} | {statistics.median(v):.2f} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -269,11 +288,14 @@ def summarize_lm_head(bench_jsonl, trace, fetch, write, out_md, command_bench, c
         f.write("\n".join(out) + "\n")
 
 
-def read_traffic(path, workload, steps):
-    """Counted HBM bytes per attention launch, or None when the record does not apply.
+def read_traffic(path, workload):
+    """Counted HBM bytes over algorithmic bytes of the attention launch, or None
+    when the record does not apply.
 
-    The record applies only to the same workload and step count and to the
-    kernel source it was measured on.
+    The ratio, not a byte count, is what carries over between runs of
+    different lengths (the prefix, hence the bytes per launch, grows with the
+    steps). The record applies only to the same workload and to the kernel
+    source it was measured on.
     """
     if not os.path.exists(path):
         return None
@@ -283,10 +305,10 @@ def read_traffic(path, workload, steps):
             if ": " in ln:
                 k, v = ln.rstrip("\n").split(": ", 1)
                 rec[k] = v
-    if (rec.get("source_sha256") != attn_source_hash() or rec.get("workload") != workload
-            or int(rec.get("steps", -1)) != steps):
+    if rec.get("source_sha256") != attn_source_hash() or rec.get("workload") != workload:
         return None
-    return float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
+    counted = float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
+    return counted / float(rec["algorithmic_bytes_per_launch"])
 
 
 def main():
@@ -308,12 +330,14 @@ def main():
         ap = argparse.ArgumentParser()
         ap.add_argument("mode")
         ap.add_argument("--configs-jsonl", required=True)
-        ap.add_argument("--trace", required=True)
+        ap.add_argument("--trace", action="append", required=True,
+                        help="WORKLOAD=DIR, one per workload traced alone")
         ap.add_argument("--out-md", required=True)
         ap.add_argument("--command-bench", default="")
         ap.add_argument("--command-trace", default="")
         a = ap.parse_args()
-        summarize_configs(a.configs_jsonl, a.trace, a.out_md, a.command_bench, a.command_trace)
+        traces = [tuple(t.split("=", 1)) for t in a.trace]
+        summarize_configs(a.configs_jsonl, traces, a.out_md, a.command_bench, a.command_trace)
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True)

@@ -213,6 +213,30 @@ class WindowStep:
         self.entropy_select(st, logits, stream)
         if mark is not None:
             mark("entropy_end")
+        self._commit_after_select(st, k, v, commit_len, stream)
+
+    def capture(self, st, q, k, v, logits, max_prefix_len=None, commit_len=None):
+        """A HIP graph of one whole step (``run`` with these arguments), to replay.
+
+        Every launch of the step becomes a kernel node (the step enqueues no
+        copy or memset), so a replay costs one graph launch instead of one
+        host call per kernel. The graph reads and writes the same device
+        buffers at every replay: it runs the step on whatever window state
+        ``st`` holds then (restore a snapshot between replays to repeat one
+        step). It includes the reorder when ``st`` is not already ordered by
+        this step; ``st.ordered_by`` is left as it was, since capturing runs
+        nothing.
+        """
+        self._attn_mpl(max_prefix_len)  # any workspace growth happens before capture
+        ordered = st.ordered_by
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            # stream=None: the library launches on the capturing stream
+            self.run(st, q, k, v, logits, max_prefix_len=max_prefix_len, commit_len=commit_len)
+        st.ordered_by = ordered
+        return g
+
+    def _commit_after_select(self, st, k, v, commit_len, stream):
         # the commit below changes the window without reordering it
         st.ordered_by = None
         if self.fused_rope and self.fused_append:

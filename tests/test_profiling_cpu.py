@@ -17,18 +17,19 @@ def test_short_name_strips_return_type_and_arguments():
 def _record(tmp_path, sha, workload="w", steps=256):
     p = tmp_path / "t.txt"
     p.write_text(f"kernel: k\nsource_sha256: {sha}\nworkload: {workload}\nsteps: {steps}\n"
-                 "fetch_bytes_per_launch: 100\nwrite_bytes_per_launch: 20\n")
+                 "fetch_bytes_per_launch: 100\nwrite_bytes_per_launch: 20\n"
+                 "algorithmic_bytes_per_launch: 96\n")
     return str(p)
 
 
 def test_traffic_record_applies_only_to_the_measured_source(tmp_path):
     good = _record(tmp_path, profiling.attn_source_hash())
-    assert profiling.read_traffic(good, "w", 256) == 120.0
-    assert profiling.read_traffic(good, "other", 256) is None
-    assert profiling.read_traffic(good, "w", 8) is None
+    # the counted / algorithmic ratio, whatever the step count of the reader
+    assert profiling.read_traffic(good, "w") == 120.0 / 96.0
+    assert profiling.read_traffic(good, "other") is None
     stale = _record(tmp_path, "0" * 64)
-    assert profiling.read_traffic(stale, "w", 256) is None
-    assert profiling.read_traffic(str(tmp_path / "missing.txt"), "w", 256) is None
+    assert profiling.read_traffic(stale, "w") is None
+    assert profiling.read_traffic(str(tmp_path / "missing.txt"), "w") is None
 
 
 def test_committed_record_is_well_formed():
@@ -43,18 +44,30 @@ def test_committed_record_is_well_formed():
 
 def test_config_summary_from_files(tmp_path):
     import json
-    (tmp_path / "trace").mkdir()
-    line = {"workload": "w", "step_us": {"median": 10.0, "p10": 9.0, "p90": 11.0},
-            "attn_us": {"median": 6.0}, "entropy_us": {"median": 3.0},
-            "attn_hbm_gbps_at_median": 100.0, "entropy_hbm_gbps_at_median": 50.0}
-    (tmp_path / "c.jsonl").write_text(json.dumps(line) + "\n")
+    hist = {"bins": ["[0,1)", "[1,2)"], "counts": [0, 3], "min": 1.5, "median": 1.7,
+            "mask_slots": 3, "mask_slots_below_tau": 1}
+    lines = []
+    for w in ("w", "x"):
+        lines.append({"workload": w, "step_us": {"median": 10.0, "p10": 9.0, "p90": 11.0},
+                      "eager_step_us": {"median": 12.0}, "attn_segment_us": {"median": 6.0},
+                      "entropy_tail_segment_us": {"median": 3.0}, "step_hbm_gbps_at_median": 80.0,
+                      "attn_hbm_gbps_at_segment_median": 100.0,
+                      "entropy_hbm_gbps_at_segment_median": 50.0, "entropy_histogram": hist})
+    (tmp_path / "c.jsonl").write_text("\n".join(json.dumps(x) for x in lines) + "\n")
     hdr = "Kernel_Name,Grid_Size_X,Grid_Size_Y,Workgroup_Size_X,Start_Timestamp,End_Timestamp\n"
-    rows = ['"void wedlm::k_a<4>(int)",1024,1,256,0,5000', '"void wedlm::k_a<4>(int)",1024,1,256,0,7000',
-            '"other_kernel",64,1,64,0,1']
-    (tmp_path / "trace" / "run_kernel_trace.csv").write_text(hdr + "\n".join(rows) + "\n")
+    for d, rows in (("tw", ['"void wedlm::k_a<4>(int)",1024,1,256,0,5000',
+                            '"void wedlm::k_a<4>(int)",1024,1,256,0,7000', '"other_kernel",64,1,64,0,1']),
+                    ("tx", ['"void wedlm::k_a<4>(int)",1024,1,256,0,9000'])):
+        (tmp_path / d).mkdir()
+        (tmp_path / d / "run_kernel_trace.csv").write_text(hdr + "\n".join(rows) + "\n")
     out = tmp_path / "o.md"
-    profiling.summarize_configs(str(tmp_path / "c.jsonl"), str(tmp_path / "trace"), str(out), "b", "t")
+    profiling.summarize_configs(str(tmp_path / "c.jsonl"),
+                                [("w", str(tmp_path / "tw")), ("x", str(tmp_path / "tx"))],
+                                str(out), "b", "t")
     text = out.read_text()
-    assert "| `w` | 10.0 | 9.0 | 11.0 | 6.0 | 3.0 | 100 | 50 |" in text
+    assert "| `w` | 10.0 | 9.0 | 11.0 | 12.0 | 6.0 | 3.0 | 80 | 100 | 50 | 1.50 / 1.70 | 1 of 3 |" in text
+    # each workload's kernels in their own table: the same launch shape twice
     assert "| `wedlm::k_a<4>` | 4 x 1 | 256 | 2 | 6.00 |" in text
+    assert "| `wedlm::k_a<4>` | 4 x 1 | 256 | 1 | 9.00 |" in text
     assert "other_kernel" not in text
+    assert "* `w`: [1,2) 3" in text

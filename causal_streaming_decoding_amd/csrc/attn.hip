@@ -392,25 +392,27 @@ __device__ __forceinline__ void attend_pages2(RowState& st, const bf16x8 (&qr)[4
 // sample's memory rows), the re-reads hit in the caches only without the
 // hint (2.9 against 2.3 ms for the 16-key-block forward).
 template <bool kNt>
-__device__ __forceinline__ void lds_dma_16(const void* gptr, uint32_t lds_byte_addr) {
+__device__ __forceinline__ void lds_dma_16(uint64_t sbase, uint32_t voff, uint32_t lds_byte_addr) {
+  // scalar base + per-lane 32-bit offset: no 64-bit address arithmetic per
+  // lane and page
   uint32_t saved;
   if constexpr (kNt)
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(gptr), "s"(lds_byte_addr)
+        : "v"(voff), "s"(sbase), "s"(lds_byte_addr)
         : "memory");
   else
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(gptr), "s"(lds_byte_addr)
+        : "v"(voff), "s"(sbase), "s"(lds_byte_addr)
         : "memory");
 }
 
@@ -427,15 +429,41 @@ __device__ __forceinline__ int load_page_id(const int32_t* p) {
   return v;
 }
 
+// Two block-table entries with one wait (both scalar loads in flight together).
+__device__ __forceinline__ void load_page_ids2(const int32_t* p0, const int32_t* p1, int& v0,
+                                               int& v1) {
+  auto su = [](const int32_t* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    return (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32)))
+            << 32) |
+           static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u)));
+  };
+  asm volatile(
+      "s_load_dword %0, %2, 0x0\n\t"
+      "s_load_dword %1, %3, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(v0), "=&s"(v1)
+      : "s"(su(p0)), "s"(su(p1))
+      : "memory");
+}
+
+// Block-table entry of logical page pg of a sequence's table row, the page
+// index clamped to the table and the entry to the pool: the id a DMA reads.
+__device__ __forceinline__ const int32_t* page_entry(const int32_t* bt, int pg, int max_pages) {
+  return bt + __builtin_amdgcn_readfirstlane(min(max(pg, 0), max_pages - 1));
+}
+
 template <int NW>
 struct DmaShape {
   static constexpr int kPerWave = kPageVecs / (kWave * NW) > 0 ? kPageVecs / (kWave * NW) : 1;
   static constexpr int kIssuers = kPageVecs / (kWave * kPerWave);  // waves that issue
 };
 
+// DMA of one page (K then V of kv head kvh) into a ring stage; id_raw is the
+// page's block-table entry (clamped to the pool here).
 template <int NW, bool kNt>
-__device__ __forceinline__ void stage_dma(Stage& sg, int wave, int lane, int pg, const int32_t* bt,
-                                          int max_pages, int num_pages, int Hkv, int kvh,
+__device__ __forceinline__ void stage_dma(Stage& sg, int wave, int lane, int id_raw,
+                                          int num_pages, int Hkv, int kvh,
                                           const uint16_t* kc_layer, const uint16_t* vc_layer) {
   constexpr size_t page_elems = static_cast<size_t>(kHeadDim) * kPage;
   using S = DmaShape<NW>;
@@ -444,14 +472,20 @@ __device__ __forceinline__ void stage_dma(Stage& sg, int wave, int lane, int pg,
   const uint32_t lds_base = static_cast<uint32_t>(
       reinterpret_cast<size_t>((__attribute__((address_space(3))) char*)(&sg)));
   // the page id is wave-uniform: keep it in SGPRs
-  const int pgc = __builtin_amdgcn_readfirstlane(min(max(pg, 0), max_pages - 1));
-  const int pid = min(max(load_page_id(bt + pgc), 0), num_pages - 1);
+  const int pid = __builtin_amdgcn_readfirstlane(min(max(id_raw, 0), num_pages - 1));
   const size_t off = (static_cast<size_t>(pid) * Hkv + kvh) * page_elems;
+  const uint32_t voff = static_cast<uint32_t>(lane) * 16u;  // lane's 16 bytes of 1 KB
 #pragma unroll
   for (int i = 0; i < S::kPerWave; ++i) {
     const int v0 = (i * S::kIssuers + wave) * kWave;  // first vector (wave-uniform)
-    const uint16_t* base = (v0 < 256 ? kc_layer + off : vc_layer + off - 256 * 8);
-    lds_dma_16<kNt>(base + (v0 + lane) * 8, __builtin_amdgcn_readfirstlane(lds_base + v0 * 16));
+    // vectors 0..255 are the K part, 256..511 the V part of the page
+    const uint16_t* part = (v0 < 256 ? kc_layer : vc_layer) + off + (v0 % 256) * 8;
+    const uint64_t sbase = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(
+                                static_cast<uint32_t>(reinterpret_cast<uint64_t>(part) >> 32)))
+                            << 32) |
+                           static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+                               static_cast<uint32_t>(reinterpret_cast<uint64_t>(part))));
+    lds_dma_16<kNt>(sbase, voff, __builtin_amdgcn_readfirstlane(lds_base + v0 * 16));
   }
 }
 
@@ -461,6 +495,12 @@ __device__ __forceinline__ void stage_dma(Stage& sg, int wave, int lane, int pg,
 template <int N>
 __device__ __forceinline__ void stage_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS reuse only: this thread's LDS accesses have
+// completed; its global stores (the committed rows) may still be in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Wait for the oldest in-flight stage when `behind` (<= N) later stages,
@@ -502,10 +542,12 @@ __device__ __forceinline__ void rope_pair(u32x4& lo, u32x4& hi, double t, const 
 // L..L+c-1, with c the run length clamped to the window and to the pages the
 // table holds (the commit rule of the commit step). Keys as 16-byte slices,
 // values as 2-byte elements of the transposed page; positions of the page
-// other than the appended ones are not touched.
+// other than the appended ones are not touched. have_ids: pre0 / pre1 are
+// already the block-table entries of the chunk's two pages.
 __device__ __forceinline__ void append_committed(const AttnArgs& a, const Stage& sg,
                                                  const int32_t* bt, int b, int layer, int kvh,
-                                                 int kw0, int tid, int nthreads) {
+                                                 int kw0, int tid, int nthreads, bool have_ids,
+                                                 int pre0, int pre1) {
   const int Lc = max(a.prefix_len[b], 0);
   int c = min(max(a.commit_run[b], 0), a.W);
   c = min(c, max(a.max_pages * kPage - Lc, 0));
@@ -513,11 +555,19 @@ __device__ __forceinline__ void append_committed(const AttnArgs& a, const Stage&
   if (rows <= 0) return;
   uint16_t* kcl = a.kc_w + static_cast<size_t>(layer) * a.cache_layer_stride;
   uint16_t* vcl = a.vc_w + static_cast<size_t>(layer) * a.cache_layer_stride;
+  // the chunk's rows lie in at most two pages: their ids once, as scalars
+  const int pg0 = (Lc + kw0) / kPage;
+  int id0 = pre0, id1 = pre1;  // chunk 0: fetched at the start of the workgroup
+  if (!have_ids)
+    load_page_ids2(page_entry(bt, pg0, a.max_pages), page_entry(bt, pg0 + 1, a.max_pages), id0,
+                   id1);
+  id0 = min(max(id0, 0), a.num_pages - 1);
+  id1 = min(max(id1, 0), a.num_pages - 1);
   constexpr int kTasksPerRow = 16 + kHeadDim;  // 16 key slices, 128 value elements
   for (int idx = tid; idx < rows * kTasksPerRow; idx += nthreads) {
     const int j = idx / kTasksPerRow, r = idx % kTasksPerRow;
     const int t = Lc + kw0 + j;
-    const int pid = min(max(bt[t / kPage], 0), a.num_pages - 1);
+    const int pid = t / kPage == pg0 ? id0 : id1;
     const size_t page = (static_cast<size_t>(pid) * a.Hkv + kvh) * kPartElems;
     if (r < 16) {
       *reinterpret_cast<u32x4*>(kcl + page + (r * kPage + t % kPage) * 8) =
@@ -538,9 +588,9 @@ __device__ __forceinline__ void append_committed(const AttnArgs& a, const Stage&
 // below min_pages, for which the sequences' split counts fit in S: it lies in
 // [ceil(P / S), ceil((P - B) / (S - B))] with P = sum u_b, and the upper end
 // always fits (ceil(u/K) <= (u - 1)/K + 1 for u >= 1), so a binary search over
-// that interval finds it. Every wave of the workgroup evaluates this with the
-// same inputs and gets the same wave-uniform result; workgroups past the last
-// split return at once.
+// that interval finds it. The first wave of the workgroup evaluates it and
+// shares the result through LDS; workgroups past the last split return at
+// once.
 struct SplitSlot {
   int b;        // sequence, or -1 when this workgroup has no split
   int split;    // index of this split within its sequence
@@ -552,6 +602,20 @@ struct SplitSlot {
 __device__ __forceinline__ int seq_units(const AttnArgs& a, int b) {
   const int L = min(max(a.prefix_len[b], 0), a.max_prefix_len);
   return (L + kPage - 1) / kPage + (a.W + kPage - 1) / kPage;
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP (no LDS traffic): shifts
+// by 1, 2, 4, 8 lanes within each 16-lane row, then each row adds the last
+// lane of the row before it (rows 1 and 3 from rows 0 and 2), then rows 2
+// and 3 add lane 31. Lanes whose DPP source lies outside the row add 0.
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
 }
 
 __device__ __forceinline__ long long wave_sum_ll(long long x) {
@@ -573,12 +637,25 @@ __device__ __forceinline__ long long split_total(const AttnArgs& a, int K, int l
 
 __device__ SplitSlot find_split(const AttnArgs& a, int j, int lane) {
   const long long S = a.cols, Bn = a.B;  // S > B in split mode
-  const long long P = split_total(a, 1, lane);
+  // a batch of at most one wavefront's sequences keeps each lane's units in a
+  // register, and while every count stays below 2^25 (64 of them sum below
+  // 2^31) the sums are 32-bit DPP scans: the search below reads prefix_len
+  // once and touches no LDS
+  const unsigned u_own = (a.B <= kWave && lane < a.B) ? static_cast<unsigned>(seq_units(a, lane)) : 0u;
+  const bool one = a.B <= kWave && __ballot(u_own >= (1u << 25)) == 0;
+  const unsigned u_lane = one ? u_own : 0u;
+  auto total = [&](int K) -> long long {
+    if (one)
+      return static_cast<long long>(__builtin_amdgcn_readlane(
+          wave_incl_scan((u_lane + K - 1) / static_cast<unsigned>(K)), kWave - 1));
+    return split_total(a, K, lane);
+  };
+  const long long P = total(1);
   long long lo = max(static_cast<long long>(a.min_pages), (P + S - 1) / S);
   long long hi = max(lo, (P - Bn + (S - Bn) - 1) / (S - Bn));
   while (lo < hi) {
     const long long mid = (lo + hi) / 2;
-    if (split_total(a, static_cast<int>(mid), lane) <= S)
+    if (total(static_cast<int>(mid)) <= S)
       hi = mid;
     else
       lo = mid + 1;
@@ -588,13 +665,11 @@ __device__ SplitSlot find_split(const AttnArgs& a, int j, int lane) {
   long long base = 0;  // workgroups taken by the sequences before this chunk
   for (int b0 = 0; b0 < a.B; b0 += kWave) {
     const int b = b0 + lane;
-    const int n = b < a.B ? (seq_units(a, b) + K - 1) / K : 0;
-    int incl = n;  // inclusive prefix sum over the chunk's lanes
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int t = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += t;
-    }
+    const int u = one ? static_cast<int>(u_lane) : (b < a.B ? seq_units(a, b) : 0);
+    const int n = b < a.B ? (u + K - 1) / K : 0;
+    // inclusive prefix sum over the chunk's lanes (split counts are at most
+    // S, so the chunk's sum fits in 32 bits)
+    const int incl = static_cast<int>(wave_incl_scan(static_cast<unsigned>(n)));
     const long long lo_j = base + incl - n;
     const unsigned long long hit = __ballot(n > 0 && j >= lo_j && j < base + incl);
     if (hit) {
@@ -622,10 +697,15 @@ k_window_attn_bf16(AttnArgs a) {
   constexpr int kAhead = Ring<NW>::kAhead;
   __shared__ Stage stage[kStages];
   __shared__ double s_omega[kRope ? kHeadDim / 2 : 1];
+  // the sequence's window order (physical row -> slot, clamped) and logical
+  // positions, read once from HBM
+  __shared__ int s_perm[kRope ? WEDLM_MAX_WINDOW : 1];
+  __shared__ int s_pos[kRope ? WEDLM_MAX_WINDOW : 1];
+  __shared__ int s_split[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int col = lane & 15, grp = lane >> 4;
 
   // Consecutive workgroups go to different XCDs (round robin). With the
@@ -650,17 +730,27 @@ k_window_attn_bf16(AttnArgs a) {
   const int layer = bid / a.Hkv;
   int b = j, split = 0, n_split = 1, K = 0;
   if (a.split) {
-    const SplitSlot sl = find_split(a, j, lane);
-    if (sl.b < 0) return;  // every wave of the workgroup takes this branch
-    b = __builtin_amdgcn_readfirstlane(sl.b);
-    split = __builtin_amdgcn_readfirstlane(sl.split);
-    n_split = __builtin_amdgcn_readfirstlane(sl.n_split);
-    K = __builtin_amdgcn_readfirstlane(sl.K);
+    if (wave == 0) {
+      const SplitSlot sl = find_split(a, j, lane);
+      if (lane == 0) {
+        s_split[0] = sl.b;
+        s_split[1] = sl.split;
+        s_split[2] = sl.n_split;
+        s_split[3] = sl.K;
+      }
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(s_split[0]);
+    if (b < 0) return;  // every wave of the workgroup takes this branch
+    split = __builtin_amdgcn_readfirstlane(s_split[1]);
+    n_split = __builtin_amdgcn_readfirstlane(s_split[2]);
+    K = __builtin_amdgcn_readfirstlane(s_split[3]);
   }
   const int group = (layer * a.B + b) * a.Hkv + kvh;
   const size_t slot = static_cast<size_t>(layer * a.Hkv + kvh) * a.cols + j;
 
-  const int L = min(max(a.prefix_len[b], 0), a.max_prefix_len);
+  const int pl_b = a.prefix_len[b];  // read once: the append's pages need it too
+  const int L = min(max(pl_b, 0), a.max_prefix_len);
   const int npages = (L + kPage - 1) / kPage;
   const int pg_begin = a.split ? min(npages, split * K) : 0;
   const int pg_end = a.split ? min(npages, pg_begin + K) : npages;
@@ -679,26 +769,79 @@ k_window_attn_bf16(AttnArgs a) {
   const int prow = row / a.g, hh = row % a.g;
   int qslot = row_ok ? prow : 0;  // window row holding this query row
   int qpos = 0;
-  if constexpr (kRope) {
-    // frequencies to LDS and this row's slot and position, all before any
-    // asynchronous load is issued (the waits the compiler adds for these are
-    // then free)
-    if (tid < kHeadDim / 2) s_omega[tid] = a.omega[tid];
-    qslot = min(max(a.perm[b * a.W + qslot], 0), a.W - 1);
-    qpos = a.pos[b * a.W + (row_ok ? prow : 0)];
-    __syncthreads();
-  }
+  const int32_t* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
+  const int npg = pg_end - pg_begin;
+  const uint16_t* kc_layer = a.kc + static_cast<size_t>(layer) * a.cache_layer_stride;
+  const uint16_t* vc_layer = a.vc + static_cast<size_t>(layer) * a.cache_layer_stride;
+  const int pro = min(kAhead, npg);
+  // The first min(kAhead, npg) pages are requested before the loop; their
+  // block-table entries are fetched (scalar loads) while the window order
+  // is on its way. The entries of the pages the first chunk of committed
+  // rows is appended to (positions L, L + 1, ...) follow the first DMAs.
+  constexpr int kAhead2 = (kAhead + 1) / 2 * 2;
+  int id_pro[kAhead2];
+  const bool appends = kRope && a.commit_run != nullptr && part == 0 && with_window;
+  int app_id0 = 0, app_id1 = 0;
   u32x4 qv[4];
   {
-    const uint16_t* qrow =
-        a.q + ((lb * a.W + qslot) * a.Hq + kvh * a.g + (row_ok ? hh : 0)) * kHeadDim;
-    // qpos is an input so that its load has completed before the query loads
+    int pm = 0, ps = 0;
+    if constexpr (kRope) {
+      if (tid < a.W) {
+        pm = a.perm[b * a.W + tid];
+        ps = a.pos[b * a.W + tid];
+      }
+    }
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      asm volatile("global_load_dwordx4 %0, %1, off"
-                   : "=v"(qv[s])
-                   : "v"(qrow + s * 32 + grp * 8), "v"(qpos)
-                   : "memory");
+    for (int q = 0; q < kAhead2; q += 2)
+      load_page_ids2(page_entry(bt, pg_begin + q, a.max_pages),
+                     page_entry(bt, pg_begin + q + 1, a.max_pages), id_pro[q], id_pro[q + 1]);
+    if constexpr (kRope) {
+      // frequencies, window order and positions to LDS, all before any
+      // asynchronous load is issued (the waits the compiler adds for these
+      // are then free)
+      if (tid < kHeadDim / 2) s_omega[tid] = a.omega[tid];
+      if (tid < a.W) {
+        s_perm[tid] = min(max(pm, 0), a.W - 1);
+        s_pos[tid] = ps;
+      }
+      __syncthreads();
+      qslot = s_perm[qslot];
+      qpos = s_pos[row_ok ? prow : 0];
+    }
+    {
+      // Loaded through asm, before the first pages' DMAs, and retired below
+      // with an explicit vmcnt that lets those DMAs stay in flight. (Rows
+      // past M read row 0 of the group - valid memory - and are never stored.)
+      const uint16_t* qrow =
+          a.q + ((lb * a.W + qslot) * a.Hq + kvh * a.g + (row_ok ? hh : 0)) * kHeadDim;
+      // qpos is an input so that its load has completed before the query loads
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        asm volatile("global_load_dwordx4 %0, %1, off"
+                     : "=v"(qv[s])
+                     : "v"(qrow + s * 32 + grp * 8), "v"(qpos)
+                     : "memory");
+    }
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j)
+      if (j < pro)
+        stage_dma<NW, kNt>(stage[j], wave, lane, id_pro[j], a.num_pages, a.Hkv, kvh, kc_layer,
+                           vc_layer);
+    if (appends) {
+      const int Lc = max(pl_b, 0);
+      load_page_ids2(page_entry(bt, Lc / kPage, a.max_pages),
+                     page_entry(bt, Lc / kPage + 1, a.max_pages), app_id0, app_id1);
+    }
+    // Retire the query loads: only the kAhead stages issued after them may
+    // remain. Waves that issue no DMA (none with 4 or 8 waves), and every
+    // wave when the split has fewer than kAhead pages, wait for everything
+    // first; that asm has no register operands, so nothing touches the query
+    // registers before the tied wait below.
+    if (wave >= DmaShape<NW>::kIssuers || pro < kAhead)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%4)"
+                 : "+v"(qv[0]), "+v"(qv[1]), "+v"(qv[2]), "+v"(qv[3])
+                 : "n"(kAhead * kDma));
   }
   RowState st;
   st.m = -INFINITY;
@@ -707,29 +850,6 @@ k_window_attn_bf16(AttnArgs a) {
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // waves past the part's last row tile only move data
   const bool computes = wave * 16 < a.part_rows && row0 + wave * 16 < a.M;
-
-  // ---- paged prefix: pages through the LDS ring ----------------------------
-  const int32_t* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
-  const uint16_t* kc_layer = a.kc + static_cast<size_t>(layer) * a.cache_layer_stride;
-  const uint16_t* vc_layer = a.vc + static_cast<size_t>(layer) * a.cache_layer_stride;
-  const int npg = pg_end - pg_begin;
-  // The first min(kAhead, npg) pages are requested before the loop.
-  const int pro = min(kAhead, npg);
-#pragma unroll
-  for (int j = 0; j < kAhead; ++j)
-    if (j < pro)
-      stage_dma<NW, kNt>(stage[j], wave, lane, pg_begin + j, bt, a.max_pages, a.num_pages, a.Hkv, kvh,
-                    kc_layer, vc_layer);
-  // Retire the query loads: only the kAhead stages issued after them may
-  // remain. Waves that issue no DMA (none with 4 or 8 waves), and every wave when the split
-  // has fewer than kAhead pages, wait for everything first; that asm has no
-  // register operands, so nothing touches the query registers before the
-  // tied wait below.
-  if (wave >= DmaShape<NW>::kIssuers || pro < kAhead)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  asm volatile("s_waitcnt vmcnt(%4)"
-               : "+v"(qv[0]), "+v"(qv[1]), "+v"(qv[2]), "+v"(qv[3])
-               : "n"(kAhead * kDma));
   if constexpr (kRope) {
     // this lane holds dims s*32 + grp*8 .. +7: slices s and s+2 are a RoPE pair
     rope_pair(qv[0], qv[2], static_cast<double>(qpos), s_omega, grp * 8);
@@ -748,18 +868,67 @@ k_window_attn_bf16(AttnArgs a) {
   // The deep rings (kPair) take pages i and i+1 per barrier and refill the two
   // stages computed before them (kAhead = kStages - 2); an odd last page is
   // taken alone.
+  // The first window chunk's rows are requested by DMA once no page is left
+  // to request, into the two stages the last pages no longer need: raw keys
+  // (gathered through the window order, slice-major as a page's K part) into
+  // stage win_a, raw values in the same order into stage win_b's K part. After
+  // the ring the keys are rotated in place and the values transposed into
+  // win_a's V part, with no global access left in the window phase.
+  const int row_stride = a.Hkv * kHeadDim;
+  const uint16_t* kwin = a.k + lb * a.W * row_stride + kvh * kHeadDim;
+  const uint16_t* vwin = a.v + lb * a.W * row_stride + kvh * kHeadDim;
+  constexpr bool kPrefetchWin = kRope && NW == 4;
+  int win_a = 0, win_b = 1;
+  bool win_issued = false;
+  // x: the first page taken at this barrier; pages x-2 and x-1 (stages
+  // (x+2)%4 and (x+3)%4) were computed before it and no page is refilled
+  auto prefetch_window = [&](int x) {
+    if constexpr (kPrefetchWin) {
+      if (!with_window || win_issued) return;
+      win_issued = true;
+      win_a = (x + 2) % kStages;
+      win_b = (x + 3) % kStages;
+      // wave w moves slices 4w .. 4w+3 of the 16 keys: K, then V
+      const int j = lane & 15, sl = wave * 4 + (lane >> 4);
+      const int slot = s_perm[min(j, a.W - 1)];  // keys past W: a valid row, never used
+      const uint16_t* kr = kwin + slot * row_stride + sl * 8;
+      const uint16_t* vr = vwin + slot * row_stride + sl * 8;
+      const uint32_t la = static_cast<uint32_t>(
+          reinterpret_cast<size_t>((__attribute__((address_space(3))) char*)(&stage[win_a])));
+      const uint32_t lb_ = static_cast<uint32_t>(
+          reinterpret_cast<size_t>((__attribute__((address_space(3))) char*)(&stage[win_b])));
+      uint32_t saved;
+      asm volatile(
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %3\n\t"
+          "global_load_lds_dwordx4 %1, off\n\t"
+          "s_mov_b32 m0, %4\n\t"
+          "global_load_lds_dwordx4 %2, off\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "v"(kr), "v"(vr), "s"(__builtin_amdgcn_readfirstlane(la + wave * 1024)),
+            "s"(__builtin_amdgcn_readfirstlane(lb_ + wave * 1024))
+          : "memory");
+    }
+  };
   int i0 = 0;
   if constexpr (Ring<NW>::kPair) {
     for (; i0 + 1 < npg; i0 += 2) {
       const int pg = pg_begin + i0;
       // pages requested after page i0+1: up to kAhead-2, fewer near the end
       stage_wait_behind<kDma, kAhead - 2>(min(kAhead - 2, npg - 2 - i0));
-      if (i0 + kAhead < npg)
-        stage_dma<NW, kNt>(stage[(i0 + kAhead) % kStages], wave, lane, pg + kAhead, bt, a.max_pages,
-                      a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
-      if (i0 + kAhead + 1 < npg)
-        stage_dma<NW, kNt>(stage[(i0 + kAhead + 1) % kStages], wave, lane, pg + kAhead + 1, bt,
-                      a.max_pages, a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
+      if (i0 + kAhead >= npg) prefetch_window(i0);  // after the last page's DMA
+      if (i0 + kAhead < npg) {
+        // both pages' block-table entries with one scalar wait
+        int id0, id1;
+        load_page_ids2(page_entry(bt, pg + kAhead, a.max_pages),
+                       page_entry(bt, pg + kAhead + 1, a.max_pages), id0, id1);
+        stage_dma<NW, kNt>(stage[(i0 + kAhead) % kStages], wave, lane, id0, a.num_pages, a.Hkv,
+                           kvh, kc_layer, vc_layer);
+        if (i0 + kAhead + 1 < npg)
+          stage_dma<NW, kNt>(stage[(i0 + kAhead + 1) % kStages], wave, lane, id1, a.num_pages,
+                             a.Hkv, kvh, kc_layer, vc_layer);
+      }
       if (computes)
         attend_pages2(st, qr, stage[i0 % kStages], stage[(i0 + 1) % kStages], lane,
                       L - pg * kPage, L - (pg + 1) * kPage, a.scale_log2);
@@ -769,9 +938,11 @@ k_window_attn_bf16(AttnArgs a) {
     const int pg = pg_begin + i;
     // pages requested after page i: up to kAhead-1, fewer near the end
     stage_wait_behind<kDma, kAhead - 1>(min(kAhead - 1, npg - 1 - i));
+    if (i + kAhead >= npg) prefetch_window(i);
     if (i + kAhead < npg)
-      stage_dma<NW, kNt>(stage[(i + kAhead) % kStages], wave, lane, pg + kAhead, bt, a.max_pages,
-                    a.num_pages, a.Hkv, kvh, kc_layer, vc_layer);
+      stage_dma<NW, kNt>(stage[(i + kAhead) % kStages], wave, lane,
+                         load_page_id(page_entry(bt, pg + kAhead, a.max_pages)), a.num_pages,
+                         a.Hkv, kvh, kc_layer, vc_layer);
     if (computes)
       attend_page(st, qr, stage[i % kStages], lane, L - pg * kPage, L - pg * kPage, a.scale_log2);
   }
@@ -783,11 +954,13 @@ k_window_attn_bf16(AttnArgs a) {
 
   // ---- the window's own keys, causal over physical order -------------------
   if (with_window) {
-    const int row_stride = a.Hkv * kHeadDim;
-    const uint16_t* kwin = a.k + lb * a.W * row_stride + kvh * kHeadDim;
-    const uint16_t* vwin = a.v + lb * a.W * row_stride + kvh * kHeadDim;
+    if (kPrefetchWin && !win_issued) {
+      // no page at all: every stage is free
+      prefetch_window(0);
+      stage_wait_barrier<0>();
+    }
     for (int kw0 = 0; kw0 < a.W; kw0 += kPage) {
-      Stage& sg = stage[0];
+      Stage& sg = stage[win_a];
       // 16 keys x 16 slices of 8 dims: K goes to [slice][key][8], V is transposed
       auto put = [&](int j, int sl, u32x4 kv, u32x4 vv) {
         *reinterpret_cast<u32x4*>(&sg.k[(sl * kPage + j) * 8]) = kv;
@@ -803,16 +976,27 @@ k_window_attn_bf16(AttnArgs a) {
         // 32-bit word), the two dims of the word rotated with their partners
         // (small tasks keep the registers of the running O free)
         uint32_t* kw = reinterpret_cast<uint32_t*>(sg.k);
+        // chunk 0 was moved in raw by DMA: keys in place in sg.k, values in
+        // stage win_b's K part; every (key, slice pair, word) task reads and
+        // writes only its own two words
+        const bool pre = kPrefetchWin && kw0 == 0;
+        const uint32_t* vraw = reinterpret_cast<const uint32_t*>(stage[win_b].k);
         for (int idx = tid; idx < kPage * 8 * 4; idx += kWave * NW) {
           const int j = idx >> 5, sl = (idx >> 2) & 7, w = idx & 3;
           const int key = kw0 + j;
           uint32_t lo = 0u, hi = 0u;
           if (key < a.W) {
-            const int slot = min(max(a.perm[b * a.W + key], 0), a.W - 1);
-            const uint16_t* kr = kwin + slot * row_stride + sl * 8 + 2 * w;
-            const uint32_t x = *reinterpret_cast<const uint32_t*>(kr);
-            const uint32_t y = *reinterpret_cast<const uint32_t*>(kr + kHeadDim / 2);
-            const double t = static_cast<double>(a.pos[b * a.W + key]);
+            uint32_t x, y;
+            if (pre) {
+              x = kw[((sl * kPage + j) * 8) / 2 + w];
+              y = kw[(((sl + 8) * kPage + j) * 8) / 2 + w];
+            } else {
+              const int slot = s_perm[key];
+              const uint16_t* kr = kwin + slot * row_stride + sl * 8 + 2 * w;
+              x = *reinterpret_cast<const uint32_t*>(kr);
+              y = *reinterpret_cast<const uint32_t*>(kr + kHeadDim / 2);
+            }
+            const double t = static_cast<double>(s_pos[key]);
             float c0, s0, c1, s1;
             rope_cos_sin(t, s_omega[sl * 8 + 2 * w], c0, s0);
             rope_cos_sin(t, s_omega[sl * 8 + 2 * w + 1], c1, s1);
@@ -828,10 +1012,9 @@ k_window_attn_bf16(AttnArgs a) {
           const int j = idx >> 4, sl = idx & 15;
           const int key = kw0 + j;
           u32x4 vv = {0u, 0u, 0u, 0u};
-          if (key < a.W) {
-            const int slot = min(max(a.perm[b * a.W + key], 0), a.W - 1);
-            vv = *reinterpret_cast<const u32x4*>(vwin + slot * row_stride + sl * 8);
-          }
+          if (key < a.W)
+            vv = pre ? *reinterpret_cast<const u32x4*>(vraw + (sl * kPage + j) * 4)
+                     : *reinterpret_cast<const u32x4*>(vwin + s_perm[key] * row_stride + sl * 8);
           uint16_t* vt = &sg.v[(sl * 8) * kPage + j];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -851,16 +1034,19 @@ k_window_attn_bf16(AttnArgs a) {
           put(j, sl, kv, vv);
         }
       }
-      __syncthreads();
+      lds_barrier();
       if constexpr (kRope) {
-        if (a.commit_run != nullptr && part == 0)
-          append_committed(a, sg, bt, b, layer, kvh, kw0, tid, kWave * NW);
+        if (appends)
+          append_committed(a, sg, bt, b, layer, kvh, kw0, tid, kWave * NW, kw0 == 0, app_id0,
+                           app_id1);
       }
+      // the appended rows' stores may still be in flight at the barrier below:
+      // it only protects the stage for the next chunk
       if (computes) {
         const int lim = min(a.W, prow + 1) - kw0;  // window key kw0 + kk visible iff kk < lim
         attend_page(st, qr, sg, lane, lim, kPage, a.scale_log2);
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 
@@ -901,7 +1087,7 @@ constexpr int kCombineBatch = 8;
 __global__ void __launch_bounds__(256)
 k_window_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
                       const int2* __restrict__ ws_plan, uint16_t* __restrict__ out, int n_groups,
-                      int M, int W, int Hq, int Hkv, int g) {
+                      int M, int W, int Hq, int Hkv, int g, int cols, long long n_slots) {
   const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int quads = kHeadDim / 4;
   const long long total = static_cast<long long>(n_groups) * M * quads;
@@ -909,8 +1095,12 @@ k_window_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ 
   const int d4 = static_cast<int>(idx % quads);
   const int row = static_cast<int>((idx / quads) % M);
   const int group = static_cast<int>(idx / (static_cast<long long>(quads) * M));
-  const int2 plan = ws_plan[group];
-  const int n_splits = plan.y;
+  int2 plan = ws_plan[group];
+  // the plan entry is device data: keep its slots inside the partials (a
+  // column holds cols of them), whatever it holds
+  plan.x = static_cast<int>(min(max(static_cast<long long>(plan.x), 0LL), n_slots - 1));
+  const int n_splits = static_cast<int>(
+      min(static_cast<long long>(min(max(plan.y, 0), cols)), n_slots - plan.x));
   float m = -INFINITY, lsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < n_splits; s0 += kCombineBatch) {
@@ -1326,7 +1516,7 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   const long long threads = groups * a.M * (kHeadDim / 4);
   hipLaunchKernelGGL(k_window_attn_combine, dim3(static_cast<unsigned>((threads + 255) / 256)),
                      dim3(256), 0, s, a.ws_o, a.ws_ml, a.ws_plan, a.out, static_cast<int>(groups),
-                     a.M, W, Hq, Hkv, a.g);
+                     a.M, W, Hq, Hkv, a.g, a.cols, static_cast<long long>(a.units));
   return launch_status();
 }
 

@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--event-every", type=int, default=8,
                     help="record the attention / entropy timing events on every n-th timed "
                          "step (each record idles the GPU for a few microseconds)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run each step's entropy chunk pass on a second stream beside the "
+                         "attention (fused tail only)")
     ap.add_argument("--separate-tail", action="store_true",
                     help="chained steps run selection, state commit and reorder as three calls "
                          "instead of the fused tail")
@@ -195,6 +198,8 @@ def config_latencies(args):
     once as a HIP graph and replayed between two timing events: nothing else
     sits between the step's kernels. Reported: the median, p10 and p90 of the
     replayed step; the same step launched eagerly (one host call per kernel);
+    eagerly with the entropy chunk pass on a second stream beside the
+    attention (it reads only the logits);
     and, from an eager pass with timing events between the kernels, the
     attention and entropy + tail segments (each event record adds a few
     microseconds of idle GPU, so these are upper bounds of the kernels; the
@@ -254,6 +259,10 @@ def config_latencies(args):
         g_span = timed(lambda mark: graph.replay(), False)
         e_span = timed(lambda mark: step.run(st, q, k, v, logits), False)
         m_span = timed(lambda mark: step.run(st, q, k, v, logits, mark=mark), True)
+        # the entropy chunk pass on a second stream beside the attention
+        step.set_overlap(torch.cuda.Stream())
+        o_span = timed(lambda mark: step.run(st, q, k, v, logits), False)
+        step.set_overlap(None)
         L = np.asarray(inp["prefix_len"], np.int64)
         commits = step.commit_len.cpu().numpy()
         b = step_bytes(wl, L, commits)
@@ -272,6 +281,7 @@ def config_latencies(args):
             "warmup": args.config_warmup, "unit": "us",
             "step_us": stats(g_span["step"]), "step_launch": "one HIP graph replay",
             "eager_step_us": stats(e_span["step"]),
+            "overlap_step_us": stats(o_span["step"]),
             "attn_segment_us": stats(m_span["attn"]),
             "entropy_tail_segment_us": stats(m_span["entropy"]),
             "step_algorithmic_bytes": int(step_bytes_total),
@@ -633,6 +643,8 @@ def main():
     inp = make_step_inputs(wl, steps=n_inputs)
     st, _, _, _, _, L0 = upload_step_inputs(wl, inp, dev)
     step = make_window_step(wl, inp, dev, L0 + wl.W * n_inputs, fused_tail=not args.separate_tail)
+    if args.overlap and not args.separate_tail:
+        step.set_overlap(torch.cuda.Stream())
     ins = [stream_step_inputs(wl, s, dev) for s in range(n_inputs)]
     commit_log = torch.zeros((n_inputs, wl.B), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
@@ -751,6 +763,7 @@ def main():
                    "kv_heads": wl.Hkv, "head_dim": wl.D, "window": wl.W, "vocab": wl.V,
                    "initial_prefix": int(L0), "page_size": wl.page_size,
                    "step_tail": "separate" if args.separate_tail else "fused",
+                   "entropy_stream": "side" if (args.overlap and not args.separate_tail) else "same",
                    "parallelism": "single GPU"},
         "timing": f"median of {reps} repetitions of steps 0..{K - 1} from the start state "
                   f"(window-steps/s per repetition: "

@@ -24,6 +24,10 @@
 //   next step's reorder, in one wavefront per sequence.
 // wedlm_entropy_select_noalloc runs the same two kernels with the chunk
 // partials in a fixed device array instead of a caller workspace.
+// wedlm_entropy_partials and wedlm_select_commit_reorder_partials are the two
+// halves of wedlm_select_commit_reorder as separate calls, so that the chunk
+// pass, which reads only the logits, can run on another stream beside the
+// step's attention.
 #include "window_ops.hpp"
 
 #include <mutex>
@@ -347,13 +351,41 @@ extern "C" int wedlm_entropy_select_noalloc(int dtype, int B, int W, int V, cons
                             as_stream(stream));
 }
 
-extern "C" int wedlm_select_commit_reorder(
-    int dtype, int B, int W, int V, const void* logits, float lambda, float tau, int min_fill,
-    int page_size, int num_pages, int max_pages, int commit_rule, const int32_t* block_table,
-    int32_t* run_len, int32_t* tokens, uint8_t* filled, int32_t* prefix_len, int32_t* commit_len,
-    int32_t* cache_slot, int32_t mask_id, float* entropy, float* score, int32_t* argmax_tok,
-    uint8_t* selected, int32_t* perm, int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
-    void* workspace, size_t workspace_bytes, void* stream) {
+extern "C" int wedlm_entropy_partials(int dtype, int B, int W, int V, const void* logits,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype)) return WEDLM_ERR_UNSUPPORTED;
+  if (B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW || V <= 0 || !logits) return WEDLM_ERR_INVALID;
+  if (1LL * B * W > 65535) return WEDLM_ERR_UNSUPPORTED;
+  EntPlan pl = plan_entropy(dtype, B, W, V);
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) pl.vec = false;
+  const size_t need = static_cast<size_t>(B) * W * pl.n_chunks * sizeof(EntPartial);
+  if (workspace == nullptr || workspace_bytes < need) return WEDLM_ERR_WORKSPACE;
+  launch_entropy_partials(dtype, B, W, V, logits, pl, static_cast<EntPartial*>(workspace),
+                          as_stream(stream));
+  return launch_status();
+}
+
+// The tail launch shared by both tail entry points.
+static int launch_step_tail(int W, float lambda, float tau, int min_fill, int page_size,
+                            int num_pages, int max_pages, int commit_rule, int B,
+                            const int32_t* block_table, int32_t* run_len, int32_t* tokens,
+                            uint8_t* filled, int32_t* prefix_len, int32_t* commit_len,
+                            int32_t* cache_slot, int32_t mask_id, float* entropy, float* score,
+                            int32_t* argmax_tok, uint8_t* selected, int32_t* perm,
+                            int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
+                            const EntPartial* part, int n_chunks, hipStream_t s) {
+  hipLaunchKernelGGL(k_step_tail, dim3(B), dim3(kWave), 0, s, part, n_chunks, W, lambda, tau,
+                     min_fill, page_size, num_pages, max_pages,
+                     commit_rule == WEDLM_COMMIT_BLOCK ? 1 : 0, block_table, tokens, filled,
+                     prefix_len, run_len, commit_len, cache_slot, mask_id, entropy, score,
+                     argmax_tok, selected, perm, inv_perm, pos, n_obs);
+  return launch_status();
+}
+
+// Host-side checks shared by both tail entry points (logits aside).
+static int validate_tail(int dtype, int B, int W, int V, float lambda, float tau, int min_fill,
+                         int page_size, int num_pages, int max_pages, int commit_rule,
+                         const void* const* ptrs, int n_ptrs) {
   if (!valid_dtype(dtype)) return WEDLM_ERR_UNSUPPORTED;
   if (B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW || V <= 0) return WEDLM_ERR_INVALID;
   if (min_fill != 0 && min_fill != 1) return WEDLM_ERR_INVALID;
@@ -362,11 +394,47 @@ extern "C" int wedlm_select_commit_reorder(
     return WEDLM_ERR_INVALID;
   if (page_size <= 0 || num_pages <= 0 || max_pages <= 0) return WEDLM_ERR_INVALID;
   if (page_size != 16) return WEDLM_ERR_UNSUPPORTED;
-  if (!logits || !block_table || !run_len || !tokens || !filled || !prefix_len || !commit_len ||
-      !cache_slot || !entropy || !score || !argmax_tok || !selected || !perm || !inv_perm ||
-      !pos || !n_obs)
-    return WEDLM_ERR_INVALID;
+  for (int i = 0; i < n_ptrs; ++i)
+    if (ptrs[i] == nullptr) return WEDLM_ERR_INVALID;
   if (1LL * B * W > 65535) return WEDLM_ERR_UNSUPPORTED;
+  return WEDLM_OK;
+}
+
+extern "C" int wedlm_select_commit_reorder_partials(
+    int dtype, int B, int W, int V, float lambda, float tau, int min_fill, int page_size,
+    int num_pages, int max_pages, int commit_rule, const int32_t* block_table, int32_t* run_len,
+    int32_t* tokens, uint8_t* filled, int32_t* prefix_len, int32_t* commit_len,
+    int32_t* cache_slot, int32_t mask_id, float* entropy, float* score, int32_t* argmax_tok,
+    uint8_t* selected, int32_t* perm, int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
+    const void* workspace, size_t workspace_bytes, void* stream) {
+  const void* ptrs[] = {block_table, run_len, tokens, filled, prefix_len, commit_len, cache_slot,
+                        entropy, score, argmax_tok, selected, perm, inv_perm, pos, n_obs};
+  const int v = validate_tail(dtype, B, W, V, lambda, tau, min_fill, page_size, num_pages,
+                              max_pages, commit_rule, ptrs, 15);
+  if (v != WEDLM_OK) return v;
+  const EntPlan pl = plan_entropy(dtype, B, W, V);
+  const size_t need = static_cast<size_t>(B) * W * pl.n_chunks * sizeof(EntPartial);
+  if (workspace == nullptr || workspace_bytes < need) return WEDLM_ERR_WORKSPACE;
+  return launch_step_tail(W, lambda, tau, min_fill, page_size, num_pages, max_pages, commit_rule,
+                          B, block_table, run_len, tokens, filled, prefix_len, commit_len,
+                          cache_slot, mask_id, entropy, score, argmax_tok, selected, perm,
+                          inv_perm, pos, n_obs, static_cast<const EntPartial*>(workspace),
+                          pl.n_chunks, as_stream(stream));
+}
+
+extern "C" int wedlm_select_commit_reorder(
+    int dtype, int B, int W, int V, const void* logits, float lambda, float tau, int min_fill,
+    int page_size, int num_pages, int max_pages, int commit_rule, const int32_t* block_table,
+    int32_t* run_len, int32_t* tokens, uint8_t* filled, int32_t* prefix_len, int32_t* commit_len,
+    int32_t* cache_slot, int32_t mask_id, float* entropy, float* score, int32_t* argmax_tok,
+    uint8_t* selected, int32_t* perm, int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  const void* ptrs[] = {logits, block_table, run_len, tokens, filled, prefix_len, commit_len,
+                        cache_slot, entropy, score, argmax_tok, selected, perm, inv_perm, pos,
+                        n_obs};
+  const int v = validate_tail(dtype, B, W, V, lambda, tau, min_fill, page_size, num_pages,
+                              max_pages, commit_rule, ptrs, 16);
+  if (v != WEDLM_OK) return v;
   EntPlan pl = plan_entropy(dtype, B, W, V);
   if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) pl.vec = false;
   const size_t need = static_cast<size_t>(B) * W * pl.n_chunks * sizeof(EntPartial);
@@ -376,10 +444,8 @@ extern "C" int wedlm_select_commit_reorder(
   launch_entropy_partials(dtype, B, W, V, logits, pl, part, s);
   const int st = launch_status();
   if (st != WEDLM_OK) return st;
-  hipLaunchKernelGGL(k_step_tail, dim3(B), dim3(kWave), 0, s, part, pl.n_chunks, W, lambda, tau,
-                     min_fill, page_size, num_pages, max_pages,
-                     commit_rule == WEDLM_COMMIT_BLOCK ? 1 : 0, block_table, tokens, filled,
-                     prefix_len, run_len, commit_len, cache_slot, mask_id, entropy, score,
-                     argmax_tok, selected, perm, inv_perm, pos, n_obs);
-  return launch_status();
+  return launch_step_tail(W, lambda, tau, min_fill, page_size, num_pages, max_pages, commit_rule,
+                          B, block_table, run_len, tokens, filled, prefix_len, commit_len,
+                          cache_slot, mask_id, entropy, score, argmax_tok, selected, perm,
+                          inv_perm, pos, n_obs, part, pl.n_chunks, s);
 }

@@ -92,6 +92,9 @@ class WindowStep:
         self._size_attn_workspace(max_prefix_len)
         self.ent_ws_bytes = W_.wedlm_entropy_select_workspace_size(self.dt, B, W, V)
         self.ent_ws = torch.empty((max(self.ent_ws_bytes, 1),), dtype=torch.uint8, device=device)
+        # optional side stream for the entropy chunk pass (set_overlap)
+        self.overlap = None
+        self._ev_in = self._ev_ent = None
 
     def _size_attn_workspace(self, max_prefix_len):
         self.attn_ws_bytes = W_.wedlm_window_attn_workspace_size(
@@ -195,6 +198,9 @@ class WindowStep:
         tail = self.fused_tail and self.fused_rope and self.fused_append
         if not (tail and self.ordered(st)):
             self.reorder(st, stream)
+        if tail and self.overlap is not None:
+            self._run_overlapped(st, q, k, v, logits, max_prefix_len, commit_len, stream, mark)
+            return
         if not self.fused_rope:
             self.rope(q, k, v, stream)
         if mark is not None:
@@ -214,6 +220,47 @@ class WindowStep:
         if mark is not None:
             mark("entropy_end")
         self._commit_after_select(st, k, v, commit_len, stream)
+
+    def _run_overlapped(self, st, q, k, v, logits, max_prefix_len, commit_len, stream, mark):
+        """The fused-tail step with the entropy chunk pass on ``self.overlap``.
+
+        The chunk pass reads only the logits, so it runs on the side stream
+        while the attention runs on the main one; it starts after everything
+        already enqueued on the main stream (the previous step's tail reads
+        the same partials), and the tail waits for it.
+        """
+        main = torch.cuda.current_stream() if stream is None else stream
+        side = self.overlap
+        self._ev_in.record(main)
+        side.wait_event(self._ev_in)
+        W_.wedlm_entropy_partials(self.dt, self.B, self.W, self.V, logits, self.ent_ws,
+                                  self.ent_ws_bytes, side)
+        self._ev_ent.record(side)
+        if mark is not None:
+            mark("attn_start")
+        self.attn_rope(st, q, k, v, max_prefix_len, main, append=True)
+        if mark is not None:
+            mark("attn_end")
+        main.wait_event(self._ev_ent)
+        W_.wedlm_select_commit_reorder_partials(
+            self.dt, self.B, self.W, self.V, self.lam, self.tau, self.min_fill, self.page_size,
+            self.num_pages, self.max_pages, self.commit_rule, st.block_table, self.run_len,
+            st.tokens, st.filled, st.prefix_len,
+            self.commit_len if commit_len is None else commit_len, self.cache_slot, self.mask_id,
+            self.entropy, self.score, self.argmax, self.selected, self.perm, self.inv, self.pos,
+            self.n_obs, self.ent_ws, self.ent_ws_bytes, main)
+        st.ordered_by = self
+        if mark is not None:
+            mark("entropy_end")
+
+    def set_overlap(self, side_stream):
+        """Run the entropy chunk pass on ``side_stream`` (a torch stream of
+        default priority) beside the attention, or on the launch stream again
+        when None. Only the fused-tail step uses it."""
+        self.overlap = side_stream
+        if side_stream is not None and self._ev_in is None:
+            self._ev_in = torch.cuda.Event()
+            self._ev_ent = torch.cuda.Event()
 
     def capture(self, st, q, k, v, logits, max_prefix_len=None, commit_len=None):
         """A HIP graph of one whole step (``run`` with these arguments), to replay.

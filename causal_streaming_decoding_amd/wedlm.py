@@ -54,6 +54,10 @@ _SIGNATURES = {
     "wedlm_read_probe": (_c_int, [_p, _c_size, _p, _c_int, _p, _c_int, _p]),
     "wedlm_select_commit_reorder": (_c_int, [_c_int] * 4 + [_p, _c_float, _c_float] + [_c_int] * 5
                                     + [_p] * 7 + [ctypes.c_int32] + [_p] * 9 + [_c_size, _p]),
+    "wedlm_entropy_partials": (_c_int, [_c_int] * 4 + [_p, _p, _c_size, _p]),
+    "wedlm_select_commit_reorder_partials": (_c_int, [_c_int] * 4 + [_c_float, _c_float]
+                                             + [_c_int] * 5 + [_p] * 7 + [ctypes.c_int32]
+                                             + [_p] * 9 + [_c_size, _p]),
 }
 
 _lib = None
@@ -251,6 +255,25 @@ def wedlm_select_commit_reorder(dtype, B, W, V, logits, lam, tau, min_fill, page
     _check("wedlm_select_commit_reorder", lib().wedlm_select_commit_reorder(
         dtype, B, W, V, _ptr(logits), float(lam), float(tau), int(min_fill), page_size, num_pages,
         max_pages, int(commit_rule), _ptr(block_table), _ptr(run_len), _ptr(tokens), _ptr(filled),
+        _ptr(prefix_len), _ptr(commit_len), _ptr(cache_slot), int(mask_id), _ptr(entropy),
+        _ptr(score), _ptr(argmax_tok), _ptr(selected), _ptr(perm), _ptr(inv_perm), _ptr(pos),
+        _ptr(n_obs), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def wedlm_entropy_partials(dtype, B, W, V, logits, workspace, workspace_bytes, stream=None):
+    _check("wedlm_entropy_partials", lib().wedlm_entropy_partials(
+        dtype, B, W, V, _ptr(logits), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def wedlm_select_commit_reorder_partials(dtype, B, W, V, lam, tau, min_fill, page_size,
+                                         num_pages, max_pages, commit_rule, block_table, run_len,
+                                         tokens, filled, prefix_len, commit_len, cache_slot,
+                                         mask_id, entropy, score, argmax_tok, selected, perm,
+                                         inv_perm, pos, n_obs, workspace, workspace_bytes,
+                                         stream=None):
+    _check("wedlm_select_commit_reorder_partials", lib().wedlm_select_commit_reorder_partials(
+        dtype, B, W, V, float(lam), float(tau), int(min_fill), page_size, num_pages, max_pages,
+        int(commit_rule), _ptr(block_table), _ptr(run_len), _ptr(tokens), _ptr(filled),
         _ptr(prefix_len), _ptr(commit_len), _ptr(cache_slot), int(mask_id), _ptr(entropy),
         _ptr(score), _ptr(argmax_tok), _ptr(selected), _ptr(perm), _ptr(inv_perm), _ptr(pos),
         _ptr(n_obs), _ptr(workspace), workspace_bytes, _stream(stream)))

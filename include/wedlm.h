@@ -438,6 +438,39 @@ int wedlm_select_commit_reorder(int dtype, int B, int W, int V, const void* logi
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * wedlm_entropy_partials / wedlm_select_commit_reorder_partials - the two
+ * halves of wedlm_select_commit_reorder as separate calls. The first reads
+ * only the logits: it reduces every row's chunks of the vocabulary to
+ * partial (max, sum, weighted sum, argmax) records in `workspace`; the second
+ * merges them and runs the selection, window-state commit and next reorder
+ * exactly as wedlm_select_commit_reorder does. Since the chunk pass needs
+ * nothing the step's attention writes, it can run on a second stream
+ * concurrently with wedlm_window_attn_rope (hyper.ai summary of WeDLM,
+ * "Method": the entropy rule reads the forward pass's predictions; with
+ * synthetic inputs those are given before the attention runs); the caller
+ * orders the tail after both (and the next chunk pass after this tail, which
+ * reads the same workspace).
+ *
+ * Results are bitwise those of wedlm_select_commit_reorder on the same
+ * inputs. Both calls take the same dtype, B, W, V and a workspace of at least
+ * wedlm_entropy_select_workspace_size(dtype, B, W, V) bytes; other arguments
+ * and layouts as there (logits 16-byte aligned for the vector path).
+ */
+int wedlm_entropy_partials(int dtype, int B, int W, int V, const void* logits, void* workspace,
+                           size_t workspace_bytes, void* stream);
+int wedlm_select_commit_reorder_partials(int dtype, int B, int W, int V, float lambda, float tau,
+                                         int min_fill, int page_size, int num_pages,
+                                         int max_pages, int commit_rule,
+                                         const int32_t* block_table, int32_t* run_len,
+                                         int32_t* tokens, uint8_t* filled, int32_t* prefix_len,
+                                         int32_t* commit_len, int32_t* cache_slot,
+                                         int32_t mask_id, float* entropy, float* score,
+                                         int32_t* argmax_tok, uint8_t* selected, int32_t* perm,
+                                         int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
+                                         const void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/*
  * wedlm_read_probe - HBM read-rate probe, a measurement aid beside the step
  * (not a step of the method): the rate this GPU reaches on a plain streaming
  * read and on the paged cache's pattern gives the step kernels' roofline

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(W.LIB_PATH),
 
 def test_exports_every_declared_function():
     declared = W.header_functions()
-    assert len(declared) == 19
+    assert len(declared) == 21
     lib = W.lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -250,3 +250,23 @@ def test_entropy_select_noalloc_validation():
     assert big > 4 << 20
     a = list(args); a[1] = 1000; a[2] = 64
     assert _raw("wedlm_entropy_select_noalloc", *a) == -5
+
+
+def test_split_tail_validation():
+    # the chunk pass alone: sizes, dtype, null logits, workspace
+    assert _raw("wedlm_entropy_partials", 1, 0, 16, 1000, 1, 1, 10**6, None) == -1
+    assert _raw("wedlm_entropy_partials", 1, 1, 16, 1000, None, 1, 10**6, None) == -1
+    assert _raw("wedlm_entropy_partials", 9, 1, 16, 1000, 1, 1, 10**6, None) == -2
+    assert _raw("wedlm_entropy_partials", 1, 1, 16, 1000, 1, None, 10**6, None) == -3
+    need = W.wedlm_entropy_select_workspace_size(1, 1, 16, 1000)
+    assert _raw("wedlm_entropy_partials", 1, 1, 16, 1000, 1, 1, need - 1, None) == -3
+    # the tail from partials: rule, page size, null pointers, workspace
+    base = [1, 1, 16, 1000, 0.1, 1.0, 1, 16, 4, 4, 0] + [1] * 7 + [-1] + [1] * 9 + [need, None]
+    a = list(base); a[10] = 3
+    assert _raw("wedlm_select_commit_reorder_partials", *a) == -1     # commit rule
+    a = list(base); a[7] = 8
+    assert _raw("wedlm_select_commit_reorder_partials", *a) == -2     # page size
+    a = list(base); a[12] = None
+    assert _raw("wedlm_select_commit_reorder_partials", *a) == -1     # run_len
+    a = list(base); a[-2] = need - 1
+    assert _raw("wedlm_select_commit_reorder_partials", *a) == -3     # workspace

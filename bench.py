@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--event-every", type=int, default=8,
                     help="record the attention / entropy timing events on every n-th timed "
                          "step (each record idles the GPU for a few microseconds)")
+    ap.add_argument("--separate-entropy", action="store_true",
+                    help="run each step's entropy chunk pass as its own launch after the "
+                         "attention (by default it rides in the attention's launch)")
     ap.add_argument("--overlap", action="store_true",
                     help="run each step's entropy chunk pass on a second stream beside the "
                          "attention (fused tail only)")
@@ -196,10 +199,11 @@ def config_latencies(args):
     streaming loop's launch sequence (reorder, attention with fused RoPE and
     append, split combine where split, entropy pass, fused tail), captured
     once as a HIP graph and replayed between two timing events: nothing else
-    sits between the step's kernels. Reported: the median, p10 and p90 of the
+    sits between the step's kernels (for bf16 the entropy chunk pass rides in
+    the attention's launch). Reported: the median, p10 and p90 of the
     replayed step; the same step launched eagerly (one host call per kernel);
-    eagerly with the entropy chunk pass on a second stream beside the
-    attention (it reads only the logits);
+    eagerly with the entropy chunk pass as a launch of its own after the
+    attention, and on a second stream beside it (it reads only the logits);
     and, from an eager pass with timing events between the kernels, the
     attention and entropy + tail segments (each event record adds a few
     microseconds of idle GPU, so these are upper bounds of the kernels; the
@@ -259,14 +263,22 @@ def config_latencies(args):
         g_span = timed(lambda mark: graph.replay(), False)
         e_span = timed(lambda mark: step.run(st, q, k, v, logits), False)
         m_span = timed(lambda mark: step.run(st, q, k, v, logits, mark=mark), True)
-        # the entropy chunk pass on a second stream beside the attention
+        # the entropy chunk pass as a launch of its own after the attention
+        # (bf16 runs it in the attention's launch by default) ...
+        default_fuse = step.fuse_entropy
+        step.fuse_entropy = False
+        s_span = timed(lambda mark: step.run(st, q, k, v, logits), False)
+        # ... and on a second stream beside the attention
         step.set_overlap(torch.cuda.Stream())
         o_span = timed(lambda mark: step.run(st, q, k, v, logits), False)
         step.set_overlap(None)
+        step.fuse_entropy = default_fuse
         L = np.asarray(inp["prefix_len"], np.int64)
         commits = step.commit_len.cpu().numpy()
         b = step_bytes(wl, L, commits)
         attn_bytes = b["kv"] + b["window"] + b["attn_out"] + b["commit"]
+        if default_fuse:
+            attn_bytes += b["logits"]  # the attention launch reads the logits too
         ent = entropy_report(step.entropy.cpu().numpy(), inp["filled"], step.score.cpu().numpy(),
                              wl.tau)
 
@@ -280,7 +292,9 @@ def config_latencies(args):
             "workload": wl.name, "dtype": wl.dtype, "steps": args.config_steps,
             "warmup": args.config_warmup, "unit": "us",
             "step_us": stats(g_span["step"]), "step_launch": "one HIP graph replay",
+            "entropy_pass": "in the attention's launch" if default_fuse else "own launch",
             "eager_step_us": stats(e_span["step"]),
+            "eager_separate_entropy_step_us": stats(s_span["step"]),
             "overlap_step_us": stats(o_span["step"]),
             "attn_segment_us": stats(m_span["attn"]),
             "entropy_tail_segment_us": stats(m_span["entropy"]),
@@ -288,7 +302,8 @@ def config_latencies(args):
             "step_hbm_gbps_at_median": step_bytes_total / (float(np.median(g_span["step"])) * 1e-6) / 1e9,
             "attn_algorithmic_bytes": int(attn_bytes), "logits_bytes": int(b["logits"]),
             "attn_hbm_gbps_at_segment_median": attn_bytes / (med["attn"] * 1e-6) / 1e9,
-            "entropy_hbm_gbps_at_segment_median": b["logits"] / (med["entropy"] * 1e-6) / 1e9,
+            "entropy_hbm_gbps_at_segment_median": (None if default_fuse else
+                                                   b["logits"] / (med["entropy"] * 1e-6) / 1e9),
             "entropy_histogram": ent,
             "data": "synthetic",
         }
@@ -645,6 +660,8 @@ def main():
     step = make_window_step(wl, inp, dev, L0 + wl.W * n_inputs, fused_tail=not args.separate_tail)
     if args.overlap and not args.separate_tail:
         step.set_overlap(torch.cuda.Stream())
+    step.fuse_entropy = step.fuse_entropy and not (args.separate_entropy or args.overlap or
+                                                   args.separate_tail)
     ins = [stream_step_inputs(wl, s, dev) for s in range(n_inputs)]
     commit_log = torch.zeros((n_inputs, wl.B), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
@@ -712,17 +729,21 @@ def main():
         for key in tot:
             tot[key] += b[key]
         a = b["kv"] + b["window"] + b["attn_out"] + b["commit"]
+        if step.fuse_entropy:
+            a += b["logits"]  # the launch also reads every logit once
         attn_bytes_all += a
         if s in sampled:
             attn_bytes += a
-            ent_bytes += b["logits"]
+            ent_bytes += 0 if step.fuse_entropy else b["logits"]
         L += commits[s]
     attn_bytes *= reps  # the event samples of every repetition
     ent_bytes *= reps
     total_bytes = sum(tot.values())
     committed = int(commits.sum())
     attn_gbps = attn_bytes / (attn_ms.sum() * 1e-3) / 1e9
-    ent_gbps = ent_bytes / (ent_ms.sum() * 1e-3) / 1e9
+    # with the chunk pass in the attention's launch the second interval is the
+    # tail alone (selection, state commit, next reorder)
+    ent_gbps = ent_bytes / (ent_ms.sum() * 1e-3) / 1e9 if ent_bytes else None
     both_gbps = (attn_bytes + ent_bytes) / ((attn_ms.sum() + ent_ms.sum()) * 1e-3) / 1e9
     step_gbps = total_bytes / elapsed / 1e9
     alg_per_launch = attn_bytes / (len(sampled) * reps)
@@ -763,7 +784,8 @@ def main():
                    "kv_heads": wl.Hkv, "head_dim": wl.D, "window": wl.W, "vocab": wl.V,
                    "initial_prefix": int(L0), "page_size": wl.page_size,
                    "step_tail": "separate" if args.separate_tail else "fused",
-                   "entropy_stream": "side" if (args.overlap and not args.separate_tail) else "same",
+                   "entropy_stream": ("side" if (args.overlap and not args.separate_tail) else
+                                      "attention launch" if step.fuse_entropy else "same"),
                    "parallelism": "single GPU"},
         "timing": f"median of {reps} repetitions of steps 0..{K - 1} from the start state "
                   f"(window-steps/s per repetition: "
@@ -777,7 +799,9 @@ def main():
         "entropy_hbm_gbps": ent_gbps,
         "bytes_per_step_avg": {k_: v_ / K for k_, v_ in tot.items()},
         "entropy_histogram": ent_hist,
-        "roofline": {"kernel": "k_window_attn_bf16", "bound": "hbm", "achieved": attn_gbps,
+        "roofline": {"kernel": "k_window_attn_bf16" + (" (carrying the entropy chunk pass)"
+                                                        if step.fuse_entropy else ""),
+                     "bound": "hbm", "achieved": attn_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": attn_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "traffic_over_algorithmic": ratio,
                      "avg_launch_ms": float(attn_ms.mean()),

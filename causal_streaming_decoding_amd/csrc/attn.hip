@@ -43,6 +43,7 @@
 // split with the causal rule (row p sees window rows 0..p), staged into LDS in
 // the same page layout.
 #include "common.hpp"
+#include "entropy_ops.hpp"
 
 #include <cmath>
 
@@ -118,6 +119,13 @@ struct AttnArgs {
   const int32_t* commit_run;
   uint16_t* kc_w;
   uint16_t* vc_w;
+  // optional entropy chunk pass of the same step, carried by the workgroups
+  // past the attention's (wedlm_window_attn_rope_entropy): bf16 logits
+  // [rows][V], ent_chunks chunks of ent_chunk_elems per row, partials out
+  long long attn_blocks;  // workgroups of the attention itself
+  const uint16_t* ent_logits;
+  EntPartial* ent_part;
+  int ent_V, ent_chunk_elems, ent_chunks, ent_vec;
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -703,6 +711,20 @@ k_window_attn_bf16(AttnArgs a) {
   __shared__ int s_pos[kRope ? WEDLM_MAX_WINDOW : 1];
   __shared__ int s_split[4];
 
+  if (blockIdx.x >= a.attn_blocks) {
+    // one chunk of one logit row (4 waves = kEntThreads threads)
+    __shared__ EntPartial red[kEntThreads / kWave];
+    const long long e = blockIdx.x - a.attn_blocks;
+    const int chunk = static_cast<int>(e % a.ent_chunks);
+    const int row = static_cast<int>(e / a.ent_chunks);
+    if (a.ent_vec)
+      entropy_chunk_block<uint16_t, true>(a.ent_logits, a.ent_V, a.ent_chunk_elems, a.ent_chunks,
+                                          a.ent_part, chunk, row, red);
+    else
+      entropy_chunk_block<uint16_t, false>(a.ent_logits, a.ent_V, a.ent_chunk_elems,
+                                           a.ent_chunks, a.ent_part, chunk, row, red);
+    return;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
@@ -1410,7 +1432,9 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
                        const int32_t* perm, const int32_t* pos, const void* k_cache,
                        const void* v_cache, const int32_t* block_table, const int32_t* prefix_len,
                        const int32_t* commit_run, void* out_phys, void* workspace,
-                       size_t workspace_bytes, int flags, void* stream) {
+                       size_t workspace_bytes, int flags, void* stream, int V = 0,
+                       const void* logits = nullptr, void* ent_workspace = nullptr,
+                       size_t ent_workspace_bytes = 0) {
   int st = validate_attn(dtype, n_layers, B, W, Hq, Hkv, D, page_size, max_prefix_len);
   if (st != WEDLM_OK) return st;
   if ((flags & ~WEDLM_ATTN_SHARED_PAGES) != 0) return WEDLM_ERR_INVALID;
@@ -1498,8 +1522,26 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   a.kc_w = commit_run ? static_cast<uint16_t*>(const_cast<void*>(k_cache)) : nullptr;
   a.vc_w = commit_run ? static_cast<uint16_t*>(const_cast<void*>(v_cache)) : nullptr;
   const long long groups = 1LL * n_layers * B * Hkv;
-  const long long blocks =
+  const long long attn_blocks =
       pl.parts == 1 ? a.units : (a.units + kNumXcds - 1) / kNumXcds * kNumXcds * pl.parts;
+  a.attn_blocks = attn_blocks;
+  a.ent_logits = static_cast<const uint16_t*>(logits);
+  a.ent_part = static_cast<EntPartial*>(ent_workspace);
+  a.ent_V = 0;
+  a.ent_chunk_elems = 0;
+  a.ent_chunks = 1;
+  a.ent_vec = 0;
+  long long ent_blocks = 0;
+  if (logits != nullptr) {
+    EntPlan ep = plan_entropy(dtype, B, W, V);
+    if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) ep.vec = false;
+    a.ent_V = V;
+    a.ent_chunk_elems = ep.chunk_elems;
+    a.ent_chunks = ep.n_chunks;
+    a.ent_vec = ep.vec ? 1 : 0;
+    ent_blocks = 1LL * B * W * ep.n_chunks;
+  }
+  const long long blocks = attn_blocks + ent_blocks;
   if (blocks > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
   const dim3 grid(static_cast<unsigned>(blocks));
   auto go = [&](auto kernel, int waves) {
@@ -1531,6 +1573,27 @@ extern "C" int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, 
                      max_prefix_len, scale, 0.0, q_phys, k_phys, v_phys, nullptr, nullptr, k_cache,
                      v_cache, block_table, prefix_len, nullptr, out_phys, workspace,
                      workspace_bytes, flags, stream);
+}
+
+extern "C" int wedlm_window_attn_rope_entropy(
+    int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D, int page_size, int num_pages,
+    int max_pages, int max_prefix_len, float scale, double theta, const void* q, const void* k,
+    const void* v, const int32_t* perm, const int32_t* pos, void* k_cache, void* v_cache,
+    const int32_t* block_table, const int32_t* prefix_len, const int32_t* commit_run,
+    void* out_phys, void* workspace, size_t workspace_bytes, int flags, int V,
+    const void* logits, void* ent_workspace, size_t ent_workspace_bytes, void* stream) {
+  if (dtype != WEDLM_BF16) return WEDLM_ERR_UNSUPPORTED;  // the chunk blocks read bf16
+  if (V <= 0 || logits == nullptr) return WEDLM_ERR_INVALID;
+  if (B > 0 && W > 0 && 1LL * B * W > 65535) return WEDLM_ERR_UNSUPPORTED;
+  if (B > 0 && W > 0 && W <= WEDLM_MAX_WINDOW) {
+    const EntPlan ep = plan_entropy(dtype, B, W, V);
+    const size_t need = static_cast<size_t>(B) * W * ep.n_chunks * sizeof(EntPartial);
+    if (ent_workspace == nullptr || ent_workspace_bytes < need) return WEDLM_ERR_WORKSPACE;
+  }
+  return launch_attn(true, dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages,
+                     max_prefix_len, scale, theta, q, k, v, perm, pos, k_cache, v_cache,
+                     block_table, prefix_len, commit_run, out_phys, workspace, workspace_bytes,
+                     flags, stream, V, logits, ent_workspace, ent_workspace_bytes);
 }
 
 extern "C" int wedlm_window_attn_rope(int dtype, int n_layers, int B, int W, int Hq, int Hkv,

@@ -1,0 +1,155 @@
+// Chunk pass of the full-vocabulary entropy (one block per chunk of a logit
+// row), shared by the entropy kernels and by the attention kernel, whose
+// launch can carry the chunk blocks of the same step after its own
+// workgroups.
+//
+// Entropy of softmax(z) in one streaming pass, in base-2 units: with
+// u = (z - m) log2(e), s = sum 2^u and t = sum u 2^u, H = ln2 (log2 s - t / s).
+// Each thread keeps (m, s, t) for its strided 16-byte vectors; when a pass
+// raises the running max the sums are rescaled by 2^(m_old - m_new) (exact
+// identity: t' = (t + d s) 2^d with d = (m_old - m_new) log2 e). The argmax is
+// tracked as the vector where the thread's max last rose, whose raw bits are
+// kept in registers; at the end the lowest index holding the max is found in
+// them, so no logit is read twice.
+#pragma once
+
+#include "common.hpp"
+
+namespace wedlm {
+
+constexpr int kEntThreads = 256;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct EVec {
+  static constexpr int N = 16 / sizeof(T);
+  union {
+    u32x4 raw;
+    T e[N];
+  };
+};
+
+// Vectors (16 bytes, or single elements when !VEC) per thread per block: all
+// of a thread's loads are issued before any is reduced.
+constexpr int kEntIter = 8;
+
+// Chunk `chunk` of logit row `row` reduced to (m, s, t, argmax) by a block of
+// kEntThreads threads, written to part[row * n_chunks + chunk]; red is the
+// block's LDS scratch. VEC: rows are 16-byte aligned and V is a multiple of
+// the vector width.
+template <typename T, bool VEC>
+__device__ __forceinline__ void entropy_chunk_block(const T* __restrict__ logits, int V,
+                                                    int chunk_elems, int n_chunks,
+                                                    EntPartial* __restrict__ part, int chunk,
+                                                    int row, EntPartial* red) {
+  constexpr int N = VEC ? EVec<T>::N : 1;
+  const int begin = chunk * chunk_elems;
+  const int end = min(V, begin + chunk_elems);
+  const T* z = logits + static_cast<size_t>(row) * V;
+  float m = kNegBig, s = 0.f, t = 0.f;
+  int best = -1;       // first element index of the vector where the max last rose
+  u32x4 best_raw = {0u, 0u, 0u, 0u};
+  // one pass of this loop when VEC (the chunk is exactly kEntIter vectors per
+  // thread), 16 / sizeof(T) passes of single elements otherwise
+  for (int base = begin; base < end; base += kEntThreads * kEntIter * N) {
+    EVec<T> vv[kEntIter];
+#pragma unroll
+    for (int it = 0; it < kEntIter; ++it) {
+      const int i0 = base + (it * kEntThreads + threadIdx.x) * N;
+      if constexpr (VEC) {
+        vv[it].raw = i0 < end ? *reinterpret_cast<const u32x4*>(z + i0) : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        vv[it].raw = u32x4{0u, 0u, 0u, 0u};
+        if (i0 < end) vv[it].e[0] = z[i0];
+      }
+    }
+    // all of this pass's logits are in registers: first their max (and the
+    // vector where it first appears), then the sums against one reference
+    float mpass = kNegBig;
+#pragma unroll
+    for (int it = 0; it < kEntIter; ++it) {
+      const int i0 = base + (it * kEntThreads + threadIdx.x) * N;
+      if (i0 >= end) continue;  // (no break: the loop must unroll fully)
+      float mz = Elt<T>::load(&vv[it].e[0]);
+#pragma unroll
+      for (int e = 1; e < N; ++e) mz = fmaxf(mz, Elt<T>::load(&vv[it].e[e]));
+      if (mz > mpass) {
+        mpass = mz;
+        if (mz > m) {
+          best = i0;
+          best_raw = vv[it].raw;
+        }
+      }
+    }
+    if (mpass > m) {  // rescale the running sums to the new reference
+      const float d = (m - mpass) * kLog2eF;
+      const float f = __builtin_amdgcn_exp2f(d);
+      t = (t + d * s) * f;
+      s = s * f;
+      m = mpass;
+    }
+    const float mb = m * kLog2eF;
+#pragma unroll
+    for (int it = 0; it < kEntIter; ++it) {
+      const int i0 = base + (it * kEntThreads + threadIdx.x) * N;
+      if (i0 >= end) continue;
+#pragma unroll
+      for (int e = 0; e < N; ++e) {
+        const float u = fmaf(Elt<T>::load(&vv[it].e[e]), kLog2eF, -mb);
+        const float p = __builtin_amdgcn_exp2f(u);
+        s += p;
+        t = fmaf(p, u, t);
+      }
+    }
+  }
+  EntPartial acc{m, s, t, 0x7fffffff};
+  if (best >= 0) {
+    EVec<T> bv;
+    bv.raw = best_raw;
+#pragma unroll
+    for (int e = N - 1; e >= 0; --e)
+      if (Elt<T>::load(&bv.e[e]) == m) acc.idx = best + e;
+  }
+  // wavefront then block reduction
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    EntPartial o;
+    o.m = __shfl_xor(acc.m, off, kWave);
+    o.s = __shfl_xor(acc.s, off, kWave);
+    o.t = __shfl_xor(acc.t, off, kWave);
+    o.idx = __shfl_xor(acc.idx, off, kWave);
+    merge(acc, o);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    EntPartial r = red[0];
+    for (int w = 1; w < kEntThreads / kWave; ++w) merge(r, red[w]);
+    part[static_cast<size_t>(row) * n_chunks + chunk] = r;
+  }
+}
+
+// Chunking of the rows: kEntIter 16-byte vectors per thread (the same element
+// count on the single-element path, so the workspace does not depend on
+// alignment).
+struct EntPlan {
+  int chunk_elems, n_chunks;
+  bool vec;
+};
+
+inline EntPlan plan_entropy(int dtype, int B, int W, int V) {
+  EntPlan pl{};
+  const int N = 16 / static_cast<int>(elt_size(dtype));
+  pl.vec = (V % N) == 0;
+  // a chunk is kEntIter 16-byte vectors per thread (the same element count on
+  // the single-element path, so the workspace does not depend on alignment)
+  pl.chunk_elems = kEntThreads * kEntIter * N;
+  pl.n_chunks = (V + pl.chunk_elems - 1) / pl.chunk_elems;
+  (void)B;
+  (void)W;
+  return pl;
+}
+
+}  // namespace wedlm

@@ -10,7 +10,9 @@ attention and commit calls (wedlm_window_attn_rope, wedlm_commit_prefix_rope)
 instead of as its own pass over the window. With ``fused_tail`` the selection,
 the window-state commit and the next step's reorder run as one call
 (wedlm_select_commit_reorder), so a chain of steps is one reorder followed by
-(attention, tail) pairs. Device buffers are allocated once; ``run`` only
+(attention, tail) pairs; for bf16 the entropy chunk pass then rides in the
+attention's launch (wedlm_window_attn_rope_entropy, then
+wedlm_select_commit_reorder_partials). Device buffers are allocated once; ``run`` only
 enqueues kernels and never synchronises, so steps can be chained or timed back
 to back.
 """
@@ -94,6 +96,10 @@ class WindowStep:
         self.ent_ws = torch.empty((max(self.ent_ws_bytes, 1),), dtype=torch.uint8, device=device)
         # optional side stream for the entropy chunk pass (set_overlap)
         self.overlap = None
+        # fused tail on bf16: the entropy chunk blocks run in the attention's
+        # launch (wedlm_window_attn_rope_entropy); they fill the CUs the
+        # attention leaves idle (measured faster on every workload)
+        self.fuse_entropy = dtype == torch.bfloat16
         self._ev_in = self._ev_ent = None
 
     def _size_attn_workspace(self, max_prefix_len):
@@ -201,6 +207,23 @@ class WindowStep:
         if tail and self.overlap is not None:
             self._run_overlapped(st, q, k, v, logits, max_prefix_len, commit_len, stream, mark)
             return
+        if tail and self.fuse_entropy:
+            # the entropy chunk blocks ride in the attention's launch
+            if mark is not None:
+                mark("attn_start")
+            mpl = self._attn_mpl(max_prefix_len)
+            W_.wedlm_window_attn_rope_entropy(
+                self.dt, self.n_layers, self.B, self.W, self.Hq, self.Hkv, self.D,
+                self.page_size, self.num_pages, self.max_pages, mpl, self.scale, self.theta, q, k,
+                v, self.perm, self.pos, st.k_cache, st.v_cache, st.block_table, st.prefix_len,
+                self.run_len, self.out_phys, self.attn_ws, self.attn_ws_bytes, 0, self.V, logits,
+                self.ent_ws, self.ent_ws_bytes, stream)
+            if mark is not None:
+                mark("attn_end")
+            self._tail_from_partials(st, commit_len, stream)
+            if mark is not None:
+                mark("entropy_end")
+            return
         if not self.fused_rope:
             self.rope(q, k, v, stream)
         if mark is not None:
@@ -242,16 +265,21 @@ class WindowStep:
         if mark is not None:
             mark("attn_end")
         main.wait_event(self._ev_ent)
+        self._tail_from_partials(st, commit_len, main)
+        if mark is not None:
+            mark("entropy_end")
+
+    def _tail_from_partials(self, st, commit_len, stream):
+        """Selection, state commit and next reorder from the chunk partials
+        already in the entropy workspace."""
         W_.wedlm_select_commit_reorder_partials(
             self.dt, self.B, self.W, self.V, self.lam, self.tau, self.min_fill, self.page_size,
             self.num_pages, self.max_pages, self.commit_rule, st.block_table, self.run_len,
             st.tokens, st.filled, st.prefix_len,
             self.commit_len if commit_len is None else commit_len, self.cache_slot, self.mask_id,
             self.entropy, self.score, self.argmax, self.selected, self.perm, self.inv, self.pos,
-            self.n_obs, self.ent_ws, self.ent_ws_bytes, main)
+            self.n_obs, self.ent_ws, self.ent_ws_bytes, stream)
         st.ordered_by = self
-        if mark is not None:
-            mark("entropy_end")
 
     def set_overlap(self, side_stream):
         """Run the entropy chunk pass on ``side_stream`` (a torch stream of

@@ -55,6 +55,8 @@ _SIGNATURES = {
     "wedlm_select_commit_reorder": (_c_int, [_c_int] * 4 + [_p, _c_float, _c_float] + [_c_int] * 5
                                     + [_p] * 7 + [ctypes.c_int32] + [_p] * 9 + [_c_size, _p]),
     "wedlm_entropy_partials": (_c_int, [_c_int] * 4 + [_p, _p, _c_size, _p]),
+    "wedlm_window_attn_rope_entropy": (_c_int, [_c_int] * 11 + [_c_float, _c_double] + [_p] * 12
+                                       + [_c_size, _c_int, _c_int, _p, _p, _c_size, _p]),
     "wedlm_select_commit_reorder_partials": (_c_int, [_c_int] * 4 + [_c_float, _c_float]
                                              + [_c_int] * 5 + [_p] * 7 + [ctypes.c_int32]
                                              + [_p] * 9 + [_c_size, _p]),
@@ -258,6 +260,19 @@ def wedlm_select_commit_reorder(dtype, B, W, V, logits, lam, tau, min_fill, page
         _ptr(prefix_len), _ptr(commit_len), _ptr(cache_slot), int(mask_id), _ptr(entropy),
         _ptr(score), _ptr(argmax_tok), _ptr(selected), _ptr(perm), _ptr(inv_perm), _ptr(pos),
         _ptr(n_obs), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def wedlm_window_attn_rope_entropy(dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages,
+                                   max_pages, max_prefix_len, scale, theta, q, k, v, perm, pos,
+                                   k_cache, v_cache, block_table, prefix_len, commit_run, out_phys,
+                                   workspace, workspace_bytes, flags, V, logits, ent_workspace,
+                                   ent_workspace_bytes, stream=None):
+    _check("wedlm_window_attn_rope_entropy", lib().wedlm_window_attn_rope_entropy(
+        dtype, n_layers, B, W, Hq, Hkv, D, page_size, num_pages, max_pages, max_prefix_len,
+        float(scale), float(theta), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(pos),
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(prefix_len), _ptr(commit_run),
+        _ptr(out_phys), _ptr(workspace), workspace_bytes, flags, V, _ptr(logits),
+        _ptr(ent_workspace), ent_workspace_bytes, _stream(stream)))
 
 
 def wedlm_entropy_partials(dtype, B, W, V, logits, workspace, workspace_bytes, stream=None):

@@ -240,6 +240,35 @@ int wedlm_window_attn_rope(int dtype, int n_layers, int B, int W, int Hq, int Hk
                            const int32_t* commit_run, void* out_phys, void* workspace,
                            size_t workspace_bytes, int flags, void* stream);
 
+/*
+ * wedlm_window_attn_rope_entropy - wedlm_window_attn_rope and the entropy
+ * chunk pass of the same step (wedlm_entropy_partials) in one launch: the
+ * workgroups past the attention's each reduce one chunk of one logit row, so
+ * the chunk pass fills the GPU wherever the attention leaves it idle (a
+ * batch too small to occupy every CU, the workgroups of a ragged batch that
+ * end early, a last partial round) without a second stream. hyper.ai summary
+ * of WeDLM, "Method": one forward pass yields the attention outputs and the
+ * predictions whose entropies the selection ranks; with synthetic inputs the
+ * logits are given, and the two reductions are independent.
+ *
+ * Arguments up to flags are those of wedlm_window_attn_rope (bf16 only, else
+ * WEDLM_ERR_UNSUPPORTED); V, logits [B][W][V] bf16 and ent_workspace (at
+ * least wedlm_entropy_select_workspace_size(dtype, B, W, V) bytes, else
+ * WEDLM_ERR_WORKSPACE) are those of wedlm_entropy_partials. Results are
+ * bitwise those of the two calls; follow with
+ * wedlm_select_commit_reorder_partials on the same stream.
+ */
+int wedlm_window_attn_rope_entropy(int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D,
+                                   int page_size, int num_pages, int max_pages,
+                                   int max_prefix_len, float scale, double theta, const void* q,
+                                   const void* k, const void* v, const int32_t* perm,
+                                   const int32_t* pos, void* k_cache, void* v_cache,
+                                   const int32_t* block_table, const int32_t* prefix_len,
+                                   const int32_t* commit_run, void* out_phys, void* workspace,
+                                   size_t workspace_bytes, int flags, int V, const void* logits,
+                                   void* ent_workspace, size_t ent_workspace_bytes,
+                                   void* stream);
+
 /* Bytes of workspace wedlm_entropy_select needs (per-chunk partial reductions). */
 size_t wedlm_entropy_select_workspace_size(int dtype, int B, int W, int V);
 

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(W.LIB_PATH),
 
 def test_exports_every_declared_function():
     declared = W.header_functions()
-    assert len(declared) == 21
+    assert len(declared) == 22
     lib = W.lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -31,8 +31,9 @@ def test_status_strings_and_version():
     assert "unsupported" in W.wedlm_status_string(-2)
     assert "workspace" in W.wedlm_status_string(-3)
     assert W.wedlm_abi_version() >> 16 == 1
-    assert W.wedlm_abi_version() & 0xffff >= 6  # fused RoPE, LM head, commit rules, step tail,
-    #                                               attention flags, workspace-free selection
+    assert W.wedlm_abi_version() & 0xffff >= 7  # fused RoPE, LM head, commit rules, step tail,
+    #                          attention flags, workspace-free selection, split tail, entropy in
+    #                          the attention launch
     assert "scratch" in W.wedlm_status_string(-5)
 
 
@@ -270,3 +271,18 @@ def test_split_tail_validation():
     assert _raw("wedlm_select_commit_reorder_partials", *a) == -1     # run_len
     a = list(base); a[-2] = need - 1
     assert _raw("wedlm_select_commit_reorder_partials", *a) == -3     # workspace
+
+
+def test_attn_rope_entropy_validation():
+    need = W.wedlm_entropy_select_workspace_size(1, 1, 16, 1000)
+    # wedlm_window_attn_rope's arguments, then V, logits, entropy workspace
+    base = ([1, 1, 1, 16, 32, 8, 128, 16, 200, 200, 2048, 0.088, 1e6] + [1] * 12
+            + [1 << 30, 0, 1000, 1, 1, need, None])
+    a = list(base); a[0] = 0
+    assert _raw("wedlm_window_attn_rope_entropy", *a) == -2    # bf16 only
+    a = list(base); a[-4] = None
+    assert _raw("wedlm_window_attn_rope_entropy", *a) == -1    # logits
+    a = list(base); a[-2] = need - 1
+    assert _raw("wedlm_window_attn_rope_entropy", *a) == -3    # entropy workspace
+    a = list(base); a[-5] = 0
+    assert _raw("wedlm_window_attn_rope_entropy", *a) == -1    # V

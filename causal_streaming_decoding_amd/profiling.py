@@ -34,7 +34,7 @@ import os
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-ATTN_SOURCES = ("csrc/attn.hip", "csrc/common.hpp")
+ATTN_SOURCES = ("csrc/attn.hip", "csrc/common.hpp", "csrc/entropy_ops.hpp")
 ATTN_KERNEL = "k_window_attn_bf16"
 CALIBRATION_KIB = 1 << 20  # the 1 GiB copy, read once and written once
 
@@ -96,8 +96,17 @@ def counter_values(pmc_dir, counter):
     return per, calib
 
 
+def _bench_line(path):
+    with open(path) as f:
+        return json.loads([ln for ln in f if ln.startswith("{")][-1])
+
+
 def summarize(trace, fetch, write, bench_json, steps, out_md, out_traffic, command_trace,
-              command_fetch, command_write):
+              command_fetch, command_write, counter_bench_json=None):
+    """counter_bench_json: the bench line of the counter runs, when they ran
+    fewer steps than the traced command (its algorithmic bytes per launch
+    then go with the counted bytes; the trace's line still gives the timed
+    launch duration)."""
     stats = kernel_stats(trace)
     fetch_kib, fetch_cal = counter_values(fetch, "FETCH_SIZE")
     write_kib, write_cal = counter_values(write, "WRITE_SIZE")
@@ -105,9 +114,9 @@ def summarize(trace, fetch, write, bench_json, steps, out_md, out_traffic, comma
         raise SystemExit("no calibration copy in the counter runs (bench.py --calibrate-copy)")
     f_fac = fetch_cal / CALIBRATION_KIB
     w_fac = write_cal / CALIBRATION_KIB
-    with open(bench_json) as f:
-        bench = json.loads([ln for ln in f if ln.startswith("{")][-1])
+    bench = _bench_line(bench_json)
     roof = bench["roofline"]
+    croof = _bench_line(counter_bench_json)["roofline"] if counter_bench_json else roof
 
     def per_launch(d, name, fac):
         vals = d.get(name, [])[-steps:]  # the timed steps are the last dispatches
@@ -117,7 +126,7 @@ def summarize(trace, fetch, write, bench_json, steps, out_md, out_traffic, comma
     a_fetch = per_launch(fetch_kib, attn, f_fac)
     a_write = per_launch(write_kib, attn, w_fac)
     # the counters cover every timed launch; the events a uniform sample of them
-    alg = roof.get("algorithmic_bytes_per_launch_all_steps", roof["algorithmic_bytes_per_launch"])
+    alg = croof.get("algorithmic_bytes_per_launch_all_steps", croof["algorithmic_bytes_per_launch"])
     trace_avg = next(t[2] for t in stats if t[0] == attn)
 
     lines = [f"# Window step kernels: {bench['config']['workload']}", "",
@@ -143,9 +152,11 @@ def summarize(trace, fetch, write, bench_json, steps, out_md, out_traffic, comma
         if r is None or w is None:
             continue
         lines.append(f"| `{n}` | {r / 1e6:.2f} | {w / 1e6:.2f} |")
-    lines += ["", f"Window attention: algorithmic {alg / 1e6:.1f} MB per launch (KV prefix + window "
-              f"q/k/v read, output and committed rows written); counted {(a_fetch + a_write) / 1e6:.1f} MB "
-              f"({(a_fetch + a_write) / alg:.3f} x)."]
+    what = ("KV prefix, window q/k/v and the step's logits (the launch carries the entropy "
+            "chunk pass) read, output and committed rows written") if "entropy" in roof.get(
+                "kernel", "") else "KV prefix + window q/k/v read, output and committed rows written"
+    lines += ["", f"Window attention: algorithmic {alg / 1e6:.1f} MB per launch ({what}); counted "
+              f"{(a_fetch + a_write) / 1e6:.1f} MB ({(a_fetch + a_write) / alg:.3f} x)."]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(out_traffic, "w") as f:
@@ -349,6 +360,7 @@ def main():
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
     ap.add_argument("--bench-json", required=True)
+    ap.add_argument("--counter-bench-json", default=None)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--out-md", required=True)
     ap.add_argument("--out-traffic", required=True)
@@ -357,7 +369,7 @@ def main():
     ap.add_argument("--command-write", default="")
     a = ap.parse_args()
     summarize(a.trace, a.fetch, a.write, a.bench_json, a.steps, a.out_md, a.out_traffic,
-              a.command_trace, a.command_fetch, a.command_write)
+              a.command_trace, a.command_fetch, a.command_write, a.counter_bench_json)
 
 
 if __name__ == "__main__":

@@ -1478,7 +1478,7 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
     if (st != WEDLM_OK || commit_run == nullptr) return st;
     // the f32 path appends the committed rows with the commit step's own kernel
     return commit_rows_rope(dtype, n_layers, B, W, Hkv, D, page_size, num_pages, max_pages,
-                            theta, commit_run, prefix_len, k, v, block_table,
+                            theta, commit_run, prefix_len, pos, k, v, block_table,
                             const_cast<void*>(k_cache), const_cast<void*>(v_cache), s);
   }
   const AttnPlan pl = plan_bf16(n_layers, B, W, Hq, Hkv, max_prefix_len);

@@ -42,14 +42,17 @@ struct CommitRope {
 
 // kRope: k_phys / v_phys are the window rows in slot order before RoPE (the
 // committed rows 0..c-1 are slots 0..c-1 either way); each committed key is
-// rotated at its logical position L + j as it is written.
+// rotated as it is written, at rot_pos[b][j] when rot_pos is given (the
+// positions an attention call rotated the same rows at), else at its logical
+// position L + j. The two agree when rot_pos comes from the window reorder.
 template <typename T, bool kRope>
 __global__ void __launch_bounds__(kCommitThreads)
 k_commit_rows(int B, int W, int Hkv, int D, int P, int num_pages, int max_pages,
               const int32_t* __restrict__ run_len, const int32_t* __restrict__ prefix_len,
               const T* __restrict__ k_phys, const T* __restrict__ v_phys,
               const int32_t* __restrict__ block_table, T* __restrict__ k_cache,
-              T* __restrict__ v_cache, long long cache_layer_stride, CommitRope rope) {
+              T* __restrict__ v_cache, long long cache_layer_stride, CommitRope rope,
+              const int32_t* __restrict__ rot_pos) {
   constexpr int X = 16 / sizeof(T);         // elements per 16-byte K slice
   constexpr int kLineElems = 64 / sizeof(T);
   constexpr int kDimsPerLine = kLineElems / 16;  // value dimensions per line (P = 16)
@@ -95,10 +98,12 @@ k_commit_rows(int B, int W, int Hkv, int D, int P, int num_pages, int max_pages,
           } own, mate, out;
           own.v = line[e];
           mate.v = *reinterpret_cast<const u32x4*>(krow + (lower ? sl + hs : sl - hs) * X);
+          const double tr = rot_pos ? static_cast<double>(rot_pos[b * W + (t - L)])
+                                    : static_cast<double>(t);
 #pragma unroll
           for (int x = 0; x < X; ++x) {
             float c, sn;
-            rope_cos_sin(static_cast<double>(t), rope.omega[j0 + x], c, sn);
+            rope_cos_sin(tr, rope.omega[j0 + x], c, sn);
             const float a = Elt<T>::load(&own.e[x]), m = Elt<T>::load(&mate.e[x]);
             // lower half: a cos - mate sin; upper half: a cos + mate sin
             Elt<T>::store(&out.e[x], lower ? a * c - m * sn : a * c + m * sn);
@@ -168,12 +173,13 @@ k_commit_state(int W, int P, int num_pages, int max_pages, const int32_t* __rest
 using namespace wedlm;
 
 // Rows part of the fused commit (used by the f32 attention path, which has no
-// rows of its own to append): rotated keys and values of rows 0..c-1.
+// rows of its own to append): rotated keys and values of rows 0..c-1, the keys
+// rotated at rot_pos[b][j] (the attention's positions).
 int wedlm::commit_rows_rope(int dtype, int n_layers, int B, int W, int Hkv, int D, int page_size,
                             int num_pages, int max_pages, double theta, const int32_t* run_len,
-                            const int32_t* prefix_len, const void* k_rows, const void* v_rows,
-                            const int32_t* block_table, void* k_cache, void* v_cache,
-                            hipStream_t s) {
+                            const int32_t* prefix_len, const int32_t* rot_pos, const void* k_rows,
+                            const void* v_rows, const int32_t* block_table, void* k_cache,
+                            void* v_cache, hipStream_t s) {
   const int X = 16 / static_cast<int>(elt_size(dtype));
   if (D % (2 * X) != 0 || D > kCommitMaxD || page_size != 16) return WEDLM_ERR_UNSUPPORTED;
   const long long stride = 1LL * num_pages * Hkv * D * page_size;
@@ -185,13 +191,13 @@ int wedlm::commit_rows_rope(int dtype, int n_layers, int B, int W, int Hkv, int 
                        Hkv, D, page_size, num_pages, max_pages, run_len, prefix_len,
                        static_cast<const uint16_t*>(k_rows), static_cast<const uint16_t*>(v_rows),
                        block_table, static_cast<uint16_t*>(k_cache),
-                       static_cast<uint16_t*>(v_cache), stride, tab);
+                       static_cast<uint16_t*>(v_cache), stride, tab, rot_pos);
   else
     hipLaunchKernelGGL((k_commit_rows<float, true>), grid, dim3(kCommitThreads), 0, s, B, W, Hkv,
                        D, page_size, num_pages, max_pages, run_len, prefix_len,
                        static_cast<const float*>(k_rows), static_cast<const float*>(v_rows),
                        block_table, static_cast<float*>(k_cache), static_cast<float*>(v_cache),
-                       stride, tab);
+                       stride, tab, rot_pos);
   return launch_status();
 }
 
@@ -229,7 +235,7 @@ static int launch_commit(bool rope, int dtype, int n_layers, int B, int W, int H
     hipLaunchKernelGGL(kernel, grid, dim3(kCommitThreads), 0, s, B, W, Hkv, D, page_size,
                        num_pages, max_pages, run_len, prefix_len, static_cast<const T*>(k_rows),
                        static_cast<const T*>(v_rows), block_table, static_cast<T*>(k_cache),
-                       static_cast<T*>(v_cache), stride, tab);
+                       static_cast<T*>(v_cache), stride, tab, nullptr);
   };
   if (rows) {
     if (dtype == WEDLM_BF16) {

@@ -223,10 +223,12 @@ int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv, in
  *
  * commit_run (device [B], may be NULL): when given, the call also performs the
  * cache half of the commit (hyper.ai summary, "Method": the leftmost filled
- * run is committed at once): rows 0..c-1 of the window, rotated, are written to
- * positions L..L+c-1 of k_cache / v_cache through block_table, with
- * c = commit_run[b] clamped to [0, W] and to max_pages * P - L, and
- * L = max(prefix_len[b], 0) - the rows wedlm_commit_prefix_rope would write.
+ * run is committed at once): rows 0..c-1 of the window, rotated at pos[b][0..c-1]
+ * as for the attention, are written to positions L..L+c-1 of k_cache / v_cache
+ * through block_table, with c = commit_run[b] clamped to [0, W] and to
+ * max_pages * P - L, and L = max(prefix_len[b], 0). With pos from
+ * wedlm_window_reorder, pos[b][j] = L + j for these rows: they are the rows
+ * wedlm_commit_prefix_rope would write.
  * Pass run_len from wedlm_window_reorder, then call wedlm_commit_prefix_rope
  * with k = v = NULL for the window-state half. The appended positions are
  * never among those the call reads (they are >= L). k_cache / v_cache are

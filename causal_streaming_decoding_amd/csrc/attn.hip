@@ -42,6 +42,7 @@
 // the long pole (find_split). The window's own keys are processed by the last
 // split with the causal rule (row p sees window rows 0..p), staged into LDS in
 // the same page layout.
+#include "attn_combine.hpp"
 #include "common.hpp"
 #include "entropy_ops.hpp"
 
@@ -1098,79 +1099,11 @@ k_window_attn_bf16(AttnArgs a) {
   }
 }
 
-// Merge of the per-split partials: out = sum_s O_s 2^(m_s - m) / sum_s l_s 2^(m_s - m).
-// One thread per (group, row, 4 dims), one pass over the group's splits (the
-// plan entry its split 0 wrote: first slot, count) in split order with a
-// running reference max; the partials are read kCombineBatch
-// splits at a time, all loads of a batch issued before any is used, so the
-// latency is paid once per batch rather than once per split.
-constexpr int kCombineBatch = 8;
-
-__global__ void __launch_bounds__(256)
-k_window_attn_combine(const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
-                      const int2* __restrict__ ws_plan, uint16_t* __restrict__ out, int n_groups,
-                      int M, int W, int Hq, int Hkv, int g, int cols, long long n_slots) {
+// Merge of the per-split partials (combine_quad, attn_combine.hpp): one
+// thread per (group, row, 4 value dimensions).
+__global__ void __launch_bounds__(256) k_window_attn_combine(CombineArgs c) {
   const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int quads = kHeadDim / 4;
-  const long long total = static_cast<long long>(n_groups) * M * quads;
-  if (idx >= total) return;
-  const int d4 = static_cast<int>(idx % quads);
-  const int row = static_cast<int>((idx / quads) % M);
-  const int group = static_cast<int>(idx / (static_cast<long long>(quads) * M));
-  int2 plan = ws_plan[group];
-  // the plan entry is device data: keep its slots inside the partials (a
-  // column holds cols of them), whatever it holds
-  plan.x = static_cast<int>(min(max(static_cast<long long>(plan.x), 0LL), n_slots - 1));
-  const int n_splits = static_cast<int>(
-      min(static_cast<long long>(min(max(plan.y, 0), cols)), n_slots - plan.x));
-  float m = -INFINITY, lsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < n_splits; s0 += kCombineBatch) {
-    float2 ml[kCombineBatch];
-    float4 o[kCombineBatch];
-#pragma unroll
-    for (int k = 0; k < kCombineBatch; ++k) {
-      const int s = s0 + k;
-      const size_t part = (static_cast<size_t>(plan.x) + s) * M + row;
-      ml[k] = s < n_splits ? reinterpret_cast<const float2*>(ws_ml)[part]
-                           : make_float2(-INFINITY, 0.f);
-      o[k] = s < n_splits ? *reinterpret_cast<const float4*>(ws_o + part * kHeadDim + d4 * 4)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    // a split with no keys (l = 0, m = -inf) contributes nothing
-    float bm = m;
-#pragma unroll
-    for (int k = 0; k < kCombineBatch; ++k)
-      if (ml[k].y != 0.f) bm = fmaxf(bm, ml[k].x);
-    if (bm > m) {
-      const float r = __builtin_amdgcn_exp2f(m - bm);  // 0 while m = -inf
-      acc.x *= r;
-      acc.y *= r;
-      acc.z *= r;
-      acc.w *= r;
-      lsum *= r;
-      m = bm;
-    }
-#pragma unroll
-    for (int k = 0; k < kCombineBatch; ++k) {
-      if (ml[k].y == 0.f) continue;
-      const float w = __builtin_amdgcn_exp2f(ml[k].x - m);
-      acc.x += o[k].x * w;
-      acc.y += o[k].y * w;
-      acc.z += o[k].z * w;
-      acc.w += o[k].w * w;
-      lsum += ml[k].y * w;
-    }
-  }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  const int kvh = group % Hkv;
-  const int lbi = group / Hkv;  // layer * B + b
-  const int p = row / g, hh = row % g;
-  uint16_t* orow = out + ((static_cast<size_t>(lbi) * W + p) * Hq + kvh * g + hh) * kHeadDim;
-  uint2 w;
-  w.x = pack_bf16x2(acc.x * inv, acc.y * inv);
-  w.y = pack_bf16x2(acc.z * inv, acc.w * inv);
-  *reinterpret_cast<uint2*>(orow + d4 * 4) = w;
+  if (idx < c.threads) combine_quad(c, idx);
 }
 
 // ---------------------------------------------------------------------------
@@ -1393,6 +1326,26 @@ static AttnPlan plan_bf16(int n_layers, int B, int W, int Hq, int Hkv, int max_p
   return pl;
 }
 
+// The merge of a split launch: its partials and plan in the workspace
+// (layout of plan_bf16), the output rows it writes.
+static CombineArgs combine_of(const AttnPlan& pl, const AttnArgs& a, long long groups) {
+  CombineArgs c{};
+  c.ws_o = a.ws_o;
+  c.ws_ml = a.ws_ml;
+  c.ws_plan = a.ws_plan;
+  c.out = a.out;
+  c.n_groups = static_cast<int>(groups);
+  c.M = a.M;
+  c.W = a.W;
+  c.Hq = a.Hq;
+  c.Hkv = a.Hkv;
+  c.g = a.g;
+  c.cols = pl.cols;
+  c.n_slots = a.units;
+  c.threads = pl.split ? groups * a.M * (kHeadDim / 4) : 0;
+  return c;
+}
+
 }  // namespace wedlm
 
 using namespace wedlm;
@@ -1437,7 +1390,7 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
                        size_t ent_workspace_bytes = 0) {
   int st = validate_attn(dtype, n_layers, B, W, Hq, Hkv, D, page_size, max_prefix_len);
   if (st != WEDLM_OK) return st;
-  if ((flags & ~WEDLM_ATTN_SHARED_PAGES) != 0) return WEDLM_ERR_INVALID;
+  if ((flags & ~(WEDLM_ATTN_SHARED_PAGES | WEDLM_ATTN_DEFER_COMBINE)) != 0) return WEDLM_ERR_INVALID;
   if (num_pages <= 0 || max_pages <= 0 || static_cast<long long>(max_pages) * page_size <
                                                static_cast<long long>(max_prefix_len))
     return WEDLM_ERR_INVALID;
@@ -1554,12 +1507,40 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   rope ? pick(k_window_attn_bf16<4, true, true>, k_window_attn_bf16<4, true, false>, pl.waves)
        : pick(k_window_attn_bf16<4, false, true>, k_window_attn_bf16<4, false, false>, pl.waves);
   st = launch_status();
-  if (st != WEDLM_OK || !pl.split) return st;
-  const long long threads = groups * a.M * (kHeadDim / 4);
-  hipLaunchKernelGGL(k_window_attn_combine, dim3(static_cast<unsigned>((threads + 255) / 256)),
-                     dim3(256), 0, s, a.ws_o, a.ws_ml, a.ws_plan, a.out, static_cast<int>(groups),
-                     a.M, W, Hq, Hkv, a.g, a.cols, static_cast<long long>(a.units));
+  // a deferred merge is launched by the step tail (wedlm_select_commit_reorder_combine)
+  if (st != WEDLM_OK || !pl.split || (flags & WEDLM_ATTN_DEFER_COMBINE)) return st;
+  CombineArgs c = combine_of(pl, a, groups);
+  hipLaunchKernelGGL(k_window_attn_combine, dim3(static_cast<unsigned>((c.threads + 255) / 256)),
+                     dim3(256), 0, s, c);
   return launch_status();
+}
+
+int wedlm::attn_combine_args(int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D,
+                             int page_size, int max_prefix_len, const void* workspace,
+                             size_t workspace_bytes, void* out, CombineArgs* c) {
+  *c = CombineArgs{};
+  const int st = validate_attn(dtype, n_layers, B, W, Hq, Hkv, D, page_size, max_prefix_len);
+  if (st != WEDLM_OK) return st;
+  if (dtype != WEDLM_BF16) return WEDLM_OK;  // the f32 path never splits
+  const AttnPlan pl = plan_bf16(n_layers, B, W, Hq, Hkv, max_prefix_len);
+  if (!pl.split) return WEDLM_OK;
+  const size_t need = pl.ws_o_bytes + pl.ws_ml_bytes + pl.ws_plan_bytes;
+  if (workspace == nullptr || workspace_bytes < need) return WEDLM_ERR_WORKSPACE;
+  if (out == nullptr) return WEDLM_ERR_INVALID;
+  AttnArgs a{};
+  char* ws = static_cast<char*>(const_cast<void*>(workspace));
+  a.ws_o = reinterpret_cast<float*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(ws + pl.ws_o_bytes);
+  a.ws_plan = reinterpret_cast<int2*>(ws + pl.ws_o_bytes + pl.ws_ml_bytes);
+  a.out = static_cast<uint16_t*>(out);
+  a.W = W;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.g = Hq / Hkv;
+  a.M = W * a.g;
+  a.units = 1LL * n_layers * Hkv * pl.cols;
+  *c = combine_of(pl, a, 1LL * n_layers * B * Hkv);
+  return WEDLM_OK;
 }
 
 extern "C" int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D,

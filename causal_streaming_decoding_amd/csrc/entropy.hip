@@ -21,7 +21,10 @@
 // wedlm_entropy_partials and wedlm_select_commit_reorder_partials are the two
 // halves of wedlm_select_commit_reorder as separate calls, so that the chunk
 // pass, which reads only the logits, can run on another stream beside the
-// step's attention.
+// step's attention. wedlm_select_commit_reorder_combine adds the merge of the
+// step's split attention partials (combine_quad) as workgroups past the B
+// tail wavefronts of the same launch.
+#include "attn_combine.hpp"
 #include "entropy_ops.hpp"
 #include "window_ops.hpp"
 
@@ -56,9 +59,12 @@ k_entropy_select(const EntPartial* __restrict__ part, int n_chunks, int W,
 // window shift and refill, and the next step's reorder of the new window -
 // the same three operations as k_entropy_select, k_commit_state and
 // k_window_reorder in one launch. run_len is read as this step's run and
-// overwritten with the next step's.
+// overwritten with the next step's. Workgroups past the first B (the grid's
+// tail part, B = tail_blocks) each merge kWave (group, row, 4 dims) outputs of
+// the attention's split partials (comb; none when comb.threads = 0).
 __global__ void __launch_bounds__(kWave)
-k_step_tail(const EntPartial* __restrict__ part, int n_chunks, int W, float lambda, float tau,
+k_step_tail(int tail_blocks, CombineArgs comb, const EntPartial* __restrict__ part, int n_chunks,
+            int W, float lambda, float tau,
             int min_fill, int P, int num_pages, int max_pages, int block_rule,
             const int32_t* __restrict__ block_table, int32_t* __restrict__ tokens,
             uint8_t* __restrict__ filled, int32_t* __restrict__ prefix_len,
@@ -68,6 +74,12 @@ k_step_tail(const EntPartial* __restrict__ part, int n_chunks, int W, float lamb
             uint8_t* __restrict__ selected, int32_t* __restrict__ perm,
             int32_t* __restrict__ inv_perm, int32_t* __restrict__ pos,
             int32_t* __restrict__ n_obs) {
+  if (static_cast<int>(blockIdx.x) >= tail_blocks) {
+    const long long idx =
+        static_cast<long long>(blockIdx.x - tail_blocks) * kWave + threadIdx.x;
+    if (idx < comb.threads) combine_quad(comb, idx);
+    return;
+  }
   const int b = blockIdx.x;
   const int i = threadIdx.x;
   bool f = false;
@@ -246,8 +258,12 @@ static int launch_step_tail(int W, float lambda, float tau, int min_fill, int pa
                             int32_t* cache_slot, int32_t mask_id, float* entropy, float* score,
                             int32_t* argmax_tok, uint8_t* selected, int32_t* perm,
                             int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
-                            const EntPartial* part, int n_chunks, hipStream_t s) {
-  hipLaunchKernelGGL(k_step_tail, dim3(B), dim3(kWave), 0, s, part, n_chunks, W, lambda, tau,
+                            const EntPartial* part, int n_chunks, hipStream_t s,
+                            const CombineArgs& comb = CombineArgs{}) {
+  const long long blocks = B + (comb.threads + kWave - 1) / kWave;
+  if (blocks > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(k_step_tail, dim3(static_cast<unsigned>(blocks)), dim3(kWave), 0, s, B,
+                     comb, part, n_chunks, W, lambda, tau,
                      min_fill, page_size, num_pages, max_pages,
                      commit_rule == WEDLM_COMMIT_BLOCK ? 1 : 0, block_table, tokens, filled,
                      prefix_len, run_len, commit_len, cache_slot, mask_id, entropy, score,
@@ -293,6 +309,35 @@ extern "C" int wedlm_select_commit_reorder_partials(
                           cache_slot, mask_id, entropy, score, argmax_tok, selected, perm,
                           inv_perm, pos, n_obs, static_cast<const EntPartial*>(workspace),
                           pl.n_chunks, as_stream(stream));
+}
+
+extern "C" int wedlm_select_commit_reorder_combine(
+    int dtype, int B, int W, int V, float lambda, float tau, int min_fill, int page_size,
+    int num_pages, int max_pages, int commit_rule, const int32_t* block_table, int32_t* run_len,
+    int32_t* tokens, uint8_t* filled, int32_t* prefix_len, int32_t* commit_len,
+    int32_t* cache_slot, int32_t mask_id, float* entropy, float* score, int32_t* argmax_tok,
+    uint8_t* selected, int32_t* perm, int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
+    const void* workspace, size_t workspace_bytes, int attn_n_layers, int attn_Hq, int attn_Hkv,
+    int attn_D, int attn_max_prefix_len, const void* attn_workspace,
+    size_t attn_workspace_bytes, void* attn_out, void* stream) {
+  const void* ptrs[] = {block_table, run_len, tokens, filled, prefix_len, commit_len, cache_slot,
+                        entropy, score, argmax_tok, selected, perm, inv_perm, pos, n_obs};
+  const int v = validate_tail(dtype, B, W, V, lambda, tau, min_fill, page_size, num_pages,
+                              max_pages, commit_rule, ptrs, 15);
+  if (v != WEDLM_OK) return v;
+  const EntPlan pl = plan_entropy(dtype, B, W, V);
+  const size_t need = static_cast<size_t>(B) * W * pl.n_chunks * sizeof(EntPartial);
+  if (workspace == nullptr || workspace_bytes < need) return WEDLM_ERR_WORKSPACE;
+  CombineArgs comb;
+  const int c = attn_combine_args(dtype, attn_n_layers, B, W, attn_Hq, attn_Hkv, attn_D,
+                                  page_size, attn_max_prefix_len, attn_workspace,
+                                  attn_workspace_bytes, attn_out, &comb);
+  if (c != WEDLM_OK) return c;
+  return launch_step_tail(W, lambda, tau, min_fill, page_size, num_pages, max_pages, commit_rule,
+                          B, block_table, run_len, tokens, filled, prefix_len, commit_len,
+                          cache_slot, mask_id, entropy, score, argmax_tok, selected, perm,
+                          inv_perm, pos, n_obs, static_cast<const EntPartial*>(workspace),
+                          pl.n_chunks, as_stream(stream), comb);
 }
 
 extern "C" int wedlm_select_commit_reorder(

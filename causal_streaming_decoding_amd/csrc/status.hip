@@ -14,4 +14,4 @@ extern "C" const char* wedlm_status_string(int status) {
   }
 }
 
-extern "C" int wedlm_abi_version(void) { return (1 << 16) | 7; }
+extern "C" int wedlm_abi_version(void) { return (1 << 16) | 8; }

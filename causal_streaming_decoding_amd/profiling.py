@@ -187,7 +187,10 @@ def summarize_configs(configs_jsonl, traces, out_md, command_bench, command_trac
              "read that evicts the caches; times in microseconds (median, p10, p90 over the timed "
              "steps). *graph*: the step captured once as a HIP graph and replayed between two "
              "timing events (nothing else between its kernels); *eager*: the same launches as one "
-             "host call each; bf16 runs the entropy chunk pass in the attention's launch, also "
+             "host call each; *chained*: eagerly, the window already reordered by the previous "
+             "step's tail, as in a decoding loop (the cold step runs the reorder first); bf16 "
+             "runs the entropy chunk pass in the attention's launch and a split attention's "
+             "merge in the tail's launch, the chunk pass also "
              "timed as a launch of its own and on a second stream beside the attention. The "
              "attention and entropy + tail segments come from an eager pass "
              "with timing events between the kernels (each record idles the GPU a few "
@@ -195,15 +198,17 @@ def summarize_configs(configs_jsonl, traces, out_md, command_bench, command_trac
              "H: slot entropies in nats (min / median), and the mask slots whose score clears the "
              "threshold. In the commands, `<repo>` is the repository root.", "",
              "```", command_bench, "```", "",
-             "| workload | graph step median | p10 | p90 | eager step | eager, entropy pass own "
-             "launch | eager, entropy pass on a second stream | attention segment | entropy + tail "
-             "segment | step GB/s | attention GB/s | H min / median | mask slots below tau |",
-             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+             "| workload | graph step median | p10 | p90 | eager step | chained step | eager, "
+             "entropy pass own launch | eager, entropy pass on a second stream | attention segment "
+             "| entropy + tail segment | step GB/s | attention GB/s | H min / median | mask slots "
+             "below tau |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         h = r["entropy_histogram"]
+        chained = (f"{r['chained_step_us']['median']:.1f}" if "chained_step_us" in r else "-")
         lines.append(
             f"| `{r['workload']}` | {r['step_us']['median']:.1f} | {r['step_us']['p10']:.1f} | "
-            f"{r['step_us']['p90']:.1f} | {r['eager_step_us']['median']:.1f} | "
+            f"{r['step_us']['p90']:.1f} | {r['eager_step_us']['median']:.1f} | {chained} | "
             f"{r['eager_separate_entropy_step_us']['median']:.1f} | "
             f"{r['overlap_step_us']['median']:.1f} | "
             f"{r['attn_segment_us']['median']:.1f} | {r['entropy_tail_segment_us']['median']:.1f} | "

@@ -100,6 +100,10 @@ class WindowStep:
         # launch (wedlm_window_attn_rope_entropy); they fill the CUs the
         # attention leaves idle (measured faster on every workload)
         self.fuse_entropy = dtype == torch.bfloat16
+        # with the entropy in the attention's launch, the merge of split
+        # attention partials runs in the tail's launch
+        # (wedlm_select_commit_reorder_combine) instead of a launch of its own
+        self.defer_combine = True
         self._ev_in = self._ev_ent = None
 
     def _size_attn_workspace(self, max_prefix_len):
@@ -212,15 +216,19 @@ class WindowStep:
             if mark is not None:
                 mark("attn_start")
             mpl = self._attn_mpl(max_prefix_len)
+            flags = W_.WEDLM_ATTN_DEFER_COMBINE if self.defer_combine else 0
             W_.wedlm_window_attn_rope_entropy(
                 self.dt, self.n_layers, self.B, self.W, self.Hq, self.Hkv, self.D,
                 self.page_size, self.num_pages, self.max_pages, mpl, self.scale, self.theta, q, k,
                 v, self.perm, self.pos, st.k_cache, st.v_cache, st.block_table, st.prefix_len,
-                self.run_len, self.out_phys, self.attn_ws, self.attn_ws_bytes, 0, self.V, logits,
-                self.ent_ws, self.ent_ws_bytes, stream)
+                self.run_len, self.out_phys, self.attn_ws, self.attn_ws_bytes, flags, self.V,
+                logits, self.ent_ws, self.ent_ws_bytes, stream)
             if mark is not None:
                 mark("attn_end")
-            self._tail_from_partials(st, commit_len, stream)
+            if self.defer_combine:
+                self._tail_combine(st, commit_len, stream, mpl)
+            else:
+                self._tail_from_partials(st, commit_len, stream)
             if mark is not None:
                 mark("entropy_end")
             return
@@ -279,6 +287,19 @@ class WindowStep:
             self.commit_len if commit_len is None else commit_len, self.cache_slot, self.mask_id,
             self.entropy, self.score, self.argmax, self.selected, self.perm, self.inv, self.pos,
             self.n_obs, self.ent_ws, self.ent_ws_bytes, stream)
+        st.ordered_by = self
+
+    def _tail_combine(self, st, commit_len, stream, max_prefix_len):
+        """The tail from the chunk partials, with the merge of the attention's
+        split partials (deferred by the attention call) in the same launch."""
+        W_.wedlm_select_commit_reorder_combine(
+            self.dt, self.B, self.W, self.V, self.lam, self.tau, self.min_fill, self.page_size,
+            self.num_pages, self.max_pages, self.commit_rule, st.block_table, self.run_len,
+            st.tokens, st.filled, st.prefix_len,
+            self.commit_len if commit_len is None else commit_len, self.cache_slot, self.mask_id,
+            self.entropy, self.score, self.argmax, self.selected, self.perm, self.inv, self.pos,
+            self.n_obs, self.ent_ws, self.ent_ws_bytes, self.n_layers, self.Hq, self.Hkv, self.D,
+            max_prefix_len, self.attn_ws, self.attn_ws_bytes, self.out_phys, stream)
         st.ordered_by = self
 
     def set_overlap(self, side_stream):

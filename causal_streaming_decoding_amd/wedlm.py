@@ -21,6 +21,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "wedlm.h")
 WEDLM_F32 = 0
 WEDLM_BF16 = 1
 WEDLM_ATTN_SHARED_PAGES = 1  # attention flag: rows of the block table share pages
+WEDLM_ATTN_DEFER_COMBINE = 2  # attention flag: the split merge runs in the combine tail
 MAX_WINDOW = 64
 
 _c_int, _c_size, _c_float, _c_double, _p = (ctypes.c_int, ctypes.c_size_t, ctypes.c_float,
@@ -60,6 +61,10 @@ _SIGNATURES = {
     "wedlm_select_commit_reorder_partials": (_c_int, [_c_int] * 4 + [_c_float, _c_float]
                                              + [_c_int] * 5 + [_p] * 7 + [ctypes.c_int32]
                                              + [_p] * 9 + [_c_size, _p]),
+    "wedlm_select_commit_reorder_combine": (_c_int, [_c_int] * 4 + [_c_float, _c_float]
+                                            + [_c_int] * 5 + [_p] * 7 + [ctypes.c_int32]
+                                            + [_p] * 9 + [_c_size] + [_c_int] * 5
+                                            + [_p, _c_size, _p, _p]),
 }
 
 _lib = None
@@ -292,6 +297,24 @@ def wedlm_select_commit_reorder_partials(dtype, B, W, V, lam, tau, min_fill, pag
         _ptr(prefix_len), _ptr(commit_len), _ptr(cache_slot), int(mask_id), _ptr(entropy),
         _ptr(score), _ptr(argmax_tok), _ptr(selected), _ptr(perm), _ptr(inv_perm), _ptr(pos),
         _ptr(n_obs), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def wedlm_select_commit_reorder_combine(dtype, B, W, V, lam, tau, min_fill, page_size,
+                                        num_pages, max_pages, commit_rule, block_table, run_len,
+                                        tokens, filled, prefix_len, commit_len, cache_slot,
+                                        mask_id, entropy, score, argmax_tok, selected, perm,
+                                        inv_perm, pos, n_obs, workspace, workspace_bytes,
+                                        attn_n_layers, attn_Hq, attn_Hkv, attn_D,
+                                        attn_max_prefix_len, attn_workspace, attn_workspace_bytes,
+                                        attn_out, stream=None):
+    _check("wedlm_select_commit_reorder_combine", lib().wedlm_select_commit_reorder_combine(
+        dtype, B, W, V, float(lam), float(tau), int(min_fill), page_size, num_pages, max_pages,
+        int(commit_rule), _ptr(block_table), _ptr(run_len), _ptr(tokens), _ptr(filled),
+        _ptr(prefix_len), _ptr(commit_len), _ptr(cache_slot), int(mask_id), _ptr(entropy),
+        _ptr(score), _ptr(argmax_tok), _ptr(selected), _ptr(perm), _ptr(inv_perm), _ptr(pos),
+        _ptr(n_obs), _ptr(workspace), workspace_bytes, attn_n_layers, attn_Hq, attn_Hkv, attn_D,
+        attn_max_prefix_len, _ptr(attn_workspace), attn_workspace_bytes, _ptr(attn_out),
+        _stream(stream)))
 
 
 def wedlm_read_probe(src, nbytes, block_order, n_blocks, sink, grid, stream=None):

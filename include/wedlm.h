@@ -78,9 +78,10 @@ enum wedlm_status {
 /* Element types. */
 enum wedlm_dtype { WEDLM_F32 = 0, WEDLM_BF16 = 1 };
 
-/* flags of wedlm_window_attn / wedlm_window_attn_rope */
+/* flags of wedlm_window_attn / wedlm_window_attn_rope / wedlm_window_attn_rope_entropy */
 enum wedlm_attn_flags {
-  WEDLM_ATTN_SHARED_PAGES = 1 /* rows of block_table reference the same pages */
+  WEDLM_ATTN_SHARED_PAGES = 1, /* rows of block_table reference the same pages */
+  WEDLM_ATTN_DEFER_COMBINE = 2 /* leave the split merge to wedlm_select_commit_reorder_combine */
 };
 
 /* Largest window the kernels accept (one 64-lane wavefront per sequence). */
@@ -195,8 +196,13 @@ size_t wedlm_window_attn_workspace_size(int dtype, int n_layers, int B, int W, i
  * WEDLM_ATTN_SHARED_PAGES when rows share pages (a shared prefix; the
  * dual-stream forward, where every block of a sample reads the sample's
  * memory rows): the loads keep the default cache policy so that the re-reads
- * hit in the caches. Results are identical either way; any other bit is
- * WEDLM_ERR_INVALID.
+ * hit in the caches. Results are identical either way.
+ * WEDLM_ATTN_DEFER_COMBINE (bf16): when the call splits key ranges across
+ * workgroups (few groups for the GPU), it launches no merge of the split
+ * partials: out_phys is then written by wedlm_select_commit_reorder_combine,
+ * which must follow on the same stream with the same shapes, workspace and
+ * out_phys, before the workspace is reused. Without a split the flag changes
+ * nothing. Any other bit is WEDLM_ERR_INVALID.
  */
 int wedlm_window_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv, int D, int page_size,
                       int num_pages, int max_pages, int max_prefix_len, float scale,
@@ -500,6 +506,40 @@ int wedlm_select_commit_reorder_partials(int dtype, int B, int W, int V, float l
                                          int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
                                          const void* workspace, size_t workspace_bytes,
                                          void* stream);
+
+/*
+ * wedlm_select_commit_reorder_combine - wedlm_select_commit_reorder_partials
+ * and the merge of the step's split attention partials in one launch: the
+ * merge a wedlm_window_attn* call with WEDLM_ATTN_DEFER_COMBINE left out
+ * runs as workgroups beside the per-sequence tail. The merge
+ * (out = sum_s O_s 2^(m_s - m) / sum_s l_s 2^(m_s - m) over the splits, the
+ * online-softmax merge of FlashAttention, mlsanity.com page on WeDLM,
+ * "Builds on") and the tail (hyper.ai summary of WeDLM, "Method": selection,
+ * commit and refill of the window) read disjoint data, so one launch replaces
+ * two at the end of a step.
+ *
+ * Arguments up to workspace_bytes are those of
+ * wedlm_select_commit_reorder_partials (B and W are shared with the
+ * attention). attn_n_layers, attn_Hq, attn_Hkv, attn_D, attn_max_prefix_len,
+ * attn_workspace / attn_workspace_bytes and attn_out are the shapes,
+ * workspace and out_phys of the preceding attention call (same dtype), which
+ * must have run on the same stream with WEDLM_ATTN_DEFER_COMBINE. When those
+ * shapes make no split, only the tail runs. Results are bitwise those of the
+ * attention call without the flag followed by
+ * wedlm_select_commit_reorder_partials. Errors: as the tail's, plus the
+ * attention's shape checks; WEDLM_ERR_WORKSPACE when attn_workspace is
+ * smaller than the attention's; WEDLM_ERR_INVALID for a NULL attn_out with a
+ * split.
+ */
+int wedlm_select_commit_reorder_combine(
+    int dtype, int B, int W, int V, float lambda, float tau, int min_fill, int page_size,
+    int num_pages, int max_pages, int commit_rule, const int32_t* block_table, int32_t* run_len,
+    int32_t* tokens, uint8_t* filled, int32_t* prefix_len, int32_t* commit_len,
+    int32_t* cache_slot, int32_t mask_id, float* entropy, float* score, int32_t* argmax_tok,
+    uint8_t* selected, int32_t* perm, int32_t* inv_perm, int32_t* pos, int32_t* n_obs,
+    const void* workspace, size_t workspace_bytes, int attn_n_layers, int attn_Hq, int attn_Hkv,
+    int attn_D, int attn_max_prefix_len, const void* attn_workspace,
+    size_t attn_workspace_bytes, void* attn_out, void* stream);
 
 /*
  * wedlm_read_probe - HBM read-rate probe, a measurement aid beside the step

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(W.LIB_PATH),
 
 def test_exports_every_declared_function():
     declared = W.header_functions()
-    assert len(declared) == 22
+    assert len(declared) == 23
     lib = W.lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -31,9 +31,9 @@ def test_status_strings_and_version():
     assert "unsupported" in W.wedlm_status_string(-2)
     assert "workspace" in W.wedlm_status_string(-3)
     assert W.wedlm_abi_version() >> 16 == 1
-    assert W.wedlm_abi_version() & 0xffff >= 7  # fused RoPE, LM head, commit rules, step tail,
+    assert W.wedlm_abi_version() & 0xffff >= 8  # fused RoPE, LM head, commit rules, step tail,
     #                          attention flags, workspace-free selection, split tail, entropy in
-    #                          the attention launch
+    #                          the attention launch, split merge in the tail launch
     assert "scratch" in W.wedlm_status_string(-5)
 
 
@@ -68,7 +68,7 @@ def test_attn_validation_and_workspace():
     assert W.wedlm_window_attn_workspace_size(1, 1, 1, 16, 32, 8, 64, 16, 2048) == 0
     base = [1, 1, 4, 16, 32, 8, 128, 16, 8196, 2049, 32768, 0.088] + [1] * 9 + [0, 0, None]
     assert _raw("wedlm_window_attn", *base) == -3        # split planned, no workspace
-    a = list(base); a[-2] = 2
+    a = list(base); a[-2] = 4
     assert _raw("wedlm_window_attn", *a) == -1           # unknown flag bit
     need = W.wedlm_window_attn_workspace_size(1, 1, 4, 16, 32, 8, 128, 16, 32768)
     assert need > 0
@@ -286,3 +286,27 @@ def test_attn_rope_entropy_validation():
     assert _raw("wedlm_window_attn_rope_entropy", *a) == -3    # entropy workspace
     a = list(base); a[-5] = 0
     assert _raw("wedlm_window_attn_rope_entropy", *a) == -1    # V
+
+
+def test_combine_tail_validation():
+    need = W.wedlm_entropy_select_workspace_size(1, 4, 16, 1000)
+    # the tail's arguments (as wedlm_select_commit_reorder_partials), then the
+    # attention's: n_layers, Hq, Hkv, D, max_prefix_len, workspace, bytes, out
+    tail = [1, 4, 16, 1000, 0.1, 1.0, 1, 16, 4096, 2048, 0] + [1] * 7 + [-1] + [1] * 9 + [need]
+    attn_need = W.wedlm_window_attn_workspace_size(1, 1, 4, 16, 32, 8, 128, 16, 32768)
+    assert attn_need > 0  # 4 sequences x 8 kv heads split their key ranges
+    base = tail + [1, 32, 8, 128, 32768, 1, attn_need, 1, None]
+    a = list(base); a[10] = 3
+    assert _raw("wedlm_select_commit_reorder_combine", *a) == -1     # commit rule
+    a = list(base); a[28] = need - 1
+    assert _raw("wedlm_select_commit_reorder_combine", *a) == -3     # entropy workspace
+    a = list(base); a[-3] = attn_need - 1
+    assert _raw("wedlm_select_commit_reorder_combine", *a) == -3     # attention workspace
+    a = list(base); a[-4] = None
+    assert _raw("wedlm_select_commit_reorder_combine", *a) == -3
+    a = list(base); a[-2] = None
+    assert _raw("wedlm_select_commit_reorder_combine", *a) == -1     # attention output
+    a = list(base); a[32] = 64
+    assert _raw("wedlm_select_commit_reorder_combine", *a) == -2     # bf16 attention needs D = 128
+    a = list(base); a[30] = 12
+    assert _raw("wedlm_select_commit_reorder_combine", *a) == -1     # Hq % Hkv

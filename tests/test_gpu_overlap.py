@@ -3,10 +3,13 @@
 Two forms: wedlm_entropy_partials on a side stream beside
 wedlm_window_attn_rope, and wedlm_window_attn_rope_entropy, whose launch
 carries the chunk blocks after the attention's workgroups; in both,
-wedlm_select_commit_reorder_partials merges afterwards. The computations are
-those of the one-stream step, so every output of every step of a chained run
-must be bitwise the same. The chain checks the ordering between a step's tail
-and the next step's chunk pass, which write and read the same workspace.
+wedlm_select_commit_reorder_partials merges afterwards. The one-launch form
+also runs with the merge of split attention partials deferred to the tail's
+launch (WEDLM_ATTN_DEFER_COMBINE + wedlm_select_commit_reorder_combine). The
+computations are those of the one-stream step, so every output of every step
+of a chained run must be bitwise the same. The chain checks the ordering
+between a step's tail and the next step's chunk pass, which write and read the
+same workspace.
 """
 
 import dataclasses
@@ -24,13 +27,14 @@ OUTPUTS = ("out_phys", "entropy", "score", "argmax", "selected", "commit_len", "
            "perm", "inv", "pos", "n_obs", "run_len")
 
 
-def _chain(wl, steps, overlap, fuse=False):
+def _chain(wl, steps, overlap, fuse=False, defer=False):
     inp = make_step_inputs(wl, steps=steps)
     st, _, _, _, _, L0 = upload_step_inputs(wl, inp, "cuda")
     step = make_window_step(wl, inp, "cuda", L0 + wl.W * steps, fused_tail=True)
     if overlap:
         step.set_overlap(torch.cuda.Stream())
     step.fuse_entropy = fuse
+    step.defer_combine = defer
     log = []
     for s in range(steps):
         q, k, v, logits = stream_step_inputs(wl, s, "cuda")
@@ -55,7 +59,9 @@ def _chain(wl, steps, overlap, fuse=False):
 def test_overlapped_step_bitwise_equal(wl):
     print(f"[overlap] {wl.name}: {wl.steps} chained steps", flush=True)
     one, st1 = _chain(wl, wl.steps, overlap=False)
-    for form, kw in (("two streams", dict(overlap=True)), ("one launch", dict(overlap=False, fuse=True))):
+    for form, kw in (("two streams", dict(overlap=True)),
+                     ("one launch", dict(overlap=False, fuse=True)),
+                     ("one launch, merge in the tail", dict(overlap=False, fuse=True, defer=True))):
         two, st2 = _chain(wl, wl.steps, **kw)
         for s, (a, b) in enumerate(zip(one, two)):
             for key in a:

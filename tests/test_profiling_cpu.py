@@ -49,7 +49,7 @@ def test_config_summary_from_files(tmp_path):
     lines = []
     for w in ("w", "x"):
         lines.append({"workload": w, "step_us": {"median": 10.0, "p10": 9.0, "p90": 11.0},
-                      "eager_step_us": {"median": 12.0},
+                      "eager_step_us": {"median": 12.0}, "chained_step_us": {"median": 8.5},
                       "eager_separate_entropy_step_us": {"median": 13.0},
                       "overlap_step_us": {"median": 11.0},
                       "attn_segment_us": {"median": 6.0},
@@ -68,7 +68,8 @@ def test_config_summary_from_files(tmp_path):
                                 [("w", str(tmp_path / "tw")), ("x", str(tmp_path / "tx"))],
                                 str(out), "b", "t")
     text = out.read_text()
-    assert "| `w` | 10.0 | 9.0 | 11.0 | 12.0 | 13.0 | 11.0 | 6.0 | 3.0 | 80 | 100 | 1.50 / 1.70 | 1 of 3 |" in text
+    assert ("| `w` | 10.0 | 9.0 | 11.0 | 12.0 | 8.5 | 13.0 | 11.0 | 6.0 | 3.0 | 80 | 100 | "
+            "1.50 / 1.70 | 1 of 3 |") in text
     # each workload's kernels in their own table: the same launch shape twice
     assert "| `wedlm::k_a<4>` | 4 x 1 | 256 | 2 | 6.00 |" in text
     assert "| `wedlm::k_a<4>` | 4 x 1 | 256 | 1 | 9.00 |" in text

@@ -34,7 +34,7 @@ import os
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-ATTN_SOURCES = ("csrc/attn.hip", "csrc/common.hpp", "csrc/entropy_ops.hpp")
+ATTN_SOURCES = ("csrc/attn.hip", "csrc/attn_combine.hpp", "csrc/common.hpp", "csrc/entropy_ops.hpp")
 ATTN_KERNEL = "k_window_attn_bf16"
 CALIBRATION_KIB = 1 << 20  # the 1 GiB copy, read once and written once
 
@@ -240,6 +240,66 @@ def summarize_configs(configs_jsonl, traces, out_md, command_bench, command_trac
         f.write("\n".join(lines) + "\n")
 
 
+def summarize_counters(csv_paths, out_md, title, intro, commands, xcds=8, cus=256, simds=4,
+                       clock_ghz=2.4, mfma_per_wave_page=12):
+    """SQ / GRBM counter passes of the attention kernel, one table per launch
+    shape (workgroups), medians over the dispatches, and the ratios read from
+    them: MFMA busy, instruction mix per MFMA, LDS bank conflicts, waits.
+
+    ``csv_paths``: run_counter_collection.csv of each pass (counters summed
+    over the chip by rocprofv3, GRBM_GUI_ACTIVE over the XCDs)."""
+    import collections
+    import statistics
+
+    per_shape = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in csv_paths:
+        per_dispatch = collections.defaultdict(dict)
+        shape = {}
+        for r in csv.DictReader(open(path)):
+            d = r["Dispatch_Id"]
+            per_dispatch[d][r["Counter_Name"]] = float(r["Counter_Value"])
+            shape[d] = int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1)
+        for d, vals in per_dispatch.items():
+            for k, v in vals.items():
+                per_shape[shape[d]][k].append(v)
+    shapes = sorted(per_shape)
+    med = {w: {k: statistics.median(v) for k, v in per_shape[w].items()} for w in shapes}
+    names = sorted({k for w in shapes for k in med[w]})
+    lines = [f"# {title}", "", intro, "", "```"] + list(commands) + ["```", "",
+             "| counter | " + " | ".join(f"{w} workgroups" for w in shapes) + " |",
+             "|---|" + "---|" * len(shapes)]
+    for k in names:
+        lines.append(f"| `{k}` | " + " | ".join(
+            f"{med[w][k]:.4g}" if k in med[w] else "-" for w in shapes) + " |")
+    lines += ["", "Derived, per launch shape:", ""]
+    for w in shapes:
+        m = med[w]
+        need = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+                "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+                "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU_TRANS_F32")
+        if any(k not in m for k in need):
+            continue
+        active = m["GRBM_GUI_ACTIVE"] / xcds
+        mf = m["SQ_INSTS_MFMA"]
+        lines.append(
+            f"* {w} workgroups: GPU-active {active / (clock_ghz * 1e3):.1f} us per dispatch; MFMA "
+            f"busy {100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (active * cus * simds):.1f} % "
+            f"(MFMA-busy cycles / (active cycles x {cus} CUs x {simds} SIMDs)); per MFMA "
+            f"instruction {m['SQ_INSTS_VALU'] / mf:.2f} VALU (of them "
+            f"{m['SQ_INSTS_VALU_TRANS_F32'] / mf:.2f} transcendental), "
+            f"{m['SQ_INSTS_SALU'] / mf:.2f} SALU, {m['SQ_INSTS_LDS'] / mf:.2f} LDS, i.e. per "
+            f"wavefront and 16-key page ({mfma_per_wave_page} MFMAs) "
+            f"{mfma_per_wave_page * m['SQ_INSTS_VALU'] / mf:.0f} VALU, "
+            f"{mfma_per_wave_page * m['SQ_INSTS_SALU'] / mf:.0f} SALU, "
+            f"{mfma_per_wave_page * m['SQ_INSTS_LDS'] / mf:.0f} LDS; LDS bank conflicts "
+            f"{100 * m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.1f} % of LDS-active "
+            f"cycles; wave cycles waiting on a dependency "
+            f"{100 * m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.1f} %, issuing "
+            f"{100 * m['SQ_ACTIVE_INST_ANY'] / m['SQ_WAVE_CYCLES']:.1f} %.")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def _dispatch_runs(csv_path, name_prefix, value_key, counter=None):
     """Runs of consecutive dispatches of one kernel with the same (name, grid),
     in dispatch order: [(name, grid, [values])]."""
@@ -346,6 +406,17 @@ def main():
         a = ap.parse_args()
         summarize_lm_head(a.bench_jsonl, a.trace, a.fetch, a.write, a.out_md, a.command_bench,
                           a.command_trace, a.command_fetch, a.command_write)
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        ap = argparse.ArgumentParser()
+        ap.add_argument("mode")
+        ap.add_argument("--csv", action="append", required=True)
+        ap.add_argument("--out-md", required=True)
+        ap.add_argument("--title", required=True)
+        ap.add_argument("--intro", default="")
+        ap.add_argument("--command", action="append", default=[])
+        a = ap.parse_args()
+        summarize_counters(a.csv, a.out_md, a.title, a.intro, a.command)
         return
     if len(sys.argv) > 1 and sys.argv[1] == "configs":
         ap = argparse.ArgumentParser()

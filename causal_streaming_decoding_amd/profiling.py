@@ -296,6 +296,12 @@ def summarize_counters(csv_paths, out_md, title, intro, commands, xcds=8, cus=25
             f"cycles; wave cycles waiting on a dependency "
             f"{100 * m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.1f} %, issuing "
             f"{100 * m['SQ_ACTIVE_INST_ANY'] / m['SQ_WAVE_CYCLES']:.1f} %.")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in m and "SQ_WAIT_ANY" in m:
+            lines.append(
+                f"  {w} workgroups: of the MFMA-busy cycles, "
+                f"{100 * m['SQ_VALU_MFMA_COEXEC_CYCLES'] / m['SQ_VALU_MFMA_BUSY_CYCLES']:.1f} % have "
+                f"a VALU instruction executing beside them; wave cycles waiting on anything "
+                f"(counters, barriers, dependencies) {100 * m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.1f} %.")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 

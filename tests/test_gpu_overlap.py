@@ -55,6 +55,10 @@ def _chain(wl, steps, overlap, fuse=False, defer=False):
     # row parts, ragged split plan, an odd vocabulary (element-wise chunk path)
     dataclasses.replace(WL.QWEN25_7B_RAGGED, name="overlap_gqa7_odd_vocab", B=3, V=5001,
                         fill=("none",), spike=("prob", 0.9, 16.0, 20.0), steps=5),
+    # 100 sequences: the tail launch's 100 per-sequence wavefronts before the
+    # merge workgroups, a split plan scanning sequences in wavefront-wide chunks
+    dataclasses.replace(WL.QWEN3_8B_BS1, name="overlap_b100_split", B=100, V=4096,
+                        prefix=("uniform", 16, 600), steps=3),
 ], ids=lambda w: w.name)
 def test_overlapped_step_bitwise_equal(wl):
     print(f"[overlap] {wl.name}: {wl.steps} chained steps", flush=True)

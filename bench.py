@@ -521,9 +521,11 @@ def dual_stream_latencies(args):
     streams' q / k / v read and outputs written once, the memory rows written
     to the cache and read back once (every block re-reads its prefix, but a
     sample's memory rows - 16 MB - stay in the caches, so the re-reads are
-    not HBM traffic; they are reported separately). Flops: QK and PV over
-    each block's visible keys. The roofline is the one the intensity selects
-    (MFMA for these shapes).
+    not HBM traffic; they are reported separately). Flops: both streams, QK
+    and PV over each query's visible keys at 2 flops per multiply-add (the
+    memory stream in its 16-key windows, the prediction stream in Bk-key
+    blocks). The roofline is the one the intensity selects (MFMA for these
+    shapes).
     """
     import numpy as np
     import torch
@@ -547,11 +549,15 @@ def dual_stream_latencies(args):
         torch.cuda.synchronize()
         us = np.array([hev.elapsed_ms(a_, b_) for a_, b_ in ev[3:]]) * 1e3
         hev.destroy()
-        nb = N // Bk
         row = Hkv * D * 2                                   # bytes of one position's k (or v)
-        prefix_reads = 2 * S * sum(j * Bk for j in range(nb)) * 2 * row
+        # every window reads its prefix's k and v once
+        prefix_keys = lambda w: sum(j * w for j in range(N // w))
+        prefix_reads = S * (prefix_keys(DualStreamAttention.MEMORY_WINDOW) + prefix_keys(Bk)) * 2 * row
         byts = 2 * S * N * (Hq * D * 2 * 2 + 2 * row) + 2 * S * N * 2 * row
-        flops = 2 * S * Hq * D * 2 * sum(Bk * (j * Bk + (Bk + 1) / 2) for j in range(nb))
+        # (query, visible key) pairs of one head: block j of w queries sees the
+        # j*w keys before it and, causally, (w + 1) / 2 of its own on average
+        pairs = lambda w: sum(w * (j * w + (w + 1) / 2) for j in range(N // w))
+        flops = 4 * S * Hq * D * (pairs(DualStreamAttention.MEMORY_WINDOW) + pairs(Bk))
         med = float(np.median(us))
         ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
         if flops / byts < ridge:

@@ -514,7 +514,8 @@ def decode_modes(args):
 
 def dual_stream_latencies(args):
     """Dual-stream masking attention forward of one layer, one JSON line per
-    block size: 4 samples x 4096 positions, Qwen3-8B heads (32 / 8, D = 128),
+    attention kernel (the block kernel, then the window kernel) and block
+    size: 4 samples x 4096 positions, Qwen3-8B heads (32 / 8, D = 128),
     bf16, half of the prediction stream observed. Timed with HIP events around
     the whole forward (memory rows into the cache, both attentions, both
     reorders), 20 calls after 3 warm-up calls. Algorithmic bytes: both
@@ -539,8 +540,8 @@ def dual_stream_latencies(args):
     qm, km, vm, qp, kp, vp = r(Hq), r(Hkv), r(Hkv), r(Hq), r(Hkv), r(Hkv)
     filled = (torch.rand((S, N), generator=g, device=dev) < 0.5).to(torch.uint8)
     hev = HipEvents(torch.cuda.current_stream().cuda_stream)
-    for Bk in (16, 32, 64):
-        ds = DualStreamAttention(S, N, Bk, Hq, Hkv, D, theta, torch.bfloat16, dev)
+    for kernel, Bk in [(kn, b) for kn in ("block", "window") for b in (16, 32, 64)]:
+        ds = DualStreamAttention(S, N, Bk, Hq, Hkv, D, theta, torch.bfloat16, dev, kernel=kernel)
         ev = [(hev.create(), hev.create()) for _ in range(23)]
         for a_, b_ in ev:
             hev.record(a_)
@@ -570,6 +571,8 @@ def dual_stream_latencies(args):
         roof["traffic"] = None
         line = {
             "workload": f"dual_stream_S{S}_N{N}_Bk{Bk}_qwen3_8b_heads",
+            "kernel": {"block": "wedlm_block_attn_rope",
+                       "window": "wedlm_window_attn_rope"}[kernel],
             "metric": "dual-stream attention forward latency", "unit": "us", "dtype": "bf16",
             "us": {"median": med, "p10": float(np.percentile(us, 10)),
                    "p90": float(np.percentile(us, 90))},

@@ -32,10 +32,10 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-# Per-file additions. attn.hip: no NaN reaches a maximum or comparison there
-# (scores of invisible keys are set to -inf before any maximum), so the
-# compiler need not quiet NaN operands before every v_max_f32.
-FILE_CFLAGS = {"attn.hip": ["-fno-honor-nans"]}
+# Per-file additions. attn.hip, block_attn.hip: no NaN reaches a maximum or
+# comparison there (scores of invisible keys are set to -inf before any
+# maximum), so the compiler need not quiet NaN operands before every v_max_f32.
+FILE_CFLAGS = {"attn.hip": ["-fno-honor-nans"], "block_attn.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src, verbose):

@@ -43,26 +43,13 @@
 // split with the causal rule (row p sees window rows 0..p), staged into LDS in
 // the same page layout.
 #include "attn_combine.hpp"
+#include "attn_device.hpp"
 #include "common.hpp"
 #include "entropy_ops.hpp"
 
 #include <cmath>
 
 namespace wedlm {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kHeadDim = 128;
-constexpr int kPage = 16;
-constexpr int kMaxRows = 256;       // M = W*g rows: at most four 4-wave row parts
-constexpr int kPageVecs = 512;      // 16-byte vectors of one page of one kv head (K 4 KB + V 4 KB)
-constexpr int kPartElems = 2048;    // bf16 elements of one 4 KB page part
-constexpr int kNumCUs = 256;        // MI355X compute units
-constexpr int kNumXcds = 8;         // MI355X: 8 XCDs of 32 CUs, workgroups dealt round-robin
 
 // LDS ring (one 8 KB page per stage) per workgroup size. A CU holds 4
 // workgroups of 4 waves (4 wavefronts per SIMD); the ring keeps 8 pages
@@ -83,8 +70,6 @@ struct Ring {
   static constexpr bool kPair = true;
   static constexpr int kAhead = kStages - (kPair ? 2 : 1);  // pages in flight during compute
 };
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleLog2 = 8.f;
 
 struct AttnArgs {
   // physical order and rotated; with RoPE fused: slot order, before RoPE
@@ -129,13 +114,7 @@ struct AttnArgs {
   int ent_V, ent_chunk_elems, ent_chunks, ent_vec;
 };
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// One stage of the ring: one page of one kv head in the cache layout.
-struct Stage {
-  uint16_t k[kPartElems];  // [D/8][16 keys][8]
-  uint16_t v[kPartElems];  // [D][16 keys]
-};
 
 struct RowState {
   f32x4 o[8];  // O^T accumulators per 16-dim tile: lane holds dims 4q..4q+3 of row (lane & 15)
@@ -159,21 +138,11 @@ __device__ __forceinline__ void mfma_result_guard(f32x4 (&o)[8]) {
 }
 
 // Reductions over the four lanes holding one query row (lanes c, c+16, c+32,
-// c+48) with the gfx950 row-swap permutes. v_permlane16_swap exchanges the
-// odd 16-lane rows of one register with the even rows of another, and
-// v_permlane32_swap the upper 32 lanes of one with the lower 32 of another:
-// applied to two copies of x, every lane ends up holding the values of both
-// rows of its pair, in the same two registers. Every lane therefore combines
-// the same operands in the same order, and all four lanes of a row get
-// bitwise equal results. The swaps are issued from asm because the compiler's
-// builtins for them treat the two results as one value; the s_nop provides the
-// wait states between a VALU write and a permute read.
-__device__ __forceinline__ void row_swap16(float& a, float& b) {
-  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void row_swap32(float& a, float& b) {
-  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
+// c+48) with the gfx950 row-swap permutes (row_swap16 / row_swap32): applied
+// to two copies of x, every lane ends up holding the values of both rows of
+// its pair, in the same two registers. Every lane therefore combines the same
+// operands in the same order, and all four lanes of a row get bitwise equal
+// results.
 __device__ __forceinline__ float row_max4(float x) {
   float a = x, b = x;
   row_swap16(a, b);
@@ -383,84 +352,7 @@ __device__ __forceinline__ void attend_pages2(RowState& st, const bf16x8 (&qr)[4
   pv_page(st, s1, col, grp, p[4], p[5], p[6], p[7], lim1);
 }
 
-// Asynchronous page staging: global -> LDS DMA (global_load_lds_dwordx4).
-// Each instruction moves 64 lanes x 16 B = 1 KB: lane l's 16 bytes land at
-// M0 + 16 l in LDS. A stage is 512 vectors (K then V of one page); wavefront w
-// issues instructions for vectors (i*NW + w)*64 .. +63 (two each for 4 waves,
-// one each for 8).
-// The DMA is issued from inline asm so that the compiler does not add its own
-// conservative vmcnt waits before every LDS read of the ring; the waits are
-// explicit (stage_wait_barrier) and counted per thread in issue order.
-// M0 is a reserved register: it is saved and restored around the DMA.
-// kNt: the loads carry the non-temporal hint (nt). When every page is read
-// once per launch (each sequence owns its pages, as in decoding), the pages
-// should not displace other lines on their way through the caches: on the
-// 36-layer streaming shape this took the launch from 5.1 to 5.5 TB/s (the
-// scope bits sc0 / sc1 on top of it changed nothing). When block-table rows
-// share pages (the dual-stream forward: every block of a sample reads the
-// sample's memory rows), the re-reads hit in the caches only without the
-// hint (2.9 against 2.3 ms for the 16-key-block forward).
-template <bool kNt>
-__device__ __forceinline__ void lds_dma_16(uint64_t sbase, uint32_t voff, uint32_t lds_byte_addr) {
-  // scalar base + per-lane 32-bit offset: no 64-bit address arithmetic per
-  // lane and page
-  uint32_t saved;
-  if constexpr (kNt)
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "global_load_lds_dwordx4 %1, %2 nt\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voff), "s"(sbase), "s"(lds_byte_addr)
-        : "memory");
-  else
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voff), "s"(sbase), "s"(lds_byte_addr)
-        : "memory");
-}
 
-// A wave-uniform block-table entry through the scalar cache (read only).
-// Scalar loads count against lgkmcnt, not vmcnt, so reading the table never
-// waits for the DMAs in flight.
-__device__ __forceinline__ int load_page_id(const int32_t* p) {
-  const uint64_t u = reinterpret_cast<uint64_t>(p);
-  const uint64_t su =
-      (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32))) << 32) |
-      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u)));
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(su) : "memory");
-  return v;
-}
-
-// Two block-table entries with one wait (both scalar loads in flight together).
-__device__ __forceinline__ void load_page_ids2(const int32_t* p0, const int32_t* p1, int& v0,
-                                               int& v1) {
-  auto su = [](const int32_t* p) {
-    const uint64_t u = reinterpret_cast<uint64_t>(p);
-    return (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32)))
-            << 32) |
-           static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u)));
-  };
-  asm volatile(
-      "s_load_dword %0, %2, 0x0\n\t"
-      "s_load_dword %1, %3, 0x0\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&s"(v0), "=&s"(v1)
-      : "s"(su(p0)), "s"(su(p1))
-      : "memory");
-}
-
-// Block-table entry of logical page pg of a sequence's table row, the page
-// index clamped to the table and the entry to the pool: the id a DMA reads.
-__device__ __forceinline__ const int32_t* page_entry(const int32_t* bt, int pg, int max_pages) {
-  return bt + __builtin_amdgcn_readfirstlane(min(max(pg, 0), max_pages - 1));
-}
 
 template <int NW>
 struct DmaShape {
@@ -527,24 +419,6 @@ __device__ __forceinline__ void stage_wait_behind(int behind) {
   }
 }
 
-// Rotates a 16-byte slice pair of one row by RoPE: lo holds dims j0..j0+7,
-// hi dims j0+64..j0+71 (rotate-half pairing, D = 128), position t.
-__device__ __forceinline__ void rope_pair(u32x4& lo, u32x4& hi, double t, const double* omega,
-                                          int j0) {
-  u32x4 ylo, yhi;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    float c0, s0, c1, s1;
-    rope_cos_sin(t, omega[j0 + 2 * w], c0, s0);
-    rope_cos_sin(t, omega[j0 + 2 * w + 1], c1, s1);
-    const float a0 = bf16_lo(lo[w]), a1 = bf16_hi(lo[w]);
-    const float h0 = bf16_lo(hi[w]), h1 = bf16_hi(hi[w]);
-    ylo[w] = pack_bf16x2(a0 * c0 - h0 * s0, a1 * c1 - h1 * s1);
-    yhi[w] = pack_bf16x2(h0 * c0 + a0 * s0, h1 * c1 + a1 * s1);
-  }
-  lo = ylo;
-  hi = yhi;
-}
 
 // Appends the committed window rows held by the staged chunk (physical rows
 // kw0 .. kw0+15, rotated) to the caches: rows 0..c-1 go to positions

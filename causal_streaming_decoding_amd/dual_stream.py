@@ -15,15 +15,20 @@ the library's calls with one "sequence" per (sample, block):
      identity order and positions; wedlm_commit_prefix_rope writes every
      memory block's rotated keys and values into a paged cache (one 16-token
      page list per sample, shared by all its blocks' block-table rows);
-  2. wedlm_window_attn_rope over the memory blocks: causal attention of the
-     memory stream (block j over the memory prefix plus itself). The memory
+  2. the attention of the memory blocks: causal attention of the memory
+     stream (block j over the memory prefix plus itself). The memory
      stream's attention is plain causal attention over the whole sequence, so
      its result does not depend on the block size: it runs in 16-key windows
-     whatever Bk is (the fastest window shape of the attention kernel), and
-     its output, in identity order, has the same layout as Bk-key blocks;
+     whatever Bk is, and its output, in identity order, has the same layout
+     as Bk-key blocks;
   3. wedlm_window_reorder of the prediction stream's observed flags, then
-     wedlm_window_attn_rope over the prediction blocks against the same
-     memory prefix.
+     the attention of the prediction blocks against the same memory prefix.
+
+The attentions run wedlm_block_attn_rope (the windows of a sample end to
+end, 256 query rows of consecutive windows per key tile) where it has a
+kernel (bf16, D = 128, 256 % (Hq / Hkv) == 0), else wedlm_window_attn_rope
+with one block-table row per (sample, block), all rows of a sample sharing
+its pages; both compute the same windows.
 
 Argument marshalling and buffer management only: every operation runs in the
 library's kernels. Outputs are in physical order per block (as the attention
@@ -69,9 +74,18 @@ class DualStreamAttention:
 
     MEMORY_WINDOW = 16
 
-    def __init__(self, S, N, Bk, Hq, Hkv, D, theta, dtype, device, scale=None):
+    def __init__(self, S, N, Bk, Hq, Hkv, D, theta, dtype, device, scale=None, kernel=None):
+        """kernel: "block" (wedlm_block_attn_rope), "window"
+        (wedlm_window_attn_rope) or None for the block kernel where it has
+        one."""
         if N % Bk or N % PAGE or not (1 <= Bk <= W_.MAX_WINDOW):
             raise ValueError("N must be a multiple of Bk and of 16, and Bk <= 64")
+        has_block = dtype == torch.bfloat16 and D == 128 and 256 % (Hq // Hkv) == 0
+        if kernel is None:
+            kernel = "block" if has_block else "window"
+        if kernel not in ("block", "window") or (kernel == "block" and not has_block):
+            raise ValueError(f"no {kernel!r} attention kernel for these shapes")
+        self.kernel = kernel
         self.S, self.N, self.Bk, self.Hq, self.Hkv, self.D = S, N, Bk, Hq, Hkv, D
         self.theta = theta
         self.dt = W_.dtype_code(dtype)
@@ -81,6 +95,7 @@ class DualStreamAttention:
         i32 = dict(dtype=torch.int32, device=device)
         # one page list per sample, shared by the block-table rows of all its blocks
         pages = torch.arange(self.num_pages, **i32).view(S, 1, self.max_pages)
+        self.sample_table = pages.view(S, self.max_pages)
         self.mem_blocks = _Blocks(S, N, self.MEMORY_WINDOW, Hq, Hkv, D, self.dt, dtype, device,
                                   pages)
         self.pred_blocks = _Blocks(S, N, Bk, Hq, Hkv, D, self.dt, dtype, device, pages)
@@ -113,6 +128,12 @@ class DualStreamAttention:
 
     def _attend(self, q, k, v, blk, stream):
         o = blk.order
+        if self.kernel == "block":
+            W_.wedlm_block_attn_rope(self.dt, self.S, self.N, blk.W, self.Hq, self.Hkv, self.D,
+                                     PAGE, self.num_pages, self.max_pages, self.scale, self.theta,
+                                     q, k, v, o["perm"], o["pos"], self.k_cache, self.v_cache,
+                                     self.sample_table, blk.out, stream)
+            return
         W_.wedlm_window_attn_rope(self.dt, 1, blk.Bp, blk.W, self.Hq, self.Hkv, self.D, PAGE,
                                   self.num_pages, self.max_pages, self.N - blk.W, self.scale,
                                   self.theta, q, k, v, o["perm"], o["pos"], self.k_cache,

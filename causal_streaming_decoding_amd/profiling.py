@@ -34,7 +34,8 @@ import os
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-ATTN_SOURCES = ("csrc/attn.hip", "csrc/attn_combine.hpp", "csrc/common.hpp", "csrc/entropy_ops.hpp")
+ATTN_SOURCES = ("csrc/attn.hip", "csrc/attn_combine.hpp", "csrc/attn_device.hpp", "csrc/common.hpp",
+                "csrc/entropy_ops.hpp")
 ATTN_KERNEL = "k_window_attn_bf16"
 CALIBRATION_KIB = 1 << 20  # the 1 GiB copy, read once and written once
 

@@ -65,6 +65,7 @@ _SIGNATURES = {
                                             + [_c_int] * 5 + [_p] * 7 + [ctypes.c_int32]
                                             + [_p] * 9 + [_c_size] + [_c_int] * 5
                                             + [_p, _c_size, _p, _p]),
+    "wedlm_block_attn_rope": (_c_int, [_c_int] * 10 + [_c_float, _c_double] + [_p] * 10),
 }
 
 _lib = None
@@ -315,6 +316,15 @@ def wedlm_select_commit_reorder_combine(dtype, B, W, V, lam, tau, min_fill, page
         _ptr(n_obs), _ptr(workspace), workspace_bytes, attn_n_layers, attn_Hq, attn_Hkv, attn_D,
         attn_max_prefix_len, _ptr(attn_workspace), attn_workspace_bytes, _ptr(attn_out),
         _stream(stream)))
+
+
+def wedlm_block_attn_rope(dtype, S, N, W, Hq, Hkv, D, page_size, num_pages, max_pages, scale,
+                          theta, q, k, v, perm, pos, k_cache, v_cache, block_table, out,
+                          stream=None):
+    _check("wedlm_block_attn_rope", lib().wedlm_block_attn_rope(
+        dtype, S, N, W, Hq, Hkv, D, page_size, num_pages, max_pages, float(scale), float(theta),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(pos), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_table), _ptr(out), _stream(stream)))
 
 
 def wedlm_read_probe(src, nbytes, block_order, n_blocks, sink, grid, stream=None):

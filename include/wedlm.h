@@ -542,6 +542,43 @@ int wedlm_select_commit_reorder_combine(
     size_t attn_workspace_bytes, void* attn_out, void* stream);
 
 /*
+ * wedlm_block_attn_rope - the attention of the windows of S sequences laid
+ * end to end (hyper.ai summary of WeDLM, "Method": in training, a masked
+ * prediction stream is cut into blocks that are reordered inside; a block's
+ * tokens attend to the memory stream's context before the block and,
+ * causally, to their own block; the memory stream itself is causal).
+ *
+ * Sequence s holds N positions as nb = N / W consecutive windows; window j
+ * of sequence s is batch row b = s * nb + j of q, k, v, perm, pos and out.
+ * The result is that of wedlm_window_attn_rope (n_layers = 1, B = S * nb,
+ * flags = WEDLM_ATTN_SHARED_PAGES, no commit_run) with prefix_len[b] = j * W
+ * and block-table row b = row s of block_table: window j attends to cache
+ * positions 0 .. jW-1 of its sequence and to its own W keys causally in
+ * physical order (physical row p reads slot perm[b][p], rotated at pos[b][p]).
+ * Up to rounding order: the key tiles are visited in another order, and each
+ * workgroup takes 256 query rows of consecutive windows against every key
+ * tile it reads (bf16, D = 128, P = 16 only).
+ *
+ * q [S*nb][W][Hq][D], k, v [S*nb][W][Hkv][D] (slot order, before RoPE);
+ * perm, pos [S*nb][W]; k_cache / v_cache the cache layout of
+ * wedlm_window_attn (one layer), read only; block_table [S][max_pages]
+ * (entries clamped to the pool); out [S*nb][W][Hq][D] in physical order.
+ * Every position below N - W of each sequence that some window attends to
+ * must hold its key and value (e.g. written by wedlm_commit_prefix_rope).
+ * All device pointers; caller-owned; one kernel on stream.
+ *
+ * Errors: WEDLM_ERR_INVALID for NULL pointers, sizes <= 0, W > 64, N % W != 0,
+ * Hq % Hkv != 0, scale <= 0, theta <= 0, max_pages * P < N - W;
+ * WEDLM_ERR_UNSUPPORTED unless dtype is bf16, D = 128, page_size = 16 and
+ * 256 % (Hq / Hkv) == 0.
+ */
+int wedlm_block_attn_rope(int dtype, int S, int N, int W, int Hq, int Hkv, int D, int page_size,
+                          int num_pages, int max_pages, float scale, double theta, const void* q,
+                          const void* k, const void* v, const int32_t* perm, const int32_t* pos,
+                          const void* k_cache, const void* v_cache, const int32_t* block_table,
+                          void* out, void* stream);
+
+/*
  * wedlm_read_probe - HBM read-rate probe, a measurement aid beside the step
  * (not a step of the method): the rate this GPU reaches on a plain streaming
  * read and on the paged cache's pattern gives the step kernels' roofline

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(W.LIB_PATH),
 
 def test_exports_every_declared_function():
     declared = W.header_functions()
-    assert len(declared) == 23
+    assert len(declared) == 24
     lib = W.lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -310,3 +310,34 @@ def test_combine_tail_validation():
     assert _raw("wedlm_select_commit_reorder_combine", *a) == -2     # bf16 attention needs D = 128
     a = list(base); a[30] = 12
     assert _raw("wedlm_select_commit_reorder_combine", *a) == -1     # Hq % Hkv
+
+
+def test_block_attn_validation():
+    # dtype, S, N, W, Hq, Hkv, D, page_size, num_pages, max_pages, scale, theta,
+    # q, k, v, perm, pos, k_cache, v_cache, block_table, out, stream
+    base = [1, 4, 4096, 16, 32, 8, 128, 16, 1024, 256, 0.088, 1e6] + [1] * 9 + [None]
+    a = list(base); a[3] = 24
+    assert _raw("wedlm_block_attn_rope", *a) == -1    # N % W
+    a = list(base); a[3] = 65
+    assert _raw("wedlm_block_attn_rope", *a) == -1    # W > 64
+    a = list(base); a[4] = 12
+    assert _raw("wedlm_block_attn_rope", *a) == -1    # Hq % Hkv
+    a = list(base); a[4] = 56
+    assert _raw("wedlm_block_attn_rope", *a) == -2    # 256 % g with g = 7
+    a = list(base); a[0] = 0
+    assert _raw("wedlm_block_attn_rope", *a) == -2    # bf16 only
+    a = list(base); a[0] = 5
+    assert _raw("wedlm_block_attn_rope", *a) == -2    # unknown dtype
+    a = list(base); a[6] = 64
+    assert _raw("wedlm_block_attn_rope", *a) == -2    # D = 128 only
+    a = list(base); a[7] = 32
+    assert _raw("wedlm_block_attn_rope", *a) == -2    # 16-key pages only
+    a = list(base); a[9] = 254
+    assert _raw("wedlm_block_attn_rope", *a) == -1    # table shorter than the last prefix
+    a = list(base); a[10] = 0.0
+    assert _raw("wedlm_block_attn_rope", *a) == -1    # scale
+    a = list(base); a[11] = -1.0
+    assert _raw("wedlm_block_attn_rope", *a) == -1    # theta
+    for i in range(12, 21):
+        a = list(base); a[i] = None
+        assert _raw("wedlm_block_attn_rope", *a) == -1, i

@@ -31,11 +31,11 @@
 // Per 32 keys and wavefront (v_mfma_f32_32x32x16_bf16):
 //   S^T (32 keys x 32 rows)  = K . Q^T                     8 K-steps of 16 dims
 //   O^T (32 dims x 32 rows) += V^T . P^T (hi and lo part)   per 32-dim tile
-// The score accumulator leaves 16 keys of one query row in each lane (keys
-// 8*(r/4) + 4*(l/32) + r%4 in register r of lane l), which are the B operand
-// of the PV product as they stand: V^T is read as two 8-byte runs of one
-// value dimension (keys 4h .. 4h+3 and 8+4h .. 8+4h+3 of a page). A row's max
-// and sum take one swap of the two lane halves. The online softmax is the
+// The score accumulator leaves 16 keys of one query row in each lane; with
+// the K rows loaded in a permuted order (kperm) they are 8 consecutive keys
+// of each page per lane half, the B operand of the PV product as they stand,
+// against one 16-byte run of V^T per lane read from a bank-swizzled V page
+// (vslot). A row's max and sum take one swap of the two lane halves. The online softmax is the
 // window kernel's (scores in log2 units, the reference max raised lazily),
 // and P enters the PV product as a bf16 hi + lo pair (~16 mantissa bits).
 #include "attn_device.hpp"
@@ -104,6 +104,20 @@ __device__ __forceinline__ float half_sum(float x) {
   return a + b;
 }
 
+// Key order of the score product: A row i of a 32-key block holds key
+// kperm(i), i with bits 2 and 3 swapped. The accumulator's register r of lane
+// half h then holds key 16 (r / 8) + 8 h + r % 8: the B operand of the PV
+// K-step over page r / 8 is 8 consecutive keys per lane half, matched by one
+// 16-byte run of V^T.
+__device__ __forceinline__ int kperm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+// 16-byte LDS slot of value dimension d, keys 8 hv .. 8 hv + 7, in a V page:
+// the two halves of the dimensions with bit 3 set trade places, so that the
+// 16 lanes of one read (16 consecutive dimensions, one half) fall in 16
+// different bank groups. The cache page's vector 2 d + hv lands in slot
+// vslot(d, hv) = its index with bit 0 flipped when bit 4 is set.
+__device__ __forceinline__ int vslot(int d, int hv) { return 2 * d + (hv ^ ((d >> 3) & 1)); }
+
 // One block of 32 keys: keys 0..15 are page pa, 16..31 page pb. Key kk of
 // page A is visible to this lane's row iff loa <= kk < hia (page B: lob, hib).
 // V elements of keys >= vlima / vlimb (wave-uniform) are cleared from the
@@ -115,7 +129,7 @@ __device__ __forceinline__ void attend32(RowState32& st, const bf16x8 (&qr)[8], 
   const int li = lane & 31, h = lane >> 5;
   // A operand of the scores: lane l reads key li (page li / 16) at dims
   // 16 s + 8 h .. +7 (slice 2 s + h of the K page)
-  const uint16_t* kb = (li < kPage ? pa.k : pb.k) + (h * kPage + (li & 15)) * 8;
+  const uint16_t* kb = (li < kPage ? pa.k : pb.k) + (h * kPage + (kperm(li) & 15)) * 8;
   f32x16 sc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) sc[r] = 0.f;
@@ -131,7 +145,7 @@ __device__ __forceinline__ void attend32(RowState32& st, const bf16x8 (&qr)[8], 
   if (__ballot(loa > 0 || hia < kPage || lob > 0 || hib < kPage)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * h + (r & 3);
+      const int key = 16 * (r >> 3) + 8 * h + (r & 7);
       const bool vis = key < kPage ? (key >= loa && key < hia)
                                    : (key - kPage >= lob && key - kPage < hib);
       if (!vis) x[r] = -INFINITY;
@@ -171,21 +185,19 @@ __device__ __forceinline__ void attend32(RowState32& st, const bf16x8 (&qr)[8], 
   for (int kk = 0; kk < 2; ++kk) {
     const Stage& sg = kk == 0 ? pa : pb;
     const int vlim = kk == 0 ? vlima : vlimb;
-    // lane (dim li of the tile, half h): keys 4h .. 4h+3 and 8+4h .. 8+4h+3
-    const uint16_t* vb = sg.v + li * kPage + 4 * h;
+    // lane (dim li of the tile, half h): keys 8h .. 8h+7, one 16-byte read
     u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
     if (vlim < kPage) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const int k0 = (w < 2 ? 0 : 8) + 4 * h + 2 * (w & 1);
+        const int k0 = 8 * h + 2 * w;
         vmask[w] = (k0 < vlim ? 0x0000ffffu : 0u) | (k0 + 1 < vlim ? 0xffff0000u : 0u);
       }
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const u32x2 a0 = *reinterpret_cast<const u32x2*>(vb + dt * 32 * kPage);
-      const u32x2 a1 = *reinterpret_cast<const u32x2*>(vb + dt * 32 * kPage + 8);
-      const u32x4 va = u32x4{a0[0], a0[1], a1[0], a1[1]} & vmask;
+      const u32x4 va =
+          *reinterpret_cast<const u32x4*>(sg.v + vslot(dt * 32 + li, h) * 8) & vmask;
       st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(bh[kk]),
                                                          st.o[dt], 0, 0, 0);
       st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(bl[kk]),
@@ -256,6 +268,9 @@ __global__ void __launch_bounds__(kBlkThreads) k_block_attn_bf16(BlockAttnArgs a
   const int32_t* bt = a.block_table + static_cast<size_t>(s) * a.max_pages;
   constexpr size_t kPageElems = static_cast<size_t>(kHeadDim) * kPage;
   const int v0 = wave * kWave;  // this wavefront's first vector of a page (wave-uniform)
+  // source of this lane's 16 bytes: K in order, V through the slot swizzle
+  const uint32_t vlane =
+      16u * static_cast<uint32_t>(v0 < 256 ? lane : (lane ^ ((lane >> 4) & 1)));
   auto issue_tile = [&](int t) {
     int id[kTilePages];
     load_page_ids2(page_entry(bt, 4 * t, a.max_pages), page_entry(bt, 4 * t + 1, a.max_pages),
@@ -276,7 +291,7 @@ __global__ void __launch_bounds__(kBlkThreads) k_block_attn_bf16(BlockAttnArgs a
               __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uint64_t>(part))));
       const uint32_t lds = static_cast<uint32_t>(
           reinterpret_cast<size_t>((__attribute__((address_space(3))) char*)(&dst.pg[i])));
-      lds_dma_16<false>(sbase, static_cast<uint32_t>(lane) * 16u,
+      lds_dma_16<false>(sbase, vlane,
                         __builtin_amdgcn_readfirstlane(lds + v0 * 16));
     }
   };
@@ -344,8 +359,9 @@ __global__ void __launch_bounds__(kBlkThreads) k_block_attn_bf16(BlockAttnArgs a
       Stage& pg = own.pg[kk >> 4];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        pg.v[(dv * 8 + 2 * w) * kPage + (kk & 15)] = static_cast<uint16_t>(val[w] & 0xffffu);
-        pg.v[(dv * 8 + 2 * w + 1) * kPage + (kk & 15)] = static_cast<uint16_t>(val[w] >> 16);
+        const int key = kk & 15;
+        pg.v[vslot(dv * 8 + 2 * w, key >> 3) * 8 + (key & 7)] = static_cast<uint16_t>(val[w] & 0xffffu);
+        pg.v[vslot(dv * 8 + 2 * w + 1, key >> 3) * 8 + (key & 7)] = static_cast<uint16_t>(val[w] >> 16);
       }
     }
     __syncthreads();

@@ -398,11 +398,6 @@ __device__ __forceinline__ void stage_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-// Workgroup barrier for LDS reuse only: this thread's LDS accesses have
-// completed; its global stores (the committed rows) may still be in flight.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Wait for the oldest in-flight stage when `behind` (<= N) later stages,
 // kDma DMAs each, may stay in flight, then synchronise the workgroup. The

@@ -88,6 +88,13 @@ __device__ __forceinline__ void lds_dma_16(uint64_t sbase, uint32_t voff, uint32
         : "memory");
 }
 
+// Workgroup barrier for LDS reuse only: this thread's LDS accesses have
+// completed; its global memory operations (DMAs, stores) may still be in
+// flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // A wave-uniform block-table entry through the scalar cache (read only).
 // Scalar loads count against lgkmcnt, not vmcnt, so reading the table never
 // waits for the DMAs in flight.

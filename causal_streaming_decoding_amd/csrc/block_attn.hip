@@ -28,16 +28,26 @@
 //     workgroup touches), through a 3-stage LDS ring filled by global->LDS
 //     DMA, two tiles in flight while one is computed; a row of window j sees
 //     the positions below jW. Workgroups are launched longest prefix first.
-// Per 32 keys and wavefront (v_mfma_f32_32x32x16_bf16):
-//   S^T (32 keys x 32 rows)  = K . Q^T                     8 K-steps of 16 dims
-//   O^T (32 dims x 32 rows) += V^T . P^T (hi and lo part)   per 32-dim tile
+// Per 32 keys and wavefront:
+//   S^T (32 keys x 32 rows)  = K . Q^T   v_mfma_f32_32x32x16_bf16, 8 K-steps of 16 dims
+//   O^T (32 dims x 32 rows) += V^T . P^T  v_mfma_f32_32x32x16_f16, per page and 32-dim tile
 // The score accumulator leaves 16 keys of one query row in each lane; with
 // the K rows loaded in a permuted order (kperm) they are 8 consecutive keys
 // of each page per lane half, the B operand of the PV product as they stand,
 // against one 16-byte run of V^T per lane read from a bank-swizzled V page
-// (vslot). A row's max and sum take one swap of the two lane halves. The online softmax is the
-// window kernel's (scores in log2 units, the reference max raised lazily),
-// and P enters the PV product as a bf16 hi + lo pair (~16 mantissa bits).
+// (vslot). A row's max and sum take one swap of the two lane halves. The
+// online softmax is the window kernel's (scores in log2 units, the reference
+// max raised lazily).
+//
+// The PV product runs in fp16: each tile's values are converted in LDS once
+// (bf16 -> fp16 is exact for magnitudes in [2^-14, 65504]), and each
+// probability p in [0, 1] is rounded once to fp16 (relative error <= 2^-11),
+// the row sum l being accumulated from the fp32 probabilities. The output
+// then differs from the exact softmax average by at most 2^-11 max|v| (the
+// largest value magnitude the row attends to): 2e-3 for |v| <= 4. The window
+// kernel carries 16 bits of p as a bf16 hi + lo pair instead, which costs a
+// second PV MFMA per page and three VALU operations per score; a single bf16
+// part (2^-9) would not meet that bound.
 #include "attn_device.hpp"
 #include "common.hpp"
 
@@ -46,6 +56,21 @@
 namespace wedlm {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 u) { return __builtin_bit_cast(f16x8, u); }
+
+// Two floats to fp16, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
+}
+
+// A 32-bit word of two bf16 values as two fp16 values: exact for magnitudes
+// in [2^-14, 65504] (fp16 holds every 8-bit significand there); below, fp16
+// subnormals keep it within 2^-25.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) { return pack_f16x2(bf16_lo(w), bf16_hi(w)); }
 
 constexpr int kBlkWaves = 8;
 constexpr int kBlkThreads = kBlkWaves * kWave;  // 512
@@ -170,17 +195,13 @@ __device__ __forceinline__ void attend32(RowState32& st, const bf16x8 (&qr)[8], 
   for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(x[r], scale_log2, -base));
   st.l += (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]))) +
           (((p[8] + p[9]) + (p[10] + p[11])) + ((p[12] + p[13]) + (p[14] + p[15])));
-  // B operands of the PV product: K-step kk (page kk) takes registers 8kk .. 8kk+7
-  u32x4 bh[2], bl[2];
+  // B operands of the PV product (fp16): K-step kk (page kk) takes registers
+  // 8kk .. 8kk+7
+  u32x4 bp[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float p0 = p[8 * kk + 2 * w], p1 = p[8 * kk + 2 * w + 1];
-      const uint32_t hi = pack_bf16x2(p0, p1);
-      bh[kk][w] = hi;
-      bl[kk][w] = pack_bf16x2(p0 - bf16_lo(hi), p1 - bf16_hi(hi));
-    }
+    for (int w = 0; w < 4; ++w) bp[kk][w] = pack_f16x2(p[8 * kk + 2 * w], p[8 * kk + 2 * w + 1]);
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const Stage& sg = kk == 0 ? pa : pb;
@@ -198,12 +219,26 @@ __device__ __forceinline__ void attend32(RowState32& st, const bf16x8 (&qr)[8], 
     for (int dt = 0; dt < 4; ++dt) {
       const u32x4 va =
           *reinterpret_cast<const u32x4*>(sg.v + vslot(dt * 32 + li, h) * 8) & vmask;
-      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(bh[kk]),
-                                                         st.o[dt], 0, 0, 0);
-      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(bl[kk]),
-                                                         st.o[dt], 0, 0, 0);
+      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(va), as_f16x8(bp[kk]), st.o[dt],
+                                                        0, 0, 0);
     }
   }
+}
+
+// rope_pair with the cosines and sines of the row's position taken from a
+// table: cs[f] = (cos, sin) of frequency f at that position.
+__device__ __forceinline__ void rope_pair_tab(u32x4& lo, u32x4& hi, const f32x2* cs, int j0) {
+  u32x4 ylo, yhi;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const f32x2 t0 = cs[j0 + 2 * w], t1 = cs[j0 + 2 * w + 1];
+    const float a0 = bf16_lo(lo[w]), a1 = bf16_hi(lo[w]);
+    const float h0 = bf16_lo(hi[w]), h1 = bf16_hi(hi[w]);
+    ylo[w] = pack_bf16x2(a0 * t0[0] - h0 * t0[1], a1 * t1[0] - h1 * t1[1]);
+    yhi[w] = pack_bf16x2(h0 * t0[0] + a0 * t0[1], h1 * t1[0] + a1 * t1[1]);
+  }
+  lo = ylo;
+  hi = yhi;
 }
 
 // Wait until at most `behind` (<= 1) later tiles' DMAs are in flight for
@@ -300,6 +335,23 @@ __global__ void __launch_bounds__(kBlkThreads) k_block_attn_bf16(BlockAttnArgs a
   // also covers the DMAs, and the ring's explicit counts start from zero.
   for (int t = 0; t < kBlkAhead && t < n_tiles; ++t) issue_tile(t);
 
+  // RoPE of the query rows and own keys: when the own positions fit one
+  // tile (64 positions), their (cos, sin) at every frequency are formed once
+  // into ring stage kBlkAhead, which no DMA fills before the ring's first
+  // barrier; otherwise each row computes its own.
+  static_assert(kBlkAhead < kBlkStages, "the RoPE table needs a ring stage the prologue leaves free");
+  const bool tab = n_own <= kTileKeys;  // workgroup-uniform
+  f32x2* cs_tab = reinterpret_cast<f32x2*>(&ring[kBlkAhead]);  // [64 positions][64 frequencies]
+  static_assert(sizeof(Tile) >= kTileKeys * (kHeadDim / 2) * sizeof(f32x2), "RoPE table size");
+  if (tab) {
+    for (int e = tid; e < n_own * (kHeadDim / 2); e += kBlkThreads) {
+      float c, sn;
+      rope_cos_sin(static_cast<double>(s_pos[e >> 6]), s_omega[e & 63], c, sn);
+      cs_tab[e] = f32x2{c, sn};
+    }
+    __syncthreads();
+  }
+
   // query rows: lane half h holds dims 16 s + 8 h .. +7 (B operand of K-step s)
   bf16x8 qr[8];
   {
@@ -309,10 +361,16 @@ __global__ void __launch_bounds__(kBlkThreads) k_block_attn_bf16(BlockAttnArgs a
     u32x4 qv[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qv[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * h);
-    const double t = static_cast<double>(s_pos[Rc - own_begin]);
     // dims 16 ks + 8 h + e and 16 (ks + 4) + 8 h + e are a rotate-half pair
+    if (tab) {
+      const f32x2* cs = cs_tab + (Rc - own_begin) * (kHeadDim / 2);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) rope_pair(qv[ks], qv[ks + 4], t, s_omega, 16 * ks + 8 * h);
+      for (int ks = 0; ks < 4; ++ks) rope_pair_tab(qv[ks], qv[ks + 4], cs, 16 * ks + 8 * h);
+    } else {
+      const double t = static_cast<double>(s_pos[Rc - own_begin]);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) rope_pair(qv[ks], qv[ks + 4], t, s_omega, 16 * ks + 8 * h);
+    }
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qr[ks] = as_bf16x8(qv[ks]);
   }
@@ -340,7 +398,10 @@ __global__ void __launch_bounds__(kBlkThreads) k_block_attn_bf16(BlockAttnArgs a
         const uint16_t* krow = a.k + (e * a.Hkv + kvh) * kHeadDim;
         lo = *reinterpret_cast<const u32x4*>(krow + sl * 8);
         hi = *reinterpret_cast<const u32x4*>(krow + 64 + sl * 8);
-        rope_pair(lo, hi, static_cast<double>(s_pos[i]), s_omega, sl * 8);
+        if (tab)
+          rope_pair_tab(lo, hi, cs_tab + i * (kHeadDim / 2), sl * 8);
+        else
+          rope_pair(lo, hi, static_cast<double>(s_pos[i]), s_omega, sl * 8);
       }
       Stage& pg = own.pg[kk >> 4];
       *reinterpret_cast<u32x4*>(&pg.k[(sl * kPage + (kk & 15)) * 8]) = lo;
@@ -360,8 +421,9 @@ __global__ void __launch_bounds__(kBlkThreads) k_block_attn_bf16(BlockAttnArgs a
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const int key = kk & 15;
-        pg.v[vslot(dv * 8 + 2 * w, key >> 3) * 8 + (key & 7)] = static_cast<uint16_t>(val[w] & 0xffffu);
-        pg.v[vslot(dv * 8 + 2 * w + 1, key >> 3) * 8 + (key & 7)] = static_cast<uint16_t>(val[w] >> 16);
+        const uint32_t hw = bf16x2_to_f16x2(val[w]);
+        pg.v[vslot(dv * 8 + 2 * w, key >> 3) * 8 + (key & 7)] = static_cast<uint16_t>(hw & 0xffffu);
+        pg.v[vslot(dv * 8 + 2 * w + 1, key >> 3) * 8 + (key & 7)] = static_cast<uint16_t>(hw >> 16);
       }
     }
     __syncthreads();
@@ -381,7 +443,18 @@ __global__ void __launch_bounds__(kBlkThreads) k_block_attn_bf16(BlockAttnArgs a
   for (int t = 0; t < n_tiles; ++t) {
     tile_wait_barrier(min(kBlkAhead - 1, n_tiles - 1 - t));
     if (t + kBlkAhead < n_tiles) issue_tile(t + kBlkAhead);
-    const Tile& tl = ring[t % kBlkStages];
+    Tile& tl = ring[t % kBlkStages];
+    // the tile's values to fp16 in place: 2 of its 1024 16-byte V vectors per thread
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int u = c * kBlkThreads + tid;
+      u32x4* vp = reinterpret_cast<u32x4*>(&tl.pg[u >> 8].v[(u & 255) * 8]);
+      u32x4 w = *vp;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = bf16x2_to_f16x2(w[e]);
+      *vp = w;
+    }
+    lds_barrier();
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int pa = t * kTileKeys + 32 * hf;

@@ -555,9 +555,13 @@ int wedlm_select_commit_reorder_combine(
  * and block-table row b = row s of block_table: window j attends to cache
  * positions 0 .. jW-1 of its sequence and to its own W keys causally in
  * physical order (physical row p reads slot perm[b][p], rotated at pos[b][p]).
- * Up to rounding order: the key tiles are visited in another order, and each
- * workgroup takes 256 query rows of consecutive windows against every key
- * tile it reads (bf16, D = 128, P = 16 only).
+ * Up to rounding: the key tiles are visited in another order, each workgroup
+ * takes 256 query rows of consecutive windows against every key tile it reads
+ * (bf16, D = 128, P = 16 only), and the probabilities enter the PV product in
+ * fp16 (the values converted from bf16 exactly), so each output row is within
+ * 2^-11 * max|v| of the exact softmax average over its keys, max|v| being the
+ * largest value magnitude the row attends to. Values must lie within fp16's
+ * range (|v| <= 65504).
  *
  * q [S*nb][W][Hq][D], k, v [S*nb][W][Hkv][D] (slot order, before RoPE);
  * perm, pos [S*nb][W]; k_cache / v_cache the cache layout of

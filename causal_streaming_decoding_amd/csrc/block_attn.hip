@@ -145,12 +145,11 @@ __device__ __forceinline__ int vslot(int d, int hv) { return 2 * d + (hv ^ ((d >
 
 // One block of 32 keys: keys 0..15 are page pa, 16..31 page pb. Key kk of
 // page A is visible to this lane's row iff loa <= kk < hia (page B: lob, hib).
-// V elements of keys >= vlima / vlimb (wave-uniform) are cleared from the
-// operand: cache positions not written yet may hold any bits, and 0 * NaN is
-// NaN.
+// The values of keys no row may see hold zeros (cache positions not written
+// yet may hold any bits, and 0 * NaN is NaN): the caller clears them.
 __device__ __forceinline__ void attend32(RowState32& st, const bf16x8 (&qr)[8], const Stage& pa,
                                          const Stage& pb, int lane, int loa, int hia, int lob,
-                                         int hib, int vlima, int vlimb, float scale_log2) {
+                                         int hib, float scale_log2) {
   const int li = lane & 31, h = lane >> 5;
   // A operand of the scores: lane l reads key li (page li / 16) at dims
   // 16 s + 8 h .. +7 (slice 2 s + h of the K page)
@@ -205,20 +204,10 @@ __device__ __forceinline__ void attend32(RowState32& st, const bf16x8 (&qr)[8], 
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const Stage& sg = kk == 0 ? pa : pb;
-    const int vlim = kk == 0 ? vlima : vlimb;
     // lane (dim li of the tile, half h): keys 8h .. 8h+7, one 16-byte read
-    u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
-    if (vlim < kPage) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int k0 = 8 * h + 2 * w;
-        vmask[w] = (k0 < vlim ? 0x0000ffffu : 0u) | (k0 + 1 < vlim ? 0xffff0000u : 0u);
-      }
-    }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const u32x4 va =
-          *reinterpret_cast<const u32x4*>(sg.v + vslot(dt * 32 + li, h) * 8) & vmask;
+      const u32x4 va = *reinterpret_cast<const u32x4*>(sg.v + vslot(dt * 32 + li, h) * 8);
       st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(va), as_f16x8(bp[kk]), st.o[dt],
                                                         0, 0, 0);
     }
@@ -435,7 +424,7 @@ __global__ void __launch_bounds__(kBlkThreads) k_block_attn_bf16(BlockAttnArgs a
       const int lo = lim - pa, hi = Rc + 1 - pa;  // visible: lo <= key < hi of the 32
       if (!__ballot(lo < 32 && hi > 0)) continue;  // wave-uniform
       attend32(st, qr, own.pg[2 * hf], own.pg[2 * hf + 1], lane, lo, hi, lo - kPage, hi - kPage,
-               kPage, kPage, a.scale_log2);
+               a.scale_log2);
     }
   }
 
@@ -444,14 +433,25 @@ __global__ void __launch_bounds__(kBlkThreads) k_block_attn_bf16(BlockAttnArgs a
     tile_wait_barrier(min(kBlkAhead - 1, n_tiles - 1 - t));
     if (t + kBlkAhead < n_tiles) issue_tile(t + kBlkAhead);
     Tile& tl = ring[t % kBlkStages];
-    // the tile's values to fp16 in place: 2 of its 1024 16-byte V vectors per thread
+    // the tile's values to fp16 in place, 2 of its 1024 16-byte V vectors per
+    // thread; in the last tile, positions >= n_cache (no row sees them; they
+    // may not be written) are cleared
+    const int nv = n_cache - t * kTileKeys;  // keys of the tile below n_cache (workgroup-uniform)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int u = c * kBlkThreads + tid;
-      u32x4* vp = reinterpret_cast<u32x4*>(&tl.pg[u >> 8].v[(u & 255) * 8]);
+      const int slot = u & 255;
+      u32x4* vp = reinterpret_cast<u32x4*>(&tl.pg[u >> 8].v[slot * 8]);
       u32x4 w = *vp;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = bf16x2_to_f16x2(w[e]);
+      if (nv < kTileKeys) {
+        // vector slot holds keys 8 hv .. 8 hv + 7 of page u >> 8 (vslot inverted)
+        const int key0 = (u >> 8) * kPage + 8 * ((slot & 1) ^ ((slot >> 4) & 1));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] &= (key0 + 2 * e < nv ? 0x0000ffffu : 0u) | (key0 + 2 * e + 1 < nv ? 0xffff0000u : 0u);
+      }
       *vp = w;
     }
     lds_barrier();
@@ -460,7 +460,7 @@ __global__ void __launch_bounds__(kBlkThreads) k_block_attn_bf16(BlockAttnArgs a
       const int pa = t * kTileKeys + 32 * hf;
       if (!__ballot(lim > pa)) continue;  // no row of this wavefront sees these keys
       attend32(st, qr, tl.pg[2 * hf], tl.pg[2 * hf + 1], lane, 0, lim - pa, 0, lim - pa - kPage,
-               n_cache - pa, n_cache - pa - kPage, a.scale_log2);
+               a.scale_log2);
     }
   }
 

@@ -524,8 +524,8 @@ def dual_stream_latencies(args):
     sample's memory rows - 16 MB - stay in the caches, so the re-reads are
     not HBM traffic; they are reported separately). Flops: both streams, QK
     and PV over each query's visible keys at 2 flops per multiply-add (the
-    memory stream in its 16-key windows, the prediction stream in Bk-key
-    blocks). The roofline is the one the intensity selects (MFMA for these
+    memory stream in its own windows, the prediction stream in Bk-key
+    blocks; causal attention counts the same pairs whatever the window). The roofline is the one the intensity selects (MFMA for these
     shapes).
     """
     import numpy as np
@@ -553,12 +553,12 @@ def dual_stream_latencies(args):
         row = Hkv * D * 2                                   # bytes of one position's k (or v)
         # every window reads its prefix's k and v once
         prefix_keys = lambda w: sum(j * w for j in range(N // w))
-        prefix_reads = S * (prefix_keys(DualStreamAttention.MEMORY_WINDOW) + prefix_keys(Bk)) * 2 * row
+        prefix_reads = S * (prefix_keys(ds.memory_window) + prefix_keys(Bk)) * 2 * row
         byts = 2 * S * N * (Hq * D * 2 * 2 + 2 * row) + 2 * S * N * 2 * row
         # (query, visible key) pairs of one head: block j of w queries sees the
         # j*w keys before it and, causally, (w + 1) / 2 of its own on average
         pairs = lambda w: sum(w * (j * w + (w + 1) / 2) for j in range(N // w))
-        flops = 4 * S * Hq * D * (pairs(DualStreamAttention.MEMORY_WINDOW) + pairs(Bk))
+        flops = 4 * S * Hq * D * (pairs(ds.memory_window) + pairs(Bk))
         med = float(np.median(us))
         ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
         if flops / byts < ridge:

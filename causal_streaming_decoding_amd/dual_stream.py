@@ -18,9 +18,10 @@ the library's calls with one "sequence" per (sample, block):
   2. the attention of the memory blocks: causal attention of the memory
      stream (block j over the memory prefix plus itself). The memory
      stream's attention is plain causal attention over the whole sequence, so
-     its result does not depend on the block size: it runs in 16-key windows
-     whatever Bk is, and its output, in identity order, has the same layout
-     as Bk-key blocks;
+     its result does not depend on the block size: it runs in windows of its
+     own size whatever Bk is (64 keys with the block kernel, whose cache tiles
+     then need no mask; 16 with the window kernel, its fastest window shape),
+     and its output, in identity order, has the same layout as Bk-key blocks;
   3. wedlm_window_reorder of the prediction stream's observed flags, then
      the attention of the prediction blocks against the same memory prefix.
 
@@ -72,7 +73,8 @@ class DualStreamAttention:
     (D = 128) or f32 projections [S, N, H, D] of both streams.
     """
 
-    MEMORY_WINDOW = 16
+    MEMORY_WINDOW = 16        # memory-stream window of the window kernel
+    MEMORY_WINDOW_BLOCK = 64  # and of the block kernel (when N is a multiple of it)
 
     def __init__(self, S, N, Bk, Hq, Hkv, D, theta, dtype, device, scale=None, kernel=None):
         """kernel: "block" (wedlm_block_attn_rope), "window"
@@ -96,7 +98,10 @@ class DualStreamAttention:
         # one page list per sample, shared by the block-table rows of all its blocks
         pages = torch.arange(self.num_pages, **i32).view(S, 1, self.max_pages)
         self.sample_table = pages.view(S, self.max_pages)
-        self.mem_blocks = _Blocks(S, N, self.MEMORY_WINDOW, Hq, Hkv, D, self.dt, dtype, device,
+        self.memory_window = (self.MEMORY_WINDOW_BLOCK
+                              if kernel == "block" and N % self.MEMORY_WINDOW_BLOCK == 0
+                              else self.MEMORY_WINDOW)
+        self.mem_blocks = _Blocks(S, N, self.memory_window, Hq, Hkv, D, self.dt, dtype, device,
                                   pages)
         self.pred_blocks = _Blocks(S, N, Bk, Hq, Hkv, D, self.dt, dtype, device, pages)
         self.mem, self.pred = self.mem_blocks.order, self.pred_blocks.order

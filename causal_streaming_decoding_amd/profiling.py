@@ -422,8 +422,11 @@ def main():
         ap.add_argument("--title", required=True)
         ap.add_argument("--intro", default="")
         ap.add_argument("--command", action="append", default=[])
+        ap.add_argument("--mfma-per-wave-page", type=int, default=12,
+                        help="MFMA instructions per wavefront and 16-key page of the kernel")
         a = ap.parse_args()
-        summarize_counters(a.csv, a.out_md, a.title, a.intro, a.command)
+        summarize_counters(a.csv, a.out_md, a.title, a.intro, a.command,
+                           mfma_per_wave_page=a.mfma_per_wave_page)
         return
     if len(sys.argv) > 1 and sys.argv[1] == "configs":
         ap = argparse.ArgumentParser()

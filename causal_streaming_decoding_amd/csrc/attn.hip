@@ -44,6 +44,7 @@
 // the same page layout.
 #include "attn_combine.hpp"
 #include "attn_device.hpp"
+#include "attn_tile32.hpp"
 #include "common.hpp"
 #include "entropy_ops.hpp"
 
@@ -968,6 +969,283 @@ k_window_attn_bf16(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide groups: M = W*g of 129..256 query rows (g = 7 with W = 32, g = 4 with
+// W = 64, ...). One workgroup of 8 wavefronts per (layer, sequence, kv head,
+// key-range split) takes all M rows with the 32-row tiles of attn_tile32.hpp
+// (wavefront w: rows 32w .. 32w+31, row = physical row * g + head), so every
+// page is read once per split; the 16-row kernel runs such a group as several
+// 4-wave row parts, each reading every page (at the g = 7, W = 32 shape the
+// page stream alone, with no compute, took 56 us for 4 parts). The split's
+// pages come in 64-key tiles through a 3-stage LDS ring (one workgroup per
+// CU, two tiles in flight while one is computed); the last split stages the
+// window's own keys once into a tile of its own - gathered through the
+// window order and rotated at their logical positions, the committed rows
+// appended to the cache from there - and attends to them causally in
+// physical order. Split plan, partial layout and merge are the 16-row
+// kernel's (find_split, ws_o / ws_ml / ws_plan, combine_quad).
+// ---------------------------------------------------------------------------
+constexpr int kWideStages = 3;
+constexpr int kWideAhead = kWideStages - 1;  // tiles in flight while one is computed
+static_assert(kWideAhead == 2, "tile_wait_barrier covers one tile behind the computed one");
+
+template <bool kRope, bool kNt>
+__global__ void __launch_bounds__(kTileThreads) k_window_attn_wide(AttnArgs a) {
+  __shared__ Tile ring[kWideStages];
+  __shared__ Tile own;  // the window's own keys (W <= 64): K rotated, V plain then fp16
+  __shared__ double s_omega[kRope ? kHeadDim / 2 : 1];
+  __shared__ int s_perm[kRope ? WEDLM_MAX_WINDOW : 1];
+  __shared__ int s_pos[kRope ? WEDLM_MAX_WINDOW : 1];
+  __shared__ int s_split[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, h = lane >> 5;
+
+  int bid = blockIdx.x;
+  const int j = bid % a.cols;  // sequence, or (sequence, split) in split mode
+  bid /= a.cols;
+  const int kvh = bid % a.Hkv;
+  const int layer = bid / a.Hkv;
+  int b = j, split = 0, n_split = 1;
+  int K = 0;
+  if (a.split) {
+    if (wave == 0) {
+      const SplitSlot sl = find_split(a, j, lane);
+      if (lane == 0) {
+        s_split[0] = sl.b;
+        s_split[1] = sl.split;
+        s_split[2] = sl.n_split;
+        s_split[3] = sl.K;
+      }
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(s_split[0]);
+    if (b < 0) return;  // every wave of the workgroup takes this branch
+    split = __builtin_amdgcn_readfirstlane(s_split[1]);
+    n_split = __builtin_amdgcn_readfirstlane(s_split[2]);
+    K = __builtin_amdgcn_readfirstlane(s_split[3]);
+  }
+  const int group = (layer * a.B + b) * a.Hkv + kvh;
+  const size_t slot = static_cast<size_t>(layer * a.Hkv + kvh) * a.cols + j;
+  const int pl_b = a.prefix_len[b];
+  const int L = min(max(pl_b, 0), a.max_prefix_len);
+  const int npages = (L + kPage - 1) / kPage;
+  const int pg_begin = a.split ? min(npages, split * K) : 0;
+  const int pg_end = a.split ? min(npages, pg_begin + K) : npages;
+  const bool with_window = split == n_split - 1;
+  if (a.split && split == 0 && tid == 0)
+    a.ws_plan[group] = make_int2(static_cast<int>(slot), n_split);
+  // the split's keys: positions key_begin .. key_end - 1
+  const int key_begin = pg_begin * kPage;
+  const int key_end = min(L, pg_end * kPage);
+  const int n_tiles = max(key_end - key_begin, 0) / kTileKeys +
+                      (max(key_end - key_begin, 0) % kTileKeys != 0 ? 1 : 0);
+  const bool appends = kRope && a.commit_run != nullptr && with_window;
+
+  // this lane's query row (rows past M take row 0's inputs and are never stored)
+  const size_t lb = static_cast<size_t>(layer) * a.B + b;
+  const int r = wave * 32 + li;
+  const bool row_ok = r < a.M;
+  const int rr = row_ok ? r : 0;
+  const int prow = rr / a.g, hh = rr % a.g;
+  const int32_t* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
+  const uint16_t* kc_layer = a.kc + static_cast<size_t>(layer) * a.cache_layer_stride;
+  const uint16_t* vc_layer = a.vc + static_cast<size_t>(layer) * a.cache_layer_stride;
+
+  if constexpr (kRope) {
+    if (tid < kHeadDim / 2) s_omega[tid] = a.omega[tid];
+    if (tid < a.W) {
+      s_perm[tid] = min(max(a.perm[b * a.W + tid], 0), a.W - 1);
+      s_pos[tid] = a.pos[b * a.W + tid];
+    }
+  }
+  __syncthreads();
+
+  auto issue_tile = [&](int t) {
+    const int pg = pg_begin + t * kTilePages;  // pages past the split: valid memory, cleared
+    int id[kTilePages];
+    load_page_ids2(page_entry(bt, pg, a.max_pages), page_entry(bt, pg + 1, a.max_pages), id[0],
+                   id[1]);
+    load_page_ids2(page_entry(bt, pg + 2, a.max_pages), page_entry(bt, pg + 3, a.max_pages),
+                   id[2], id[3]);
+    tile_dma<kNt>(ring[t % kWideStages], id, kc_layer, vc_layer, a.Hkv, kvh, a.num_pages, wave,
+                  lane);
+  };
+  // The DMAs are issued before the plain loads below: those complete in
+  // order after them, so every wait the compiler places for its own loads
+  // also covers the DMAs, and the ring's explicit counts start from zero.
+  for (int t = 0; t < kWideAhead && t < n_tiles; ++t) issue_tile(t);
+
+  // (cos, sin) of the window rows' positions at every frequency, formed once
+  // into ring stage kWideAhead, which no DMA fills before the ring's first
+  // barrier
+  static_assert(sizeof(Tile) >= WEDLM_MAX_WINDOW * (kHeadDim / 2) * sizeof(f32x2),
+                "RoPE table size");
+  const f32x2* cs_tab = reinterpret_cast<const f32x2*>(&ring[kWideAhead]);
+  if constexpr (kRope) {
+    f32x2* tab = reinterpret_cast<f32x2*>(&ring[kWideAhead]);
+    for (int e = tid; e < a.W * (kHeadDim / 2); e += kTileThreads) {
+      float c, sn;
+      rope_cos_sin(static_cast<double>(s_pos[e >> 6]), s_omega[e & 63], c, sn);
+      tab[e] = f32x2{c, sn};
+    }
+    __syncthreads();
+  }
+
+  // query rows: lane half h holds dims 16 s + 8 h .. +7 (B operand of K-step s)
+  bf16x8 qr[8];
+  {
+    const int qslot = kRope ? s_perm[prow] : prow;
+    const uint16_t* qrow =
+        a.q + ((lb * a.W + qslot) * a.Hq + static_cast<size_t>(kvh) * a.g + hh) * kHeadDim;
+    u32x4 qv[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qv[ks] = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * h);
+    if constexpr (kRope) {
+      // dims 16 ks + 8 h + e and 16 (ks + 4) + 8 h + e are a rotate-half pair
+      const f32x2* cs = cs_tab + prow * (kHeadDim / 2);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) rope_pair_tab(qv[ks], qv[ks + 4], cs, 16 * ks + 8 * h);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qr[ks] = as_bf16x8(qv[ks]);
+  }
+
+  RowState32 st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st.o[dt][e] = 0.f;
+
+  // ---- the window's own keys, causal over physical order -------------------
+  if (with_window) {
+    const int row_stride = a.Hkv * kHeadDim;
+    const uint16_t* kwin = a.k + lb * a.W * row_stride + kvh * kHeadDim;
+    const uint16_t* vwin = a.v + lb * a.W * row_stride + kvh * kHeadDim;
+    {
+      // keys: one (key, slice pair) per thread, rotated at the key's position
+      const int kk = tid & 63, sl = tid >> 6;
+      u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+      if (kk < a.W) {
+        const uint16_t* krow = kwin + (kRope ? s_perm[kk] : kk) * row_stride;
+        lo = *reinterpret_cast<const u32x4*>(krow + sl * 8);
+        hi = *reinterpret_cast<const u32x4*>(krow + kHeadDim / 2 + sl * 8);
+        if constexpr (kRope) rope_pair_tab(lo, hi, cs_tab + kk * (kHeadDim / 2), sl * 8);
+      }
+      Stage& pg = own.pg[kk >> 4];
+      *reinterpret_cast<u32x4*>(&pg.k[(sl * kPage + (kk & 15)) * 8]) = lo;
+      *reinterpret_cast<u32x4*>(&pg.k[((sl + 8) * kPage + (kk & 15)) * 8]) = hi;
+    }
+    // values, plain [dim][key] bf16 (the layout the committed-row append reads)
+    for (int task = tid; task < kTileKeys * 16; task += kTileThreads) {
+      const int kk = task & 63, dv = task >> 6;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (kk < a.W)
+        val = *reinterpret_cast<const u32x4*>(vwin + (kRope ? s_perm[kk] : kk) * row_stride +
+                                              dv * 8);
+      uint16_t* vt = &own.pg[kk >> 4].v[(dv * 8) * kPage + (kk & 15)];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        vt[(2 * w) * kPage] = static_cast<uint16_t>(val[w] & 0xffffu);
+        vt[(2 * w + 1) * kPage] = static_cast<uint16_t>(val[w] >> 16);
+      }
+    }
+    __syncthreads();
+    if constexpr (kRope) {
+      if (appends) {
+        for (int kw0 = 0; kw0 < a.W; kw0 += kPage)
+          append_committed(a, own.pg[kw0 / kPage], bt, b, layer, kvh, kw0, tid, kTileThreads,
+                           false, 0, 0);
+        __syncthreads();  // the append's LDS reads are done before V is rewritten
+      }
+    }
+    {
+      // values to fp16, in the vslot order: dimension d of page p (its two
+      // 16-byte vectors, keys 0..7 and 8..15) per thread
+      const int p = tid >> 7, d = tid & 127;
+      uint16_t* v = own.pg[p].v;
+      u32x4 w0 = *reinterpret_cast<const u32x4*>(v + (2 * d) * 8);
+      u32x4 w1 = *reinterpret_cast<const u32x4*>(v + (2 * d + 1) * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w0[e] = bf16x2_to_f16x2(w0[e]);
+        w1[e] = bf16x2_to_f16x2(w1[e]);
+      }
+      *reinterpret_cast<u32x4*>(v + vslot(d, 0) * 8) = w0;
+      *reinterpret_cast<u32x4*>(v + vslot(d, 1) * 8) = w1;
+    }
+    __syncthreads();
+    // window key kk is visible to physical row prow iff kk <= prow (and kk < W)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int pa = 32 * hf;
+      const int hi = min(prow + 1, a.W) - pa;
+      if (!__ballot(hi > 0)) continue;  // wave-uniform
+      attend32(st, qr, own.pg[2 * hf], own.pg[2 * hf + 1], lane, 0, hi, 0, hi - kPage,
+               a.scale_log2);
+    }
+  }
+
+  // ---- the split's cache tiles ------------------------------------------------
+  for (int t = 0; t < n_tiles; ++t) {
+    tile_wait_barrier(min(kWideAhead - 1, n_tiles - 1 - t));
+    if (t + kWideAhead < n_tiles) issue_tile(t + kWideAhead);
+    Tile& tl = ring[t % kWideStages];
+    // keys of the tile inside the split (every row sees all of them); the
+    // rest are cleared from the values and masked from the scores
+    const int nv = key_end - (key_begin + t * kTileKeys);
+    tile_v_to_f16(tl, tid, nv);
+    lds_barrier();
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int pa = 32 * hf;
+      if (nv <= pa) continue;  // workgroup-uniform
+      attend32(st, qr, tl.pg[2 * hf], tl.pg[2 * hf + 1], lane, 0, nv - pa, 0, nv - pa - kPage,
+               a.scale_log2);
+    }
+  }
+  // no DMA may be in flight when the workgroup ends (n_tiles = 0: none issued)
+
+  // ---- write out ----------------------------------------------------------------
+  mfma32_guard(st.o[0]);
+  mfma32_guard(st.o[1]);
+  mfma32_guard(st.o[2]);
+  mfma32_guard(st.o[3]);
+  st.l = half_sum(st.l);  // every lane takes part in the swap
+  if (!row_ok) return;
+  if (!a.split) {
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    uint16_t* orow =
+        a.out + ((lb * a.W + prow) * a.Hq + static_cast<size_t>(kvh) * a.g + hh) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 w = {pack_bf16x2(st.o[dt][4 * q] * inv, st.o[dt][4 * q + 1] * inv),
+                         pack_bf16x2(st.o[dt][4 * q + 2] * inv, st.o[dt][4 * q + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + dt * 32 + 8 * q + 4 * h) = w;
+      }
+  } else {
+    float* o = a.ws_o + (slot * a.M + r) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(o + dt * 32 + 8 * q + 4 * h) =
+            make_float4(st.o[dt][4 * q], st.o[dt][4 * q + 1], st.o[dt][4 * q + 2],
+                        st.o[dt][4 * q + 3]);
+    if (h == 0) {
+      float* ml = a.ws_ml + (slot * a.M + r) * 2;
+      ml[0] = st.m;
+      ml[1] = st.l;
+    }
+  }
+}
+
 // Merge of the per-split partials (combine_quad, attn_combine.hpp): one
 // thread per (group, row, 4 value dimensions).
 __global__ void __launch_bounds__(256) k_window_attn_combine(CombineArgs c) {
@@ -1146,7 +1424,8 @@ struct AttnPlan {
   int part_rows;
   bool split;
   int min_pages;
-  int waves;  // wavefronts per workgroup: 4, 8 or 16 (one 16-row tile each)
+  int waves;  // wavefronts per workgroup: 4 (one 16-row tile each), or 8 for wide groups
+  bool wide;  // 129..256 rows: k_window_attn_wide, all rows in one workgroup (32-row tiles)
   size_t ws_o_bytes, ws_ml_bytes, ws_plan_bytes;
 };
 
@@ -1155,15 +1434,17 @@ static AttnPlan plan_bf16(int n_layers, int B, int W, int Hq, int Hkv, int max_p
   const int g = Hq / Hkv;
   const int M = W * g;
   const int tiles = ceil_div(M, 16);
-  // more than 4 row tiles: one 4-wave workgroup per 4 tiles of the work unit
-  // (row parts on one XCD). Larger workgroups measured slower: for the
-  // dual-stream prediction blocks, 2.36 / 2.37 ms with one 8-wave workgroup
-  // (32-key blocks) or two (64-key blocks) against 2.18 / 2.22 ms, and 3.13 ms
-  // with one 16-wave workgroup (64-key blocks); the g = 7, W = 32 decoding
-  // shape is within 2 % either way.
-  pl.waves = 4;
-  pl.parts = ceil_div(tiles, 4);
-  pl.part_rows = ceil_div(tiles, pl.parts) * 16;
+  // Up to 128 rows: 16-row tiles, one 4-wave workgroup per 4 tiles of the
+  // work unit (row parts on one XCD for more than 64 rows; larger workgroups
+  // of 16-row tiles measured slower: for the dual-stream prediction blocks
+  // 2.36 / 2.37 ms with one 8-wave workgroup (32-key blocks) or two (64-key
+  // blocks) against 2.18 / 2.22 ms, 3.13 ms with one 16-wave workgroup).
+  // 129..256 rows: one 8-wave workgroup of 32-row tiles takes the whole group
+  // (k_window_attn_wide), one workgroup per CU.
+  pl.wide = M > 128 && M <= 256;
+  pl.waves = pl.wide ? 8 : 4;
+  pl.parts = pl.wide ? 1 : ceil_div(tiles, 4);
+  pl.part_rows = pl.wide ? M : ceil_div(tiles, pl.parts) * 16;
   const long long groups = 1LL * n_layers * B * Hkv;
   const long long columns = 1LL * n_layers * Hkv;
   // aim for one full round of workgroups (every CU holding as many as its
@@ -1172,7 +1453,7 @@ static AttnPlan plan_bf16(int n_layers, int B, int W, int Hq, int Hkv, int max_p
   // merging twice as many partials);
   // how the column's workgroups are shared out follows the live prefix
   // lengths on the device (find_split)
-  const int wg_per_cu = Ring<4>::kWgPerCu;
+  const int wg_per_cu = pl.wide ? 1 : Ring<4>::kWgPerCu;
   const long long target = 1LL * kNumCUs * wg_per_cu / pl.parts;  // work units per round
   pl.min_pages = 8;
   const int npages = ceil_div(max(max_prefix_len, 1), kPage);
@@ -1363,19 +1644,42 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
     a.ent_vec = ep.vec ? 1 : 0;
     ent_blocks = 1LL * B * W * ep.n_chunks;
   }
+  // Pages that several rows share are read more than once per launch: then
+  // the DMA keeps the default cache policy, otherwise it streams (kNt).
+  const bool nt = (flags & WEDLM_ATTN_SHARED_PAGES) == 0;
+  if (pl.wide) {
+    // one workgroup per CU: the entropy chunk blocks (small, many per CU)
+    // would inherit its LDS and run one per CU, so the chunk pass is a launch
+    // of its own (the same chunk function, bitwise the same partials)
+    if (a.units > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
+    a.attn_blocks = a.units;
+    const dim3 wgrid(static_cast<unsigned>(a.units));
+    auto gw = [&](auto kernel) { hipLaunchKernelGGL(kernel, wgrid, dim3(kTileThreads), 0, s, a); };
+    if (rope) {
+      if (nt) gw(k_window_attn_wide<true, true>); else gw(k_window_attn_wide<true, false>);
+    } else {
+      if (nt) gw(k_window_attn_wide<false, true>); else gw(k_window_attn_wide<false, false>);
+    }
+    st = launch_status();
+    if (st == WEDLM_OK && logits != nullptr) {
+      EntPlan ep = plan_entropy(dtype, B, W, V);
+      if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) ep.vec = false;
+      launch_entropy_partials(dtype, B, W, V, logits, ep, static_cast<EntPartial*>(ent_workspace),
+                              s);
+      st = launch_status();
+    }
+  } else {
   const long long blocks = attn_blocks + ent_blocks;
   if (blocks > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
   const dim3 grid(static_cast<unsigned>(blocks));
   auto go = [&](auto kernel, int waves) {
     hipLaunchKernelGGL(kernel, grid, dim3(kWave * waves), 0, s, a);
   };
-  // Pages that several rows share are read more than once per launch: then
-  // the DMA keeps the default cache policy, otherwise it streams (kNt).
-  const bool nt = (flags & WEDLM_ATTN_SHARED_PAGES) == 0;
   auto pick = [&](auto k_nt, auto k_cached, int waves) { nt ? go(k_nt, waves) : go(k_cached, waves); };
   rope ? pick(k_window_attn_bf16<4, true, true>, k_window_attn_bf16<4, true, false>, pl.waves)
        : pick(k_window_attn_bf16<4, false, true>, k_window_attn_bf16<4, false, false>, pl.waves);
   st = launch_status();
+  }
   // a deferred merge is launched by the step tail (wedlm_select_commit_reorder_combine)
   if (st != WEDLM_OK || !pl.split || (flags & WEDLM_ATTN_DEFER_COMBINE)) return st;
   CombineArgs c = combine_of(pl, a, groups);

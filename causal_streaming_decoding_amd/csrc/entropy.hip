@@ -112,7 +112,7 @@ int launch_entropy_select(const EntPartial* part, int n_chunks, int B, int W,
 
 using namespace wedlm;
 
-static void launch_entropy_partials(int dtype, int B, int W, int V, const void* logits,
+void wedlm::launch_entropy_partials(int dtype, int B, int W, int V, const void* logits,
                                     const EntPlan& pl, EntPartial* part, hipStream_t s) {
   const dim3 grid(pl.n_chunks, B * W);
   if (dtype == WEDLM_BF16) {

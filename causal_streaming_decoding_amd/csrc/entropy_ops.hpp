@@ -152,4 +152,9 @@ inline EntPlan plan_entropy(int dtype, int B, int W, int V) {
   return pl;
 }
 
+// Host side (entropy.hip): the chunk pass as a launch of its own (grid
+// n_chunks x B*W of k_entropy_partial) over pl's chunking, enqueued on s.
+void launch_entropy_partials(int dtype, int B, int W, int V, const void* logits,
+                             const EntPlan& pl, EntPartial* part, hipStream_t s);
+
 }  // namespace wedlm

@@ -177,6 +177,11 @@ size_t wedlm_window_attn_workspace_size(int dtype, int n_layers, int B, int W, i
  *   keys   = the L_b cached keys (positions 0..L_b-1) then window rows 0..p,
  *   out[l][b][p][h] = softmax(scale * q_phys . keys) @ values.
  * Online softmax with fp32 accumulation; output rounded once to the element type.
+ * bf16: scores from bf16 q and k in fp32; in the PV product the probabilities
+ * carry ~16 bits (a bf16 hi + lo pair) for groups of up to 128 query rows
+ * (W * Hq / Hkv), and are rounded once to fp16 against fp16 values (converted
+ * from bf16 exactly; |v| <= 65504) for groups of 129..256 rows, each output
+ * then within 2^-11 * max|v| of the exact softmax average over its keys.
  *
  * in : q_phys, k_phys, v_phys (physical order, rotated q/k) as written by
  *      wedlm_rope_logical; k_cache, v_cache (layouts above, num_pages pages per

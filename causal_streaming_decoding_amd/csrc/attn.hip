@@ -1064,12 +1064,8 @@ __global__ void __launch_bounds__(kTileThreads) k_window_attn_wide(AttnArgs a) {
   __syncthreads();
 
   auto issue_tile = [&](int t) {
-    const int pg = pg_begin + t * kTilePages;  // pages past the split: valid memory, cleared
-    int id[kTilePages];
-    load_page_ids2(page_entry(bt, pg, a.max_pages), page_entry(bt, pg + 1, a.max_pages), id[0],
-                   id[1]);
-    load_page_ids2(page_entry(bt, pg + 2, a.max_pages), page_entry(bt, pg + 3, a.max_pages),
-                   id[2], id[3]);
+    int id[kTilePages];  // pages past the split: valid memory, cleared below
+    load_page_ids4(bt, pg_begin + t * kTilePages, a.max_pages, id);
     tile_dma<kNt>(ring[t % kWideStages], id, kc_layer, vc_layer, a.Hkv, kvh, a.num_pages, wave,
                   lane);
   };
@@ -1191,15 +1187,24 @@ __global__ void __launch_bounds__(kTileThreads) k_window_attn_wide(AttnArgs a) {
   }
 
   // ---- the split's cache tiles ------------------------------------------------
+  // Tile t + 1's values are converted to fp16 while tile t is computed, so one
+  // barrier per tile both publishes them and frees the stage tile t + 2 takes.
+  // In each tile the keys past the split (pages past it, or positions past
+  // the prefix) are cleared from the values and masked from the scores.
+  auto tile_keys = [&](int t) { return key_end - (key_begin + t * kTileKeys); };
+  if (n_tiles > 0) {
+    tile_wait_barrier(min(kWideAhead - 1, n_tiles - 1));  // tile 0 has landed
+    tile_v_to_f16(ring[0], tid, tile_keys(0));
+  }
   for (int t = 0; t < n_tiles; ++t) {
-    tile_wait_barrier(min(kWideAhead - 1, n_tiles - 1 - t));
+    // only tile t + 1's DMAs can be in flight here: after this barrier it has
+    // landed everywhere, tile t's values are fp16 everywhere, and tile t - 1's
+    // stage is free
+    tile_wait_barrier(0);
     if (t + kWideAhead < n_tiles) issue_tile(t + kWideAhead);
-    Tile& tl = ring[t % kWideStages];
-    // keys of the tile inside the split (every row sees all of them); the
-    // rest are cleared from the values and masked from the scores
-    const int nv = key_end - (key_begin + t * kTileKeys);
-    tile_v_to_f16(tl, tid, nv);
-    lds_barrier();
+    if (t + 1 < n_tiles) tile_v_to_f16(ring[(t + 1) % kWideStages], tid, tile_keys(t + 1));
+    const Tile& tl = ring[t % kWideStages];
+    const int nv = tile_keys(t);  // every row sees the keys of the tile below nv
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int pa = 32 * hf;

@@ -126,6 +126,45 @@ __device__ __forceinline__ void load_page_ids2(const int32_t* p0, const int32_t*
       : "memory");
 }
 
+// The block-table entries of logical pages pg .. pg+3 (a 64-key tile) of a
+// table row holding max_pages entries, each clamped into the row: one 16-byte
+// scalar load when the four lie inside the row, else four clamped loads; one
+// wait either way. Scalar loads count against lgkmcnt, not vmcnt.
+typedef uint32_t su32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void load_page_ids4(const int32_t* bt, int pg, int max_pages,
+                                               int (&id)[4]) {
+  auto su = [](const int32_t* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    return (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32)))
+            << 32) |
+           static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u)));
+  };
+  pg = __builtin_amdgcn_readfirstlane(pg);
+  if (pg >= 0 && pg + 3 < max_pages) {
+    su32x4 v;
+    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                 : "=s"(v)
+                 : "s"(su(bt + pg))
+                 : "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) id[i] = static_cast<int>(v[i]);
+  } else {
+    const int32_t* p0 = bt + min(max(pg, 0), max_pages - 1);
+    const int32_t* p1 = bt + min(max(pg + 1, 0), max_pages - 1);
+    const int32_t* p2 = bt + min(max(pg + 2, 0), max_pages - 1);
+    const int32_t* p3 = bt + min(max(pg + 3, 0), max_pages - 1);
+    asm volatile(
+        "s_load_dword %0, %4, 0x0\n\t"
+        "s_load_dword %1, %5, 0x0\n\t"
+        "s_load_dword %2, %6, 0x0\n\t"
+        "s_load_dword %3, %7, 0x0\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(id[0]), "=&s"(id[1]), "=&s"(id[2]), "=&s"(id[3])
+        : "s"(su(p0)), "s"(su(p1)), "s"(su(p2)), "s"(su(p3))
+        : "memory");
+  }
+}
+
 // Block-table entry of logical page pg of a sequence's table row, the page
 // index clamped to the table and the entry to the pool: the id a DMA reads.
 __device__ __forceinline__ const int32_t* page_entry(const int32_t* bt, int pg, int max_pages) {

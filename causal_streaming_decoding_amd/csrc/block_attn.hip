@@ -119,10 +119,7 @@ __global__ void __launch_bounds__(kBlkThreads) k_block_attn_bf16(BlockAttnArgs a
   const int32_t* bt = a.block_table + static_cast<size_t>(s) * a.max_pages;
   auto issue_tile = [&](int t) {
     int id[kTilePages];
-    load_page_ids2(page_entry(bt, 4 * t, a.max_pages), page_entry(bt, 4 * t + 1, a.max_pages),
-                   id[0], id[1]);
-    load_page_ids2(page_entry(bt, 4 * t + 2, a.max_pages),
-                   page_entry(bt, 4 * t + 3, a.max_pages), id[2], id[3]);
+    load_page_ids4(bt, 4 * t, a.max_pages, id);
     tile_dma<false>(ring[t % kBlkStages], id, a.kc, a.vc, a.Hkv, kvh, a.num_pages, wave, lane);
   };
   // The DMAs are issued before the plain loads below: those complete in
@@ -235,14 +232,23 @@ __global__ void __launch_bounds__(kBlkThreads) k_block_attn_bf16(BlockAttnArgs a
   }
 
   // ---- cache tiles: positions 64 t .. 64 t + 63 ------------------------------
+  // Tile t + 1's values are converted to fp16 while tile t is computed, so one
+  // barrier per tile both publishes them and frees the stage tile t + 2
+  // takes; in the last tile, positions >= n_cache (no row sees them; they may
+  // not be written) are cleared.
+  if (n_tiles > 0) {
+    tile_wait_barrier(min(kBlkAhead - 1, n_tiles - 1));  // tile 0 has landed
+    tile_v_to_f16(ring[0], tid, n_cache);
+  }
   for (int t = 0; t < n_tiles; ++t) {
-    tile_wait_barrier(min(kBlkAhead - 1, n_tiles - 1 - t));
+    // only tile t + 1's DMAs can be in flight here: after this barrier it has
+    // landed everywhere, tile t's values are fp16 everywhere, and tile t - 1's
+    // stage is free
+    tile_wait_barrier(0);
     if (t + kBlkAhead < n_tiles) issue_tile(t + kBlkAhead);
-    Tile& tl = ring[t % kBlkStages];
-    // the tile's values to fp16 in place; in the last tile, positions >=
-    // n_cache (no row sees them; they may not be written) are cleared
-    tile_v_to_f16(tl, tid, n_cache - t * kTileKeys);
-    lds_barrier();
+    if (t + 1 < n_tiles)
+      tile_v_to_f16(ring[(t + 1) % kBlkStages], tid, n_cache - (t + 1) * kTileKeys);
+    const Tile& tl = ring[t % kBlkStages];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int pa = t * kTileKeys + 32 * hf;

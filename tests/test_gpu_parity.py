@@ -115,7 +115,7 @@ def test_edge_cases(name, wl):
 @pytest.mark.parametrize("wl", [
     # one sequence per page count: splits, a ragged last page, 4 row tiles
     _variant(WL.QWEN3_8B_BS1, name="poison_bs1", B=3, prefix=("list", (77, 2047, 1000)), V=2048),
-    # 224 rows in row parts, ragged prefixes over split key ranges
+    # 224 rows (one wide workgroup per split), ragged prefixes over split key ranges
     _variant(WL.QWEN25_7B_RAGGED, name="poison_gqa7", B=4, prefix=("uniform", 1, 900), V=2048),
     # no split (many groups)
     _variant(WL.QWEN3_8B_STREAM, name="poison_layers", n_layers=6, B=6, V=2048,
@@ -154,7 +154,7 @@ def test_deterministic_bitwise():
     _variant(WL.QWEN3_8B_BS1, name="append_forms_bf16", fill=("count", 9), prefix=("fixed", 45),
              V=2048, B=3),
     _variant(WL.QWEN3_8B_BS1, name="append_forms_w64", W=64, Hq=16, Hkv=4, fill=("count", 64),
-             prefix=("fixed", 77), V=2048, B=2),  # all filled: 64 rows over 4 window chunks
+             prefix=("fixed", 77), V=2048, B=2),  # all filled: 64 rows over 4 chunks, 256-row groups
     _variant(WL.TINY_FP32, name="append_forms_fp32", n_layers=2, B=3, fill=("count", 5)),
 ])
 def test_fused_commit_forms_agree(wl):

@@ -34,8 +34,12 @@ def sources():
 
 # Per-file additions. attn.hip, block_attn.hip: no NaN reaches a maximum or
 # comparison there (scores of invisible keys are set to -inf before any
-# maximum), so the compiler need not quiet NaN operands before every v_max_f32.
-FILE_CFLAGS = {"attn.hip": ["-fno-honor-nans"], "block_attn.hip": ["-fno-honor-nans"]}
+# maximum), so the compiler need not quiet NaN operands before every v_max_f32;
+# entropy_chunks.hip (and the chunk blocks in attn.hip's launch): the logits are
+# taken to be finite. Files with host-side NaN checks of arguments keep the
+# default.
+FILE_CFLAGS = {"attn.hip": ["-fno-honor-nans"], "block_attn.hip": ["-fno-honor-nans"],
+               "entropy_chunks.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src, verbose):

@@ -10,8 +10,8 @@
 // The chunk pass (entropy_ops.hpp) reduces each chunk of a row of logits to
 // (max, sum 2^u, sum u 2^u, argmax) in one streaming pass.
 //
-// k_entropy_partial: grid (chunks, rows); each block reduces one chunk of one
-//   row to (m, s, t, argmax) in the workspace.
+// The chunk pass (k_entropy_partial, grid (chunks, rows)) is in
+// entropy_chunks.hip.
 // k_entropy_select: one wavefront per sequence merges the chunks of its W
 //   rows, forms entropy and score, and applies the threshold / floor rule.
 // k_step_tail: the same selection followed by the window-state commit and the
@@ -31,15 +31,6 @@
 #include <mutex>
 
 namespace wedlm {
-
-template <typename T, bool VEC>
-__global__ void __launch_bounds__(kEntThreads)
-k_entropy_partial(const T* __restrict__ logits, int V, int chunk_elems, int n_chunks,
-                  EntPartial* __restrict__ part) {
-  __shared__ EntPartial red[kEntThreads / kWave];
-  entropy_chunk_block<T, VEC>(logits, V, chunk_elems, n_chunks, part, blockIdx.x, blockIdx.y,
-                              red);
-}
 
 __global__ void __launch_bounds__(kWave)
 k_entropy_select(const EntPartial* __restrict__ part, int n_chunks, int W,
@@ -111,28 +102,6 @@ int launch_entropy_select(const EntPartial* part, int n_chunks, int B, int W,
 }  // namespace wedlm
 
 using namespace wedlm;
-
-void wedlm::launch_entropy_partials(int dtype, int B, int W, int V, const void* logits,
-                                    const EntPlan& pl, EntPartial* part, hipStream_t s) {
-  const dim3 grid(pl.n_chunks, B * W);
-  if (dtype == WEDLM_BF16) {
-    const uint16_t* z = static_cast<const uint16_t*>(logits);
-    if (pl.vec)
-      hipLaunchKernelGGL((k_entropy_partial<uint16_t, true>), grid, dim3(kEntThreads), 0, s, z, V,
-                         pl.chunk_elems, pl.n_chunks, part);
-    else
-      hipLaunchKernelGGL((k_entropy_partial<uint16_t, false>), grid, dim3(kEntThreads), 0, s, z, V,
-                         pl.chunk_elems, pl.n_chunks, part);
-  } else {
-    const float* z = static_cast<const float*>(logits);
-    if (pl.vec)
-      hipLaunchKernelGGL((k_entropy_partial<float, true>), grid, dim3(kEntThreads), 0, s, z, V,
-                         pl.chunk_elems, pl.n_chunks, part);
-    else
-      hipLaunchKernelGGL((k_entropy_partial<float, false>), grid, dim3(kEntThreads), 0, s, z, V,
-                         pl.chunk_elems, pl.n_chunks, part);
-  }
-}
 
 extern "C" size_t wedlm_entropy_select_workspace_size(int dtype, int B, int W, int V) {
   if (!valid_dtype(dtype) || B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW || V <= 0) return 0;

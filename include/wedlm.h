@@ -302,7 +302,8 @@ size_t wedlm_entropy_select_workspace_size(int dtype, int B, int W, int V);
  * slot with the lowest score (lowest i on equal scores) is selected.
  * tau = -INFINITY with min_fill = 1 is one-token-per-step decoding.
  *
- * in : logits [B][W][V], filled [B][W].
+ * in : logits [B][W][V], filled [B][W]. Logits are finite (no NaN; the
+ *      result of a row holding one is unspecified).
  * out: entropy, score [B][W] float32; argmax_tok [B][W] int32; selected [B][W]
  *      uint8 (0/1). workspace >= wedlm_entropy_select_workspace_size(...).
  */

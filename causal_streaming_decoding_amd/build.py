@@ -4,13 +4,21 @@ Each ``csrc/*.hip`` file is compiled to an object in ``_build/`` (in parallel)
 and the objects are linked into ``libwedlm.so`` next to this file. The build
 always recompiles. Packed fp32 VALU instructions are switched off for the
 device code (``-packed-fp32-ops``); the host pass warns that it does not know
-that feature, which is harmless.
+that feature, which is harmless. The compiler's intermediate files, the device
+assembly among them, stay in ``_build/``: before linking, ``isa_audit`` checks
+there that no register loaded by an inline-asm load is read, copied or reused
+before the counted wait that retires the load, and the build fails if one is.
 """
 
 import os
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
+
+try:
+    from . import isa_audit
+except ImportError:  # run as a script
+    import isa_audit
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -44,7 +52,8 @@ FILE_CFLAGS = {"attn.hip": ["-fno-honor-nans"], "block_attn.hip": ["-fno-honor-n
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, *FILE_CFLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_CFLAGS.get(os.path.basename(src), []), "-save-temps=obj", "-c",
+           src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                      if "packed-fp32-ops" not in line)
@@ -60,6 +69,10 @@ def build(verbose=False, jobs=8):
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), sources()))
+    found = isa_audit.audit_dir(BUILD_DIR)
+    if found:
+        lines = "\n".join(f"  {fn} line {ln}: {text} touches {regs}" for fn, ln, text, regs in found[:20])
+        raise RuntimeError("device code reads registers of inline-asm loads still in flight:\n" + lines)
     tmp = LIB_PATH + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

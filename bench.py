@@ -305,6 +305,7 @@ def config_latencies(args):
             "overlap_step_us": stats(o_span["step"]),
             "attn_segment_us": stats(m_span["attn"]),
             "entropy_tail_segment_us": stats(m_span["entropy"]),
+            "rows": wl.B * wl.W, "vocab": wl.V,
             "step_algorithmic_bytes": int(step_bytes_total),
             "step_hbm_gbps_at_median": step_bytes_total / (float(np.median(g_span["step"])) * 1e-6) / 1e9,
             "attn_algorithmic_bytes": int(attn_bytes), "logits_bytes": int(b["logits"]),
@@ -317,6 +318,11 @@ def config_latencies(args):
         print(json.dumps(line), flush=True)
         del st, q, k, v, logits, step, graph
         torch.cuda.empty_cache()
+    if args.calibrate_copy:
+        a = torch.empty(1 << 29, dtype=torch.float16, device=dev)  # 1 GiB
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
 
 
 # (name, B, W, hidden, V): the projection of the streaming workload's window

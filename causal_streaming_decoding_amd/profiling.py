@@ -376,6 +376,69 @@ def summarize_lm_head(bench_jsonl, trace, fetch, write, out_md, command_bench, c
         f.write("\n".join(out) + "\n")
 
 
+def _entropy_dispatches(trace, fetch, write, grid):
+    """Trace durations (us) and FETCH / WRITE KiB of the chunk-pass dispatches
+    whose grid has `grid` threads, in dispatch order."""
+    kern = "wedlm::k_entropy_partial"
+    dur = []
+    with open(os.path.join(trace, "run_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            if short_name(r["Kernel_Name"]).startswith(kern) and \
+                    int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) == grid:
+                dur.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    vals = {}
+    for d, counter in ((fetch, "FETCH_SIZE"), (write, "WRITE_SIZE")):
+        with open(os.path.join(d, "run_counter_collection.csv")) as f:
+            vals[counter] = [float(r["Counter_Value"]) for r in csv.DictReader(f)
+                             if r["Counter_Name"] == counter and int(r["Grid_Size"]) == grid
+                             and short_name(r["Kernel_Name"]).startswith(kern)]
+    return dur, vals["FETCH_SIZE"], vals["WRITE_SIZE"]
+
+
+def summarize_entropy(items, out_md, commands, peak_gbps=8000.0):
+    """Entropy chunk pass as a launch of its own: per workload, the trace median
+    of k_entropy_partial and its calibrated HBM bytes against the logits.
+
+    items: [(workload, rows, V, element bytes, trace dir, fetch dir, write dir)];
+    the fetch and write runs include the 1 GiB calibration copy."""
+    import statistics
+
+    out = ["# Entropy chunk pass (`k_entropy_partial`) as a launch of its own", "",
+           "MI355X (gfx950). For each workload, every launch of the full-vocabulary chunk pass "
+           "that runs as its own kernel (the ragged g = 7 step's default; the other single-step "
+           "workloads' `eager, entropy pass own launch` column; the streaming loop with "
+           "`--separate-entropy`): the trace median of the kernel, the logits it must read "
+           "(rows x V x element size, the algorithmic bytes; the partials it writes are "
+           "16 bytes per chunk and row), and the HBM bytes counted by `FETCH_SIZE` and "
+           "`WRITE_SIZE` (KiB per dispatch, calibrated by a 1 GiB device copy, mean over the "
+           "dispatches). In the commands, `<repo>` is the repository root.", "",
+           "```", *commands, "```", "",
+           "| workload | rows x V | chunk blocks | launches | kernel median us | logits MB | "
+           "read MB | written KB | read / logits | logits TB/s | % of 8 TB/s |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name, rows, V, elt, trace, fetch, write in items:
+        chunk = 256 * 8 * (16 // elt)
+        chunks = -(-V // chunk)
+        grid = chunks * 256 * rows
+        dur, fv, wv = _entropy_dispatches(trace, fetch, write, grid)
+        _, f_cal = counter_values(fetch, "FETCH_SIZE")
+        _, w_cal = counter_values(write, "WRITE_SIZE")
+        if not dur or not fv or not wv or f_cal is None or w_cal is None:
+            out.append(f"| `{name}` | {rows} x {V} | {chunks} x {rows} | 0 | - | - | - | - | - | - | - |")
+            continue
+        f_fac, w_fac = f_cal / CALIBRATION_KIB, w_cal / CALIBRATION_KIB
+        med = statistics.median(dur)
+        logits = rows * V * elt
+        rd = statistics.mean(fv) * 1024.0 / f_fac
+        wr = statistics.mean(wv) * 1024.0 / w_fac
+        tbs = logits / (med * 1e-6) / 1e12
+        out.append(f"| `{name}` | {rows} x {V} | {chunks} x {rows} | {len(dur)} | {med:.2f} | "
+                   f"{logits / 1e6:.1f} | {rd / 1e6:.1f} | {wr / 1e3:.1f} | {rd / logits:.3f} | "
+                   f"{tbs:.2f} | {100 * tbs * 1e3 / peak_gbps:.1f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(out) + "\n")
+
+
 def read_traffic(path, workload):
     """Counted HBM bytes over algorithmic bytes of the attention launch, or None
     when the record does not apply.
@@ -427,6 +490,33 @@ def main():
         a = ap.parse_args()
         summarize_counters(a.csv, a.out_md, a.title, a.intro, a.command,
                            mfma_per_wave_page=a.mfma_per_wave_page)
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "entropy":
+        ap = argparse.ArgumentParser()
+        ap.add_argument("mode")
+        ap.add_argument("--configs-jsonl", required=True)
+        ap.add_argument("--trace", required=True)
+        ap.add_argument("--fetch", required=True)
+        ap.add_argument("--write", required=True)
+        ap.add_argument("--stream-json", default=None)
+        ap.add_argument("--stream-trace", default=None)
+        ap.add_argument("--stream-fetch", default=None)
+        ap.add_argument("--stream-write", default=None)
+        ap.add_argument("--out-md", required=True)
+        ap.add_argument("--command", action="append", default=[])
+        a = ap.parse_args()
+        items = []
+        for ln in open(a.configs_jsonl):
+            if ln.startswith("{"):
+                d = json.loads(ln)
+                elt = 4 if d["dtype"] == "f32" else 2
+                items.append((d["workload"], d["rows"], d["vocab"], elt, a.trace, a.fetch, a.write))
+        if a.stream_json:
+            d = _bench_line(a.stream_json)
+            c = d["config"]
+            items.append((c["workload"] + " (--separate-entropy)", c["batch"] * c["window"],
+                          c["vocab"], 2, a.stream_trace, a.stream_fetch, a.stream_write))
+        summarize_entropy(items, a.out_md, a.command)
         return
     if len(sys.argv) > 1 and sys.argv[1] == "configs":
         ap = argparse.ArgumentParser()

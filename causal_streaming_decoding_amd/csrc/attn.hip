@@ -617,7 +617,10 @@ k_window_attn_bf16(AttnArgs a) {
     bid = (rest / a.parts) * kNumXcds + xcd;
     if (bid >= a.units) return;  // padding of the last XCD round
   }
-  const int j = bid % a.cols;  // sequence, or (sequence, split) in split mode
+  // sequence, or (sequence, split) in split mode; a split launch rotates the
+  // column's slots by the column index, so that the last splits of the
+  // groups (those that also attend to the window) fall on different XCDs
+  const int j = a.split ? (bid % a.cols + bid / a.cols) % a.cols : bid % a.cols;
   bid /= a.cols;
   const int kvh = bid % a.Hkv;
   const int layer = bid / a.Hkv;
@@ -1004,7 +1007,10 @@ __global__ void __launch_bounds__(kTileThreads) k_window_attn_wide(AttnArgs a) {
   const int li = lane & 31, h = lane >> 5;
 
   int bid = blockIdx.x;
-  const int j = bid % a.cols;  // sequence, or (sequence, split) in split mode
+  // sequence, or (sequence, split) in split mode; a split launch rotates the
+  // column's slots by the column index, so that the last splits of the
+  // groups (those that also attend to the window) fall on different XCDs
+  const int j = a.split ? (bid % a.cols + bid / a.cols) % a.cols : bid % a.cols;
   bid /= a.cols;
   const int kvh = bid % a.Hkv;
   const int layer = bid / a.Hkv;
@@ -1453,14 +1459,14 @@ static AttnPlan plan_bf16(int n_layers, int B, int W, int Hq, int Hkv, int max_p
   const long long groups = 1LL * n_layers * B * Hkv;
   const long long columns = 1LL * n_layers * Hkv;
   // aim for one full round of workgroups (every CU holding as many as its
-  // registers allow) but keep >= 8 pages per split (4 measured slower where it
-  // mattered: the bs1, L = 2048 step took 43.0 against 38.6 us, its combine
-  // merging twice as many partials);
+  // registers allow) but keep >= 6 pages per split (bs1, L = 2048: 8 pages
+  // per split took 21.2 us per chained step, 6 pages 20.7, 4 pages 22.8 as
+  // the merge of the split partials grows);
   // how the column's workgroups are shared out follows the live prefix
   // lengths on the device (find_split)
   const int wg_per_cu = pl.wide ? 1 : Ring<4>::kWgPerCu;
   const long long target = 1LL * kNumCUs * wg_per_cu / pl.parts;  // work units per round
-  pl.min_pages = 8;
+  pl.min_pages = 6;
   const int npages = ceil_div(max(max_prefix_len, 1), kPage);
   pl.cols = B;
   pl.split = false;

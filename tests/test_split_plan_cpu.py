@@ -56,7 +56,7 @@ def test_split_plan_covers_each_page_once(seed):
     max_prefix = int(rng.integers(0, 6000))
     lengths = rng.integers(-2, max_prefix + 30, size=B)
     W = int(rng.integers(1, 65))
-    min_pages = int(rng.choice([4, 8]))
+    min_pages = int(rng.choice([4, 6, 8]))
     S = B + int(rng.integers(1, 1300))
     K, pages, assignment = plan(lengths, W, S, min_pages, max_prefix)
     assert K >= min_pages

@@ -242,10 +242,11 @@ def summarize_configs(configs_jsonl, traces, out_md, command_bench, command_trac
 
 
 def summarize_counters(csv_paths, out_md, title, intro, commands, xcds=8, cus=256, simds=4,
-                       clock_ghz=2.4, mfma_per_wave_page=12):
-    """SQ / GRBM counter passes of the attention kernel, one table per launch
-    shape (workgroups), medians over the dispatches, and the ratios read from
-    them: MFMA busy, instruction mix per MFMA, LDS bank conflicts, waits.
+                       clock_ghz=2.4, mfma_per_wave_page=12, unit="16-key page"):
+    """SQ / GRBM counter passes of a kernel, one column per launch (kernel
+    instantiation and workgroups), medians over the dispatches, and the ratios
+    read from them: MFMA busy, instruction mix per MFMA, LDS bank conflicts,
+    waits.
 
     ``csv_paths``: run_counter_collection.csv of each pass (counters summed
     over the chip by rocprofv3, GRBM_GUI_ACTIVE over the XCDs)."""
@@ -259,7 +260,8 @@ def summarize_counters(csv_paths, out_md, title, intro, commands, xcds=8, cus=25
         for r in csv.DictReader(open(path)):
             d = r["Dispatch_Id"]
             per_dispatch[d][r["Counter_Name"]] = float(r["Counter_Value"])
-            shape[d] = int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1)
+            wgs = int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1)
+            shape[d] = (short_name(r["Kernel_Name"]).replace("wedlm::", ""), wgs)
         for d, vals in per_dispatch.items():
             for k, v in vals.items():
                 per_shape[shape[d]][k].append(v)
@@ -267,7 +269,7 @@ def summarize_counters(csv_paths, out_md, title, intro, commands, xcds=8, cus=25
     med = {w: {k: statistics.median(v) for k, v in per_shape[w].items()} for w in shapes}
     names = sorted({k for w in shapes for k in med[w]})
     lines = [f"# {title}", "", intro, "", "```"] + list(commands) + ["```", "",
-             "| counter | " + " | ".join(f"{w} workgroups" for w in shapes) + " |",
+             "| counter | " + " | ".join(f"`{w[0]}`, {w[1]} workgroups" for w in shapes) + " |",
              "|---|" + "---|" * len(shapes)]
     for k in names:
         lines.append(f"| `{k}` | " + " | ".join(
@@ -283,13 +285,13 @@ def summarize_counters(csv_paths, out_md, title, intro, commands, xcds=8, cus=25
         active = m["GRBM_GUI_ACTIVE"] / xcds
         mf = m["SQ_INSTS_MFMA"]
         lines.append(
-            f"* {w} workgroups: GPU-active {active / (clock_ghz * 1e3):.1f} us per dispatch; MFMA "
+            f"* `{w[0]}`, {w[1]} workgroups: GPU-active {active / (clock_ghz * 1e3):.1f} us per dispatch; MFMA "
             f"busy {100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (active * cus * simds):.1f} % "
             f"(MFMA-busy cycles / (active cycles x {cus} CUs x {simds} SIMDs)); per MFMA "
             f"instruction {m['SQ_INSTS_VALU'] / mf:.2f} VALU (of them "
             f"{m['SQ_INSTS_VALU_TRANS_F32'] / mf:.2f} transcendental), "
             f"{m['SQ_INSTS_SALU'] / mf:.2f} SALU, {m['SQ_INSTS_LDS'] / mf:.2f} LDS, i.e. per "
-            f"wavefront and 16-key page ({mfma_per_wave_page} MFMAs) "
+            f"wavefront and {unit} ({mfma_per_wave_page} MFMAs) "
             f"{mfma_per_wave_page * m['SQ_INSTS_VALU'] / mf:.0f} VALU, "
             f"{mfma_per_wave_page * m['SQ_INSTS_SALU'] / mf:.0f} SALU, "
             f"{mfma_per_wave_page * m['SQ_INSTS_LDS'] / mf:.0f} LDS; LDS bank conflicts "
@@ -299,7 +301,7 @@ def summarize_counters(csv_paths, out_md, title, intro, commands, xcds=8, cus=25
             f"{100 * m['SQ_ACTIVE_INST_ANY'] / m['SQ_WAVE_CYCLES']:.1f} %.")
         if "SQ_VALU_MFMA_COEXEC_CYCLES" in m and "SQ_WAIT_ANY" in m:
             lines.append(
-                f"  {w} workgroups: of the MFMA-busy cycles, "
+                f"  `{w[0]}`, {w[1]} workgroups: of the MFMA-busy cycles, "
                 f"{100 * m['SQ_VALU_MFMA_COEXEC_CYCLES'] / m['SQ_VALU_MFMA_BUSY_CYCLES']:.1f} % have "
                 f"a VALU instruction executing beside them; wave cycles waiting on anything "
                 f"(counters, barriers, dependencies) {100 * m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.1f} %.")
@@ -486,10 +488,11 @@ def main():
         ap.add_argument("--intro", default="")
         ap.add_argument("--command", action="append", default=[])
         ap.add_argument("--mfma-per-wave-page", type=int, default=12,
-                        help="MFMA instructions per wavefront and 16-key page of the kernel")
+                        help="MFMA instructions per wavefront and work unit of the kernel")
+        ap.add_argument("--unit", default="16-key page", help="the work unit's name")
         a = ap.parse_args()
         summarize_counters(a.csv, a.out_md, a.title, a.intro, a.command,
-                           mfma_per_wave_page=a.mfma_per_wave_page)
+                           mfma_per_wave_page=a.mfma_per_wave_page, unit=a.unit)
         return
     if len(sys.argv) > 1 and sys.argv[1] == "entropy":
         ap = argparse.ArgumentParser()

@@ -75,3 +75,53 @@ def test_config_summary_from_files(tmp_path):
     assert "| `wedlm::k_a<4>` | 4 x 1 | 256 | 1 | 9.00 |" in text
     assert "other_kernel" not in text
     assert "* `w`: [1,2) 3" in text
+
+
+def _write_csv(path, header, rows):
+    path.parent.mkdir(parents=True, exist_ok=True)
+    path.write_text(",".join(header) + "\n" + "\n".join(",".join(str(x) for x in r) for r in rows) + "\n")
+
+
+def test_entropy_summary_from_files(tmp_path):
+    # one bf16 workload: 2 rows x 20000 logits -> 2 chunks of 16384, grid 2 x 256 x 2 threads
+    rows, V = 2, 20000
+    grid_x, grid_y = 2 * 256, rows
+    k = '"void wedlm::k_entropy_partial<unsigned short, true>(unsigned short const*, int)"'
+    _write_csv(tmp_path / "tr" / "run_kernel_trace.csv",
+               ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Grid_Size_Y",
+                "Grid_Size_Z"],
+               [[k, 1000, 5000, grid_x, grid_y, 1], [k, 9000, 11000, grid_x, grid_y, 1],
+                ['"void wedlm::k_other(int)"', 0, 99999, grid_x, grid_y, 1]])
+    cal = ['"__amd_rocclr_copyBuffer"', 1 << 20]
+    for name, counter, kib, cal_kib in (("fe", "FETCH_SIZE", 40.0, 1 << 19), ("wr", "WRITE_SIZE", 0.5, 1 << 20)):
+        _write_csv(tmp_path / name / "run_counter_collection.csv",
+                   ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"],
+                   [[1, k, grid_x * grid_y, counter, kib], [2, k, grid_x * grid_y, counter, kib],
+                    [3, cal[0], cal[1], counter, cal_kib]])
+    out = tmp_path / "e.md"
+    items = [("w", rows, V, 2, str(tmp_path / "tr"), str(tmp_path / "fe"), str(tmp_path / "wr"))]
+    profiling.summarize_entropy(items, str(out), ["cmd"])
+    row = [ln for ln in out.read_text().splitlines() if ln.startswith("| `w`")][0].split("|")
+    cells = [c.strip() for c in row[1:-1]]
+    assert cells[1] == "2 x 20000" and cells[2] == "2 x 2" and cells[3] == "2"
+    assert float(cells[4]) == 3.0                       # median of 4 and 2 us (timestamps in ns)
+    logits = rows * V * 2
+    read = 40.0 * 1024 / 0.5                            # FETCH calibrated by 0.5
+    assert abs(float(cells[5]) - logits / 1e6) < 0.05
+    assert abs(float(cells[8]) - read / logits) < 1e-3
+
+
+def test_counter_summary_keys_by_kernel_and_launch(tmp_path):
+    hdr = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Name", "Counter_Value"]
+    rows = []
+    for d, (kern, grid) in enumerate((("void wedlm::k_a<1>(int)", 256 * 10),
+                                      ("void wedlm::k_a<2>(int)", 256 * 10))):
+        rows.append([d, f'"{kern}"', grid, 256, "SQ_WAVES", 40 * (d + 1)])
+    _write_csv(tmp_path / "p" / "run_counter_collection.csv", hdr, rows)
+    out = tmp_path / "c.md"
+    profiling.summarize_counters([str(tmp_path / "p" / "run_counter_collection.csv")], str(out), "t",
+                                 "", [])
+    text = out.read_text()
+    # same launch size, different instantiations: two columns
+    assert "`k_a<1>`, 10 workgroups" in text and "`k_a<2>`, 10 workgroups" in text
+    assert "| `SQ_WAVES` | 40 | 80 |" in text

@@ -56,7 +56,8 @@ __device__ __forceinline__ int h_swz(int r, int u) { return u ^ (((r >> 1) & 7) 
 
 // One 16-byte load per lane into registers through asm, so that the
 // compiler adds no wait of its own (the waits are explicit and counted, and
-// name the loaded registers). It reads the packed projection, which streams
+// name the loaded registers; the build's assembly audit, isa_audit.py, checks
+// that no instruction reads, copies or reuses them before that wait). It reads the packed projection, which streams
 // through once per launch (a second row group on the same XCD finds it in
 // L2 all the same): the non-temporal hint (nt) took the 16-row shape from
 // 250 to 221 us and helped every other shape too.

@@ -138,7 +138,8 @@ inline bool valid_dtype(int dtype) { return dtype == WEDLM_F32 || dtype == WEDLM
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+// ceil(a / b) for b > 0, without forming a + b - 1 (no overflow near INT_MAX)
+inline int ceil_div(int a, int b) { return a / b + (a % b > 0 ? 1 : 0); }
 
 // Internal (not part of the C ABI): the rows half of wedlm_commit_prefix_rope,
 // enqueued on `s`, with the keys rotated at rot_pos[b][j] (physical rows 0..c-1

@@ -176,7 +176,7 @@ inline EntPlan plan_entropy(int dtype, int B, int W, int V) {
   // a chunk is kEntIter 16-byte vectors per thread (the same element count on
   // the single-element path, so the workspace does not depend on alignment)
   pl.chunk_elems = kEntThreads * kEntIter * N;
-  pl.n_chunks = (V + pl.chunk_elems - 1) / pl.chunk_elems;
+  pl.n_chunks = ceil_div(V, pl.chunk_elems);
   (void)B;
   (void)W;
   return pl;

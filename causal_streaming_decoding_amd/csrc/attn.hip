@@ -1517,6 +1517,8 @@ static int validate_attn(int dtype, int n_layers, int B, int W, int Hq, int Hkv,
   if (n_layers <= 0 || B <= 0 || W <= 0 || W > WEDLM_MAX_WINDOW || Hq <= 0 || Hkv <= 0 || D <= 0)
     return WEDLM_ERR_INVALID;
   if (Hq % Hkv != 0 || max_prefix_len < 0) return WEDLM_ERR_INVALID;
+  // keeps every launch-plan product (layers x sequences x heads x rows) in range
+  if (n_layers > kMaxShapeDim || B > kMaxShapeDim || Hq > kMaxShapeDim) return WEDLM_ERR_UNSUPPORTED;
   if (page_size != kPage) return WEDLM_ERR_UNSUPPORTED;
   if (dtype == WEDLM_BF16) {
     if (D != kHeadDim) return WEDLM_ERR_UNSUPPORTED;

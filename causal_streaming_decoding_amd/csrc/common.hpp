@@ -138,6 +138,9 @@ inline bool valid_dtype(int dtype) { return dtype == WEDLM_F32 || dtype == WEDLM
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Largest layer, sequence and head counts the host-side launch plans take.
+constexpr int kMaxShapeDim = 65535;
+
 // ceil(a / b) for b > 0, without forming a + b - 1 (no overflow near INT_MAX)
 inline int ceil_div(int a, int b) { return a / b + (a % b > 0 ? 1 : 0); }
 

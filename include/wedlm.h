@@ -189,8 +189,8 @@ size_t wedlm_window_attn_workspace_size(int dtype, int n_layers, int B, int W, i
  *      [0, max_prefix_len]).
  * out: out_phys [n_layers][B][W][Hq][D], physical order.
  * Host sizes: page_size P in {16}; max_prefix_len <= max_pages * P; bf16 needs
- * D == 128; f32 needs D a multiple of 4 and <= 256 (WEDLM_ERR_UNSUPPORTED
- * otherwise). Cache positions at or past prefix_len[b] in a sequence's last
+ * D == 128; f32 needs D a multiple of 4 and <= 256; n_layers, B and Hq at most
+ * 65535 (WEDLM_ERR_UNSUPPORTED otherwise). Cache positions at or past prefix_len[b] in a sequence's last
  * page may hold any bits, NaN and Inf included: they never reach the output.
  * workspace: at least
  * wedlm_window_attn_workspace_size(...) bytes (may be NULL if that is 0).

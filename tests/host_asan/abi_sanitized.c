@@ -39,6 +39,18 @@ int main(void) {
                                                     x[7], x[8]);
         (void)n;
       }
+    /* and every pair of arguments swept together */
+    for (int a = 0; a < 9; ++a)
+      for (int b = a + 1; b < 9; ++b)
+        for (int i = 0; i < NV; ++i)
+          for (int k = 0; k < NV; ++k) {
+            int x[9];
+            for (int j = 0; j < 9; ++j) x[j] = base[j];
+            x[a] = kVals[i];
+            x[b] = kVals[k];
+            (void)wedlm_window_attn_workspace_size(x[0], x[1], x[2], x[3], x[4], x[5], x[6],
+                                                   x[7], x[8]);
+          }
     EXPECT(wedlm_window_attn_workspace_size(WEDLM_BF16, 1, 1, 16, 32, 8, 64, 16, 2048) == 0);
     EXPECT(wedlm_window_attn_workspace_size(WEDLM_BF16, 1, 4, 16, 32, 8, 128, 16, 32768) > 0);
   }
@@ -50,6 +62,10 @@ int main(void) {
         x[a] = kVals[i];
         (void)wedlm_entropy_select_workspace_size(x[0], x[1], x[2], x[3]);
       }
+    for (int i = 0; i < NV; ++i)
+      for (int k = 0; k < NV; ++k)
+        for (int m = 0; m < NV; ++m)
+          (void)wedlm_entropy_select_workspace_size(WEDLM_BF16, kVals[i], kVals[k], kVals[m]);
     EXPECT(wedlm_entropy_select_workspace_size(WEDLM_BF16, 16, 16, 151936) > 0);
     EXPECT(wedlm_entropy_select_workspace_size(WEDLM_BF16, 16, 65, 151936) == 0);
   }
@@ -62,6 +78,16 @@ int main(void) {
         (void)wedlm_lm_head_select_workspace_size(x[0], x[1], x[2], x[3], x[4]);
         (void)wedlm_lm_head_packed_size(x[0], x[3], x[4]);
       }
+    for (int a = 1; a < 5; ++a)
+      for (int b = a + 1; b < 5; ++b)
+        for (int i = 0; i < NV; ++i)
+          for (int k = 0; k < NV; ++k) {
+            int x[5] = {base[0], base[1], base[2], base[3], base[4]};
+            x[a] = kVals[i];
+            x[b] = kVals[k];
+            (void)wedlm_lm_head_select_workspace_size(x[0], x[1], x[2], x[3], x[4]);
+            (void)wedlm_lm_head_packed_size(x[0], x[3], x[4]);
+          }
     EXPECT(wedlm_lm_head_packed_size(WEDLM_BF16, 4096, 151936) > 0);
     EXPECT(wedlm_lm_head_packed_size(WEDLM_BF16, 100, 151936) == 0);
   }

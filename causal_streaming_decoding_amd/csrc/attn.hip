@@ -1279,7 +1279,10 @@ struct RopeF32 {
   double omega[kF32MaxD / 2];
 };
 
-template <bool kRope>
+// kSmall (D <= 64): each lane holds one output dimension, and every key's
+// value for it is requested before the keys' scores are formed, so the
+// value loads wait alongside the key loads instead of after the softmax.
+template <bool kRope, bool kSmall>
 __global__ void __launch_bounds__(kWave)
 k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
                   const float* __restrict__ v, const float* __restrict__ kc,
@@ -1327,6 +1330,24 @@ k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
   for (int i = 0; i < kF32MaxD / kWave; ++i) o[i] = 0.f;
   for (int k0 = 0; k0 < nkeys; k0 += kWave) {
     const int key = k0 + lane;
+    const int nk = min(kWave, nkeys - k0);
+    float vk[kSmall ? kWave : 1];
+    if constexpr (kSmall) {
+#pragma unroll
+      for (int j = 0; j < kWave; ++j) {
+        const int kj = k0 + min(j, nk - 1);  // keys past nk: a valid row, weight 0 below
+        const float* src;
+        int stride = 1;
+        if (kj < L) {
+          const int pid = min(max(bt[kj / kPage], 0), num_pages - 1);
+          src = vcl + (static_cast<size_t>(pid) * Hkv + kvh) * page_elems + kj % kPage;
+          stride = kPage;
+        } else {
+          src = v + ((lb * W + slot_of(kj - L)) * Hkv + kvh) * D;
+        }
+        vk[j] = lane < D ? src[lane * stride] : 0.f;
+      }
+    }
     float sc = -INFINITY;
     if (key < nkeys) {
       float dot = 0.f;
@@ -1379,12 +1400,20 @@ k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
     m = m_new;
 #pragma unroll
     for (int i = 0; i < kF32MaxD / kWave; ++i) o[i] *= alpha;
+    if constexpr (kSmall) {
+      // the values are in registers: accumulate in key order
+#pragma unroll
+      for (int j = 0; j < kWave; ++j) {
+        const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pk), j));
+        if (j < nk) o[0] += pj * vk[j];
+      }
+      continue;
+    }
     // PV over this step's keys, kPvBatch keys at a time: the batch's values
     // are all requested before any is used (one key at a time left a chain of
     // dependent block-table and value loads per key), then accumulated in key
     // order.
     constexpr int kPvBatch = 8;
-    const int nk = min(kWave, nkeys - k0);
     for (int j0 = 0; j0 < nk; j0 += kPvBatch) {
       float pj[kPvBatch];
       float vv[kPvBatch][kF32MaxD / kWave];
@@ -1586,10 +1615,11 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
                          static_cast<float*>(out_phys), B, W, Hq, Hkv, D, num_pages, max_pages,
                          max_prefix_len, cache_layer_stride, scale_log2, rp);
     };
+    const bool small = D <= kWave;
     if (rope)
-      go(k_window_attn_f32<true>);
+      small ? go(k_window_attn_f32<true, true>) : go(k_window_attn_f32<true, false>);
     else
-      go(k_window_attn_f32<false>);
+      small ? go(k_window_attn_f32<false, true>) : go(k_window_attn_f32<false, false>);
     st = launch_status();
     if (st != WEDLM_OK || commit_run == nullptr) return st;
     // the f32 path appends the committed rows with the commit step's own kernel

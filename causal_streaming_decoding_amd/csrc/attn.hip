@@ -1317,6 +1317,17 @@ k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
   } else {
     for (int d = lane; d < D; d += kWave) qs[d] = q[((lb * W + p) * Hq + h) * D + d];
   }
+  // kSmall: the rotations of window rows 0..p, (cos, sin) per frequency,
+  // computed once by all lanes rather than per key by the lane holding it
+  __shared__ float2 s_cs[kSmall && kRope ? WEDLM_MAX_WINDOW * (kWave / 2) : 1];
+  if constexpr (kSmall && kRope) {
+    for (int e = lane; e < (p + 1) * half; e += kWave) {
+      const int r = e / half, j = e % half;
+      float c, sn;
+      rope_cos_sin(static_cast<double>(rp.pos[b * W + r]), rp.omega[j], c, sn);
+      s_cs[e] = make_float2(c, sn);
+    }
+  }
   __syncthreads();
   const int L = min(max(prefix_len[b], 0), max_prefix_len);
   const int nkeys = L + p + 1;
@@ -1377,7 +1388,13 @@ k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float c, sn;
-            rope_cos_sin(tk, rp.omega[4 * j4 + e], c, sn);
+            if constexpr (kSmall) {
+              const float2 cs = s_cs[r * half + 4 * j4 + e];
+              c = cs.x;
+              sn = cs.y;
+            } else {
+              rope_cos_sin(tk, rp.omega[4 * j4 + e], c, sn);
+            }
             dot += bl[e] * (al[e] * c - ah[e] * sn) + bh[e] * (ah[e] * c + al[e] * sn);
           }
         }

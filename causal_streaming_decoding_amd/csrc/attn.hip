@@ -45,6 +45,7 @@
 #include "attn_combine.hpp"
 #include "attn_device.hpp"
 #include "attn_tile32.hpp"
+#include "commit_ops.hpp"
 #include "common.hpp"
 #include "entropy_ops.hpp"
 
@@ -1289,9 +1290,27 @@ k_window_attn_f32(const float* __restrict__ q, const float* __restrict__ k,
                   const float* __restrict__ vc, const int32_t* __restrict__ block_table,
                   const int32_t* __restrict__ prefix_len, float* __restrict__ out, int B, int W,
                   int Hq, int Hkv, int D, int num_pages, int max_pages, int max_prefix_len,
-                  long long cache_layer_stride, float scale_log2, RopeF32 rp) {
+                  long long cache_layer_stride, float scale_log2, RopeF32 rp,
+                  long long attn_blocks, const int32_t* __restrict__ commit_run,
+                  float* __restrict__ kc_w, float* __restrict__ vc_w) {
   __shared__ float qs[kF32MaxD];
   const int lane = threadIdx.x;
+  if constexpr (kRope) {
+    // blocks past the attention's append the committed rows (commit_run given):
+    // one block per (layer, sequence, kv head), at positions the attention
+    // does not read (L and beyond), rotated at the attention's positions
+    if (static_cast<long long>(blockIdx.x) >= attn_blocks) {
+      const long long e = blockIdx.x - attn_blocks;
+      const int kvh_c = static_cast<int>(e % Hkv);
+      const int b_c = static_cast<int>((e / Hkv) % B);
+      const int layer_c = static_cast<int>(e / (1LL * Hkv * B));
+      commit_rows_block<float, true>(B, W, Hkv, D, kPage, num_pages, max_pages, commit_run,
+                                     prefix_len, k, v, block_table, kc_w, vc_w,
+                                     cache_layer_stride, rp.omega, rp.pos, b_c, kvh_c, layer_c,
+                                     lane, kWave);
+      return;
+    }
+  }
   int bid = blockIdx.x;
   const int p = bid % W;
   bid /= W;
@@ -1618,7 +1637,9 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
   if (rope)
     for (int j = 0; j < D / 2; ++j) omega[j] = std::pow(theta, -2.0 * j / D);
   if (dtype == WEDLM_F32) {
-    const long long blocks = 1LL * n_layers * B * Hq * W;
+    const long long attn_blocks = 1LL * n_layers * B * Hq * W;
+    // the committed rows are appended by blocks of the same launch
+    const long long blocks = attn_blocks + (rope && commit_run ? 1LL * n_layers * B * Hkv : 0);
     if (blocks > 0x7fffffffLL) return WEDLM_ERR_UNSUPPORTED;
     RopeF32 rp{};
     rp.perm = perm;
@@ -1630,19 +1651,16 @@ static int launch_attn(bool rope, int dtype, int n_layers, int B, int W, int Hq,
                          static_cast<const float*>(v), static_cast<const float*>(k_cache),
                          static_cast<const float*>(v_cache), block_table, prefix_len,
                          static_cast<float*>(out_phys), B, W, Hq, Hkv, D, num_pages, max_pages,
-                         max_prefix_len, cache_layer_stride, scale_log2, rp);
+                         max_prefix_len, cache_layer_stride, scale_log2, rp, attn_blocks,
+                         commit_run, static_cast<float*>(const_cast<void*>(k_cache)),
+                         static_cast<float*>(const_cast<void*>(v_cache)));
     };
     const bool small = D <= kWave;
     if (rope)
       small ? go(k_window_attn_f32<true, true>) : go(k_window_attn_f32<true, false>);
     else
       small ? go(k_window_attn_f32<false, true>) : go(k_window_attn_f32<false, false>);
-    st = launch_status();
-    if (st != WEDLM_OK || commit_run == nullptr) return st;
-    // the f32 path appends the committed rows with the commit step's own kernel
-    return commit_rows_rope(dtype, n_layers, B, W, Hkv, D, page_size, num_pages, max_pages,
-                            theta, commit_run, prefix_len, pos, k, v, block_table,
-                            const_cast<void*>(k_cache), const_cast<void*>(v_cache), s);
+    return launch_status();
   }
   const AttnPlan pl = plan_bf16(n_layers, B, W, Hq, Hkv, max_prefix_len);
   const size_t need = pl.ws_o_bytes + pl.ws_ml_bytes + pl.ws_plan_bytes;

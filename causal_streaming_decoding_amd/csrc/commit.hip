@@ -9,11 +9,13 @@
 // Two kernels on the caller's stream:
 //   k_commit_rows  grid (sequence x kv head, layer): copies the c committed rows of
 //                  k_phys / v_phys (physical rows 0..c-1 are slots 0..c-1) into
-//                  the pages at positions L..L+c-1.
+//                  the pages at positions L..L+c-1 (commit_rows_block,
+//                  commit_ops.hpp; the fp32 attention launch runs the same
+//                  function in blocks of its own to append its rows).
 //   k_commit_state one wavefront per sequence: cache slots, window shift with
 //                  the new fills, mask refill, prefix_len += c. It runs after
 //                  the copies (same stream), which read the old prefix_len.
-#include "window_ops.hpp"
+#include "commit_ops.hpp"
 
 #include <cmath>
 #include <type_traits>
@@ -22,29 +24,6 @@ namespace wedlm {
 
 constexpr int kCommitThreads = 256;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Committed rows are written as whole 64-byte lines: a line holds 4 keys of
-// one 16-byte K slice, or 16 keys of 64 / (16 * sizeof(T)) value dimensions.
-// Each line touched by the commit is read, the committed keys are merged in
-// registers (static indices, so nothing goes to scratch) and the line is
-// stored back in full - partial-line stores would make the memory system
-// read-modify-write every 2- or 16-byte piece. One thread owns one line; one
-// block covers one (sequence, kv head, layer), so a commit of c <= 16 rows
-// touches at most 5 x D/8 key lines and 2 x D/2 value lines per block: one
-// round of 256 threads for D = 128.
-constexpr int kCommitMaxD = 256;
-
-// RoPE frequencies theta^(-2j/D) for the fused variant (host-computed).
-struct CommitRope {
-  double omega[kCommitMaxD / 2];
-};
-
-// kRope: k_phys / v_phys are the window rows in slot order before RoPE (the
-// committed rows 0..c-1 are slots 0..c-1 either way); each committed key is
-// rotated as it is written, at rot_pos[b][j] when rot_pos is given (the
-// positions an attention call rotated the same rows at), else at its logical
-// position L + j. The two agree when rot_pos comes from the window reorder.
 template <typename T, bool kRope>
 __global__ void __launch_bounds__(kCommitThreads)
 k_commit_rows(int B, int W, int Hkv, int D, int P, int num_pages, int max_pages,
@@ -53,96 +32,10 @@ k_commit_rows(int B, int W, int Hkv, int D, int P, int num_pages, int max_pages,
               const int32_t* __restrict__ block_table, T* __restrict__ k_cache,
               T* __restrict__ v_cache, long long cache_layer_stride, CommitRope rope,
               const int32_t* __restrict__ rot_pos) {
-  constexpr int X = 16 / sizeof(T);         // elements per 16-byte K slice
-  constexpr int kLineElems = 64 / sizeof(T);
-  constexpr int kDimsPerLine = kLineElems / 16;  // value dimensions per line (P = 16)
-  const int b = blockIdx.x / Hkv;
-  const int kvh = blockIdx.x % Hkv;
-  const int layer = blockIdx.y;
-  const int L = max(prefix_len[b], 0);
-  const int c = commit_length(run_len[b], L, W, max_pages, P);
-  if (c == 0) return;
-  const int32_t* bt = block_table + static_cast<size_t>(b) * max_pages;
-  const size_t lb = static_cast<size_t>(layer) * B + b;
-  T* kcl = k_cache + static_cast<size_t>(layer) * cache_layer_stride;
-  T* vcl = v_cache + static_cast<size_t>(layer) * cache_layer_stride;
-  const int slices = D / X;
-  const int end = L + c;  // committed positions are L .. end-1
-
-  // keys: lines of 4 positions within one slice of one page
-  const int line0 = L / 4, nlines = (end - 1) / 4 - line0 + 1;
-  const int ktasks = nlines * slices;
-  for (int task = threadIdx.x; task < ktasks; task += kCommitThreads) {
-    const int sl = task % slices;
-    const int t0 = (line0 + task / slices) * 4;
-    const int pid = min(max(bt[t0 / P], 0), num_pages - 1);
-    u32x4* dst = reinterpret_cast<u32x4*>(
-        kcl + ((static_cast<size_t>(pid) * Hkv + kvh) * slices + sl) * P * X + (t0 % P) * X);
-    u32x4 line[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) line[e] = dst[e];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = t0 + e;
-      if (t >= L && t < end) {
-        const T* krow = k_phys + ((lb * W + (t - L)) * Hkv + kvh) * D;
-        line[e] = *reinterpret_cast<const u32x4*>(krow + sl * X);
-        if constexpr (kRope) {
-          // rotate-half: slice sl pairs with sl +- slices/2
-          const int hs = slices / 2;
-          const bool lower = sl < hs;
-          const int j0 = (lower ? sl : sl - hs) * X;  // first frequency index
-          union {
-            u32x4 v;
-            T e[X];
-          } own, mate, out;
-          own.v = line[e];
-          mate.v = *reinterpret_cast<const u32x4*>(krow + (lower ? sl + hs : sl - hs) * X);
-          const double tr = rot_pos ? static_cast<double>(rot_pos[b * W + (t - L)])
-                                    : static_cast<double>(t);
-#pragma unroll
-          for (int x = 0; x < X; ++x) {
-            float c, sn;
-            rope_cos_sin(tr, rope.omega[j0 + x], c, sn);
-            const float a = Elt<T>::load(&own.e[x]), m = Elt<T>::load(&mate.e[x]);
-            // lower half: a cos - mate sin; upper half: a cos + mate sin
-            Elt<T>::store(&out.e[x], lower ? a * c - m * sn : a * c + m * sn);
-          }
-          line[e] = out.v;
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst[e] = line[e];
-  }
-
-  // values: lines of kDimsPerLine dimensions x 16 positions of one page
-  const int pg0 = L / P, npg = (end - 1) / P - pg0 + 1;
-  const int groups = D / kDimsPerLine;
-  const int vtasks = npg * groups;
-  for (int task = threadIdx.x; task < vtasks; task += kCommitThreads) {
-    const int dg = task % groups;
-    const int pg = pg0 + task / groups;
-    const int pid = min(max(bt[pg], 0), num_pages - 1);
-    T* dst = vcl + ((static_cast<size_t>(pid) * Hkv + kvh) * D + dg * kDimsPerLine) * P;
-    union {
-      u32x4 v[4];
-      T e[kLineElems];
-    } line;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) line.v[i] = reinterpret_cast<const u32x4*>(dst)[i];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int t = pg * P + e;
-      if (t >= L && t < end) {
-        const T* src = v_phys + ((lb * W + (t - L)) * Hkv + kvh) * D + dg * kDimsPerLine;
-#pragma unroll
-        for (int dd = 0; dd < kDimsPerLine; ++dd) line.e[dd * 16 + e] = src[dd];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(dst)[i] = line.v[i];
-  }
+  commit_rows_block<T, kRope>(B, W, Hkv, D, P, num_pages, max_pages, run_len, prefix_len, k_phys,
+                              v_phys, block_table, k_cache, v_cache, cache_layer_stride,
+                              rope.omega, rot_pos, blockIdx.x / Hkv, blockIdx.x % Hkv, blockIdx.y,
+                              threadIdx.x, kCommitThreads);
 }
 
 __global__ void __launch_bounds__(kWave)
@@ -171,35 +64,6 @@ k_commit_state(int W, int P, int num_pages, int max_pages, const int32_t* __rest
 }  // namespace wedlm
 
 using namespace wedlm;
-
-// Rows part of the fused commit (used by the f32 attention path, which has no
-// rows of its own to append): rotated keys and values of rows 0..c-1, the keys
-// rotated at rot_pos[b][j] (the attention's positions).
-int wedlm::commit_rows_rope(int dtype, int n_layers, int B, int W, int Hkv, int D, int page_size,
-                            int num_pages, int max_pages, double theta, const int32_t* run_len,
-                            const int32_t* prefix_len, const int32_t* rot_pos, const void* k_rows,
-                            const void* v_rows, const int32_t* block_table, void* k_cache,
-                            void* v_cache, hipStream_t s) {
-  const int X = 16 / static_cast<int>(elt_size(dtype));
-  if (D % (2 * X) != 0 || D > kCommitMaxD || page_size != 16) return WEDLM_ERR_UNSUPPORTED;
-  const long long stride = 1LL * num_pages * Hkv * D * page_size;
-  CommitRope tab{};
-  for (int j = 0; j < D / 2; ++j) tab.omega[j] = std::pow(theta, -2.0 * j / D);
-  const dim3 grid(B * Hkv, n_layers);
-  if (dtype == WEDLM_BF16)
-    hipLaunchKernelGGL((k_commit_rows<uint16_t, true>), grid, dim3(kCommitThreads), 0, s, B, W,
-                       Hkv, D, page_size, num_pages, max_pages, run_len, prefix_len,
-                       static_cast<const uint16_t*>(k_rows), static_cast<const uint16_t*>(v_rows),
-                       block_table, static_cast<uint16_t*>(k_cache),
-                       static_cast<uint16_t*>(v_cache), stride, tab, rot_pos);
-  else
-    hipLaunchKernelGGL((k_commit_rows<float, true>), grid, dim3(kCommitThreads), 0, s, B, W, Hkv,
-                       D, page_size, num_pages, max_pages, run_len, prefix_len,
-                       static_cast<const float*>(k_rows), static_cast<const float*>(v_rows),
-                       block_table, static_cast<float*>(k_cache), static_cast<float*>(v_cache),
-                       stride, tab, rot_pos);
-  return launch_status();
-}
 
 static int launch_commit(bool rope, int dtype, int n_layers, int B, int W, int Hkv, int D,
                          int page_size, int num_pages, int max_pages, double theta,

@@ -144,15 +144,6 @@ constexpr int kMaxShapeDim = 65535;
 // ceil(a / b) for b > 0, without forming a + b - 1 (no overflow near INT_MAX)
 inline int ceil_div(int a, int b) { return a / b + (a % b > 0 ? 1 : 0); }
 
-// Internal (not part of the C ABI): the rows half of wedlm_commit_prefix_rope,
-// enqueued on `s`, with the keys rotated at rot_pos[b][j] (physical rows 0..c-1
-// of the window) when rot_pos is given, else at L + j. Defined in commit.hip.
-int commit_rows_rope(int dtype, int n_layers, int B, int W, int Hkv, int D, int page_size,
-                     int num_pages, int max_pages, double theta, const int32_t* run_len,
-                     const int32_t* prefix_len, const int32_t* rot_pos, const void* k_rows,
-                     const void* v_rows, const int32_t* block_table, void* k_cache,
-                     void* v_cache, hipStream_t s);
-
 // Internal: the selection half of wedlm_entropy_select over n_chunks partials
 // per row ([B * W][n_chunks], in vocabulary order), enqueued on `s`. Defined
 // in entropy.hip.

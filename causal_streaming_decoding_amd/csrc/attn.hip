@@ -646,11 +646,15 @@ k_window_attn_bf16(AttnArgs a) {
   const int group = (layer * a.B + b) * a.Hkv + kvh;
   const size_t slot = static_cast<size_t>(layer * a.Hkv + kvh) * a.cols + j;
 
-  const int pl_b = a.prefix_len[b];  // read once: the append's pages need it too
-  const int L = min(max(pl_b, 0), a.max_prefix_len);
-  const int npages = (L + kPage - 1) / kPage;
-  const int pg_begin = a.split ? min(npages, split * K) : 0;
-  const int pg_end = a.split ? min(npages, pg_begin + K) : npages;
+  // The prefix length, the window order and positions, the rotation
+  // frequencies and the block-table entries of the first pages are all
+  // requested before any of them is used, and complete together at one wait
+  // in the prologue below: one round trip, where taking each value as it was
+  // loaded made four in a row. The entries are those of the split's first
+  // pages, which do not depend on the prefix length (page_entry clamps the
+  // index; a split that starts past the prefix requests no page).
+  int pl_b = a.prefix_len[b];  // read once: the append's pages need it too
+  const int pg_first = a.split ? split * K : 0;
   const bool with_window = split == n_split - 1;
   if (a.split && split == 0 && part == 0 && tid == 0)
     a.ws_plan[group] = make_int2(static_cast<int>(slot), n_split);
@@ -667,10 +671,10 @@ k_window_attn_bf16(AttnArgs a) {
   int qslot = row_ok ? prow : 0;  // window row holding this query row
   int qpos = 0;
   const int32_t* bt = a.block_table + static_cast<size_t>(b) * a.max_pages;
-  const int npg = pg_end - pg_begin;
   const uint16_t* kc_layer = a.kc + static_cast<size_t>(layer) * a.cache_layer_stride;
   const uint16_t* vc_layer = a.vc + static_cast<size_t>(layer) * a.cache_layer_stride;
-  const int pro = min(kAhead, npg);
+  // set in the prologue, once the prefix length has arrived
+  int L, npages, pg_begin, pg_end, npg, pro;
   // The first min(kAhead, npg) pages are requested before the loop; their
   // block-table entries are fetched (scalar loads) while the window order
   // is on its way. The entries of the pages the first chunk of committed
@@ -682,21 +686,34 @@ k_window_attn_bf16(AttnArgs a) {
   u32x4 qv[4];
   {
     int pm = 0, ps = 0;
+    double om = 0.0;
     if constexpr (kRope) {
       if (tid < a.W) {
         pm = a.perm[b * a.W + tid];
         ps = a.pos[b * a.W + tid];
       }
+      if (tid < kHeadDim / 2) om = a.omega[tid];
     }
 #pragma unroll
     for (int q = 0; q < kAhead2; q += 2)
-      load_page_ids2(page_entry(bt, pg_begin + q, a.max_pages),
-                     page_entry(bt, pg_begin + q + 1, a.max_pages), id_pro[q], id_pro[q + 1]);
+      load_page_ids2(page_entry(bt, pg_first + q, a.max_pages),
+                     page_entry(bt, pg_first + q + 1, a.max_pages), id_pro[q], id_pro[q + 1]);
+    // Every load above is in flight: the values are taken here, together
+    // (the compiler would otherwise wait for each right after its load, to
+    // start the arithmetic on it).
+    asm volatile("" : "+v"(pl_b), "+v"(pm), "+v"(ps), "+v"(om));
+    pl_b = __builtin_amdgcn_readfirstlane(pl_b);
+    L = min(max(pl_b, 0), a.max_prefix_len);
+    npages = (L + kPage - 1) / kPage;
+    pg_begin = a.split ? min(npages, pg_first) : 0;
+    pg_end = a.split ? min(npages, pg_begin + K) : npages;
+    npg = pg_end - pg_begin;
+    pro = min(kAhead, npg);
     if constexpr (kRope) {
       // frequencies, window order and positions to LDS, all before any
       // asynchronous load is issued (the waits the compiler adds for these
       // are then free)
-      if (tid < kHeadDim / 2) s_omega[tid] = a.omega[tid];
+      if (tid < kHeadDim / 2) s_omega[tid] = om;
       if (tid < a.W) {
         s_perm[tid] = min(max(pm, 0), a.W - 1);
         s_pos[tid] = ps;

@@ -572,6 +572,7 @@ template <int NW, bool kRope, bool kNt>
 __global__ void __launch_bounds__(kWave * NW)
 __attribute__((amdgpu_waves_per_eu(Ring<NW>::kWavesPerSimd, Ring<NW>::kWavesPerSimd)))
 k_window_attn_bf16(AttnArgs a) {
+  touch_kernargs<sizeof(AttnArgs)>();
   constexpr int kDma = DmaShape<NW>::kPerWave;  // DMA instructions per issuing thread per stage
   constexpr int kStages = Ring<NW>::kStages;
   constexpr int kAhead = Ring<NW>::kAhead;
@@ -1012,6 +1013,7 @@ static_assert(kWideAhead == 2, "tile_wait_barrier covers one tile behind the com
 
 template <bool kRope, bool kNt>
 __global__ void __launch_bounds__(kTileThreads) k_window_attn_wide(AttnArgs a) {
+  touch_kernargs<sizeof(AttnArgs)>();
   __shared__ Tile ring[kWideStages];
   __shared__ Tile own;  // the window's own keys (W <= 64): K rotated, V plain then fp16
   __shared__ double s_omega[kRope ? kHeadDim / 2 : 1];

@@ -44,6 +44,24 @@ template <> struct Elt<uint16_t> {
   static __device__ __forceinline__ void store(uint16_t* p, float x) { *p = f32_to_bf16(x); }
 };
 
+// ---- kernel arguments ------------------------------------------------------
+
+// The compiler reads each kernel argument where it is first used, and each
+// read of a new 64-byte line of the argument segment waits for that line (a
+// launch-latency cost on short kernels: several such waits in a row before the
+// first global load). This touches every line of the first kBytes bytes (all
+// inside the kernel's explicit arguments) with scalar loads issued together
+// before one wait, so the later reads hit the scalar cache.
+template <int kBytes>
+__device__ __forceinline__ void touch_kernargs() {
+  const __attribute__((address_space(4))) uint32_t* ka =
+      (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t x = 0;
+#pragma unroll
+  for (int o = 0; o + 4 <= kBytes; o += 64) x ^= ka[o / 4];
+  asm volatile("" ::"s"(x));
+}
+
 // ---- RoPE angle ---------------------------------------------------------------
 
 // cos and sin of t * omega radians (RoFormer rotation, mlsanity.com page on

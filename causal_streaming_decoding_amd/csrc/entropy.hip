@@ -65,6 +65,9 @@ k_step_tail(int tail_blocks, CombineArgs comb, const EntPartial* __restrict__ pa
             uint8_t* __restrict__ selected, int32_t* __restrict__ perm,
             int32_t* __restrict__ inv_perm, int32_t* __restrict__ pos,
             int32_t* __restrict__ n_obs) {
+  // the explicit arguments above end at byte 264 of the argument segment
+  // (the last, n_obs, at 256)
+  touch_kernargs<260>();
   if (static_cast<int>(blockIdx.x) >= tail_blocks) {
     const long long idx =
         static_cast<long long>(blockIdx.x - tail_blocks) * kWave + threadIdx.x;
